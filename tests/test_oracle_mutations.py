@@ -1,0 +1,118 @@
+"""Mutation check of the oracle's pins (CPU only).
+
+Each case plants one plausible mistake in a copy of the oracle's source (a
+dropped term, a wrong sign or index, a swapped operand, an off-by-one) and
+requires that at least one pin in test_oracle_pins fails on the mutant. The
+real oracle is untouched: the mutant is a separate module object and the pins
+see it only through a monkeypatched attribute table for the duration of one
+case.
+"""
+import os
+import sys
+import types
+
+import pytest
+
+import oracle.moe as O
+import oracle.philox as PH
+import test_oracle_pins as pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTATIONS = [
+    ("moe", "softplus -> relu",
+     "np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))", "np.maximum(z, 0.0)"),
+    ("moe", "noise not scaled by std",
+     "score = clean + widen(eps) * std", "score = clean + widen(eps)"),
+    ("moe", "ties to the higher index",
+     'return np.argsort(-key, axis=1, kind="stable")',
+     'return np.argsort(key, axis=1, kind="stable")[:, ::-1]'),
+    ("moe", "gate softmax over all experts",
+     "gates = z / z.sum(axis=1, keepdims=True)",
+     "gates = z / np.exp(score - kept.max(axis=1, keepdims=True)).sum(axis=1, keepdims=True)"),
+    ("moe", "Switch gate renormalised to one",
+     "gates = p[rows, ids]", "gates = p[rows, ids] / p[rows, ids]"),
+    ("moe", "rank-major slot order",
+     "    for t in range(T):\n        for j in range(k):\n            e = int(ids[t, j])",
+     "    for j in range(k):\n        for t in range(T):\n            e = int(ids[t, j])"),
+    ("moe", "capacity test off by one", "accepted = pos < C", "accepted = pos <= C"),
+    ("moe", "capacity ignores k", "float(k) * float(T)", "float(T)"),
+    ("moe", "CV with ddof 1",
+     "((v - m) ** 2).mean() / (m * m)", "((v - m) ** 2).sum() / (v.size - 1) / (m * m)"),
+    ("moe", "load threshold swapped",
+     "thr = np.where(inside, r.row_stats[:, 1:2], thr)",
+     "thr = np.where(inside, r.row_stats[:, :1], thr)"),
+    ("moe", "residual dropped",
+     "y = x.copy() if residual else np.zeros(D)", "y = np.zeros(D)"),
+    ("moe", "expert ReLU dropped",
+     "np.maximum(x64 @ W1e64, 0.0) @ W2e64", "(x64 @ W1e64) @ W2e64"),
+    ("moe", "dropped assignments combined", "if d.accepted[t, j]:", "if True:"),
+    ("moe", "importance counts instead of gates",
+     "np.add.at(imp, r.ids.ravel(), r.gates.ravel())", "np.add.at(imp, r.ids.ravel(), 1.0)"),
+    ("moe", "Switch f after capacity",
+     "f = d.counts.astype(np.float64) / T",
+     "f = np.minimum(d.counts, d.C).astype(np.float64) / T"),
+    ("moe", "load uses H instead of clean",
+     "diff = r.clean - thr", "diff = r.score - thr"),
+    ("philox", "wrong multiplier",
+     "0xD2E7470EE14C6C93", "0xD2E7470EE14C6C95"),
+    ("philox", "key not bumped", "k0 = k0 + _W0", "k0 = k0"),
+    ("philox", "Box-Muller without sqrt",
+     "rho = np.sqrt(-2.0 * np.log(u1))", "rho = -2.0 * np.log(u1)"),
+    ("philox", "sine branch reused as cosine",
+     "return rho * np.cos(theta), rho * np.sin(theta)",
+     "return rho * np.cos(theta), rho * np.cos(theta)"),
+]
+
+
+def _mutant(modname, old, new):
+    path = os.path.join(ROOT, "oracle", modname + ".py")
+    src = open(path).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    src = src.replace(old, new)
+    mod = types.ModuleType("oracle." + modname + "_mutant")
+    mod.__package__ = "oracle"
+    mod.__file__ = path
+    sys.modules[mod.__name__] = mod  # dataclasses look their module up here
+    try:
+        exec(compile(src, path, "exec"), mod.__dict__)
+    finally:
+        sys.modules.pop(mod.__name__, None)
+    return mod
+
+
+PIN_TESTS = [getattr(pins, n) for n in dir(pins) if n.startswith("test_")]
+
+
+def _run_pins():
+    failed = []
+    for fn in PIN_TESTS:
+        marks = getattr(fn, "pytestmark", [])
+        params = [m for m in marks if m.name == "parametrize"]
+        cases = [()]
+        if params:
+            names, values = params[0].args
+            cases = [v if isinstance(v, tuple) else (v,) for v in values]
+        for c in cases:
+            try:
+                fn(*c)
+            except Exception:
+                failed.append(fn.__name__)
+                return failed
+    return failed
+
+
+@pytest.mark.parametrize("modname,label,old,new", MUTATIONS, ids=[m[1] for m in MUTATIONS])
+def test_pins_catch_mutation(monkeypatch, modname, label, old, new):
+    mut = _mutant(modname, old, new)
+    if modname == "philox":
+        for name in ("philox4x64_10", "gaussian_noise", "_box_muller", "_mulhilo"):
+            monkeypatch.setattr(PH, name, getattr(mut, name))
+        monkeypatch.setattr(O, "gaussian_noise", mut.gaussian_noise)
+    else:
+        for name, val in vars(mut).items():
+            if callable(val) and getattr(val, "__module__", None) == mut.__name__ or \
+                    isinstance(val, types.FunctionType):
+                if hasattr(O, name):
+                    monkeypatch.setattr(O, name, val)
+    assert _run_pins(), f"no pin failed for mutation: {label}"

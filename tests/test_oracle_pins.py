@@ -1,0 +1,463 @@
+"""Pins for the CPU oracle: values the pages print, closed forms, invariants,
+brute force on tiny inputs and library routines the oracle itself does not use.
+
+Each test names the passage it pins. All run on the CPU (no GPU marker).
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+import torch
+
+from conftest import golden
+from oracle import moe as O
+from oracle import philox as P
+from sparsely_gated_mixture_amd import inputs as I
+
+LN_E_MINUS_1 = math.log(math.e - 1.0)  # softplus of this is exactly 1
+
+
+def _one_token_route(clean, eps, k, noise_scale_one=True):
+    """Route one token through the oracle with D = 1, X = 1, Wg = clean logits."""
+    E = len(clean)
+    X = np.ones((1, 1), dtype=np.float32)
+    Wg = np.asarray(clean, dtype=np.float32)[None, :]
+    Wn = np.full((1, E), LN_E_MINUS_1, dtype=np.float64)
+    return O.route(X, Wg, Wn, None, k, "noisy", True, eps=np.asarray(eps, np.float64)[None, :])
+
+
+def _dense(r, E):
+    G = np.zeros((r.ids.shape[0], E))
+    np.put_along_axis(G, r.ids.astype(np.int64), r.gates, axis=1)
+    return G
+
+
+# ------------------------------------------------------------ lesson worked example (printed values)
+
+@pytest.mark.parametrize("case,k", [("k2", 2), ("k1", 1), ("k3", 3)])
+def test_worked_example_noisy_gate(case, k):
+    """Lesson ch. 2 and 3: H = [2.3, 0.8, 0.6, -2.0] from clean [2, 1, .5, -.5] plus noise, scale 1."""
+    g = golden("lesson_worked_example.json")
+    clean = np.array(g["clean_logits"])
+    eps = np.array(g["noisy_scores"]) - clean
+    r = _one_token_route(clean, eps, k)
+    np.testing.assert_allclose(r.std, 1.0, atol=1e-15)
+    G = _dense(r, 4)[0]
+    want = g["gates"][case]
+    np.testing.assert_array_equal(np.round(G, want["decimals"]), want["G"])
+    assert np.count_nonzero(G) == k
+
+
+def test_worked_example_zero_noise():
+    """Lesson ch. 2, 'What noise buys you': zero noise leaves the clean logits, G = [.731, .269, 0, 0]."""
+    g = golden("lesson_worked_example.json")
+    clean = np.array(g["clean_logits"])
+    r = _one_token_route(clean, np.zeros(4), 2)
+    want = g["gates"]["k2_zero_noise"]
+    np.testing.assert_array_equal(np.round(_dense(r, 4)[0], want["decimals"]), want["G"])
+
+
+def test_worked_example_second_draw():
+    """Lesson ch. 2, 'a different noise draw': winners 1.5 (expert 3) and 1.4 (expert 1) -> .525/.475."""
+    g = golden("lesson_worked_example.json")["second_draw"]
+    clean = np.array(golden("lesson_worked_example.json")["clean_logits"])
+    eps = np.array(g["noisy_scores"]) - clean
+    r = _one_token_route(clean, eps, g["k"])
+    assert list(r.ids[0]) == [2, 0]
+    np.testing.assert_array_equal(np.round(_dense(r, 4)[0], g["decimals"]), g["G"])
+
+
+def test_worked_example_load_estimator():
+    """Summary 3.4 load estimator on the lesson ch. 5 example (page tables stripped: derived values).
+
+    kth_excluding(H, 2, i) = [0.6, 0.6, 0.8, 0.8]; the standardised margins are
+    clean - threshold = [1.4, 0.4, -0.3, -1.3]; Phi from math.erf.
+    """
+    g = golden("lesson_worked_example.json")
+    clean = np.array(g["clean_logits"])
+    H = np.array(g["noisy_scores"])
+    assert [O.kth_excluding(H, 2, i) for i in range(4)] == [0.6, 0.6, 0.8, 0.8]
+    r = _one_token_route(clean, H - clean, 2)
+    Pxi = O.load_probs(r, 2)[0]
+    phi = [0.5 * (1.0 + math.erf(z / math.sqrt(2.0))) for z in (1.4, 0.4, -0.3, -1.3)]
+    np.testing.assert_allclose(Pxi, phi, rtol=0, atol=2e-7)  # eps rounded to fp32
+
+
+@pytest.mark.parametrize("name", ["balanced", "unbalanced"])
+def test_cv_examples(name):
+    """Lesson ch. 5: CV^2 of [10,10,10] is 0 and of [25,10,1] is 0.68 (ddof 0)."""
+    c = golden("lesson_worked_example.json")["cv_examples"][name]
+    assert round(O.cv2(c["v"]), c["decimals"]) == c["value"]
+
+
+def test_cv_convention_is_population_variance():
+    v = np.array([25.0, 10.0, 1.0])
+    assert abs(O.cv2(v) - 98.0 / 144.0) < 1e-15
+    assert abs(O.cv2(v) - np.var(v, ddof=1) / v.mean() ** 2) > 0.3
+
+
+# ------------------------------------------------------------ load estimator: definition checks
+
+def test_kth_excluding_identity_matches_bruteforce():
+    """The oracle's read-off thresholds equal the brute-force kth_excluding on random rows."""
+    rng = np.random.default_rng(3)
+    for k in (1, 2, 3, 5):
+        E = 7
+        X = rng.standard_normal((40, 6)).astype(np.float32)
+        Wg = rng.standard_normal((6, E)).astype(np.float32)
+        Wn = rng.standard_normal((6, E)).astype(np.float32)
+        r = O.route(X, Wg, Wn, None, k, "noisy", True, seed=11)
+        inside = np.zeros((40, E), bool)
+        np.put_along_axis(inside, r.ids.astype(np.int64), True, axis=1)
+        for t in range(40):
+            for i in range(E):
+                thr = r.row_stats[t, 1] if inside[t, i] else r.row_stats[t, 0]
+                assert thr == O.kth_excluding(r.score[t], k, i)
+
+
+def test_load_probability_monte_carlo():
+    """Summary 3.4: P(x,i) is the chance that expert i stays in the top k when only its own
+    noise sample is redrawn. Redraw it 200k times and count (3-sigma band)."""
+    rng = np.random.default_rng(5)
+    E, k = 6, 2
+    clean = rng.standard_normal(E)
+    std = np.abs(rng.standard_normal(E)) + 0.3
+    eps = rng.standard_normal(E)
+    X = np.ones((1, 1), dtype=np.float32)
+    r = O.route(X, clean[None, :].astype(np.float32), None, None, k, "noisy", False)
+    # build the routing record by hand around fixed clean/std/eps (fp64)
+    H = clean + std * eps
+    r.clean, r.std, r.score = clean[None, :], std[None, :], H[None, :]
+    order = np.argsort(-H, kind="stable")
+    r.ids = order[None, :k].astype(np.int32)
+    r.row_stats = np.array([[H[order[k - 1]], H[order[k]]]])
+    Pxi = O.load_probs(r, k)[0]
+    n = 200_000
+    for i in range(E):
+        draws = rng.standard_normal(n)
+        Hi = np.repeat(H[None, :], n, axis=0)
+        Hi[:, i] = clean[i] + std[i] * draws
+        rank = (Hi > Hi[:, i:i + 1]).sum(axis=1)
+        freq = (rank < k).mean()
+        sigma = math.sqrt(max(Pxi[i] * (1 - Pxi[i]), 1e-12) / n)
+        assert abs(freq - Pxi[i]) < 3 * sigma + 1e-9, (i, freq, Pxi[i])
+
+
+def test_load_step_when_std_is_zero():
+    r = O.route(np.ones((1, 1), np.float32), np.array([[1.0, 0.0, -1.0]], np.float32), None,
+                None, 1, "noisy", False)
+    r.std = np.zeros((1, 3))
+    P_ = O.load_probs(r, 1)[0]
+    # thresholds: top-1 is expert 0 (thr = v2 = 0), others use v1 = 1
+    assert list(P_) == [1.0, 0.0, 0.0]
+
+
+def test_load_k_equals_E_is_one():
+    X = np.ones((2, 1), np.float32)
+    r = O.route(X, np.array([[1.0, 0.5, -1.0]], np.float32),
+                np.array([[0.2, 0.1, 0.3]], np.float32), None, 3, "noisy", True, seed=2)
+    np.testing.assert_array_equal(O.load_probs(r, 3), 1.0)
+
+
+# ------------------------------------------------------------ gate invariants and special cases
+
+def _random_route(k=4, E=16, T=64, D=8, seed=0, gating="noisy", noise=True):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((T, D)).astype(np.float32)
+    Wg = (rng.standard_normal((D, E)) / np.sqrt(D)).astype(np.float32)
+    Wn = (rng.standard_normal((D, E)) / np.sqrt(D)).astype(np.float32)
+    return X, Wg, Wn, O.route(X, Wg, Wn, None, k, gating, noise, seed=seed)
+
+
+def test_gate_has_k_nonzeros_summing_to_one():
+    """Summary 3.4 Step 3: exactly k nonzero gates, positive, summing to one."""
+    _, _, _, r = _random_route()
+    G = _dense(r, 16)
+    assert (np.count_nonzero(G, axis=1) == 4).all()
+    np.testing.assert_allclose(G.sum(axis=1), 1.0, atol=1e-14)
+    assert (r.gates > 0).all()
+
+
+def test_keep_top_k_keeps_the_largest():
+    """Summary 3.4 Step 2: every kept score is >= every dropped score."""
+    _, _, _, r = _random_route(k=3)
+    for t in range(r.ids.shape[0]):
+        kept = set(r.ids[t])
+        lo = min(r.score[t, list(kept)])
+        hi = max(r.score[t, [e for e in range(16) if e not in kept]])
+        assert lo >= hi
+
+
+def test_mask_renormalise_form_equals_softmax_of_kept():
+    """Lesson ch. 2 (appendix F form): (G_sigma * M) / sum(G_sigma * M) with the top-k mask
+    equals Softmax(KeepTopK(H, k))."""
+    _, _, _, r = _random_route(k=3)
+    Gs = scipy.special.softmax(r.score, axis=1)
+    M = np.zeros_like(Gs)
+    np.put_along_axis(M, r.ids.astype(np.int64), 1.0, axis=1)
+    alt = Gs * M / (Gs * M).sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(_dense(r, 16), alt, rtol=1e-12, atol=1e-15)
+
+
+def test_k_equals_E_is_dense_softmax():
+    """Summary results (MoE-4, every expert active): k = E gives G = softmax(H)."""
+    _, _, _, r = _random_route(k=16, E=16)
+    np.testing.assert_allclose(_dense(r, 16), scipy.special.softmax(r.score, axis=1), rtol=1e-12)
+
+
+def test_zero_router_weights_give_uniform_selection():
+    """Summary 3.4, initialisation: Wg = Wnoise = 0 gives H = ln2 * N(0,1), so every expert is
+    selected with probability k/E (chi-square over 20k tokens)."""
+    T, D, E, k = 20000, 4, 8, 2
+    X = np.random.default_rng(0).standard_normal((T, D)).astype(np.float32)
+    Z = np.zeros((D, E), np.float32)
+    r = O.route(X, Z, Z, None, k, "noisy", True, seed=123)
+    np.testing.assert_allclose(r.std, math.log(2.0), rtol=1e-15)
+    counts = np.bincount(r.ids.ravel(), minlength=E)
+    chi = scipy.stats.chisquare(counts)
+    assert chi.pvalue > 1e-4, counts
+
+
+def test_noise_scale_sets_selection_odds():
+    """Summary 3.4 Step 1: H_i = clean_i + N(0,1) * Softplus(raw_i). With two experts, clean
+    [1, 0] and Softplus = 3 for both, expert 0 wins with probability Phi(1 / (3 sqrt 2))."""
+    T = 40000
+    X = np.ones((T, 1), np.float32)
+    z = math.log(math.exp(3.0) - 1.0)
+    r = O.route(X, np.array([[1.0, 0.0]], np.float32), np.array([[z, z]]), None, 1, "noisy",
+                True, seed=77)
+    freq = (r.ids[:, 0] == 0).mean()
+    want = 0.5 * (1.0 + math.erf(1.0 / (3.0 * math.sqrt(2.0)) / math.sqrt(2.0)))
+    assert abs(freq - want) < 4.0 * math.sqrt(want * (1 - want) / T)
+
+
+def test_ties_go_to_the_lower_index():
+    """Switch explainer step 2 (first expert on ties), also for top-k: duplicated router
+    columns with no noise tie exactly and the lower index wins."""
+    rng = np.random.default_rng(1)
+    X = rng.standard_normal((32, 8)).astype(np.float32)
+    Wg = rng.standard_normal((8, 6)).astype(np.float32)
+    Wg[:, 4] = Wg[:, 1]
+    for gating, k in (("switch", 1), ("noisy", 2)):
+        r = O.route(X, Wg, None, None, k, gating, False)
+        for t in range(32):
+            s = set(r.ids[t])
+            if 4 in s:
+                assert 1 in s  # 4 can only be kept if its twin 1 is kept first
+            if r.ids[t, 0] in (1, 4):
+                assert r.ids[t, 0] == 1
+
+
+def test_switch_gate_is_selected_probability():
+    """Switch explainer steps 1-2: gate = softmax prob of the argmax expert, not renormalised;
+    the argmax is maximal over the full softmax."""
+    w = I.WORKLOADS["switch_toy"]
+    inp = I.make_inputs(w)
+    r = O.route(inp["X"], inp["Wg"], None, None, 1, "switch", False)
+    p = scipy.special.softmax(O.widen(inp["X"]) @ O.widen(inp["Wg"]), axis=1)
+    for t in range(w.T):
+        e = r.ids[t, 0]
+        assert p[t, e] == p[t].max()
+        assert abs(r.gates[t, 0] - p[t, e]) < 1e-15
+        assert r.gates[t, 0] < 1.0
+
+
+def test_noise_scale_is_softplus():
+    """Summary 3.4 Step 1: Softplus(z) = ln(1+e^z) (math.log1p(math.exp) on moderate z)."""
+    z = np.linspace(-30, 30, 61)
+    np.testing.assert_allclose(O.softplus(z), [math.log1p(math.exp(v)) for v in z], rtol=1e-14)
+    assert (O.softplus(np.array([-10.0, -50.0])) > 0).all()
+
+
+# ------------------------------------------------------------ capacity and slots
+
+def test_capacity_values():
+    """Switch explainer step 3: C = max(m, min(T, int(T*cf/E))) with m = 1, k-generalised."""
+    assert O.capacity(8, 1, 1.0, 3) == 2
+    assert O.capacity(16384, 1, 1.25, 128) == 160
+    assert O.capacity(65536, 2, 1.0, 256) == 512
+    assert O.capacity(4096, 4, 0.0, 64) == 4096  # no limit
+    assert O.capacity(8, 1, 0.1, 3) == 1  # minimum capacity
+    assert O.capacity(8, 1, 100.0, 3) == 8  # clamped to T
+
+
+def _bruteforce_slots(ids):
+    T, k = ids.shape
+    pos = np.zeros((T, k), np.int64)
+    for t in range(T):
+        for j in range(k):
+            pos[t, j] = sum(1 for t2 in range(T) for j2 in range(k)
+                            if (t2, j2) < (t, j) and ids[t2, j2] == ids[t, j])
+    return pos
+
+
+def test_slots_bruteforce_topk():
+    rng = np.random.default_rng(7)
+    E, k, T = 5, 2, 30
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    d = O.dispatch(ids, E, 4)
+    np.testing.assert_array_equal(d.pos, _bruteforce_slots(ids))
+    np.testing.assert_array_equal(d.accepted, d.pos < 4)
+    np.testing.assert_array_equal(d.counts, np.bincount(ids.ravel(), minlength=E))
+
+
+def test_slots_switch_cumsum_form():
+    """Switch explainer steps 3-4 written the page's way: exclusive cumsum of the one-hot
+    choice, positions = sum(exclusive * chosen), accepted = positions < C."""
+    w = I.WORKLOADS["switch_toy"]
+    inp = I.make_inputs(w)
+    r = O.route(inp["X"], inp["Wg"], None, None, 1, "switch", False)
+    C = O.capacity(w.T, 1, w.capacity_factor, w.E)
+    d = O.dispatch(r.ids, w.E, C)
+    chosen = torch.nn.functional.one_hot(torch.from_numpy(r.ids[:, 0].astype(np.int64)), w.E)
+    excl = chosen.cumsum(dim=0) - chosen
+    positions = (excl * chosen).sum(dim=-1).numpy()
+    np.testing.assert_array_equal(d.pos[:, 0], positions)
+    np.testing.assert_array_equal(d.accepted[:, 0], positions < C)
+    assert (~d.accepted).sum() >= w.T * w.k - w.E * C  # at least 2 of 8 tokens overflow
+    assert (~d.accepted).sum() >= 2
+
+
+def test_slots_one_token_per_slot():
+    """Switch explainer step 5: each accepted assignment has one slot, each slot <= 1 token."""
+    _, _, _, r = _random_route(k=2, E=8, T=200)
+    d = O.dispatch(r.ids, 8, 30)
+    seen = set()
+    for t, j in zip(*np.nonzero(d.accepted)):
+        key = (int(r.ids[t, j]), int(d.pos[t, j]))
+        assert key not in seen
+        seen.add(key)
+    assert (d.row_token >= 0).all()
+    for e in range(8):
+        rows = d.row_token[d.offsets[e]:d.offsets[e + 1]]
+        assert (np.diff(rows) > 0).all()  # slot order = token order
+    assert d.offsets[-1] == d.accepted.sum()
+
+
+# ------------------------------------------------------------ experts and combine
+
+def _tiny_layer(T=24, D=6, E=5, k=2, H=7, cf=0.0, seed=0, noise=True):
+    w = I.Workload("tiny", T=T, D=D, E=E, k=k, H=H, act="f32", gating="noisy", noise=noise,
+                   capacity_factor=cf, seed=seed)
+    inp = I.make_inputs(w)
+    return w, inp, O.forward(inp, w)
+
+
+def test_layer_equals_dense_sum():
+    """Summary 3.4, MoE output: y = sum_i G(x)_i E_i(x) over ALL experts (plus the residual);
+    here evaluated densely with torch matmuls in fp64."""
+    w, inp, f = _tiny_layer()
+    X = torch.from_numpy(O.widen(inp["X"]))
+    W1 = torch.from_numpy(O.widen(inp["W1"]))
+    W2 = torch.from_numpy(O.widen(inp["W2"]))
+    Eall = torch.relu(X[None] @ W1) @ W2  # [E,T,D]
+    G = torch.from_numpy(_dense(f["routing"], w.E))  # [T,E]
+    dense = X + (G.T[:, :, None] * Eall).sum(0)
+    np.testing.assert_allclose(f["Y"], dense.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_dropped_tokens_keep_the_residual():
+    """Switch explainer step 7: an overflowing token's branch is zero, Y = X exactly; a partly
+    dropped token keeps its accepted contributions with the original gates."""
+    w, inp, f = _tiny_layer(T=40, E=3, k=2, cf=0.5)
+    d, r = f["dispatch"], f["routing"]
+    X64 = O.widen(inp["X"])
+    assert (~d.accepted).any()
+    for t in range(w.T):
+        if not d.accepted[t].any():
+            np.testing.assert_array_equal(f["Y"][t], X64[t])
+    G = _dense(r, w.E) * 0
+    np.put_along_axis(G, r.ids.astype(np.int64), r.gates * d.accepted, axis=1)
+    W1 = torch.from_numpy(O.widen(inp["W1"]))
+    W2 = torch.from_numpy(O.widen(inp["W2"]))
+    Eall = (torch.relu(torch.from_numpy(X64)[None] @ W1) @ W2).numpy()
+    want = X64 + np.einsum("te,etd->td", G, Eall)
+    np.testing.assert_allclose(f["Y"], want, rtol=1e-12, atol=1e-12)
+
+
+def test_single_expert_is_plain_ffn():
+    """E = 1, k = 1, no noise, no capacity: Y = X + ReLU(X W1) W2 (torch fp64)."""
+    w = I.Workload("one", T=10, D=8, E=1, k=1, H=12, act="f32", gating="noisy", noise=False,
+                   capacity_factor=0.0, seed=3)
+    inp = I.make_inputs(w)
+    f = O.forward(inp, w)
+    X = torch.from_numpy(O.widen(inp["X"]))
+    want = X + torch.relu(X @ torch.from_numpy(O.widen(inp["W1"][0]))) @ torch.from_numpy(O.widen(inp["W2"][0]))
+    np.testing.assert_allclose(f["Y"], want.numpy(), rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------------ aux terms
+
+def test_importance_sums_to_T():
+    w, inp, f = _tiny_layer()
+    a = f["aux"]
+    assert abs(a["importance"].sum() - w.T) < 1e-12
+    assert a["out"][6] == pytest.approx(w.T, abs=1e-12)
+
+
+def test_switch_term_closed_forms():
+    """Switch explainer step 8: uniform f and P give alpha (here E*sum f P = 1); a collapsed
+    hard load with mean selected probability q gives E*q."""
+    E, T = 4, 8
+    r = O.Routing(ids=np.zeros((T, 1), np.int32), gates=np.ones((T, 1)),
+                  clean=np.zeros((T, E)), std=None, score=np.zeros((T, E)),
+                  row_stats=np.zeros((T, 2)), gap=np.zeros(T), near_tie=np.ones(T, bool))
+    d = O.dispatch(np.array([[t % E] for t in range(T)], np.int32), E, T)
+    assert O.aux(r, d, 1)["out"][2] == pytest.approx(1.0, abs=1e-15)
+    clean = np.zeros((T, E))
+    clean[:, 0] = 2.0
+    q = math.exp(2.0) / (math.exp(2.0) + 3.0)
+    r.clean = clean
+    # capacity 1 drops 7 of the 8 tokens: f still counts the choices made before capacity
+    d = O.dispatch(np.zeros((T, 1), np.int32), E, 1)
+    assert (~d.accepted).sum() == T - 1
+    assert O.aux(r, d, 1)["out"][2] == pytest.approx(E * q, rel=1e-14)
+
+
+def test_diagnostics_counts():
+    w, inp, f = _tiny_layer(T=40, E=3, k=2, cf=0.5)
+    d = f["dispatch"]
+    out = f["aux"]["out"]
+    assert out[5] == (~d.accepted).sum() == np.maximum(d.counts - d.C, 0).sum()
+    assert out[4] == pytest.approx(d.counts.max() / d.counts.mean())
+
+
+# ------------------------------------------------------------ noise generator
+
+def test_philox_matches_numpy_philox():
+    """Philox4x64-10 against numpy.random.Philox (an independent implementation). numpy
+    advances the counter before each block: its block i from state counter c is ours at c+1+i."""
+    for key, ctr in [((0, 0), (0, 0, 0, 0)), ((5, 0), (0, 0, 0, 0)), ((123456789, 0), (41, 7, 0, 0)),
+                     ((2**64 - 1, 3), (2**64 - 2, 2**63, 5, 9))]:
+        bg = np.random.Philox(key=np.array(key, np.uint64), counter=np.array(ctr, np.uint64))
+        raw = bg.random_raw(12).reshape(3, 4)
+        for i in range(3):
+            c = list(ctr)
+            carry = 1 + i
+            for w_ in range(4):  # 256-bit increment
+                s = c[w_] + carry
+                c[w_] = s % 2**64
+                carry = s // 2**64
+            mine = P.philox4x64_10(*[np.uint64(v) for v in c], np.uint64(key[0]), np.uint64(key[1]))
+            assert [int(v) for v in mine] == [int(v) for v in raw[i]]
+
+
+def test_gaussian_noise_distribution():
+    eps = P.gaussian_noise(7, 4000, 256).astype(np.float64).ravel()
+    assert abs(eps.mean()) < 4 / math.sqrt(eps.size)
+    assert abs(eps.var() - 1.0) < 0.01
+    ks = scipy.stats.kstest(eps, scipy.stats.norm.cdf)
+    assert ks.pvalue > 1e-3
+
+
+def test_gaussian_noise_is_counter_keyed():
+    a = P.gaussian_noise(3, 50, 10)
+    b = P.gaussian_noise(3, 20, 10, t0=30)
+    np.testing.assert_array_equal(a[30:], b)
+    assert not np.array_equal(P.gaussian_noise(4, 50, 10), a)
+    # components within a token and across tokens are uncorrelated
+    big = P.gaussian_noise(9, 20000, 8).astype(np.float64)
+    c = np.corrcoef(big.T)
+    assert np.abs(c - np.eye(8)).max() < 0.04
