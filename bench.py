@@ -1,0 +1,189 @@
+"""Benchmark of the MoE layer forward pass on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload top2_bf16] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch of synthetic tokens
+already resident in HBM: route -> dispatch -> expert FFN (two grouped GEMMs)
+-> combine -> aux, each through the C ABI on one stream. W untimed warm-up
+steps, then exactly K timed steps between two device synchronisations. HIP
+events recorded on that same stream between the stages give every stage's
+average duration; the grouped GEMM (the one dense contraction) is the
+roofline kernel.
+
+Prints one JSON line. The CPU baseline is the fp64 oracle, timed on a bounded
+prefix of the same workload's tokens on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def _dev(torch, a):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
+    return torch.from_numpy(a).to("cuda")
+
+
+def cpu_baseline(w, inp, budget_tokens: int):
+    """The oracle as it stands on the first `budget_tokens` tokens (slots exact for a prefix)."""
+    from oracle import moe as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    S = min(budget_tokens, w.T)
+    t0 = time.perf_counter()
+    O.forward(inp, w, t_count=S)
+    dt = time.perf_counter() - t0
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {S} of {w.T} tokens of {w.name}: route, slots, per-token expert "
+                      f"FFN loop + combine, aux; fp64 numpy; {dt:.1f} s"}
+
+
+def copy_probe(torch, nbytes: int, reps: int):
+    """Plain device copies of a known size, for scaling HBM byte counters."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="top2_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--copy-probe", type=int, default=0, help="bytes; run copies only")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this "
+              f"single-GPU build", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    if args.copy_probe:
+        copy_probe(torch, args.copy_probe, max(args.steps, 1))
+        return
+
+    from sparsely_gated_mixture_amd import inputs as I
+    from sparsely_gated_mixture_amd import moe
+
+    w = I.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    inp = I.make_inputs(w)
+    t_gen = time.perf_counter() - t_gen
+    p = moe.problem(T=w.T, D=w.D, E=w.E, H=w.H, k=w.k, dtype=w.act, gating=w.gating,
+                    noise=w.noise, capacity_factor=w.capacity_factor,
+                    min_capacity=w.min_capacity, seed=w.seed)
+    L = moe.Layer(p, _dev(torch, inp["Wg"]), _dev(torch, inp["Wnoise"]), _dev(torch, inp["bias"]),
+                  _dev(torch, inp["W1"]), _dev(torch, inp["W2"]))
+    X = _dev(torch, inp["X"])
+    torch.cuda.synchronize()
+
+    stages = ["route", "dispatch", "gemm1", "gemm2", "combine", "aux"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        L.route(X)
+        if ev is not None:
+            ev[1].record()
+        L.dispatch(X)
+        if ev is not None:
+            ev[2].record()
+        L.gemm(1)
+        if ev is not None:
+            ev[3].record()
+        L.gemm(2)
+        if ev is not None:
+            ev[4].record()
+        L.combine(X)
+        if ev is not None:
+            ev[5].record()
+        L.aux()
+        if ev is not None:
+            ev[6].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    per = {name: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
+                                for s in range(args.steps)]))
+           for i, name in enumerate(stages)}
+
+    b = L.b
+    A = int(b.offsets[-1].item())
+    el = 2 if w.act == "bf16" else 4
+    gemm_flops = 2.0 * A * w.D * w.H  # per launch; both layers have the same count
+    gemm_ms = 0.5 * (per["gemm1"] + per["gemm2"])
+    achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.act]
+    disp_bytes = w.T * w.D * el + A * w.D * el + w.T * w.k * (4 + 4 + 1) + A * 4
+    comb_bytes = A * w.D * el + 2 * w.T * w.D * el + w.T * w.k * 13
+    out = {
+        "metric": "MoE layer fwd tokens/s at 1 GPU; grouped-GEMM % MFMA peak; dispatch GB/s",
+        "value": w.T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.act,
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "D": w.D, "E": w.E, "k": w.k, "H": w.H,
+                   "gating": w.gating, "capacity_factor": w.capacity_factor,
+                   "capacity": moe.moe_capacity(p), "accepted_rows": A,
+                   "dropped": w.T * w.k - A, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "grouped_gemm", "achieved": achieved,
+                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "flops_per_launch": gemm_flops, "avg_launch_ms": gemm_ms},
+        "stages_ms": per,
+        "dispatch_GBps": disp_bytes / (per["dispatch"] * 1e-3) / 1e9,
+        "combine_GBps": comb_bytes / (per["combine"] * 1e-3) / 1e9,
+        "dispatch_hbm_frac": disp_bytes / (per["dispatch"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "combine_hbm_frac": comb_bytes / (per["combine"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "input_gen_s": t_gen,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,245 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparsely-gated Mixture-of-Experts
+ * layer, forward pass.
+ *
+ * Pages cited (by title; sections as the pages name them):
+ *   [OLNN]   "Outrageously Large Neural Networks: The Sparsely-Gated
+ *            Mixture-of-Experts Layer", paper summary page, section 3.4
+ *            ("The MoE Output and Gating Network Formulation", "Noisy Top-K
+ *            Gating" Steps 1-3, "Load-Balancing: The Importance and Load
+ *            Losses").
+ *   [SWITCH] "Switch Transformer" explainer page, "Implementation", steps 1-8.
+ *   [LESSON] "Mixture-of-Experts: Sparse Computation" lesson page, ch. 1-5.
+ *
+ * The layer: X[T,D] tokens; router weights Wg, Wnoise [D,E]; E experts, each
+ * ReLU(x W1_e) W2_e with W1_e [D,H] and W2_e [H,D]; k experts per token; a
+ * capacity factor bounds how many rows each expert accepts.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers, row-major, densely packed, owned
+ *     by the caller. The library never allocates device memory; scratch comes
+ *     from the caller as `workspace` (size from moe_workspace_size).
+ *   - `hip_stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Every entry point only enqueues work on that stream and returns; it never
+ *     synchronises. Counts and offsets stay on the device.
+ *   - Argument errors are detected on the host before anything is enqueued and
+ *     return a negative moe_status; outputs are then untouched. An error from a
+ *     HIP launch returns MOE_ERR_HIP.
+ *   - Floating-point activations (X, Xd, Hd, Z, Y) and the expert weights share
+ *     one dtype, p->dtype: fp32, or bf16 stored as raw 16-bit patterns. Router
+ *     weights, logits, gates and the aux outputs are always fp32.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* a size, pointer or option out of range       */
+  MOE_ERR_UNSUPPORTED = -2, /* valid, but outside what the kernels implement */
+  MOE_ERR_NONFINITE = -3,   /* check_finite saw a NaN/Inf (moe_check_finite) */
+  MOE_ERR_HIP = -4,         /* a HIP runtime call failed                    */
+  MOE_ERR_WORKSPACE = -5    /* workspace missing or smaller than required   */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  MOE_GATE_NOISY_TOPK = 0,  /* [OLNN] 3.4 Noisy Top-K Gating                */
+  MOE_GATE_SWITCH_TOP1 = 1  /* [SWITCH] steps 1-2                           */
+} moe_gating;
+
+/* Largest k the kernels support. */
+#define MOE_MAX_K 8
+
+typedef struct {
+  int32_t T;                /* tokens (rows of X), >= 1                      */
+  int32_t D;                /* model width, >= 1                             */
+  int32_t E;                /* experts, >= 1                                 */
+  int32_t H;                /* expert hidden width, >= 1                     */
+  int32_t k;                /* experts per token, 1 <= k <= min(E, MOE_MAX_K); 1 for Switch */
+  int32_t dtype;            /* moe_dtype of X, Xd, Hd, Z, Y, W1, W2           */
+  int32_t gating;           /* moe_gating                                    */
+  int32_t noise;            /* noisy gate only: 1 adds softplus-scaled noise */
+  float capacity_factor;    /* <= 0: no capacity limit ([SWITCH] step 3)     */
+  int32_t min_capacity;     /* lower clamp of the capacity, >= 1             */
+  uint64_t seed;            /* noise key: eps[t,e] from (seed, t, e)          */
+  int32_t check_finite;     /* 1: kernels record NaN/Inf seen in logits, expert
+                               outputs and Y; read with moe_check_finite       */
+  int32_t reserved;
+} moe_problem;
+
+/* Workspace kinds for moe_workspace_size. */
+enum { MOE_WS_ROUTE = 0, MOE_WS_DISPATCH = 1, MOE_WS_AUX = 2 };
+
+/* ------------------------------------------------------------------ sizes */
+
+/* Capacity C per expert ([SWITCH] step 3, read for k experts per token):
+ * C = max(min_capacity, min(T, floor(k*T*cf/E))), the product in double;
+ * cf <= 0 gives C = T (no expert can receive more than T rows).
+ * Returns -1 on an invalid problem. */
+int32_t moe_capacity(const moe_problem* p);
+
+/* Upper bound on accepted (token, expert) rows: min(T*k, E*C). Sizes row_token,
+ * Xd, Hd and Z. Returns -1 on an invalid problem. */
+int64_t moe_max_rows(const moe_problem* p);
+
+/* Bytes of workspace needed by moe_route / moe_dispatch / moe_aux_loss
+ * (which = MOE_WS_*). 0 on an invalid problem. */
+size_t moe_workspace_size(const moe_problem* p, int which);
+
+/* Bytes of one packed expert-weight buffer (layer 1: W1, layer 2: W2). 0 on
+ * an invalid problem. */
+size_t moe_packed_weight_bytes(const moe_problem* p, int layer);
+
+/* ------------------------------------------------------------------ router */
+
+/* moe_route -- gating network for every token.
+ *
+ * Noisy top-k ([OLNN] 3.4 "Noisy Top-K Gating", Steps 1-3):
+ *   clean = X Wg (+ bias), std = Softplus(X Wnoise), H = clean + eps * std,
+ *   keep the k largest H (ties: lower expert index first), gates = softmax
+ *   over the k kept values. With p->noise = 0, H = clean.
+ * Switch top-1 ([SWITCH] steps 1-2): expert = argmax of softmax(clean)
+ *   (first on ties), gate = its softmax probability (not renormalised).
+ * Routing is decided on fp32 scores.
+ *
+ *   X          [T,D]  p->dtype
+ *   Wg         [D,E]  fp32
+ *   Wnoise     [D,E]  fp32; required iff noisy gate with noise, else ignored
+ *   bias       [E]    fp32 added to clean, or NULL
+ *   eps        [T,E]  fp32 external noise, or NULL: eps[t,e] is then drawn in
+ *                     the kernel from (p->seed, t, e) by Philox4x64-10 and
+ *                     Box-Muller (counter (t, e/4, 0, 0), key (seed, 0); the
+ *                     four outputs feed experts 4q..4q+3 as cos, sin, cos, sin)
+ *   ids        [T,k]  int32 out: kept experts, by score descending, index ascending
+ *   gates      [T,k]  fp32 out
+ *   clean      [T,E]  fp32 out: X Wg (+ bias)
+ *   noise_std  [T,E]  fp32 out: Softplus(X Wnoise); required iff noise is used
+ *   row_stats  [T,2]  fp32 out or NULL: k-th and (k+1)-th largest score
+ *                     (-inf when k = E); these are the load estimator's
+ *                     thresholds ([OLNN] 3.4, load)
+ *   workspace  moe_workspace_size(p, MOE_WS_ROUTE) bytes (router weights are
+ *              re-laid out there on every call)
+ */
+moe_status moe_route(const moe_problem* p, const void* X, const float* Wg,
+                     const float* Wnoise, const float* bias, const float* eps,
+                     int32_t* ids, float* gates, float* clean, float* noise_std,
+                     float* row_stats, void* workspace, size_t workspace_bytes,
+                     void* hip_stream);
+
+/* --------------------------------------------------------------- dispatch */
+
+/* moe_dispatch -- capacity-bounded, stable dispatch ([SWITCH] steps 3-5).
+ *
+ * counts[e]   = assignments to e before capacity.
+ * pos[t,j]    = number of earlier assignments (token-major: lower t, then
+ *               lower j) to the same expert: a stable slot.
+ * accepted    = pos < C (C from moe_capacity).
+ * offsets     = exclusive scan of min(counts, C); offsets[E] = accepted rows.
+ * Expert e owns rows offsets[e] .. offsets[e+1]-1 of Xd, in slot order:
+ * row_token[offsets[e] + pos] = t and Xd[offsets[e] + pos] = X[t].
+ *
+ *   X         [T,D] p->dtype      ids [T,k] int32 (each row: k distinct experts)
+ *   pos       [T,k] int32 out     accepted [T,k] uint8 out (1 kept, 0 dropped)
+ *   counts    [E] int32 out       offsets [E+1] int32 out
+ *   row_token [moe_max_rows] int32 out (rows past offsets[E] untouched)
+ *   Xd        [moe_max_rows, D] p->dtype out (rows past offsets[E] untouched)
+ *   workspace moe_workspace_size(p, MOE_WS_DISPATCH) bytes
+ * ids outside [0,E) give undefined results (not checked on the device).
+ */
+moe_status moe_dispatch(const moe_problem* p, const void* X, const int32_t* ids,
+                        int32_t* pos, uint8_t* accepted, int32_t* counts,
+                        int32_t* offsets, int32_t* row_token, void* Xd,
+                        void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ---------------------------------------------------------------- experts */
+
+/* moe_pack_expert_weights -- re-lay the expert weights for the grouped GEMM.
+ * Input is the pages' layout ([SWITCH] step 6): W1 [E,D,H], W2 [E,H,D]
+ * (p->dtype). Output buffers hold moe_packed_weight_bytes(p, 1) and (p, 2)
+ * bytes. Weights are parameters: pack once, reuse for every forward call.
+ * Either input may be NULL to skip that layer. */
+moe_status moe_pack_expert_weights(const moe_problem* p, const void* W1,
+                                   const void* W2, void* W1p, void* W2p,
+                                   void* hip_stream);
+
+/* moe_grouped_gemm -- one expert layer as a single grouped GEMM over the
+ * expert-major rows (groups given by offsets, read on the device).
+ *   layer 1: C[r, 0:H] = ReLU(A[r, 0:D] W1_e)   ([SWITCH] step 6)
+ *   layer 2: C[r, 0:D] = A[r, 0:H] W2_e
+ * for every row r in offsets[e] .. offsets[e+1]-1. fp32 accumulation; C is
+ * rounded to p->dtype (bf16: nearest-even). Rows past offsets[E] untouched.
+ *   A   [moe_max_rows, D or H] p->dtype     Wp packed weights of that layer
+ *   C   [moe_max_rows, H or D] p->dtype out offsets [E+1] int32 */
+moe_status moe_grouped_gemm(const moe_problem* p, int layer, const void* A,
+                            const void* Wp, const int32_t* offsets, void* C,
+                            void* hip_stream);
+
+/* moe_expert_ffn -- both expert layers: Hd = ReLU(Xd W1_e), Z = Hd W2_e
+ * ([SWITCH] step 6; [OLNN] 3.4, experts with one ReLU hidden layer).
+ *   Xd [moe_max_rows, D]   Hd [moe_max_rows, H] out   Z [moe_max_rows, D] out */
+moe_status moe_expert_ffn(const moe_problem* p, const void* Xd, const void* W1p,
+                          const void* W2p, const int32_t* offsets, void* Hd,
+                          void* Z, void* hip_stream);
+
+/* ---------------------------------------------------------------- combine */
+
+/* moe_combine -- gate-weighted sum plus residual ([OLNN] 3.4, the MoE output
+ * y = sum_i G(x)_i E_i(x); [SWITCH] step 7):
+ *   Y[t] = R[t] + sum over accepted j, ascending, of gates[t,j] * Z[offsets[e]+pos]
+ * accumulated in fp32 and rounded once to p->dtype. A token whose assignments
+ * were all dropped gets Y[t] = R[t] exactly. residual = NULL gives R = 0.
+ *   Z [moe_max_rows, D]  ids, gates, pos, accepted [T,k]  offsets [E+1]
+ *   residual [T,D] or NULL   Y [T,D] out (p->dtype) */
+moe_status moe_combine(const moe_problem* p, const void* Z, const int32_t* ids,
+                       const float* gates, const int32_t* pos,
+                       const uint8_t* accepted, const int32_t* offsets,
+                       const void* residual, void* Y, void* hip_stream);
+
+/* --------------------------------------------------------------- aux loss */
+
+/* moe_aux_loss -- unweighted balancing terms; the caller applies the loss
+ * weights (the pages give 0.1 / 0.01 for w_importance, w_load and alpha = 0.01).
+ *   importance[e] = sum of gates routed to e, before capacity   ([OLNN] 3.4)
+ *   load[e]       = sum_t Phi((clean - thr) / std), thr = row_stats[t,1] if e is
+ *                   among ids[t], else row_stats[t,0] (the k-th largest score
+ *                   among the other experts); 0 without noise   ([OLNN] 3.4)
+ *   out[0] = CV^2(importance)   out[1] = CV^2(load)   (population variance)
+ *   out[2] = E * sum_e f_e * Pbar_e, f = counts / T (before capacity),
+ *            Pbar = mean over tokens of softmax(clean)    ([SWITCH] step 8)
+ *   out[3] = max(load) / mean(load)   out[4] = max(counts) / mean(counts)
+ *   out[5] = dropped assignments = sum_e max(counts_e - C, 0)
+ *   out[6] = sum(importance)          out[7] = 0
+ *   ids, gates [T,k]; clean [T,E]; noise_std [T,E] (NULL without noise);
+ *   row_stats [T,2] (required with noise); counts [E];
+ *   importance, load [E] fp32 out (either may be NULL); out [8] fp32 out
+ *   workspace moe_workspace_size(p, MOE_WS_AUX) bytes */
+moe_status moe_aux_loss(const moe_problem* p, const int32_t* ids,
+                        const float* gates, const float* clean,
+                        const float* noise_std, const float* row_stats,
+                        const int32_t* counts, float* importance, float* load,
+                        float* out, void* workspace, size_t workspace_bytes,
+                        void* hip_stream);
+
+/* ------------------------------------------------------------------- misc */
+
+/* Synchronises hip_stream, then returns MOE_ERR_NONFINITE if a kernel run with
+ * check_finite = 1 on the current device saw a NaN/Inf since the last call
+ * (and clears the record), MOE_ERR_HIP on a pending HIP error, else MOE_OK. */
+moe_status moe_check_finite(void* hip_stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

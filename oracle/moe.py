@@ -193,16 +193,54 @@ def expert(x64: np.ndarray, W1e64: np.ndarray, W2e64: np.ndarray) -> np.ndarray:
 
 
 class ExpertBank:
-    """fp64 copies of expert weights, widened on first use."""
+    """fp64 copies of expert weights, widened on first use (the last `keep` kept)."""
 
-    def __init__(self, W1, W2):
+    def __init__(self, W1, W2, keep: int = 64):
         self.W1, self.W2 = W1, W2
+        self.keep = keep
         self._cache = {}
 
     def __call__(self, e: int):
-        if e not in self._cache:
-            self._cache[e] = (widen(self.W1[e]), widen(self.W2[e]))
-        return self._cache[e]
+        if e in self._cache:
+            v = self._cache.pop(e)
+        else:
+            v = (widen(self.W1[e]), widen(self.W2[e]))
+            while len(self._cache) >= self.keep:
+                self._cache.pop(next(iter(self._cache)))
+        self._cache[e] = v
+        return v
+
+
+def expert_rows(X, d: Dispatch, ids: np.ndarray, bank: ExpertBank, rows) -> np.ndarray:
+    """Expert outputs for expert-major rows: row r holds token row_token[r] of
+    the expert whose range contains r ([SWITCH] steps 5-6). Rows of one expert
+    go through that expert together, as one gathered batch ([LESSON] ch. 1,
+    forward_batched)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    experts = np.searchsorted(d.offsets, rows, side="right") - 1
+    out = np.zeros((rows.size, X.shape[1]))
+    for e in np.unique(experts):
+        sel = np.nonzero(experts == e)[0]
+        W1e, W2e = bank(int(e))
+        out[sel] = expert(widen(X[d.row_token[rows[sel]]]), W1e, W2e)
+    return out
+
+
+def combine_rows(Z, r: Routing, d: Dispatch, R=None, tokens=None) -> np.ndarray:
+    """Y[t] = R[t] + sum over accepted j (ascending) of gate_tj * Z[offsets[e] + pos]
+    given expert-major outputs Z ([SWITCH] step 7; R = None means no residual)."""
+    T, k = r.ids.shape
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    Z64 = widen(Z)
+    D = Z64.shape[1]
+    out = np.zeros((tokens.size, D))
+    for n, t in enumerate(tokens):
+        y = widen(R[t]).copy() if R is not None else np.zeros(D)
+        for j in range(k):
+            if d.accepted[t, j]:
+                y = y + r.gates[t, j] * Z64[d.offsets[r.ids[t, j]] + d.pos[t, j]]
+        out[n] = y
+    return out
 
 
 def combine_tokens(X, r: Routing, d: Dispatch, bank: ExpertBank, tokens, residual: bool = True):

@@ -1,0 +1,232 @@
+// C ABI entry points: argument validation on the host, then stage launches on
+// the caller's stream. Nothing here allocates device memory or synchronises
+// (except moe_check_finite, whose job is to synchronise).
+#include <math.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "common.h"
+
+namespace moe {
+
+// Largest expert count: dispatch and the grouped GEMM keep per-expert tables
+// in LDS (dispatch: 2E+1+512 ints).
+constexpr int kMaxExperts = 4096;
+
+__device__ int g_nonfinite;
+
+moe_status launch_status() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status validate(const moe_problem* p, Dims* d) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  if (p->T < 1 || p->D < 1 || p->E < 1 || p->H < 1) return MOE_ERR_INVALID_ARG;
+  if (p->gating != MOE_GATE_NOISY_TOPK && p->gating != MOE_GATE_SWITCH_TOP1) return MOE_ERR_INVALID_ARG;
+  if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (p->k < 1 || p->k > p->E) return MOE_ERR_INVALID_ARG;
+  if (p->gating == MOE_GATE_SWITCH_TOP1 && p->k != 1) return MOE_ERR_INVALID_ARG;
+  if (p->noise != 0 && p->noise != 1) return MOE_ERR_INVALID_ARG;
+  if (p->check_finite != 0 && p->check_finite != 1) return MOE_ERR_INVALID_ARG;
+  if (!isfinite(p->capacity_factor)) return MOE_ERR_INVALID_ARG;
+  if (p->min_capacity < 1) return MOE_ERR_INVALID_ARG;
+  if (p->k > MOE_MAX_K) return MOE_ERR_UNSUPPORTED;
+  if (p->E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(p->T) * p->k > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  d->T = p->T;
+  d->D = p->D;
+  d->E = p->E;
+  d->H = p->H;
+  d->k = p->k;
+  d->dtype = p->dtype;
+  d->gating = p->gating;
+  d->noise = p->noise;
+  // capacity: [SWITCH] step 3 (floor, clamp to T, then the minimum), k-scaled
+  if (p->capacity_factor > 0.f) {
+    const double c = floor(static_cast<double>(p->k) * static_cast<double>(p->T) *
+                           static_cast<double>(p->capacity_factor) / static_cast<double>(p->E));
+    const double clamped = std::min(static_cast<double>(p->T), c);
+    d->C = std::max(p->min_capacity, static_cast<int>(clamped));
+  } else {
+    d->C = p->T;
+  }
+  d->max_rows = std::min(static_cast<int64_t>(p->T) * p->k, static_cast<int64_t>(p->E) * d->C);
+  return MOE_OK;
+}
+
+static int* nonfinite_flag(const moe_problem* p) {
+  if (!p->check_finite) return nullptr;
+  static std::mutex mu;
+  static int* ptrs[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_nonfinite)) != hipSuccess) return nullptr;
+    ptrs[dev] = static_cast<int*>(ptr);
+  }
+  return ptrs[dev];
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+#define MOE_TRY(expr)                 \
+  do {                                \
+    const moe_status s_ = (expr);     \
+    if (s_ != MOE_OK) return s_;      \
+  } while (0)
+
+static hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+static moe_status flag_for(const moe_problem* p, int** flag) {
+  *flag = nonfinite_flag(p);
+  if (p->check_finite && !*flag) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+extern "C" {
+
+int32_t moe_capacity(const moe_problem* p) {
+  Dims d;
+  return validate(p, &d) == MOE_OK ? d.C : -1;
+}
+
+int64_t moe_max_rows(const moe_problem* p) {
+  Dims d;
+  return validate(p, &d) == MOE_OK ? d.max_rows : -1;
+}
+
+size_t moe_workspace_size(const moe_problem* p, int which) {
+  Dims d;
+  if (validate(p, &d) != MOE_OK) return 0;
+  switch (which) {
+    case MOE_WS_ROUTE: return route_workspace(d);
+    case MOE_WS_DISPATCH: return dispatch_workspace(d);
+    case MOE_WS_AUX: return aux_workspace(d);
+    default: return 0;
+  }
+}
+
+size_t moe_packed_weight_bytes(const moe_problem* p, int layer) {
+  Dims d;
+  if (validate(p, &d) != MOE_OK || (layer != 1 && layer != 2)) return 0;
+  return packed_weight_bytes(d, layer);
+}
+
+moe_status moe_route(const moe_problem* p, const void* X, const float* Wg, const float* Wnoise,
+                     const float* bias, const float* eps, int32_t* ids, float* gates, float* clean,
+                     float* noise_std, float* row_stats, void* workspace, size_t workspace_bytes,
+                     void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate(p, &d));
+  const bool noise = d.gating == MOE_GATE_NOISY_TOPK && d.noise;
+  if (!X || !Wg || !ids || !gates || !clean) return MOE_ERR_INVALID_ARG;
+  if (noise && (!Wnoise || !noise_std)) return MOE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < route_workspace(d)) return MOE_ERR_WORKSPACE;
+  int* flag;
+  MOE_TRY(flag_for(p, &flag));
+  return route_launch(d, p, X, Wg, Wnoise, bias, eps, ids, gates, clean, noise_std, row_stats,
+                      workspace, flag, as_stream(hip_stream));
+}
+
+moe_status moe_dispatch(const moe_problem* p, const void* X, const int32_t* ids, int32_t* pos,
+                        uint8_t* accepted, int32_t* counts, int32_t* offsets, int32_t* row_token,
+                        void* Xd, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate(p, &d));
+  if (!X || !ids || !pos || !accepted || !counts || !offsets || !row_token || !Xd)
+    return MOE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < dispatch_workspace(d)) return MOE_ERR_WORKSPACE;
+  return dispatch_launch(d, X, ids, pos, accepted, counts, offsets, row_token, Xd, workspace,
+                         as_stream(hip_stream));
+}
+
+moe_status moe_pack_expert_weights(const moe_problem* p, const void* W1, const void* W2, void* W1p,
+                                   void* W2p, void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate(p, &d));
+  if ((W1 && !W1p) || (W2 && !W2p) || (!W1 && !W2)) return MOE_ERR_INVALID_ARG;
+  if (W1) MOE_TRY(pack_launch(d, 1, W1, W1p, as_stream(hip_stream)));
+  if (W2) MOE_TRY(pack_launch(d, 2, W2, W2p, as_stream(hip_stream)));
+  return MOE_OK;
+}
+
+moe_status moe_grouped_gemm(const moe_problem* p, int layer, const void* A, const void* Wp,
+                            const int32_t* offsets, void* C, void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate(p, &d));
+  if (layer != 1 && layer != 2) return MOE_ERR_INVALID_ARG;
+  if (!A || !Wp || !offsets || !C) return MOE_ERR_INVALID_ARG;
+  int* flag = nullptr;
+  if (layer == 2) MOE_TRY(flag_for(p, &flag));
+  return gemm_launch(d, layer, A, Wp, offsets, C, flag, as_stream(hip_stream));
+}
+
+moe_status moe_expert_ffn(const moe_problem* p, const void* Xd, const void* W1p, const void* W2p,
+                          const int32_t* offsets, void* Hd, void* Z, void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate(p, &d));
+  if (!Xd || !W1p || !W2p || !offsets || !Hd || !Z) return MOE_ERR_INVALID_ARG;
+  int* flag;
+  MOE_TRY(flag_for(p, &flag));
+  MOE_TRY(gemm_launch(d, 1, Xd, W1p, offsets, Hd, nullptr, as_stream(hip_stream)));
+  return gemm_launch(d, 2, Hd, W2p, offsets, Z, flag, as_stream(hip_stream));
+}
+
+moe_status moe_combine(const moe_problem* p, const void* Z, const int32_t* ids, const float* gates,
+                       const int32_t* pos, const uint8_t* accepted, const int32_t* offsets,
+                       const void* residual, void* Y, void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate(p, &d));
+  if (!Z || !ids || !gates || !pos || !accepted || !offsets || !Y) return MOE_ERR_INVALID_ARG;
+  int* flag;
+  MOE_TRY(flag_for(p, &flag));
+  return combine_launch(d, Z, ids, gates, pos, accepted, offsets, residual, Y, flag,
+                        as_stream(hip_stream));
+}
+
+moe_status moe_aux_loss(const moe_problem* p, const int32_t* ids, const float* gates,
+                        const float* clean, const float* noise_std, const float* row_stats,
+                        const int32_t* counts, float* importance, float* load, float* out,
+                        void* workspace, size_t workspace_bytes, void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate(p, &d));
+  const bool noise = d.gating == MOE_GATE_NOISY_TOPK && d.noise;
+  if (!ids || !gates || !clean || !counts || !out) return MOE_ERR_INVALID_ARG;
+  if (noise && (!noise_std || !row_stats)) return MOE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < aux_workspace(d)) return MOE_ERR_WORKSPACE;
+  return aux_launch(d, ids, gates, clean, noise_std, row_stats, counts, importance, load, out,
+                    workspace, as_stream(hip_stream));
+}
+
+moe_status moe_check_finite(void* hip_stream) {
+  if (hipStreamSynchronize(as_stream(hip_stream)) != hipSuccess) return MOE_ERR_HIP;
+  int v = 0;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_nonfinite), sizeof(int), 0, hipMemcpyDeviceToHost) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (v) {
+    const int zero = 0;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_nonfinite), &zero, sizeof(int), 0, hipMemcpyHostToDevice) != hipSuccess)
+      return MOE_ERR_HIP;
+    return MOE_ERR_NONFINITE;
+  }
+  return MOE_OK;
+}
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported problem";
+    case MOE_ERR_NONFINITE: return "non-finite value seen";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,249 @@
+// Auxiliary balancing terms.
+//
+// "Outrageously Large Neural Networks" summary, section 3.4, "Load-Balancing:
+// The Importance and Load Losses": Importance(X) = sum over the batch of the
+// gate vectors; Load(X)_i = sum over the batch of P(x,i) = Phi((clean_i -
+// kth_excluding(H,k,i)) / Softplus((x Wnoise)_i)); each loss is w * CV(v)^2.
+// "Switch Transformer" explainer, "Implementation" step 8: alpha * E * sum_e
+// f_e P_e with f the hard (pre-capacity) fractions and P the mean router
+// probabilities. The population variance makes the lesson page's chapter-5
+// example come out at 0.68.
+//
+// kth_excluding is read off the row: for an expert among the row's k kept ones
+// the k-th largest of the others is the row's (k+1)-th largest score,
+// otherwise its k-th; both are the router's row_stats.
+//
+// Deterministic reductions only (fixed order, no float atomics):
+//   aux_partial  block b: 128 tokens; per-row softmax statistics of clean
+//                (wave reductions), then thread-per-expert column sums of the
+//                gates, P(x,i) and softmax(clean) over the block's rows.
+//   aux_reduce   32 experts x 8 partial lanes per block, strided fixed-order
+//                sums over blocks, then a fixed tree; fp64.
+//   aux_final    one block: CV^2 (two-pass, fp64), Switch term, diagnostics.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRows = 128;
+constexpr int kThreads = 256;
+
+struct AuxArgs {
+  const int32_t* ids;
+  const float* gates;
+  const float* clean;
+  const float* std_in;
+  const float* row_stats;
+  const int32_t* counts;
+  float* importance;
+  float* load;
+  float* out;
+  float* partial;  // [3][nblk][E]
+  double* sums;    // [3][E]
+  int T, E, k, C, nblk, use_noise;
+};
+
+__device__ __forceinline__ float phi(float z) { return 0.5f * erfcf(-z * 0.70710678118654752f); }
+
+__global__ __launch_bounds__(kThreads) void aux_partial(AuxArgs a) {
+  __shared__ float sM[kRows], sS[kRows];
+  __shared__ float sR0[kRows], sR1[kRows];
+  __shared__ int sId[kRows * MOE_MAX_K];
+  __shared__ float sG[kRows * MOE_MAX_K];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int t0 = blockIdx.x * kRows;
+  const int nr = min(kRows, a.T - t0);
+  const int E = a.E, k = a.k;
+
+  for (int i = tid; i < nr * k; i += kThreads) {
+    sId[i] = a.ids[static_cast<int64_t>(t0) * k + i];
+    sG[i] = a.gates[static_cast<int64_t>(t0) * k + i];
+  }
+  for (int r = tid; r < nr; r += kThreads) {
+    if (a.use_noise) {
+      sR0[r] = a.row_stats[2 * static_cast<int64_t>(t0 + r)];
+      sR1[r] = a.row_stats[2 * static_cast<int64_t>(t0 + r) + 1];
+    }
+  }
+  for (int r = wave; r < nr; r += kThreads / 64) {
+    const float* row = a.clean + static_cast<int64_t>(t0 + r) * E;
+    float m = -INFINITY;
+    for (int e = lane; e < E; e += 64) m = fmaxf(m, row[e]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float s = 0.f;
+    for (int e = lane; e < E; e += 64) s += expf(row[e] - m);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) {
+      sM[r] = m;
+      sS[r] = s;
+    }
+  }
+  __syncthreads();
+
+  const int64_t plane = static_cast<int64_t>(a.nblk) * E;
+  for (int e = tid; e < E; e += kThreads) {
+    float imp = 0.f, load = 0.f, pb = 0.f;
+    for (int r = 0; r < nr; ++r) {
+      const int64_t ix = static_cast<int64_t>(t0 + r) * E + e;
+      const float c = a.clean[ix];
+      bool inside = false;
+      for (int j = 0; j < k; ++j)
+        if (sId[r * k + j] == e) {
+          inside = true;
+          imp += sG[r * k + j];
+        }
+      pb += expf(c - sM[r]) / sS[r];
+      if (a.use_noise) {
+        const float thr = inside ? sR1[r] : sR0[r];
+        const float sd = a.std_in[ix];
+        const float diff = c - thr;
+        float p;
+        if (sd > 0.f) p = phi(diff / sd);
+        else p = diff > 0.f ? 1.f : (diff == 0.f ? 0.5f : 0.f);
+        load += p;
+      }
+    }
+    const int64_t o = static_cast<int64_t>(blockIdx.x) * E + e;
+    a.partial[o] = imp;
+    a.partial[plane + o] = load;
+    a.partial[2 * plane + o] = pb;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void aux_reduce(AuxArgs a) {
+  __shared__ double s[3][8][32];
+  const int el = threadIdx.x & 31, bl = threadIdx.x >> 5;
+  const int e = blockIdx.x * 32 + el;
+  const int64_t plane = static_cast<int64_t>(a.nblk) * a.E;
+  double acc[3] = {0.0, 0.0, 0.0};
+  if (e < a.E)
+    for (int b = bl; b < a.nblk; b += 8)
+#pragma unroll
+      for (int q = 0; q < 3; ++q) acc[q] += a.partial[q * plane + static_cast<int64_t>(b) * a.E + e];
+#pragma unroll
+  for (int q = 0; q < 3; ++q) s[q][bl][el] = acc[q];
+  __syncthreads();
+  if (bl == 0 && e < a.E) {
+    double v[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      v[q] = ((s[q][0][el] + s[q][1][el]) + (s[q][2][el] + s[q][3][el])) +
+             ((s[q][4][el] + s[q][5][el]) + (s[q][6][el] + s[q][7][el]));
+      a.sums[q * a.E + e] = v[q];
+    }
+    if (a.importance) a.importance[e] = static_cast<float>(v[0]);
+    if (a.load) a.load[e] = static_cast<float>(v[1]);
+  }
+}
+
+// Fixed-order block sum (kThreads threads) in fp64.
+__device__ double block_sum(double v, double* sh) {
+  sh[threadIdx.x] = v;
+  __syncthreads();
+  for (int w = kThreads / 2; w >= 1; w >>= 1) {
+    if (threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
+    __syncthreads();
+  }
+  const double r = sh[0];
+  __syncthreads();
+  return r;
+}
+__device__ double block_max(double v, double* sh) {
+  sh[threadIdx.x] = v;
+  __syncthreads();
+  for (int w = kThreads / 2; w >= 1; w >>= 1) {
+    if (threadIdx.x < w) sh[threadIdx.x] = fmax(sh[threadIdx.x], sh[threadIdx.x + w]);
+    __syncthreads();
+  }
+  const double r = sh[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kThreads) void aux_final(AuxArgs a) {
+  __shared__ double sh[kThreads];
+  const int E = a.E;
+  const double* imp = a.sums;
+  const double* load = a.sums + E;
+  const double* pb = a.sums + 2 * E;
+  double si = 0, sl = 0, sfp = 0, sc = 0, mxl = -INFINITY, mxc = -INFINITY, drop = 0;
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    si += imp[e];
+    sl += load[e];
+    const double c = a.counts[e];
+    sfp += (c / a.T) * (pb[e] / a.T);
+    sc += c;
+    mxl = fmax(mxl, load[e]);
+    mxc = fmax(mxc, c);
+    drop += fmax(c - a.C, 0.0);
+  }
+  si = block_sum(si, sh);
+  sl = block_sum(sl, sh);
+  sfp = block_sum(sfp, sh);
+  sc = block_sum(sc, sh);
+  mxl = block_max(mxl, sh);
+  mxc = block_max(mxc, sh);
+  drop = block_sum(drop, sh);
+  const double mi = si / E, ml = sl / E;
+  double vi = 0, vl = 0;
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    vi += (imp[e] - mi) * (imp[e] - mi);
+    vl += (load[e] - ml) * (load[e] - ml);
+  }
+  vi = block_sum(vi, sh) / E;
+  vl = block_sum(vl, sh) / E;
+  if (threadIdx.x == 0) {
+    const double mc = sc / E;
+    a.out[0] = static_cast<float>(mi != 0 ? vi / (mi * mi) : 0.0);
+    a.out[1] = static_cast<float>(ml != 0 ? vl / (ml * ml) : 0.0);
+    a.out[2] = static_cast<float>(E * sfp);
+    a.out[3] = static_cast<float>(ml > 0 ? mxl / ml : 0.0);
+    a.out[4] = static_cast<float>(mc > 0 ? mxc / mc : 0.0);
+    a.out[5] = static_cast<float>(drop);
+    a.out[6] = static_cast<float>(si);
+    a.out[7] = 0.f;
+  }
+}
+
+}  // namespace
+
+static int aux_blocks(const Dims& d) { return ceil_div(d.T, kRows); }
+
+size_t aux_workspace(const Dims& d) {
+  return align256(3 * static_cast<size_t>(aux_blocks(d)) * d.E * sizeof(float)) +
+         align256(3 * static_cast<size_t>(d.E) * sizeof(double));
+}
+
+moe_status aux_launch(const Dims& d, const int32_t* ids, const float* gates, const float* clean,
+                      const float* noise_std, const float* row_stats, const int32_t* counts,
+                      float* importance, float* load, float* out, void* ws, hipStream_t stream) {
+  AuxArgs a;
+  a.ids = ids;
+  a.gates = gates;
+  a.clean = clean;
+  a.use_noise = (d.gating == MOE_GATE_NOISY_TOPK && d.noise) ? 1 : 0;
+  a.std_in = a.use_noise ? noise_std : nullptr;
+  a.row_stats = a.use_noise ? row_stats : nullptr;
+  a.counts = counts;
+  a.importance = importance;
+  a.load = load;
+  a.out = out;
+  a.nblk = aux_blocks(d);
+  a.partial = static_cast<float*>(ws);
+  a.sums = reinterpret_cast<double*>(static_cast<char*>(ws) +
+                                     align256(3 * static_cast<size_t>(a.nblk) * d.E * sizeof(float)));
+  a.T = d.T;
+  a.E = d.E;
+  a.k = d.k;
+  a.C = d.C;
+  aux_partial<<<a.nblk, kThreads, 0, stream>>>(a);
+  if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  aux_reduce<<<ceil_div(d.E, 32), kThreads, 0, stream>>>(a);
+  if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  aux_final<<<1, kThreads, 0, stream>>>(a);
+  return launch_status();
+}
+
+}  // namespace moe

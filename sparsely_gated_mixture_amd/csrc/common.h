@@ -1,0 +1,136 @@
+// Internal helpers shared by the HIP sources of the MoE library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ----------------------------------------------------------------- vector types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------- bf16 bits
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kVec = 4;  // elements per 16-byte vector
+  __device__ static float to_f32(float v) { return v; }
+  __device__ static float from_f32(float v) { return v; }
+};
+template <> struct Elem<uint16_t> {
+  static constexpr int kVec = 8;
+  __device__ static float to_f32(uint16_t v) { return bf16_to_f32(v); }
+  __device__ static uint16_t from_f32(float v) { return f32_to_bf16(v); }
+};
+
+// 32x32 MFMA accumulator layout (16 fp32 per lane): register i of lane l
+// holds C[row][col] with col = l % 32 and row = 8*(i/4) + 4*(l/32) + i%4.
+__device__ __forceinline__ int acc_row(int lane, int i) {
+  return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
+
+// One MFMA "k-step" on 16-byte operand fragments. Lane l supplies row/col
+// l % 32 and a contiguous run of k values selected by l / 32; A and B use the
+// same run, so the products pair up whatever order the unit sums them in.
+//   bf16: 8 values per lane, one 32x32x16 MFMA (k-step 16)
+//   fp32: 4 values per lane, four 32x32x2 MFMAs  (k-step 8); MFMA s takes
+//         k = 4*(l/32) + s from each lane
+__device__ __forceinline__ f32x16 mfma_step_bf16(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_step_f32(uint4 a, uint4 b, f32x16 c) {
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+  return c;
+}
+template <typename T> __device__ __forceinline__ f32x16 mfma_step(uint4 a, uint4 b, f32x16 c);
+template <> __device__ __forceinline__ f32x16 mfma_step<uint16_t>(uint4 a, uint4 b, f32x16 c) {
+  return mfma_step_bf16(a, b, c);
+}
+template <> __device__ __forceinline__ f32x16 mfma_step<float>(uint4 a, uint4 b, f32x16 c) {
+  return mfma_step_f32(a, b, c);
+}
+
+// 16-byte load of elements [k0, k0+kVec) of a row of length n, zero past n.
+// vec_ok: rows are 16-byte aligned and n % kVec == 0 (then only whole vectors
+// are ever partially outside, i.e. entirely outside).
+template <typename T>
+__device__ __forceinline__ uint4 load_row16(const T* row, int k0, int n, bool vec_ok) {
+  constexpr int V = Elem<T>::kVec;
+  if (vec_ok) {
+    if (k0 < n) return *reinterpret_cast<const uint4*>(row + k0);
+    return make_uint4(0, 0, 0, 0);
+  }
+  T v[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) v[i] = (k0 + i < n) ? row[k0 + i] : T(0);
+  return *reinterpret_cast<const uint4*>(v);
+}
+
+// ----------------------------------------------------------------- non-finite record
+// With check_finite on, kernels get the device's flag word and store 1 into it
+// (idempotent plain stores) when a NaN/Inf shows up; otherwise flag is null.
+__device__ __forceinline__ void note_nonfinite(int* flag, bool bad) {
+  if (bad) *flag = 1;
+}
+
+// ----------------------------------------------------------------- host-side checks
+struct Dims {
+  int T, D, E, H, k;
+  int dtype, gating, noise;
+  int C;
+  int64_t max_rows;
+};
+
+moe_status validate(const moe_problem* p, Dims* d);
+moe_status launch_status();  // MOE_ERR_HIP if the last launch failed
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace sizes of the individual stages.
+size_t route_workspace(const Dims& d);
+size_t dispatch_workspace(const Dims& d);
+size_t aux_workspace(const Dims& d);
+size_t packed_weight_bytes(const Dims& d, int layer);
+
+// Stage launchers (arguments already validated).
+moe_status route_launch(const Dims& d, const moe_problem* p, const void* X, const float* Wg,
+                        const float* Wnoise, const float* bias, const float* eps, int32_t* ids,
+                        float* gates, float* clean, float* noise_std, float* row_stats,
+                        void* ws, int* nonfinite, hipStream_t stream);
+moe_status dispatch_launch(const Dims& d, const void* X, const int32_t* ids, int32_t* pos,
+                           uint8_t* accepted, int32_t* counts, int32_t* offsets,
+                           int32_t* row_token, void* Xd, void* ws, hipStream_t stream);
+moe_status pack_launch(const Dims& d, int layer, const void* W, void* Wp, hipStream_t stream);
+moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp,
+                       const int32_t* offsets, void* C, int* nonfinite, hipStream_t stream);
+moe_status combine_launch(const Dims& d, const void* Z, const int32_t* ids, const float* gates,
+                          const int32_t* pos, const uint8_t* accepted, const int32_t* offsets,
+                          const void* residual, void* Y, int* nonfinite, hipStream_t stream);
+moe_status aux_launch(const Dims& d, const int32_t* ids, const float* gates, const float* clean,
+                      const float* noise_std, const float* row_stats, const int32_t* counts,
+                      float* importance, float* load, float* out, void* ws, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,286 @@
+"""Python binding of the MoE C ABI (libmoe.so): argument marshalling only.
+
+Every step of the layer runs in the HIP kernels behind the C ABI; this module
+turns torch CUDA tensors into device pointers and the current HIP stream, and
+raises MoEError on a negative status. PyTorch is used for device memory and
+streams only. If the library is missing the import of this module fails:
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_GATE_NOISY_TOPK, MOE_GATE_SWITCH_TOP1 = 0, 1
+MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_AUX = 0, 1, 2
+MOE_MAX_K = 8
+
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
+          -3: "MOE_ERR_NONFINITE", -4: "MOE_ERR_HIP", -5: "MOE_ERR_WORKSPACE"}
+
+ENTRY_POINTS = [
+    "moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_packed_weight_bytes",
+    "moe_route", "moe_dispatch", "moe_pack_expert_weights", "moe_grouped_gemm",
+    "moe_expert_ffn", "moe_combine", "moe_aux_loss", "moe_check_finite", "moe_status_string",
+]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({_text(status)})")
+
+
+class Problem(ctypes.Structure):
+    """Mirror of moe_problem (include/moe.h)."""
+    _fields_ = [
+        ("T", ctypes.c_int32), ("D", ctypes.c_int32), ("E", ctypes.c_int32),
+        ("H", ctypes.c_int32), ("k", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("gating", ctypes.c_int32), ("noise", ctypes.c_int32),
+        ("capacity_factor", ctypes.c_float), ("min_capacity", ctypes.c_int32),
+        ("seed", ctypes.c_uint64), ("check_finite", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"HIP library not built: {path} (run python -m sparsely_gated_mixture_amd.build)")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    P = ctypes.POINTER(Problem)
+    sig = {
+        "moe_capacity": (i32, [P]),
+        "moe_max_rows": (i64, [P]),
+        "moe_workspace_size": (sz, [P, ctypes.c_int]),
+        "moe_packed_weight_bytes": (sz, [P, ctypes.c_int]),
+        "moe_route": (ctypes.c_int, [P] + [vp] * 10 + [vp, sz, vp]),
+        "moe_dispatch": (ctypes.c_int, [P] + [vp] * 8 + [vp, sz, vp]),
+        "moe_pack_expert_weights": (ctypes.c_int, [P, vp, vp, vp, vp, vp]),
+        "moe_grouped_gemm": (ctypes.c_int, [P, ctypes.c_int, vp, vp, vp, vp, vp]),
+        "moe_expert_ffn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp]),
+        "moe_combine": (ctypes.c_int, [P] + [vp] * 8 + [vp]),
+        "moe_aux_loss": (ctypes.c_int, [P] + [vp] * 9 + [vp, sz, vp]),
+        "moe_check_finite": (ctypes.c_int, [vp]),
+        "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = load_library()
+
+
+def _text(status: int) -> str:
+    return _lib.moe_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MoEError(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def problem(T, D, E, H, k, dtype="bf16", gating="noisy", noise=True, capacity_factor=0.0,
+            min_capacity=1, seed=0, check_finite=False) -> Problem:
+    return Problem(T=T, D=D, E=E, H=H, k=k,
+                   dtype=MOE_BF16 if dtype == "bf16" else MOE_F32,
+                   gating=MOE_GATE_SWITCH_TOP1 if gating == "switch" else MOE_GATE_NOISY_TOPK,
+                   noise=1 if noise else 0, capacity_factor=float(capacity_factor),
+                   min_capacity=int(min_capacity), seed=int(seed),
+                   check_finite=1 if check_finite else 0, reserved=0)
+
+
+def torch_dtype(p: Problem):
+    return torch.bfloat16 if p.dtype == MOE_BF16 else torch.float32
+
+
+# ------------------------------------------------------------------ sizes
+def moe_capacity(p: Problem) -> int:
+    c = _lib.moe_capacity(ctypes.byref(p))
+    if c < 0:
+        raise MoEError(-1, "moe_capacity")
+    return c
+
+
+def moe_max_rows(p: Problem) -> int:
+    r = _lib.moe_max_rows(ctypes.byref(p))
+    if r < 0:
+        raise MoEError(-1, "moe_max_rows")
+    return r
+
+
+def moe_workspace_size(p: Problem, which: int) -> int:
+    return _lib.moe_workspace_size(ctypes.byref(p), which)
+
+
+def moe_packed_weight_bytes(p: Problem, layer: int) -> int:
+    return _lib.moe_packed_weight_bytes(ctypes.byref(p), layer)
+
+
+# ------------------------------------------------------------------ stages
+def moe_route(p, X, Wg, Wnoise, bias, eps, ids, gates, clean, noise_std, row_stats, ws, stream=None):
+    _check(_lib.moe_route(ctypes.byref(p), _ptr(X), _ptr(Wg), _ptr(Wnoise), _ptr(bias), _ptr(eps),
+                          _ptr(ids), _ptr(gates), _ptr(clean), _ptr(noise_std), _ptr(row_stats),
+                          _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)), "moe_route")
+
+
+def moe_dispatch(p, X, ids, pos, accepted, counts, offsets, row_token, Xd, ws, stream=None):
+    _check(_lib.moe_dispatch(ctypes.byref(p), _ptr(X), _ptr(ids), _ptr(pos), _ptr(accepted),
+                             _ptr(counts), _ptr(offsets), _ptr(row_token), _ptr(Xd), _ptr(ws),
+                             ws.numel() if ws is not None else 0, _stream(stream)), "moe_dispatch")
+
+
+def moe_pack_expert_weights(p, W1, W2, W1p, W2p, stream=None):
+    _check(_lib.moe_pack_expert_weights(ctypes.byref(p), _ptr(W1), _ptr(W2), _ptr(W1p), _ptr(W2p),
+                                        _stream(stream)), "moe_pack_expert_weights")
+
+
+def moe_grouped_gemm(p, layer, A, Wp, offsets, C, stream=None):
+    _check(_lib.moe_grouped_gemm(ctypes.byref(p), layer, _ptr(A), _ptr(Wp), _ptr(offsets), _ptr(C),
+                                 _stream(stream)), "moe_grouped_gemm")
+
+
+def moe_expert_ffn(p, Xd, W1p, W2p, offsets, Hd, Z, stream=None):
+    _check(_lib.moe_expert_ffn(ctypes.byref(p), _ptr(Xd), _ptr(W1p), _ptr(W2p), _ptr(offsets),
+                               _ptr(Hd), _ptr(Z), _stream(stream)), "moe_expert_ffn")
+
+
+def moe_combine(p, Z, ids, gates, pos, accepted, offsets, residual, Y, stream=None):
+    _check(_lib.moe_combine(ctypes.byref(p), _ptr(Z), _ptr(ids), _ptr(gates), _ptr(pos),
+                            _ptr(accepted), _ptr(offsets), _ptr(residual), _ptr(Y), _stream(stream)),
+           "moe_combine")
+
+
+def moe_aux_loss(p, ids, gates, clean, noise_std, row_stats, counts, importance, load, out, ws,
+                 stream=None):
+    _check(_lib.moe_aux_loss(ctypes.byref(p), _ptr(ids), _ptr(gates), _ptr(clean), _ptr(noise_std),
+                             _ptr(row_stats), _ptr(counts), _ptr(importance), _ptr(load), _ptr(out),
+                             _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)),
+           "moe_aux_loss")
+
+
+def moe_check_finite(stream=None):
+    _check(_lib.moe_check_finite(_stream(stream)), "moe_check_finite")
+
+
+# ------------------------------------------------------------------ whole layer
+@dataclass
+class Buffers:
+    ids: torch.Tensor
+    gates: torch.Tensor
+    clean: torch.Tensor
+    noise_std: torch.Tensor | None
+    row_stats: torch.Tensor
+    pos: torch.Tensor
+    accepted: torch.Tensor
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    row_token: torch.Tensor
+    Xd: torch.Tensor
+    Hd: torch.Tensor
+    Z: torch.Tensor
+    Y: torch.Tensor
+    importance: torch.Tensor
+    load: torch.Tensor
+    aux_out: torch.Tensor
+    ws_route: torch.Tensor
+    ws_dispatch: torch.Tensor
+    ws_aux: torch.Tensor
+
+
+class Layer:
+    """One MoE layer's device buffers plus the five C-ABI stages in order.
+
+    Weights are given in the pages' layout (W1 [E,D,H], W2 [E,H,D]) and packed
+    once at construction. forward() enqueues route, dispatch, expert FFN,
+    combine and aux on the current stream and returns the buffers.
+    """
+
+    def __init__(self, p: Problem, Wg, Wnoise, bias, W1, W2, device="cuda"):
+        self.p = p
+        dt = torch_dtype(p)
+        T, D, E, H, k = p.T, p.D, p.E, p.H, p.k
+        rows = moe_max_rows(p)
+        noisy = p.gating == MOE_GATE_NOISY_TOPK and p.noise == 1
+        e = lambda *s, dtype=torch.float32: torch.empty(*s, dtype=dtype, device=device)
+        self.Wg, self.Wnoise, self.bias = Wg, Wnoise, bias
+        self.W1p = e(moe_packed_weight_bytes(p, 1), dtype=torch.uint8)
+        self.W2p = e(moe_packed_weight_bytes(p, 2), dtype=torch.uint8)
+        moe_pack_expert_weights(p, W1, W2, self.W1p, self.W2p)
+        self.b = Buffers(
+            ids=e(T, k, dtype=torch.int32), gates=e(T, k), clean=e(T, E),
+            noise_std=e(T, E) if noisy else None, row_stats=e(T, 2),
+            pos=e(T, k, dtype=torch.int32), accepted=e(T, k, dtype=torch.uint8),
+            counts=e(E, dtype=torch.int32), offsets=e(E + 1, dtype=torch.int32),
+            row_token=e(max(rows, 1), dtype=torch.int32), Xd=e(max(rows, 1), D, dtype=dt),
+            Hd=e(max(rows, 1), H, dtype=dt), Z=e(max(rows, 1), D, dtype=dt), Y=e(T, D, dtype=dt),
+            importance=e(E), load=e(E), aux_out=e(8),
+            ws_route=e(max(moe_workspace_size(p, MOE_WS_ROUTE), 1), dtype=torch.uint8),
+            ws_dispatch=e(max(moe_workspace_size(p, MOE_WS_DISPATCH), 1), dtype=torch.uint8),
+            ws_aux=e(max(moe_workspace_size(p, MOE_WS_AUX), 1), dtype=torch.uint8),
+        )
+
+    def route(self, X, eps=None):
+        b = self.b
+        moe_route(self.p, X, self.Wg, self.Wnoise, self.bias, eps, b.ids, b.gates, b.clean,
+                  b.noise_std, b.row_stats, b.ws_route)
+
+    def dispatch(self, X):
+        b = self.b
+        moe_dispatch(self.p, X, b.ids, b.pos, b.accepted, b.counts, b.offsets, b.row_token, b.Xd,
+                     b.ws_dispatch)
+
+    def ffn(self):
+        b = self.b
+        moe_expert_ffn(self.p, b.Xd, self.W1p, self.W2p, b.offsets, b.Hd, b.Z)
+
+    def gemm(self, layer):
+        b = self.b
+        if layer == 1:
+            moe_grouped_gemm(self.p, 1, b.Xd, self.W1p, b.offsets, b.Hd)
+        else:
+            moe_grouped_gemm(self.p, 2, b.Hd, self.W2p, b.offsets, b.Z)
+
+    def combine(self, X, residual=True):
+        b = self.b
+        moe_combine(self.p, b.Z, b.ids, b.gates, b.pos, b.accepted, b.offsets,
+                    X if residual else None, b.Y)
+
+    def aux(self):
+        b = self.b
+        moe_aux_loss(self.p, b.ids, b.gates, b.clean, b.noise_std, b.row_stats, b.counts,
+                     b.importance, b.load, b.aux_out, b.ws_aux)
+
+    def forward(self, X, eps=None, residual=True, aux=True) -> Buffers:
+        self.route(X, eps)
+        self.dispatch(X)
+        self.ffn()
+        self.combine(X, residual)
+        if aux:
+            self.aux()
+        return self.b

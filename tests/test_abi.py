@@ -1,0 +1,121 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/moe.h, and rejects bad arguments on the host before any
+HIP call (so these run on a machine without a GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "sparsely_gated_mixture_amd", "libmoe.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmoe.so not built")
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def m():
+    from sparsely_gated_mixture_amd import moe
+    return moe
+
+
+def test_exports_every_declared_symbol(m):
+    names = _declared()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(m.ENTRY_POINTS) == names
+
+
+def test_problem_struct_layout(m):
+    assert ctypes.sizeof(m.Problem) == 56
+    assert m.Problem.seed.offset == 40
+
+
+def _p(m, **kw):
+    base = dict(T=64, D=32, E=8, H=48, k=2, dtype="bf16", gating="noisy", noise=True,
+                capacity_factor=1.0, seed=3)
+    base.update(kw)
+    return m.problem(**base)
+
+
+def test_capacity_formula(m):
+    # Switch explainer step 3 (floor, clamp to T, minimum), scaled by k
+    assert m.moe_capacity(_p(m, T=8, E=3, k=1, gating="switch", noise=False)) == 2
+    assert m.moe_capacity(_p(m, T=16384, E=128, k=1, capacity_factor=1.25)) == 160
+    assert m.moe_capacity(_p(m, T=65536, E=256, k=2, capacity_factor=1.0)) == 512
+    assert m.moe_capacity(_p(m, T=100, E=8, k=2, capacity_factor=0.0)) == 100
+    assert m.moe_capacity(_p(m, T=8, E=8, k=1, capacity_factor=0.01, min_capacity=3)) == 3
+    assert m.moe_max_rows(_p(m, T=65536, E=256, k=2, capacity_factor=1.0)) == 131072
+    assert m.moe_max_rows(_p(m, T=64, E=8, k=2, capacity_factor=0.5)) == 8 * 8
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=0), dict(D=0), dict(E=0), dict(H=0), dict(k=0), dict(k=9, E=4),
+    dict(gating="switch", k=2), dict(capacity_factor=math.nan), dict(capacity_factor=math.inf),
+    dict(min_capacity=0),
+])
+def test_invalid_problem(m, kw):
+    p = _p(m, **kw)
+    assert m._lib.moe_capacity(ctypes.byref(p)) == -1
+    assert m.moe_workspace_size(p, m.MOE_WS_ROUTE) == 0
+    st = m._lib.moe_route(ctypes.byref(p), *([None] * 10), None, 0, None)
+    assert st == -1
+
+
+def test_unsupported_problem(m):
+    p = _p(m, E=16, k=9)  # k above MOE_MAX_K
+    st = m._lib.moe_route(ctypes.byref(p), *([None] * 10), None, 0, None)
+    assert st == -2
+    p = _p(m, E=5000, k=2)
+    assert m._lib.moe_dispatch(ctypes.byref(p), *([None] * 8), None, 0, None) == -2
+
+
+def test_null_pointers_and_workspace(m):
+    p = _p(m)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: rejected on the host
+    # required pointer missing
+    st = m._lib.moe_route(ctypes.byref(p), fake, None, fake, None, None, fake, fake, fake, fake,
+                          None, fake, 1 << 20, None)
+    assert st == -1
+    # noisy gate without Wnoise
+    st = m._lib.moe_route(ctypes.byref(p), fake, fake, None, None, None, fake, fake, fake, fake,
+                          None, fake, 1 << 20, None)
+    assert st == -1
+    # workspace too small
+    need = m.moe_workspace_size(p, m.MOE_WS_ROUTE)
+    assert need > 0
+    st = m._lib.moe_route(ctypes.byref(p), fake, fake, fake, None, None, fake, fake, fake, fake,
+                          None, fake, need - 1, None)
+    assert st == -5
+    st = m._lib.moe_dispatch(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake,
+                             None, 0, None)
+    assert st == -5
+    st = m._lib.moe_aux_loss(ctypes.byref(p), fake, fake, fake, None, fake, fake, None, None, fake,
+                             fake, 1 << 30, None)
+    assert st == -1  # noise on but no noise_std
+    assert m._lib.moe_grouped_gemm(ctypes.byref(p), 3, fake, fake, fake, fake, None) == -1
+    assert m._lib.moe_pack_expert_weights(ctypes.byref(p), None, None, None, None, None) == -1
+
+
+def test_status_strings(m):
+    for s in (0, -1, -2, -3, -4, -5):
+        assert m._lib.moe_status_string(s).decode() != "unknown status"
+    assert m._lib.moe_status_string(7).decode() == "unknown status"
+
+
+def test_sizes_scale(m):
+    p = _p(m, T=65536, D=1024, E=256, H=4096, k=2)
+    # packed expert weights: zero padding only to 32 columns / 64-deep k stages
+    assert m.moe_packed_weight_bytes(p, 1) == 256 * 1024 * 4096 * 2
+    assert m.moe_packed_weight_bytes(p, 2) == 256 * 4096 * 1024 * 2
+    assert m.moe_packed_weight_bytes(p, 3) == 0
+    assert m.moe_workspace_size(p, m.MOE_WS_ROUTE) == 3 * 1024 * 512 * 2

@@ -377,6 +377,16 @@ def test_dropped_tokens_keep_the_residual():
     np.testing.assert_allclose(f["Y"], want, rtol=1e-12, atol=1e-12)
 
 
+def test_stage_combine_equals_token_loop():
+    """The expert-major form (expert_rows + combine_rows, the page's dispatch / combine
+    tensors) gives the same Y as the per-token loop."""
+    w, inp, f = _tiny_layer(T=40, E=3, k=2, cf=0.5)
+    r, d = f["routing"], f["dispatch"]
+    Z = O.expert_rows(inp["X"], d, r.ids, f["bank"], np.arange(d.offsets[-1]))
+    Y = O.combine_rows(Z, r, d, inp["X"])
+    np.testing.assert_allclose(Y, f["Y"], rtol=1e-13, atol=1e-13)
+
+
 def test_single_expert_is_plain_ffn():
     """E = 1, k = 1, no noise, no capacity: Y = X + ReLU(X W1) W2 (torch fp64)."""
     w = I.Workload("one", T=10, D=8, E=1, k=1, H=12, act="f32", gating="noisy", noise=False,
