@@ -67,12 +67,31 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* excl, int* wt) {
   return total;
 }
 
-template <typename T, int BM, bool kRelu>
-__global__ __launch_bounds__(kThreads) void grouped_gemm(GemmArgs g) {
+// Operands live in native vector registers (the HIP uint4 struct defeats
+// register promotion of arrays).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c);
+template <> __device__ __forceinline__ f32x16 mma<uint16_t>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x16 mma<float>(u32x4 a, u32x4 b, f32x16 c) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[s]), __uint_as_float(b[s]), c, 0, 0, 0);
+  return c;
+}
+
+// kFullK: K is a multiple of the 128-byte k stage (no tail, no bounds checks on A).
+// kVecOut: N * sizeof(T) is a multiple of 16 (row-contiguous 16-byte output stores).
+template <typename T, int BM, bool kRelu, bool kFullK, bool kVecOut>
+__global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
   constexpr int V = Elem<T>::kVec;
   constexpr int kStageElems = 128 / static_cast<int>(sizeof(T));
-  constexpr int MB = BM / 32;               // 32-row blocks per tile
+  constexpr int MB = BM / 32;                 // 32-row blocks per tile
   constexpr int kChunks = BM * 8 / kThreads;  // 16-byte A chunks per thread per stage
+  constexpr int kTStride = 32 + 16 / static_cast<int>(sizeof(T));  // epilogue tile row (elements)
 
   extern __shared__ int sCum[];  // E + 1 running row-tile counts
   __shared__ int wt[kThreads / 64];
@@ -120,40 +139,36 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm(GemmArgs g) {
 
   const T* A = static_cast<const T*>(g.A);
   const int K = g.K;
-  const bool vec_ok = (K % V) == 0;
   const int nst = g.KS / 4;
 
-  // ---- operand streams
-  auto load_a = [&](int st, uint4 regs[kChunks]) {
+  // ---- A stream: thread's chunk i is row arow0 + i*32 (clamped into the group), 16-byte
+  // segment aseg of the 128-byte k stage; LDS rows are padded to kAStride bytes.
+  const int aseg = tid & 7, arow0 = tid >> 3;
+  const T* abase = A + static_cast<int64_t>(r0) * K;
+  const bool vec_ok = (K % V) == 0;
+  u32x4 areg[kChunks];
+  auto load_a = [&](int st) {
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c >> 3, seg = c & 7;
-      const int rr = r0 + min(r, rows - 1);
-      regs[i] = load_row16<T>(A + static_cast<int64_t>(rr) * K, st * kStageElems + seg * V, K, vec_ok);
+      const T* row = abase + static_cast<int64_t>(min(arow0 + i * (kThreads / 8), rows - 1)) * K;
+      if constexpr (kFullK) {
+        areg[i] = *reinterpret_cast<const u32x4*>(row + st * kStageElems + aseg * V);
+      } else {
+        const uint4 v = load_row16<T>(row, st * kStageElems + aseg * V, K, vec_ok);
+        areg[i] = u32x4{v.x, v.y, v.z, v.w};
+      }
     }
   };
-  auto store_a = [&](int buf, const uint4 regs[kChunks]) {
+  auto store_a = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c >> 3, seg = c & 7;
-      *reinterpret_cast<uint4*>(&sA[buf][r * kAStride + seg * 16]) = regs[i];
-    }
+    for (int i = 0; i < kChunks; ++i)
+      *reinterpret_cast<u32x4*>(&sA[buf][(arow0 + i * (kThreads / 8)) * kAStride + aseg * 16]) = areg[i];
   };
-  const int nb0 = n0 / 32 + wave * 2;
-  const bool has_b[2] = {nb0 < g.NB, nb0 + 1 < g.NB};
-  const uint4* Wb[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    Wb[j] = g.Wp + (static_cast<int64_t>(e) * g.NB + (has_b[j] ? nb0 + j : 0)) * g.KS * kWave + lane;
-  auto load_b = [&](int st, uint4 b[4][2]) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[ks][j] = has_b[j] ? Wb[j][static_cast<int64_t>(st * 4 + ks) * kWave] : make_uint4(0, 0, 0, 0);
-  };
+
+  // ---- B stream: column blocks past N read a valid block (those results are never stored)
+  const u32x4* Wb = reinterpret_cast<const u32x4*>(g.Wp);
+  const u32x4* W0 = Wb + (static_cast<int64_t>(e) * g.NB + min(n0 / 32 + wave * 2, g.NB - 1)) * g.KS * kWave + lane;
+  const u32x4* W1 = Wb + (static_cast<int64_t>(e) * g.NB + min(n0 / 32 + wave * 2 + 1, g.NB - 1)) * g.KS * kWave + lane;
 
   f32x16 acc[MB][2];
 #pragma unroll
@@ -163,59 +178,98 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[m][j][i] = 0.f;
 
-  uint4 areg[kChunks];
-  uint4 bcur[4][2], bnxt[4][2];
-  load_a(0, areg);
-  load_b(0, bcur);
-  store_a(0, areg);
+  const int arow = (lane & 31) * kAStride + (lane >> 5) * 16;
+  u32x4 bq[4][2];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    bq[ks][0] = W0[ks * kWave];
+    bq[ks][1] = W1[ks * kWave];
+  }
+  load_a(0);
+  store_a(0);
   __syncthreads();
+
+  // ---- main loop: stage st computes from LDS buffer st&1 and B registers, while the next
+  // stage's A (registers, then LDS) and B (registers, one k-step at a time) stream in. Every
+  // load is unconditional (the last stage re-reads itself) so the wait counts stay exact.
+  u32x4 af[2][MB];
   for (int st = 0; st < nst; ++st) {
     const int buf = st & 1;
-    const bool more = st + 1 < nst;
-    if (more) {
-      load_a(st + 1, areg);
-      load_b(st + 1, bnxt);
-    }
+    const int stn = min(st + 1, nst - 1);
+    load_a(stn);
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+      af[0][m] = *reinterpret_cast<const u32x4*>(&sA[buf][m * 32 * kAStride + arow]);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 3) {
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+          af[(ks + 1) & 1][m] =
+              *reinterpret_cast<const u32x4*>(&sA[buf][m * 32 * kAStride + (ks + 1) * 32 + arow]);
+      }
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
-        const uint4 af = *reinterpret_cast<const uint4*>(
-            &sA[buf][(m * 32 + (lane & 31)) * kAStride + ks * 32 + (lane >> 5) * 16]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[m][j] = mfma_step<T>(af, bcur[ks][j], acc[m][j]);
+        acc[m][0] = mma<T>(af[ks & 1][m], bq[ks][0], acc[m][0]);
+        acc[m][1] = mma<T>(af[ks & 1][m], bq[ks][1], acc[m][1]);
       }
+      const int64_t kn = static_cast<int64_t>(stn * 4 + ks) * kWave;
+      bq[ks][0] = W0[kn];
+      bq[ks][1] = W1[kn];
     }
-    if (more) {
-      store_a(buf ^ 1, areg);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) bcur[ks][j] = bnxt[ks][j];
-    }
+    store_a(buf ^ 1);
     __syncthreads();
   }
 
-  // ---- epilogue: (ReLU), round to T, predicated stores
+  // ---- epilogue: (ReLU), round to T, store
   T* C = static_cast<T*>(g.C);
   const bool check = g.nonfinite != nullptr;
   bool bad = false;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = n0 + wave * 64 + j * 32 + (lane & 31);
-    if (col >= g.N) continue;
+  if constexpr (kVecOut) {
+    // each 32x32 tile goes through a wave-private LDS tile so rows leave as 16-byte stores
+    T* Ts = reinterpret_cast<T*>(&sA[0][0]) + wave * (32 * kTStride);
+    constexpr int kSegs = 32 / V;  // 16-byte segments per tile row
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = m * 32 + acc_row(lane, i);
-        if (row < rows) {
+      for (int j = 0; j < 2; ++j) {
+        const int cbase = n0 + wave * 64 + j * 32;
+        const bool col_ok = cbase + (lane & 31) < g.N;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
           float v = acc[m][j][i];
           if (kRelu) v = fmaxf(v, 0.f);
-          bad |= !isfinite(v);
-          C[static_cast<int64_t>(r0 + row) * g.N + col] = Elem<T>::from_f32(v);
+          bad |= col_ok && m * 32 + acc_row(lane, i) < rows && !isfinite(v);
+          Ts[acc_row(lane, i) * kTStride + (lane & 31)] = Elem<T>::from_f32(v);
+        }
+#pragma unroll
+        for (int h = 0; h < 32 * kSegs / 64; ++h) {
+          const int qd = lane + 64 * h;
+          const int row = qd / kSegs, seg = qd % kSegs;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(&Ts[row * kTStride + seg * V]);
+          const int grow = m * 32 + row, gcol = cbase + seg * V;
+          if (grow < rows && gcol < g.N)
+            *reinterpret_cast<u32x4*>(&C[static_cast<int64_t>(r0 + grow) * g.N + gcol]) = v;
         }
       }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wave * 64 + j * 32 + (lane & 31);
+      if (col >= g.N) continue;
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = m * 32 + acc_row(lane, i);
+          if (row < rows) {
+            float v = acc[m][j][i];
+            if (kRelu) v = fmaxf(v, 0.f);
+            bad |= !isfinite(v);
+            C[static_cast<int64_t>(r0 + row) * g.N + col] = Elem<T>::from_f32(v);
+          }
+        }
+    }
   }
   if (check) note_nonfinite(g.nonfinite, bad);
 }
@@ -281,6 +335,23 @@ moe_status pack_launch(const Dims& d, int layer, const void* W, void* Wp, hipStr
   return launch_status();
 }
 
+template <typename T, bool kRelu>
+static void launch_k(const GemmArgs& g, int grid, size_t lds, hipStream_t stream) {
+  constexpr int V = Elem<T>::kVec;
+  const bool full = g.K % (128 / static_cast<int>(sizeof(T))) == 0;
+  const bool vout = g.N % V == 0;
+  if (full && vout) grouped_gemm<T, kBM, kRelu, true, true><<<grid, kThreads, lds, stream>>>(g);
+  else if (full) grouped_gemm<T, kBM, kRelu, true, false><<<grid, kThreads, lds, stream>>>(g);
+  else if (vout) grouped_gemm<T, kBM, kRelu, false, true><<<grid, kThreads, lds, stream>>>(g);
+  else grouped_gemm<T, kBM, kRelu, false, false><<<grid, kThreads, lds, stream>>>(g);
+}
+
+template <typename T>
+static void launch_typed(const GemmArgs& g, int layer, int grid, size_t lds, hipStream_t stream) {
+  if (layer == 1) launch_k<T, true>(g, grid, lds, stream);
+  else launch_k<T, false>(g, grid, lds, stream);
+}
+
 moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp, const int32_t* offsets,
                        void* C, int* nonfinite, hipStream_t stream) {
   int K, N;
@@ -306,17 +377,11 @@ moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp, 
   const int64_t grid = ceil_div64(std::max<int64_t>(tiles, 1), kXcds) * kXcds;
   if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
   const size_t lds = (static_cast<size_t>(d.E) + 1) * sizeof(int);
-  if (d.dtype == MOE_BF16) {
-    if (layer == 1)
-      grouped_gemm<uint16_t, kBM, true><<<static_cast<int>(grid), kThreads, lds, stream>>>(g);
-    else
-      grouped_gemm<uint16_t, kBM, false><<<static_cast<int>(grid), kThreads, lds, stream>>>(g);
-  } else {
-    if (layer == 1)
-      grouped_gemm<float, kBM, true><<<static_cast<int>(grid), kThreads, lds, stream>>>(g);
-    else
-      grouped_gemm<float, kBM, false><<<static_cast<int>(grid), kThreads, lds, stream>>>(g);
-  }
+  const int gr = static_cast<int>(grid);
+  if (d.dtype == MOE_BF16)
+    launch_typed<uint16_t>(g, layer, gr, lds, stream);
+  else
+    launch_typed<float>(g, layer, gr, lds, stream);
   return launch_status();
 }
 
