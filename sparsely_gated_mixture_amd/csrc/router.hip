@@ -1,4 +1,4 @@
-// Router: gate GEMM + noise + KeepTopK + softmax, one fused kernel.
+// Router: gate GEMM + noise + KeepTopK + softmax.
 //
 // Noisy top-k gating: "Outrageously Large Neural Networks" summary, section
 // 3.4, "Noisy Top-K Gating" Steps 1-3 (clean = X.Wg, std = Softplus(X.Wnoise),
@@ -7,56 +7,74 @@
 // (fp32 softmax over all experts, argmax first on ties, gate = that
 // probability).
 //
-// Layout and work split
-//   * The router weights are re-laid out per call (router_pack) into MFMA
-//     fragment order: for every 32-column block and 16-deep (bf16) or 8-deep
-//     (fp32) k-step, the 64 lanes' 16-byte operands are contiguous, so a wave
-//     reads its B operand with one coalesced 1 KB load straight from L2.
-//     Column blocks alternate clean / noise (2j: Wg experts 32j.., 2j+1: Wnoise
-//     for the same experts), so a lane holds clean and raw of the same
-//     (token, expert) in the same accumulator slot.
-//   * bf16 X: each fp32 weight is split exactly into three bf16 pieces
-//     (hi + mid + lo); X is exactly bf16, so every product is exact in fp32 and
-//     three bf16 MFMAs accumulate the fp32 dot product. fp32 X: fp32 MFMA.
-//   * A block owns 64 token rows and walks the experts in passes of 128 (one
-//     32-expert block per wave). Per pass the X rows stream through LDS in
-//     64-byte... 128-byte-wide k stages (double buffered), the accumulators go
-//     through LDS to an epilogue that computes softplus, the Philox noise and
-//     H, stores clean / std, and merges the pass's H values into a running
-//     top-(k+1) list per row with wavefront arg-max rounds.
+// Three launches:
+//   router_pack    re-lays Wg / Wnoise into MFMA fragment order (per call; a
+//                  few microseconds). Column blocks alternate clean / noise
+//                  for the same 32 experts, so a wave's two accumulators hold
+//                  clean and raw of the same (token, expert). For bf16 X each
+//                  fp32 weight is split exactly into three bf16 pieces
+//                  (hi + mid + lo): X is exactly bf16, every product is exact
+//                  in fp32, and three bf16 MFMAs accumulate the fp32 dot
+//                  product. fp32 X uses fp32 MFMA.
+//   router_gemm    128 tokens x 256 weight columns per block, the grouped
+//                  GEMM's pipeline (X through double-buffered LDS, B fragments
+//                  streamed into registers). Epilogue through a wave-private
+//                  LDS tile: per (token, 4 experts) one Philox call gives the
+//                  four noise samples; writes clean, std and the score H.
+//   router_select  8 lanes per token row: per-lane sorted top-K lists
+//                  (K = next power of two >= k+1) merged by a bitonic
+//                  butterfly; writes ids, gates, row_stats. Switch also sums
+//                  exp(logit - max) for its gate.
 #include "common.h"
 
 namespace moe {
 namespace {
 
-constexpr int kRows = 64;          // token rows per block
-constexpr int kThreads = 256;      // 4 waves
-constexpr int kExpPass = 128;      // experts per pass (32 per wave)
-constexpr int kStageBytes = 128;   // bytes of one X row per k stage
-constexpr int kAStride = 144;      // padded LDS row stride (bytes)
-constexpr int kCStride = kExpPass + 4;
-constexpr int kList = MOE_MAX_K + 1;
-constexpr int kNone = 0x7fffffff;  // index of an empty / taken candidate
+constexpr int kThreads = 256;
+constexpr int kBM = 128;          // token rows per block
+constexpr int kBN = 256;          // weight columns per block (8 blocks of 32)
+constexpr int kAStride = 144;     // padded LDS row stride (bytes)
+constexpr int kTS = 36;           // epilogue tile row stride (floats)
+constexpr int kXcds = 8;
+constexpr int kNone = 0x7fffffff; // index of an empty / taken candidate
 
-struct RouterArgs {
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c);
+template <> __device__ __forceinline__ f32x16 mma<uint16_t>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x16 mma<float>(u32x4 a, u32x4 b, f32x16 c) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[s]), __uint_as_float(b[s]), c, 0, 0, 0);
+  return c;
+}
+
+struct GemmArgs {
   const void* X;
-  const uint4* wfrag;  // fragment-ordered router weights (workspace)
+  const u32x4* wfrag;  // fragment-ordered router weights (workspace)
   const float* bias;
   const float* eps;
-  int32_t* ids;
-  float* gates;
   float* clean;
   float* std_out;
-  float* row_stats;
+  float* H;            // noisy scores (workspace); unused without noise
   int* nonfinite;
   uint64_t seed;
-  int T, D, E, k;
-  int NB;      // 32-column blocks in wfrag (per piece)
-  int KS;      // k-steps in wfrag (per column block)
+  int T, D, E;
+  int NB;              // 32-column blocks in wfrag (per piece)
+  int KS;              // k-steps per column block (multiple of 4)
   int use_noise;
-  int switch_gate;
 };
 
+struct SelectArgs {
+  const float* score;  // H (noisy) or clean
+  int32_t* ids;
+  float* gates;
+  float* row_stats;
+  int T, E, k, switch_gate;
+};
 // ------------------------------------------------------------------ Philox4x64-10 + Box-Muller
 // Salmon et al., SC'11: ten rounds; each round multiplies counter words 0 and 2
 // by the two published constants (full 128-bit products), mixes in the key and
@@ -111,30 +129,6 @@ __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
 }
 
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(v, off);
-    const int oi = __shfl_xor(i, off);
-    if (better(ov, oi, v, i)) {
-      v = ov;
-      i = oi;
-    }
-  }
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
 // ------------------------------------------------------------------ weight re-layout
 // One thread per (column block nb, k-step ks, lane). Column n of block nb is
 // expert 32*(nb/2) + lane%32 of Wg (nb even) or Wnoise (nb odd) with noise,
@@ -180,250 +174,316 @@ __global__ void router_pack(const float* __restrict__ Wg, const float* __restric
   }
 }
 
-// ------------------------------------------------------------------ fused router
-template <typename XT>
-__global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
-  constexpr bool kBf16 = sizeof(XT) == 2;
+// ------------------------------------------------------------------ router GEMM + epilogue
+template <typename XT, bool kFullK>
+__global__ __launch_bounds__(kThreads, 2) void router_gemm(GemmArgs a) {
   constexpr int V = Elem<XT>::kVec;
-  constexpr int kPieces = kBf16 ? 3 : 1;
-  constexpr int kStageElems = kStageBytes / static_cast<int>(sizeof(XT));
+  constexpr int kPieces = sizeof(XT) == 2 ? 3 : 1;
+  constexpr int kStageElems = 128 / static_cast<int>(sizeof(XT));
+  constexpr int MB = kBM / 32;
+  constexpr int kChunks = kBM * 8 / kThreads;
 
-  __shared__ __align__(16) unsigned char sA[2][kRows * kAStride];
-  __shared__ __align__(16) float sC[2][kRows][kCStride];
-  __shared__ float sLv[kRows][kList];
-  __shared__ int sLi[kRows][kList];
-  __shared__ float sM[kRows], sS[kRows];
+  __shared__ __align__(16) unsigned char sA[2][kBM * kAStride];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int row0 = blockIdx.x * kRows;
-  const int T = a.T, D = a.D, E = a.E, K = a.k + 1;
-  const int ncol = a.use_noise ? 2 : 1;   // column blocks per expert block
-  const int EB = (E + 31) / 32;           // expert blocks
-  const int npass = (EB + 3) / 4;
-  const int kstages = a.KS / 4;           // 4 k-steps per stage
-  const int64_t piece_stride = static_cast<int64_t>(a.NB) * a.KS * kWave;
-  const XT* X = static_cast<const XT*>(a.X);
-  const bool vec_ok = (D % V) == 0;
-  const bool check = a.nonfinite != nullptr;
+  const int T = a.T, D = a.D, E = a.E;
+  const int mtiles = (T + kBM - 1) / kBM, ntiles = (a.NB + 7) / 8;
+  const int total = mtiles * ntiles;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int local = blockIdx.x / kXcds;
+  if (local >= per_xcd) return;
+  const int logical = (blockIdx.x % kXcds) * per_xcd + local;
+  if (logical >= total) return;
+  const int m_tile = logical / ntiles, n_tile = logical - m_tile * ntiles;
+  const int r0 = m_tile * kBM;
+  const int rows = min(kBM, T - r0);
+  const int nst = a.KS / 4;
 
-  for (int r = tid; r < kRows; r += kThreads) {
-    sM[r] = -INFINITY;
-    sS[r] = 0.f;
+  const XT* X = static_cast<const XT*>(a.X);
+  const int aseg = tid & 7, arow0 = tid >> 3;
+  const bool vec_ok = (D % V) == 0;
+  u32x4 areg[kChunks];
+  auto load_a = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const XT* row = X + static_cast<int64_t>(r0 + min(arow0 + i * (kThreads / 8), rows - 1)) * D;
+      if constexpr (kFullK) {
+        areg[i] = *reinterpret_cast<const u32x4*>(row + st * kStageElems + aseg * V);
+      } else {
+        const uint4 v = load_row16<XT>(row, st * kStageElems + aseg * V, D, vec_ok);
+        areg[i] = u32x4{v.x, v.y, v.z, v.w};
+      }
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i)
+      *reinterpret_cast<u32x4*>(&sA[buf][(arow0 + i * (kThreads / 8)) * kAStride + aseg * 16]) = areg[i];
+  };
+
+  // wave's two column blocks (clean, raw of one 32-expert block with noise; two clean
+  // blocks without); blocks past NB read a valid block and are never stored
+  const int cb0 = n_tile * 8 + wave * 2;
+  const int64_t piece = static_cast<int64_t>(a.NB) * a.KS * kWave;
+  const u32x4* W0 = a.wfrag + static_cast<int64_t>(min(cb0, a.NB - 1)) * a.KS * kWave + lane;
+  const u32x4* W1 = a.wfrag + static_cast<int64_t>(min(cb0 + 1, a.NB - 1)) * a.KS * kWave + lane;
+
+  f32x16 acc[MB][2];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[m][j][i] = 0.f;
+
+  const int arow = (lane & 31) * kAStride + (lane >> 5) * 16;
+  // B ring: two k-steps ahead
+  u32x4 bq[2][kPieces][2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int p = 0; p < kPieces; ++p) {
+      bq[s][p][0] = W0[p * piece + s * kWave];
+      bq[s][p][1] = W1[p * piece + s * kWave];
+    }
+  load_a(0);
+  store_a(0);
+  __syncthreads();
+
+  const int nks = a.KS;
+  u32x4 af[2][MB];
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    load_a(min(st + 1, nst - 1));
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+      af[0][m] = *reinterpret_cast<const u32x4*>(&sA[buf][m * 32 * kAStride + arow]);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 3) {
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+          af[(ks + 1) & 1][m] =
+              *reinterpret_cast<const u32x4*>(&sA[buf][m * 32 * kAStride + (ks + 1) * 32 + arow]);
+      }
+#pragma unroll
+      for (int p = 0; p < kPieces; ++p)
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+          acc[m][0] = mma<XT>(af[ks & 1][m], bq[ks & 1][p][0], acc[m][0]);
+          acc[m][1] = mma<XT>(af[ks & 1][m], bq[ks & 1][p][1], acc[m][1]);
+        }
+      const int64_t kn = static_cast<int64_t>(min(st * 4 + ks + 2, nks - 1)) * kWave;
+#pragma unroll
+      for (int p = 0; p < kPieces; ++p) {
+        bq[ks & 1][p][0] = W0[p * piece + kn];
+        bq[ks & 1][p][1] = W1[p * piece + kn];
+      }
+    }
+    store_a(buf ^ 1);
+    __syncthreads();
   }
 
-  // X stage loader: 64 rows x 128 B = 512 16-byte chunks, 2 per thread.
-  auto load_stage = [&](int st, uint4 regs[2]) {
+  // ---- epilogue, one 32-row block at a time through a wave-private LDS tile [2][32][kTS]
+  float* Ts = reinterpret_cast<float*>(&sA[0][0]) + wave * (2 * 32 * kTS);
+  const bool check = a.nonfinite != nullptr;
+  const bool full4 = (E % 4) == 0;
+  bool bad = false;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c >> 3, seg = c & 7;
-      const int t = min(row0 + r, T - 1);
-      regs[i] = load_row16<XT>(X + static_cast<int64_t>(t) * D, st * kStageElems + seg * V, D, vec_ok);
-    }
-  };
-  auto store_stage = [&](int buf, const uint4 regs[2]) {
+  for (int m = 0; m < MB; ++m) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c >> 3, seg = c & 7;
-      *reinterpret_cast<uint4*>(&sA[buf][r * kAStride + seg * 16]) = regs[i];
-    }
-  };
-
-  for (int pass = 0; pass < npass; ++pass) {
-    const int eb = pass * 4 + wave;
-    const bool active = eb < EB;
-    f32x16 acc[2][2];
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[m][c][i] = 0.f;
-
-    uint4 regs[2];
-    load_stage(0, regs);
-    __syncthreads();  // previous pass finished with sA / sC
-    store_stage(0, regs);
-    __syncthreads();
-    for (int st = 0; st < kstages; ++st) {
-      const int buf = st & 1;
-      if (st + 1 < kstages) load_stage(st + 1, regs);
-      if (active) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int kg = st * 4 + ks;
-          uint4 af[2];
-#pragma unroll
-          for (int m = 0; m < 2; ++m)
-            af[m] = *reinterpret_cast<const uint4*>(
-                &sA[buf][(m * 32 + (lane & 31)) * kAStride + ks * 32 + (lane >> 5) * 16]);
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            if (c < ncol) {
-              const int nb = eb * ncol + c;
-              const int64_t slot = (static_cast<int64_t>(nb) * a.KS + kg) * kWave + lane;
-#pragma unroll
-              for (int pc = 0; pc < kPieces; ++pc) {
-                const uint4 bf = a.wfrag[slot + pc * piece_stride];
-#pragma unroll
-                for (int m = 0; m < 2; ++m) acc[m][c] = mfma_step<XT>(af[m], bf, acc[m][c]);
-              }
-            }
-          }
-        }
-      }
-      if (st + 1 < kstages) store_stage(buf ^ 1, regs);
-      __syncthreads();
-    }
-
-    // accumulators -> LDS (row, expert-in-pass)
-    if (active) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        if (c < ncol) {
-#pragma unroll
-          for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              sC[c][m * 32 + acc_row(lane, i)][wave * 32 + (lane & 31)] = acc[m][c][i];
-        }
-      }
-    }
-    __syncthreads();
-
-    // epilogue: (row, 4 experts) items -> clean, std, eps, H
-    for (int it = tid; it < kRows * (kExpPass / 4); it += kThreads) {
-      const int r = it >> 5, g = it & 31;
-      const int t = row0 + r;
-      const int e0 = pass * kExpPass + 4 * g;
-      if (t >= T || e0 >= E) continue;
-      float cl[4], sd[4] = {0.f, 0.f, 0.f, 0.f}, ep[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        cl[i] = sC[0][r][4 * g + i];
-        if (a.bias && e0 + i < E) cl[i] += a.bias[e0 + i];
-      }
-      const int64_t base = static_cast<int64_t>(t) * E + e0;
-      const bool full4 = (E % 4 == 0);
-      bool bad = false;
-      if (a.use_noise) {
+      for (int i = 0; i < 16; ++i) Ts[(c * 32 + acc_row(lane, i)) * kTS + (lane & 31)] = acc[m][c][i];
+    if (a.use_noise) {
+      // experts of this wave: one 32-expert block, clean in Ts[0], raw in Ts[1]
+      const int eb = n_tile * 4 + wave;
+#pragma unroll 1
+      for (int h = 0; h < 4; ++h) {
+        const int it = lane + 64 * h;
+        const int row = it >> 3, g4 = it & 7;
+        const int t = r0 + m * 32 + row;
+        const int e0 = eb * 32 + 4 * g4;
+        if (t >= T || e0 >= E) continue;
+        float cl[4], sd[4], ep[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float raw = sC[1][r][4 * g + i];
-          bad |= !isfinite(raw);
+          cl[i] = Ts[row * kTS + 4 * g4 + i];
+          if (a.bias && e0 + i < E) cl[i] += a.bias[e0 + i];
+          const float raw = Ts[(32 + row) * kTS + 4 * g4 + i];
+          bad |= (e0 + i < E) && !(isfinite(raw) && isfinite(cl[i]));
           sd[i] = softplus(raw);
         }
+        const int64_t base = static_cast<int64_t>(t) * E + e0;
         if (a.eps) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) ep[i] = (e0 + i < E) ? a.eps[base + i] : 0.f;
         } else {
           noise4(a.seed, t, e0 >> 2, ep);
         }
-      }
+        float hv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bad |= !isfinite(cl[i]);
-      if (check) note_nonfinite(a.nonfinite, bad);
-      if (full4) {
-        *reinterpret_cast<float4*>(a.clean + base) = make_float4(cl[0], cl[1], cl[2], cl[3]);
-        if (a.use_noise)
+        for (int i = 0; i < 4; ++i) hv[i] = fmaf(sd[i], ep[i], cl[i]);
+        if (full4) {
+          *reinterpret_cast<float4*>(a.clean + base) = make_float4(cl[0], cl[1], cl[2], cl[3]);
           *reinterpret_cast<float4*>(a.std_out + base) = make_float4(sd[0], sd[1], sd[2], sd[3]);
-      } else {
-        for (int i = 0; i < 4 && e0 + i < E; ++i) {
-          a.clean[base + i] = cl[i];
-          if (a.use_noise) a.std_out[base + i] = sd[i];
-        }
-      }
+          *reinterpret_cast<float4*>(a.H + base) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+        } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sC[0][r][4 * g + i] = a.use_noise ? fmaf(sd[i], ep[i], cl[i]) : cl[i];
-    }
-    __syncthreads();
-
-    // merge this pass's scores into each row's running top-(k+1) list
-    for (int rr = 0; rr < kRows / 4; ++rr) {
-      const int r = wave * (kRows / 4) + rr;
-      if (row0 + r >= T) break;
-      float v[3];
-      int ix[3];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int e = pass * kExpPass + lane + 64 * h;
-        const float s = sC[0][r][lane + 64 * h];
-        const bool ok = e < E && !isnan(s);
-        v[h] = ok ? s : -INFINITY;
-        ix[h] = ok ? e : kNone;
-      }
-      if (pass > 0 && lane < K) {
-        v[2] = sLv[r][lane];
-        ix[2] = sLi[r][lane];
-      } else {
-        v[2] = -INFINITY;
-        ix[2] = kNone;
-      }
-      if (a.switch_gate) {  // online softmax statistics of the row
-        const float cm = wave_max(fmaxf(v[0], v[1]));
-        const float cs = wave_sum((ix[0] != kNone ? expf(v[0] - cm) : 0.f) +
-                                  (ix[1] != kNone ? expf(v[1] - cm) : 0.f));
-        if (lane == 0) {
-          const float m0 = sM[r], s0 = sS[r];
-          const float mn = fmaxf(m0, cm);
-          sS[r] = (m0 == -INFINITY ? 0.f : s0 * expf(m0 - mn)) + cs * expf(cm - mn);
-          sM[r] = mn;
-        }
-      }
-      float keep_v = -INFINITY;
-      int keep_i = kNone;
-      for (int s = 0; s < K; ++s) {
-        int bsel = 0;
-        if (better(v[1], ix[1], v[bsel], ix[bsel])) bsel = 1;
-        if (better(v[2], ix[2], v[bsel], ix[bsel])) bsel = 2;
-        float bv = v[bsel];
-        int bi = ix[bsel];
-        wave_argmax(bv, bi);
-        if (bi != kNone) {
-#pragma unroll
-          for (int h = 0; h < 3; ++h)
-            if (ix[h] == bi) {
-              v[h] = -INFINITY;
-              ix[h] = kNone;
+          for (int i = 0; i < 4; ++i)
+            if (e0 + i < E) {
+              a.clean[base + i] = cl[i];
+              a.std_out[base + i] = sd[i];
+              a.H[base + i] = hv[i];
             }
         }
-        if (lane == s) {
-          keep_v = bv;
-          keep_i = bi;
+      }
+    } else {
+      // experts of this wave: two consecutive 32-expert blocks, both clean
+#pragma unroll 1
+      for (int h = 0; h < 8; ++h) {
+        const int it = lane + 64 * h;
+        const int row = it >> 4, g = it & 15;
+        const int c = g >> 3, g4 = g & 7;
+        const int t = r0 + m * 32 + row;
+        const int e0 = (cb0 + c) * 32 + 4 * g4;
+        if (t >= T || e0 >= E) continue;
+        float cl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          cl[i] = Ts[(c * 32 + row) * kTS + 4 * g4 + i];
+          if (a.bias && e0 + i < E) cl[i] += a.bias[e0 + i];
+          bad |= (e0 + i < E) && !isfinite(cl[i]);
+        }
+        const int64_t base = static_cast<int64_t>(t) * E + e0;
+        if (full4) {
+          *reinterpret_cast<float4*>(a.clean + base) = make_float4(cl[0], cl[1], cl[2], cl[3]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (e0 + i < E) a.clean[base + i] = cl[i];
         }
       }
-      if (lane < K) {
-        sLv[r][lane] = keep_v;
-        sLi[r][lane] = keep_i;
-      }
     }
-    __syncthreads();
   }
+  if (check) note_nonfinite(a.nonfinite, bad);
+}
 
-  // final outputs per row
-  for (int rr = 0; rr < kRows / 4; ++rr) {
-    const int r = wave * (kRows / 4) + rr;
-    const int t = row0 + r;
-    if (t >= T) break;
-    const int k = a.k;
-    const float v0 = sLv[r][0];
-    const float vj = lane < k ? sLv[r][lane] : -INFINITY;
-    float g;
-    if (a.switch_gate) {
-      g = expf(vj - sM[r]) / sS[r];
-    } else {
-      const float ej = lane < k ? expf(vj - v0) : 0.f;
-      g = ej / wave_sum(ej);
+// ------------------------------------------------------------------ row selection
+// Candidates compare by (score descending, index ascending): a total order, so the
+// selected set and its order are unique. NaN scores never win.
+template <int KL>
+__device__ __forceinline__ void list_insert(float (&v)[KL], int (&ix)[KL], float x, int i) {
+  if (!better(x, i, v[KL - 1], ix[KL - 1])) return;
+  v[KL - 1] = x;
+  ix[KL - 1] = i;
+#pragma unroll
+  for (int j = KL - 1; j > 0; --j) {
+    if (better(v[j], ix[j], v[j - 1], ix[j - 1])) {
+      const float tv = v[j];
+      v[j] = v[j - 1];
+      v[j - 1] = tv;
+      const int ti = ix[j];
+      ix[j] = ix[j - 1];
+      ix[j - 1] = ti;
     }
-    if (lane < k) {
-      a.ids[static_cast<int64_t>(t) * k + lane] = sLi[r][lane];
-      a.gates[static_cast<int64_t>(t) * k + lane] = g;
+  }
+}
+
+// Merge the sorted list with the partner lane's (xor off): the elementwise best of
+// a[j] and b[KL-1-j] is the top KL of the union as a bitonic sequence, which a
+// bitonic network then sorts.
+template <int KL>
+__device__ __forceinline__ void list_merge(float (&v)[KL], int (&ix)[KL], int off) {
+  float pv[KL];
+  int pi[KL];
+#pragma unroll
+  for (int j = 0; j < KL; ++j) {
+    pv[j] = __shfl_xor(v[j], off);
+    pi[j] = __shfl_xor(ix[j], off);
+  }
+#pragma unroll
+  for (int j = 0; j < KL; ++j) {
+    const float bv = pv[KL - 1 - j];
+    const int bi = pi[KL - 1 - j];
+    if (better(bv, bi, v[j], ix[j])) {
+      v[j] = bv;
+      ix[j] = bi;
     }
-    if (a.row_stats && lane == 0) {
-      a.row_stats[2 * static_cast<int64_t>(t)] = sLv[r][k - 1];
-      a.row_stats[2 * static_cast<int64_t>(t) + 1] = sLv[r][k];
+  }
+#pragma unroll
+  for (int w = KL / 2; w >= 1; w >>= 1)
+#pragma unroll
+    for (int j = 0; j < KL; ++j)
+      if ((j & w) == 0 && better(v[j + w], ix[j + w], v[j], ix[j])) {
+        const float tv = v[j];
+        v[j] = v[j + w];
+        v[j + w] = tv;
+        const int ti = ix[j];
+        ix[j] = ix[j + w];
+        ix[j + w] = ti;
+      }
+}
+
+template <int KL>
+__global__ __launch_bounds__(kThreads) void router_select(SelectArgs a) {
+  const int tid = threadIdx.x;
+  const int sub = tid & 7;                       // lane within the row group
+  const int t = blockIdx.x * (kThreads / 8) + (tid >> 3);
+  const bool live = t < a.T;
+  const int E = a.E, k = a.k;
+  const float* row = a.score + static_cast<int64_t>(live ? t : 0) * E;
+  float v[KL];
+  int ix[KL];
+#pragma unroll
+  for (int j = 0; j < KL; ++j) {
+    v[j] = -INFINITY;
+    ix[j] = kNone;
+  }
+  if (live)
+    for (int e = sub; e < E; e += 8) {
+      const float x = row[e];
+      if (!isnan(x)) list_insert<KL>(v, ix, x, e);
     }
+  list_merge<KL>(v, ix, 1);
+  list_merge<KL>(v, ix, 2);
+  list_merge<KL>(v, ix, 4);
+  // every lane of the group now holds the row's top KL
+  float gsum = 0.f;
+  if (a.switch_gate) {
+    float s = 0.f;
+    if (live)
+      for (int e = sub; e < E; e += 8) {
+        const float x = row[e];
+        if (!isnan(x)) s += expf(x - v[0]);
+      }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    gsum = s;
+  } else {
+#pragma unroll
+    for (int j = 0; j < KL; ++j)
+      if (j < k) gsum += expf(v[j] - v[0]);
+  }
+  if (!live) return;
+  const int64_t o = static_cast<int64_t>(t) * k;
+#pragma unroll
+  for (int j = 0; j < KL; ++j) {
+    if (j < k && (j & 7) == sub) {
+      a.ids[o + j] = ix[j];
+      a.gates[o + j] = a.switch_gate ? expf(v[j] - v[0]) / gsum : expf(v[j] - v[0]) / gsum;
+    }
+  }
+  if (a.row_stats && sub == 0) {
+    float vk = v[0], vk1 = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+      if (j == k - 1) vk = v[j];
+      if (j == k) vk1 = v[j];
+    }
+    a.row_stats[2 * static_cast<int64_t>(t)] = vk;
+    a.row_stats[2 * static_cast<int64_t>(t) + 1] = vk1;
   }
 }
 
@@ -434,57 +494,78 @@ static int router_ks(const Dims& d) {
   const int stage = d.dtype == MOE_BF16 ? 64 : 32;  // elements per 128-byte stage
   return ceil_div(d.D, stage) * 4;
 }
-static int router_nb(const Dims& d) {
-  const bool noise = d.gating == MOE_GATE_NOISY_TOPK && d.noise;
-  return ceil_div(d.E, 32) * (noise ? 2 : 1);
+static bool router_noise(const Dims& d) { return d.gating == MOE_GATE_NOISY_TOPK && d.noise; }
+static int router_nb(const Dims& d) { return ceil_div(d.E, 32) * (router_noise(d) ? 2 : 1); }
+static size_t router_wbytes(const Dims& d) {
+  const size_t pieces = d.dtype == MOE_BF16 ? 3 : 1;
+  return align256(pieces * router_nb(d) * static_cast<size_t>(router_ks(d)) * kWave * 16);
 }
 
 size_t route_workspace(const Dims& d) {
-  const size_t pieces = d.dtype == MOE_BF16 ? 3 : 1;
-  return align256(pieces * router_nb(d) * static_cast<size_t>(router_ks(d)) * kWave * 16);
+  size_t b = router_wbytes(d);
+  if (router_noise(d)) b += align256(static_cast<size_t>(d.T) * d.E * sizeof(float));
+  return b;
 }
 
 moe_status route_launch(const Dims& d, const moe_problem* p, const void* X, const float* Wg,
                         const float* Wnoise, const float* bias, const float* eps, int32_t* ids,
                         float* gates, float* clean, float* noise_std, float* row_stats,
                         void* ws, int* nonfinite, hipStream_t stream) {
-  const bool noise = d.gating == MOE_GATE_NOISY_TOPK && d.noise;
+  const bool noise = router_noise(d);
   const int NB = router_nb(d), KS = router_ks(d);
   uint4* wfrag = static_cast<uint4*>(ws);
+  float* H = noise ? reinterpret_cast<float*>(static_cast<char*>(ws) + router_wbytes(d)) : nullptr;
   const int64_t items = static_cast<int64_t>(NB) * KS * kWave;
-  const int pb = 256;
-  const int pgrid = static_cast<int>(ceil_div64(items, pb));
+  const int pgrid = static_cast<int>(ceil_div64(items, 256));
   if (d.dtype == MOE_BF16)
-    router_pack<true><<<pgrid, pb, 0, stream>>>(Wg, noise ? Wnoise : nullptr, d.D, d.E, noise, NB, KS, wfrag);
+    router_pack<true><<<pgrid, 256, 0, stream>>>(Wg, noise ? Wnoise : nullptr, d.D, d.E, noise, NB, KS, wfrag);
   else
-    router_pack<false><<<pgrid, pb, 0, stream>>>(Wg, noise ? Wnoise : nullptr, d.D, d.E, noise, NB, KS, wfrag);
+    router_pack<false><<<pgrid, 256, 0, stream>>>(Wg, noise ? Wnoise : nullptr, d.D, d.E, noise, NB, KS, wfrag);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
 
-  RouterArgs a;
-  a.X = X;
-  a.wfrag = wfrag;
-  a.bias = bias;
-  a.eps = noise ? eps : nullptr;
-  a.ids = ids;
-  a.gates = gates;
-  a.clean = clean;
-  a.std_out = noise ? noise_std : nullptr;
-  a.row_stats = row_stats;
-  a.nonfinite = nonfinite;
-  a.seed = p->seed;
-  a.T = d.T;
-  a.D = d.D;
-  a.E = d.E;
-  a.k = d.k;
-  a.NB = NB;
-  a.KS = KS;
-  a.use_noise = noise ? 1 : 0;
-  a.switch_gate = d.gating == MOE_GATE_SWITCH_TOP1 ? 1 : 0;
-  const int grid = ceil_div(d.T, kRows);
-  if (d.dtype == MOE_BF16)
-    router_kernel<uint16_t><<<grid, kThreads, 0, stream>>>(a);
-  else
-    router_kernel<float><<<grid, kThreads, 0, stream>>>(a);
+  GemmArgs g;
+  g.X = X;
+  g.wfrag = reinterpret_cast<const u32x4*>(wfrag);
+  g.bias = bias;
+  g.eps = noise ? eps : nullptr;
+  g.clean = clean;
+  g.std_out = noise ? noise_std : nullptr;
+  g.H = H;
+  g.nonfinite = nonfinite;
+  g.seed = p->seed;
+  g.T = d.T;
+  g.D = d.D;
+  g.E = d.E;
+  g.NB = NB;
+  g.KS = KS;
+  g.use_noise = noise ? 1 : 0;
+  const int64_t tiles = static_cast<int64_t>(ceil_div(d.T, kBM)) * ceil_div(NB, 8);
+  const int grid = static_cast<int>(ceil_div64(tiles, kXcds) * kXcds);
+  const bool full = d.D % (d.dtype == MOE_BF16 ? 64 : 32) == 0;
+  if (d.dtype == MOE_BF16) {
+    if (full) router_gemm<uint16_t, true><<<grid, kThreads, 0, stream>>>(g);
+    else router_gemm<uint16_t, false><<<grid, kThreads, 0, stream>>>(g);
+  } else {
+    if (full) router_gemm<float, true><<<grid, kThreads, 0, stream>>>(g);
+    else router_gemm<float, false><<<grid, kThreads, 0, stream>>>(g);
+  }
+  if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+
+  SelectArgs sa;
+  sa.score = noise ? H : clean;
+  sa.ids = ids;
+  sa.gates = gates;
+  sa.row_stats = row_stats;
+  sa.T = d.T;
+  sa.E = d.E;
+  sa.k = d.k;
+  sa.switch_gate = d.gating == MOE_GATE_SWITCH_TOP1 ? 1 : 0;
+  const int sgrid = ceil_div(d.T, kThreads / 8);
+  const int need = d.k + 1;
+  if (need <= 2) router_select<2><<<sgrid, kThreads, 0, stream>>>(sa);
+  else if (need <= 4) router_select<4><<<sgrid, kThreads, 0, stream>>>(sa);
+  else if (need <= 8) router_select<8><<<sgrid, kThreads, 0, stream>>>(sa);
+  else router_select<16><<<sgrid, kThreads, 0, stream>>>(sa);
   return launch_status();
 }
 

@@ -118,4 +118,5 @@ def test_sizes_scale(m):
     assert m.moe_packed_weight_bytes(p, 1) == 256 * 1024 * 4096 * 2
     assert m.moe_packed_weight_bytes(p, 2) == 256 * 4096 * 1024 * 2
     assert m.moe_packed_weight_bytes(p, 3) == 0
-    assert m.moe_workspace_size(p, m.MOE_WS_ROUTE) == 3 * 1024 * 512 * 2
+    # router: three bf16 pieces of [Wg | Wnoise] plus the fp32 noisy scores [T,E]
+    assert m.moe_workspace_size(p, m.MOE_WS_ROUTE) == 3 * 1024 * 512 * 2 + 65536 * 256 * 4
