@@ -29,6 +29,24 @@ if ROOT not in sys.path:
 
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_top2_bf16_traffic.json")
+GEMM_SOURCES = [os.path.join(ROOT, "sparsely_gated_mixture_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per grouped-GEMM launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated); None if absent, for another workload,
+    or taken on a different version of the kernel source."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        src = b"".join(open(p, "rb").read() for p in GEMM_SOURCES)
+    except OSError:
+        return None
+    if t.get("workload") != workload or t.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return float(t["bytes_per_launch"])
 
 
 def _dev(torch, a):
@@ -171,7 +189,8 @@ def main():
                    "capacity": moe.moe_capacity(p), "accepted_rows": A,
                    "dropped": w.T * w.k - A, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": "grouped_gemm", "achieved": achieved,
-                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": measured_traffic(w.name), "traffic_unit": "bytes per launch",
                      "flops_per_launch": gemm_flops, "avg_launch_ms": gemm_ms},
         "stages_ms": per,
         "dispatch_GBps": disp_bytes / (per["dispatch"] * 1e-3) / 1e9,

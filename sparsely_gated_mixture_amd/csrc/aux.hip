@@ -46,6 +46,7 @@ struct AuxArgs {
 __device__ __forceinline__ float phi(float z) { return 0.5f * erfcf(-z * 0.70710678118654752f); }
 
 __global__ __launch_bounds__(kThreads) void aux_partial(AuxArgs a) {
+  constexpr int kU = 8;  // rows in flight per thread in the column pass
   __shared__ float sM[kRows], sS[kRows];
   __shared__ float sR0[kRows], sR1[kRows];
   __shared__ int sId[kRows * MOE_MAX_K];
@@ -59,22 +60,39 @@ __global__ __launch_bounds__(kThreads) void aux_partial(AuxArgs a) {
     sId[i] = a.ids[static_cast<int64_t>(t0) * k + i];
     sG[i] = a.gates[static_cast<int64_t>(t0) * k + i];
   }
-  for (int r = tid; r < nr; r += kThreads) {
-    if (a.use_noise) {
+  if (a.use_noise)
+    for (int r = tid; r < nr; r += kThreads) {
       sR0[r] = a.row_stats[2 * static_cast<int64_t>(t0 + r)];
       sR1[r] = a.row_stats[2 * static_cast<int64_t>(t0 + r) + 1];
     }
-  }
+  // per-row softmax statistics of clean: one wave per row
+  const bool vec = (E % 4) == 0;
   for (int r = wave; r < nr; r += kThreads / 64) {
     const float* row = a.clean + static_cast<int64_t>(t0 + r) * E;
-    float m = -INFINITY;
-    for (int e = lane; e < E; e += 64) m = fmaxf(m, row[e]);
+    float m = -INFINITY, s = 0.f;
+    if (vec) {
+      for (int e = lane * 4; e < E; e += 256) {
+        const float4 x = *reinterpret_cast<const float4*>(row + e);
+        const float mx = fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w));
+        const float mn = fmaxf(m, mx);
+        s = s * expf(m - mn) + expf(x.x - mn) + expf(x.y - mn) + expf(x.z - mn) + expf(x.w - mn);
+        m = mn;
+      }
+    } else {
+      for (int e = lane; e < E; e += 64) {
+        const float x = row[e];
+        const float mn = fmaxf(m, x);
+        s = s * expf(m - mn) + expf(x - mn);
+        m = mn;
+      }
+    }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    float s = 0.f;
-    for (int e = lane; e < E; e += 64) s += expf(row[e] - m);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float om = __shfl_xor(m, off), os = __shfl_xor(s, off);
+      const float mn = fmaxf(m, om);
+      s = (m == -INFINITY ? 0.f : s * expf(m - mn)) + (om == -INFINITY ? 0.f : os * expf(om - mn));
+      m = mn;
+    }
     if (lane == 0) {
       sM[r] = m;
       sS[r] = s;
@@ -82,27 +100,38 @@ __global__ __launch_bounds__(kThreads) void aux_partial(AuxArgs a) {
   }
   __syncthreads();
 
+  // column pass: thread per expert, kU rows of loads in flight
   const int64_t plane = static_cast<int64_t>(a.nblk) * E;
   for (int e = tid; e < E; e += kThreads) {
     float imp = 0.f, load = 0.f, pb = 0.f;
-    for (int r = 0; r < nr; ++r) {
-      const int64_t ix = static_cast<int64_t>(t0 + r) * E + e;
-      const float c = a.clean[ix];
-      bool inside = false;
-      for (int j = 0; j < k; ++j)
-        if (sId[r * k + j] == e) {
-          inside = true;
-          imp += sG[r * k + j];
+    for (int r0 = 0; r0 < nr; r0 += kU) {
+      float c[kU], sd[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int r = min(r0 + u, nr - 1);
+        const int64_t ix = static_cast<int64_t>(t0 + r) * E + e;
+        c[u] = a.clean[ix];
+        sd[u] = a.use_noise ? a.std_in[ix] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int r = r0 + u;
+        if (r >= nr) break;
+        bool inside = false;
+        for (int j = 0; j < k; ++j)
+          if (sId[r * k + j] == e) {
+            inside = true;
+            imp += sG[r * k + j];
+          }
+        pb += expf(c[u] - sM[r]) / sS[r];
+        if (a.use_noise) {
+          const float thr = inside ? sR1[r] : sR0[r];
+          const float diff = c[u] - thr;
+          float pr;
+          if (sd[u] > 0.f) pr = phi(diff / sd[u]);
+          else pr = diff > 0.f ? 1.f : (diff == 0.f ? 0.5f : 0.f);
+          load += pr;
         }
-      pb += expf(c - sM[r]) / sS[r];
-      if (a.use_noise) {
-        const float thr = inside ? sR1[r] : sR0[r];
-        const float sd = a.std_in[ix];
-        const float diff = c - thr;
-        float p;
-        if (sd > 0.f) p = phi(diff / sd);
-        else p = diff > 0.f ? 1.f : (diff == 0.f ? 0.5f : 0.f);
-        load += p;
       }
     }
     const int64_t o = static_cast<int64_t>(blockIdx.x) * E + e;
@@ -118,10 +147,23 @@ __global__ __launch_bounds__(kThreads) void aux_reduce(AuxArgs a) {
   const int e = blockIdx.x * 32 + el;
   const int64_t plane = static_cast<int64_t>(a.nblk) * a.E;
   double acc[3] = {0.0, 0.0, 0.0};
-  if (e < a.E)
-    for (int b = bl; b < a.nblk; b += 8)
+  if (e < a.E) {
+    int b = bl;
+    for (; b + 24 < a.nblk; b += 32) {  // four blocks of loads in flight, summed in order
+      float v[3][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) v[q][u] = a.partial[q * plane + static_cast<int64_t>(b + 8 * u) * a.E + e];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) acc[q] += v[q][u];
+    }
+    for (; b < a.nblk; b += 8)
 #pragma unroll
       for (int q = 0; q < 3; ++q) acc[q] += a.partial[q * plane + static_cast<int64_t>(b) * a.E + e];
+  }
 #pragma unroll
   for (int q = 0; q < 3; ++q) s[q][bl][el] = acc[q];
   __syncthreads();

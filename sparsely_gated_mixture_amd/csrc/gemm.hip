@@ -208,11 +208,15 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
           af[(ks + 1) & 1][m] =
               *reinterpret_cast<const u32x4*>(&sA[buf][m * 32 * kAStride + (ks + 1) * 32 + arow]);
       }
+      // raised priority while this wave's MFMAs issue: a wave with a k-step's operands
+      // ready keeps the matrix unit busy ahead of waves still waiting on loads
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
         acc[m][0] = mma<T>(af[ks & 1][m], bq[ks][0], acc[m][0]);
         acc[m][1] = mma<T>(af[ks & 1][m], bq[ks][1], acc[m][1]);
       }
+      __builtin_amdgcn_s_setprio(0);
       const int64_t kn = static_cast<int64_t>(stn * 4 + ks) * kWave;
       bq[ks][0] = W0[kn];
       bq[ks][1] = W1[kn];

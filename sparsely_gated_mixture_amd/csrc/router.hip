@@ -266,6 +266,7 @@ __global__ __launch_bounds__(kThreads, 2) void router_gemm(GemmArgs a) {
           af[(ks + 1) & 1][m] =
               *reinterpret_cast<const u32x4*>(&sA[buf][m * 32 * kAStride + (ks + 1) * 32 + arow]);
       }
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int p = 0; p < kPieces; ++p)
 #pragma unroll
@@ -273,6 +274,7 @@ __global__ __launch_bounds__(kThreads, 2) void router_gemm(GemmArgs a) {
           acc[m][0] = mma<XT>(af[ks & 1][m], bq[ks & 1][p][0], acc[m][0]);
           acc[m][1] = mma<XT>(af[ks & 1][m], bq[ks & 1][p][1], acc[m][1]);
         }
+      __builtin_amdgcn_s_setprio(0);
       const int64_t kn = static_cast<int64_t>(min(st * 4 + ks + 2, nks - 1)) * kWave;
 #pragma unroll
       for (int p = 0; p < kPieces; ++p) {
