@@ -65,27 +65,9 @@ __global__ __launch_bounds__(kThreads) void aux_partial(AuxArgs a) {
       sR0[r] = a.row_stats[2 * static_cast<int64_t>(t0 + r)];
       sR1[r] = a.row_stats[2 * static_cast<int64_t>(t0 + r) + 1];
     }
-  // per-row softmax statistics of clean: one wave per row
+  // per-row softmax statistics of clean: one wave per row, 4 rows of loads in flight
   const bool vec = (E % 4) == 0;
-  for (int r = wave; r < nr; r += kThreads / 64) {
-    const float* row = a.clean + static_cast<int64_t>(t0 + r) * E;
-    float m = -INFINITY, s = 0.f;
-    if (vec) {
-      for (int e = lane * 4; e < E; e += 256) {
-        const float4 x = *reinterpret_cast<const float4*>(row + e);
-        const float mx = fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w));
-        const float mn = fmaxf(m, mx);
-        s = s * expf(m - mn) + expf(x.x - mn) + expf(x.y - mn) + expf(x.z - mn) + expf(x.w - mn);
-        m = mn;
-      }
-    } else {
-      for (int e = lane; e < E; e += 64) {
-        const float x = row[e];
-        const float mn = fmaxf(m, x);
-        s = s * expf(m - mn) + expf(x - mn);
-        m = mn;
-      }
-    }
+  auto row_stats4 = [&](int r, float& m, float& s) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       const float om = __shfl_xor(m, off), os = __shfl_xor(s, off);
@@ -96,6 +78,38 @@ __global__ __launch_bounds__(kThreads) void aux_partial(AuxArgs a) {
     if (lane == 0) {
       sM[r] = m;
       sS[r] = s;
+    }
+  };
+  if (vec && E <= 256) {
+    // one float4 per lane per row
+    for (int rb = wave * 4; rb < nr; rb += 16) {
+      float4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = min(rb + u, nr - 1);
+        x[u] = lane * 4 < E ? *reinterpret_cast<const float4*>(a.clean + static_cast<int64_t>(t0 + r) * E + lane * 4)
+                            : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (rb + u >= nr) break;
+        float m = fmaxf(fmaxf(x[u].x, x[u].y), fmaxf(x[u].z, x[u].w));
+        float s = m == -INFINITY ? 0.f
+                                 : expf(x[u].x - m) + expf(x[u].y - m) + expf(x[u].z - m) + expf(x[u].w - m);
+        row_stats4(rb + u, m, s);
+      }
+    }
+  } else {
+    for (int r = wave; r < nr; r += kThreads / 64) {
+      const float* row = a.clean + static_cast<int64_t>(t0 + r) * E;
+      float m = -INFINITY, s = 0.f;
+      for (int e = lane; e < E; e += 64) {
+        const float x = row[e];
+        const float mn = fmaxf(m, x);
+        s = s * expf(m - mn) + expf(x - mn);
+        m = mn;
+      }
+      row_stats4(r, m, s);
     }
   }
   __syncthreads();

@@ -166,12 +166,24 @@ __global__ __launch_bounds__(kThreads) void dispatch_place(
   if (vec_ok) {
     const int nv = D / V;  // 16-byte vectors per row
     const int items = ntok * nv;
-    for (int it = tid; it < items; it += kThreads) {
-      const int tl = it / nv, c = it - tl * nv;
-      const uint4 v = reinterpret_cast<const uint4*>(X + static_cast<int64_t>(t0 + tl) * D)[c];
-      for (int j = 0; j < k; ++j) {
-        const int row = sRow[tl * k + j];
-        if (row >= 0) reinterpret_cast<uint4*>(Xd + static_cast<int64_t>(row) * D)[c] = v;
+    constexpr int kU = 4;  // vectors in flight per thread
+    for (int it0 = tid; it0 < items; it0 += kThreads * kU) {
+      uint4 v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int it = min(it0 + u * kThreads, items - 1);
+        const int tl = it / nv, c = it - tl * nv;
+        v[u] = reinterpret_cast<const uint4*>(X + static_cast<int64_t>(t0 + tl) * D)[c];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int it = it0 + u * kThreads;
+        if (it >= items) break;
+        const int tl = it / nv, c = it - tl * nv;
+        for (int j = 0; j < k; ++j) {
+          const int row = sRow[tl * k + j];
+          if (row >= 0) reinterpret_cast<uint4*>(Xd + static_cast<int64_t>(row) * D)[c] = v[u];
+        }
       }
     }
   } else {

@@ -442,11 +442,26 @@ __global__ __launch_bounds__(kThreads) void router_select(SelectArgs a) {
     v[j] = -INFINITY;
     ix[j] = kNone;
   }
-  if (live)
-    for (int e = sub; e < E; e += 8) {
-      const float x = row[e];
-      if (!isnan(x)) list_insert<KL>(v, ix, x, e);
+  if (live) {
+    if ((E % 4) == 0) {
+      // lane sub reads 16 bytes at 4*sub + 32*i: the row group reads 128 contiguous bytes
+      for (int e0 = 4 * sub; e0 < E; e0 += 64) {
+        const float4 x0 = *reinterpret_cast<const float4*>(row + e0);
+        const bool two = e0 + 32 < E;
+        const float4 x1 = two ? *reinterpret_cast<const float4*>(row + e0 + 32)
+                              : make_float4(NAN, NAN, NAN, NAN);
+        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (!isnan(xs[i])) list_insert<KL>(v, ix, xs[i], e0 + (i & 3) + 32 * (i >> 2));
+      }
+    } else {
+      for (int e = sub; e < E; e += 8) {
+        const float x = row[e];
+        if (!isnan(x)) list_insert<KL>(v, ix, x, e);
+      }
     }
+  }
   list_merge<KL>(v, ix, 1);
   list_merge<KL>(v, ix, 2);
   list_merge<KL>(v, ix, 4);
