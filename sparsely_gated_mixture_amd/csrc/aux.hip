@@ -14,9 +14,15 @@
 // otherwise its k-th; both are the router's row_stats.
 //
 // Deterministic reductions only (fixed order, no float atomics):
-//   aux_partial  block b: 128 tokens; per-row softmax statistics of clean
-//                (wave reductions), then thread-per-expert column sums of the
-//                gates, P(x,i) and softmax(clean) over the block's rows.
+//   aux_rows     (E a multiple of 4, E <= 1024) block b: 64 tokens, one wave
+//                per row at a time holding the whole row of clean (and std) as
+//                float4 per lane: the row's softmax statistics come from two
+//                wave reductions over registers, so clean is read once; each
+//                lane keeps running sums for its experts over the wave's rows,
+//                and the four waves are added in fixed order at the end.
+//   aux_partial  (any other E) block b: 64 tokens; per-row softmax statistics
+//                of clean (wave reductions), then thread-per-expert column
+//                sums of the gates, P(x,i) and softmax(clean) over the rows.
 //   aux_reduce   32 experts x 8 partial lanes per block, strided fixed-order
 //                sums over blocks, then a fixed tree; fp64.
 //   aux_final    one block: CV^2 (two-pass, fp64), Switch term, diagnostics.
@@ -25,7 +31,7 @@
 namespace moe {
 namespace {
 
-constexpr int kRows = 128;
+constexpr int kRows = 64;
 constexpr int kThreads = 256;
 
 struct AuxArgs {
@@ -41,6 +47,7 @@ struct AuxArgs {
   float* partial;  // [3][nblk][E]
   double* sums;    // [3][E]
   int T, E, k, C, nblk, use_noise;
+  int vec;  // E % 4 == 0 and clean / std 16-byte aligned: float4 row reads
 };
 
 __device__ __forceinline__ float phi(float z) { return 0.5f * erfcf(-z * 0.70710678118654752f); }
@@ -65,9 +72,8 @@ __global__ __launch_bounds__(kThreads) void aux_partial(AuxArgs a) {
       sR0[r] = a.row_stats[2 * static_cast<int64_t>(t0 + r)];
       sR1[r] = a.row_stats[2 * static_cast<int64_t>(t0 + r) + 1];
     }
-  // per-row softmax statistics of clean: one wave per row, 4 rows of loads in flight
-  const bool vec = (E % 4) == 0;
-  auto row_stats4 = [&](int r, float& m, float& s) {
+  // per-row softmax statistics of clean: one wave per row
+  auto row_stats = [&](int r, float& m, float& s) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       const float om = __shfl_xor(m, off), os = __shfl_xor(s, off);
@@ -80,37 +86,16 @@ __global__ __launch_bounds__(kThreads) void aux_partial(AuxArgs a) {
       sS[r] = s;
     }
   };
-  if (vec && E <= 256) {
-    // one float4 per lane per row
-    for (int rb = wave * 4; rb < nr; rb += 16) {
-      float4 x[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = min(rb + u, nr - 1);
-        x[u] = lane * 4 < E ? *reinterpret_cast<const float4*>(a.clean + static_cast<int64_t>(t0 + r) * E + lane * 4)
-                            : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (rb + u >= nr) break;
-        float m = fmaxf(fmaxf(x[u].x, x[u].y), fmaxf(x[u].z, x[u].w));
-        float s = m == -INFINITY ? 0.f
-                                 : expf(x[u].x - m) + expf(x[u].y - m) + expf(x[u].z - m) + expf(x[u].w - m);
-        row_stats4(rb + u, m, s);
-      }
+  for (int r = wave; r < nr; r += kThreads / 64) {
+    const float* row = a.clean + static_cast<int64_t>(t0 + r) * E;
+    float m = -INFINITY, s = 0.f;
+    for (int e = lane; e < E; e += 64) {
+      const float x = row[e];
+      const float mn = fmaxf(m, x);
+      s = s * expf(m - mn) + expf(x - mn);
+      m = mn;
     }
-  } else {
-    for (int r = wave; r < nr; r += kThreads / 64) {
-      const float* row = a.clean + static_cast<int64_t>(t0 + r) * E;
-      float m = -INFINITY, s = 0.f;
-      for (int e = lane; e < E; e += 64) {
-        const float x = row[e];
-        const float mn = fmaxf(m, x);
-        s = s * expf(m - mn) + expf(x - mn);
-        m = mn;
-      }
-      row_stats4(r, m, s);
-    }
+    row_stats(r, m, s);
   }
   __syncthreads();
 
@@ -152,6 +137,156 @@ __global__ __launch_bounds__(kThreads) void aux_partial(AuxArgs a) {
     a.partial[o] = imp;
     a.partial[plane + o] = load;
     a.partial[2 * plane + o] = pb;
+  }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// NV float4 chunks per lane per row: lane l holds experts 256*v + 4*l + i.
+template <int NV>
+__global__ __launch_bounds__(kThreads) void aux_rows(AuxArgs a) {
+  constexpr int kWaves = kThreads / 64;
+  constexpr int U = 4 / NV;  // rows of loads in flight per wave
+  __shared__ float sR0[kRows], sR1[kRows];
+  __shared__ int sId[kRows * MOE_MAX_K];
+  __shared__ float sG[kRows * MOE_MAX_K];
+  __shared__ float4 sRed[kWaves - 1][3][NV * 64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int t0 = blockIdx.x * kRows;
+  const int nr = min(kRows, a.T - t0);
+  const int E = a.E, k = a.k;
+  const bool noise = a.use_noise != 0;
+
+  for (int i = tid; i < nr * k; i += kThreads) {
+    sId[i] = a.ids[static_cast<int64_t>(t0) * k + i];
+    sG[i] = a.gates[static_cast<int64_t>(t0) * k + i];
+  }
+  if (noise)
+    for (int r = tid; r < nr; r += kThreads) {
+      sR0[r] = a.row_stats[2 * static_cast<int64_t>(t0 + r)];
+      sR1[r] = a.row_stats[2 * static_cast<int64_t>(t0 + r) + 1];
+    }
+  __syncthreads();
+
+  float imp[NV][4], lsum[NV][4], pb[NV][4];
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) imp[v][i] = lsum[v][i] = pb[v][i] = 0.f;
+
+  for (int rb = wave; rb < nr; rb += kWaves * U) {
+    float4 c[U][NV], sd[U][NV];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = min(rb + kWaves * u, nr - 1);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int e = 256 * v + 4 * lane;
+        const int64_t ix = static_cast<int64_t>(t0 + r) * E + e;
+        c[u][v] = e < E ? *reinterpret_cast<const float4*>(a.clean + ix)
+                        : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        sd[u][v] = (noise && e < E) ? *reinterpret_cast<const float4*>(a.std_in + ix)
+                                    : make_float4(1.f, 1.f, 1.f, 1.f);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = rb + kWaves * u;
+      if (r >= nr) break;  // uniform across the wave
+      float m = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+        m = fmaxf(m, fmaxf(fmaxf(c[u][v].x, c[u][v].y), fmaxf(c[u][v].z, c[u][v].w)));
+      m = wave_max(m);
+      float ex[NV][4], s = 0.f;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        ex[v][0] = expf(c[u][v].x - m);
+        ex[v][1] = expf(c[u][v].y - m);
+        ex[v][2] = expf(c[u][v].z - m);
+        ex[v][3] = expf(c[u][v].w - m);
+        s += (ex[v][0] + ex[v][1]) + (ex[v][2] + ex[v][3]);
+      }
+      const float inv = 1.f / wave_sum(s);
+      bool in[NV][4];
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) in[v][i] = false;
+      for (int j = 0; j < k; ++j) {
+        const int d = sId[r * k + j] - 4 * lane;
+        const float g = sG[r * k + j];
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool hit = d == 256 * v + i;
+            in[v][i] |= hit;
+            imp[v][i] += hit ? g : 0.f;
+          }
+      }
+      const float r0 = noise ? sR0[r] : 0.f, r1 = noise ? sR1[r] : 0.f;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const float cv[4] = {c[u][v].x, c[u][v].y, c[u][v].z, c[u][v].w};
+        const float sv[4] = {sd[u][v].x, sd[u][v].y, sd[u][v].z, sd[u][v].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[v][i] += ex[v][i] * inv;
+          if (noise) {
+            const float diff = cv[i] - (in[v][i] ? r1 : r0);
+            float pr;
+            if (sv[i] > 0.f) pr = phi(diff / sv[i]);
+            else pr = diff > 0.f ? 1.f : (diff == 0.f ? 0.5f : 0.f);
+            lsum[v][i] += pr;
+          }
+        }
+      }
+    }
+  }
+
+  // fixed-order sum over the waves: wave 0 + wave 1 + wave 2 + wave 3
+  if (wave > 0)
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      sRed[wave - 1][0][v * 64 + lane] = make_float4(imp[v][0], imp[v][1], imp[v][2], imp[v][3]);
+      sRed[wave - 1][1][v * 64 + lane] = make_float4(lsum[v][0], lsum[v][1], lsum[v][2], lsum[v][3]);
+      sRed[wave - 1][2][v * 64 + lane] = make_float4(pb[v][0], pb[v][1], pb[v][2], pb[v][3]);
+    }
+  __syncthreads();
+  if (wave == 0) {
+    const int64_t plane = static_cast<int64_t>(a.nblk) * E;
+    float* out[3] = {a.partial, a.partial + plane, a.partial + 2 * plane};
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int e = 256 * v + 4 * lane;
+      if (e >= E) continue;
+      float4 q[3] = {make_float4(imp[v][0], imp[v][1], imp[v][2], imp[v][3]),
+                     make_float4(lsum[v][0], lsum[v][1], lsum[v][2], lsum[v][3]),
+                     make_float4(pb[v][0], pb[v][1], pb[v][2], pb[v][3])};
+#pragma unroll
+      for (int w = 0; w < kWaves - 1; ++w)
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          const float4 o = sRed[w][t][v * 64 + lane];
+          q[t].x += o.x;
+          q[t].y += o.y;
+          q[t].z += o.z;
+          q[t].w += o.w;
+        }
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        *reinterpret_cast<float4*>(out[t] + static_cast<int64_t>(blockIdx.x) * E + e) = q[t];
+    }
   }
 }
 
@@ -294,7 +429,12 @@ moe_status aux_launch(const Dims& d, const int32_t* ids, const float* gates, con
   a.E = d.E;
   a.k = d.k;
   a.C = d.C;
-  aux_partial<<<a.nblk, kThreads, 0, stream>>>(a);
+  a.vec = (d.E % 4 == 0 && (reinterpret_cast<uintptr_t>(clean) | reinterpret_cast<uintptr_t>(a.std_in)) % 16 == 0)
+              ? 1 : 0;
+  if (a.vec && d.E <= 256) aux_rows<1><<<a.nblk, kThreads, 0, stream>>>(a);
+  else if (a.vec && d.E <= 512) aux_rows<2><<<a.nblk, kThreads, 0, stream>>>(a);
+  else if (a.vec && d.E <= 1024) aux_rows<4><<<a.nblk, kThreads, 0, stream>>>(a);
+  else aux_partial<<<a.nblk, kThreads, 0, stream>>>(a);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   aux_reduce<<<ceil_div(d.E, 32), kThreads, 0, stream>>>(a);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;

@@ -125,6 +125,12 @@ EDGE = [
     # large k
     I.Workload("k8", T=257, D=128, E=20, k=8, H=64, act="f32", gating="noisy", noise=True,
                capacity_factor=1.0, seed=11),
+    # E between 256 and 512: two float4 chunks per lane in the per-row aux pass
+    I.Workload("e384", T=150, D=32, E=384, k=3, H=32, act="bf16", gating="noisy", noise=True,
+               capacity_factor=1.0, seed=12),
+    # E above 1024 (a multiple of 4): the per-expert column aux pass
+    I.Workload("e1100", T=40, D=32, E=1100, k=2, H=16, act="f32", gating="noisy", noise=True,
+               capacity_factor=0.0, seed=13),
 ]
 
 
