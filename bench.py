@@ -163,12 +163,18 @@ def main():
            for i, name in enumerate(stages)}
 
     b = L.b
-    A = int(b.offsets[-1].item())
+    offs = b.offsets.cpu().numpy()
+    A = int(offs[-1])
+    U = int(np.count_nonzero(np.diff(offs)))  # experts that received rows
     el = 2 if w.act == "bf16" else 4
     gemm_flops = 2.0 * A * w.D * w.H  # per launch; both layers have the same count
+    # per launch, either layer: the used experts' weights once, the input rows once,
+    # the output rows once
+    gemm_bytes = U * w.D * w.H * el + A * (w.D + w.H) * el
     gemm_ms = 0.5 * (per["gemm1"] + per["gemm2"])
     achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.act]
+    traffic = measured_traffic(w.name)
     disp_bytes = w.T * w.D * el + A * w.D * el + w.T * w.k * (4 + 4 + 1) + A * 4
     comb_bytes = A * w.D * el + 2 * w.T * w.D * el + w.T * w.k * 13
     out = {
@@ -190,8 +196,13 @@ def main():
                    "dropped": w.T * w.k - A, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": "grouped_gemm", "achieved": achieved,
                      "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": measured_traffic(w.name), "traffic_unit": "bytes per launch",
-                     "flops_per_launch": gemm_flops, "avg_launch_ms": gemm_ms},
+                     "traffic": traffic, "traffic_unit": "bytes per launch",
+                     "flops_per_launch": gemm_flops, "avg_launch_ms": gemm_ms,
+                     "alg_bytes_per_launch": gemm_bytes,
+                     "hbm_frac_alg": gemm_bytes / (gemm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "hbm_frac_measured": (None if traffic is None else
+                                           traffic / (gemm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS)},
+        "tokens_per_s_without_aux": w.T / ((ms_per_step - per["aux"]) * 1e-3),
         "stages_ms": per,
         "dispatch_GBps": disp_bytes / (per["dispatch"] * 1e-3) / 1e9,
         "combine_GBps": comb_bytes / (per["combine"] * 1e-3) / 1e9,

@@ -31,7 +31,7 @@
 namespace moe {
 namespace {
 
-constexpr int kRows = 64;
+constexpr int kRows = 64;  // most token rows per block (fewer when T is small)
 constexpr int kThreads = 256;
 
 struct AuxArgs {
@@ -47,6 +47,7 @@ struct AuxArgs {
   float* partial;  // [3][nblk][E]
   double* sums;    // [3][E]
   int T, E, k, C, nblk, use_noise;
+  int rows;  // token rows per block, <= kRows
   int vec;  // E % 4 == 0 and clean / std 16-byte aligned: float4 row reads
 };
 
@@ -59,8 +60,8 @@ __global__ __launch_bounds__(kThreads) void aux_partial(AuxArgs a) {
   __shared__ int sId[kRows * MOE_MAX_K];
   __shared__ float sG[kRows * MOE_MAX_K];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int t0 = blockIdx.x * kRows;
-  const int nr = min(kRows, a.T - t0);
+  const int t0 = blockIdx.x * a.rows;
+  const int nr = min(a.rows, a.T - t0);
   const int E = a.E, k = a.k;
 
   for (int i = tid; i < nr * k; i += kThreads) {
@@ -161,8 +162,8 @@ __global__ __launch_bounds__(kThreads) void aux_rows(AuxArgs a) {
   __shared__ float sG[kRows * MOE_MAX_K];
   __shared__ float4 sRed[kWaves - 1][3][NV * 64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int t0 = blockIdx.x * kRows;
-  const int nr = min(kRows, a.T - t0);
+  const int t0 = blockIdx.x * a.rows;
+  const int nr = min(a.rows, a.T - t0);
   const int E = a.E, k = a.k;
   const bool noise = a.use_noise != 0;
 
@@ -400,7 +401,14 @@ __global__ __launch_bounds__(kThreads) void aux_final(AuxArgs a) {
 
 }  // namespace
 
-static int aux_blocks(const Dims& d) { return ceil_div(d.T, kRows); }
+// Rows per block: kRows, halved (down to 4) while that leaves fewer than 1024 blocks, so
+// small batches still spread over the chip.
+static int aux_rows_per_block(const Dims& d) {
+  int r = kRows;
+  while (r > 4 && ceil_div(d.T, r) < 1024) r >>= 1;
+  return r;
+}
+static int aux_blocks(const Dims& d) { return ceil_div(d.T, aux_rows_per_block(d)); }
 
 size_t aux_workspace(const Dims& d) {
   return align256(3 * static_cast<size_t>(aux_blocks(d)) * d.E * sizeof(float)) +
@@ -422,6 +430,7 @@ moe_status aux_launch(const Dims& d, const int32_t* ids, const float* gates, con
   a.load = load;
   a.out = out;
   a.nblk = aux_blocks(d);
+  a.rows = aux_rows_per_block(d);
   a.partial = static_cast<float*>(ws);
   a.sums = reinterpret_cast<double*>(static_cast<char*>(ws) +
                                      align256(3 * static_cast<size_t>(a.nblk) * d.E * sizeof(float)));

@@ -21,7 +21,7 @@
 //                  streamed into registers). Epilogue through a wave-private
 //                  LDS tile: per (token, 4 experts) one Philox call gives the
 //                  four noise samples; writes clean, std and the score H.
-//   router_select  8 lanes per token row: per-lane sorted top-K lists
+//   router_select  8-64 lanes per token row: per-lane sorted top-K lists
 //                  (K = next power of two >= k+1) merged by a bitonic
 //                  butterfly; writes ids, gates, row_stats. Switch also sums
 //                  exp(logit - max) for its gate.
@@ -31,7 +31,6 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBM = 128;          // token rows per block
 constexpr int kBN = 256;          // weight columns per block (8 blocks of 32)
 constexpr int kAStride = 144;     // padded LDS row stride (bytes)
 constexpr int kTS = 36;           // epilogue tile row stride (floats)
@@ -74,6 +73,7 @@ struct SelectArgs {
   float* gates;
   float* row_stats;
   int T, E, k, switch_gate;
+  int vec;             // E % 4 == 0 and score 16-byte aligned: float4 reads
 };
 // ------------------------------------------------------------------ Philox4x64-10 + Box-Muller
 // Salmon et al., SC'11: ten rounds; each round multiplies counter words 0 and 2
@@ -175,19 +175,23 @@ __global__ void router_pack(const float* __restrict__ Wg, const float* __restric
 }
 
 // ------------------------------------------------------------------ router GEMM + epilogue
-template <typename XT, bool kFullK>
+// BM token rows per block (128, or 64 / 32 when T is small).
+template <typename XT, bool kFullK, int BM>
 __global__ __launch_bounds__(kThreads, 2) void router_gemm(GemmArgs a) {
   constexpr int V = Elem<XT>::kVec;
   constexpr int kPieces = sizeof(XT) == 2 ? 3 : 1;
   constexpr int kStageElems = 128 / static_cast<int>(sizeof(XT));
-  constexpr int MB = kBM / 32;
-  constexpr int kChunks = kBM * 8 / kThreads;
+  constexpr int MB = BM / 32;
+  constexpr int kChunks = BM * 8 / kThreads;
+  // one A stage buffer; the two together also hold the epilogue tiles [4 waves][2][32][kTS]
+  constexpr int kEpiHalf = (kThreads / 64) * 2 * 32 * kTS * 4 / 2;
+  constexpr int kStage = BM * kAStride > kEpiHalf ? BM * kAStride : kEpiHalf;
 
-  __shared__ __align__(16) unsigned char sA[2][kBM * kAStride];
+  __shared__ __align__(16) unsigned char sA[2][kStage];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int T = a.T, D = a.D, E = a.E;
-  const int mtiles = (T + kBM - 1) / kBM, ntiles = (a.NB + 7) / 8;
+  const int mtiles = (T + BM - 1) / BM, ntiles = (a.NB + 7) / 8;
   const int total = mtiles * ntiles;
   const int per_xcd = (total + kXcds - 1) / kXcds;
   const int local = blockIdx.x / kXcds;
@@ -195,8 +199,8 @@ __global__ __launch_bounds__(kThreads, 2) void router_gemm(GemmArgs a) {
   const int logical = (blockIdx.x % kXcds) * per_xcd + local;
   if (logical >= total) return;
   const int m_tile = logical / ntiles, n_tile = logical - m_tile * ntiles;
-  const int r0 = m_tile * kBM;
-  const int rows = min(kBM, T - r0);
+  const int r0 = m_tile * BM;
+  const int rows = min(BM, T - r0);
   const int nst = a.KS / 4;
 
   const XT* X = static_cast<const XT*>(a.X);
@@ -427,11 +431,12 @@ __device__ __forceinline__ void list_merge(float (&v)[KL], int (&ix)[KL], int of
       }
 }
 
-template <int KL>
+// LPR lanes per token row (a power of two, 8..64, within one wave).
+template <int KL, int LPR>
 __global__ __launch_bounds__(kThreads) void router_select(SelectArgs a) {
   const int tid = threadIdx.x;
-  const int sub = tid & 7;                       // lane within the row group
-  const int t = blockIdx.x * (kThreads / 8) + (tid >> 3);
+  const int sub = tid & (LPR - 1);               // lane within the row group
+  const int t = blockIdx.x * (kThreads / LPR) + tid / LPR;
   const bool live = t < a.T;
   const int E = a.E, k = a.k;
   const float* row = a.score + static_cast<int64_t>(live ? t : 0) * E;
@@ -443,40 +448,39 @@ __global__ __launch_bounds__(kThreads) void router_select(SelectArgs a) {
     ix[j] = kNone;
   }
   if (live) {
-    if ((E % 4) == 0) {
-      // lane sub reads 16 bytes at 4*sub + 32*i: the row group reads 128 contiguous bytes
-      for (int e0 = 4 * sub; e0 < E; e0 += 64) {
+    if (a.vec) {
+      // lane sub reads 16 bytes at 4*sub (+ 4*LPR): the row group reads 16*LPR contiguous
+      // bytes per load
+      for (int e0 = 4 * sub; e0 < E; e0 += 8 * LPR) {
         const float4 x0 = *reinterpret_cast<const float4*>(row + e0);
-        const bool two = e0 + 32 < E;
-        const float4 x1 = two ? *reinterpret_cast<const float4*>(row + e0 + 32)
+        const bool two = e0 + 4 * LPR < E;
+        const float4 x1 = two ? *reinterpret_cast<const float4*>(row + e0 + 4 * LPR)
                               : make_float4(NAN, NAN, NAN, NAN);
         const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          if (!isnan(xs[i])) list_insert<KL>(v, ix, xs[i], e0 + (i & 3) + 32 * (i >> 2));
+          if (!isnan(xs[i])) list_insert<KL>(v, ix, xs[i], e0 + (i & 3) + 4 * LPR * (i >> 2));
       }
     } else {
-      for (int e = sub; e < E; e += 8) {
+      for (int e = sub; e < E; e += LPR) {
         const float x = row[e];
         if (!isnan(x)) list_insert<KL>(v, ix, x, e);
       }
     }
   }
-  list_merge<KL>(v, ix, 1);
-  list_merge<KL>(v, ix, 2);
-  list_merge<KL>(v, ix, 4);
+#pragma unroll
+  for (int off = 1; off < LPR; off <<= 1) list_merge<KL>(v, ix, off);
   // every lane of the group now holds the row's top KL
   float gsum = 0.f;
   if (a.switch_gate) {
     float s = 0.f;
     if (live)
-      for (int e = sub; e < E; e += 8) {
+      for (int e = sub; e < E; e += LPR) {
         const float x = row[e];
         if (!isnan(x)) s += expf(x - v[0]);
       }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) s += __shfl_xor(s, off);
     gsum = s;
   } else {
 #pragma unroll
@@ -487,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void router_select(SelectArgs a) {
   const int64_t o = static_cast<int64_t>(t) * k;
 #pragma unroll
   for (int j = 0; j < KL; ++j) {
-    if (j < k && (j & 7) == sub) {
+    if (j < k && (j & (LPR - 1)) == sub) {
       a.ids[o + j] = ix[j];
       a.gates[o + j] = a.switch_gate ? expf(v[j] - v[0]) / gsum : expf(v[j] - v[0]) / gsum;
     }
@@ -524,6 +528,32 @@ size_t route_workspace(const Dims& d) {
   return b;
 }
 
+template <typename XT, bool kFullK>
+static void router_gemm_bm(int bm, int grid, const GemmArgs& g, hipStream_t stream) {
+  if (bm == 128) router_gemm<XT, kFullK, 128><<<grid, kThreads, 0, stream>>>(g);
+  else if (bm == 64) router_gemm<XT, kFullK, 64><<<grid, kThreads, 0, stream>>>(g);
+  else router_gemm<XT, kFullK, 32><<<grid, kThreads, 0, stream>>>(g);
+}
+
+template <int KL>
+static void select_lpr(int lpr, const SelectArgs& sa, hipStream_t stream) {
+  const int T = sa.T;
+  switch (lpr) {
+    case 8: router_select<KL, 8><<<ceil_div(T, kThreads / 8), kThreads, 0, stream>>>(sa); break;
+    case 16: router_select<KL, 16><<<ceil_div(T, kThreads / 16), kThreads, 0, stream>>>(sa); break;
+    case 32: router_select<KL, 32><<<ceil_div(T, kThreads / 32), kThreads, 0, stream>>>(sa); break;
+    default: router_select<KL, 64><<<ceil_div(T, kThreads / 64), kThreads, 0, stream>>>(sa); break;
+  }
+}
+static void select_launch(int kl, int lpr, const SelectArgs& sa, hipStream_t stream) {
+  switch (kl) {
+    case 2: select_lpr<2>(lpr, sa, stream); break;
+    case 4: select_lpr<4>(lpr, sa, stream); break;
+    case 8: select_lpr<8>(lpr, sa, stream); break;
+    default: select_lpr<16>(lpr, sa, stream); break;
+  }
+}
+
 moe_status route_launch(const Dims& d, const moe_problem* p, const void* X, const float* Wg,
                         const float* Wnoise, const float* bias, const float* eps, int32_t* ids,
                         float* gates, float* clean, float* noise_std, float* row_stats,
@@ -556,15 +586,18 @@ moe_status route_launch(const Dims& d, const moe_problem* p, const void* X, cons
   g.NB = NB;
   g.KS = KS;
   g.use_noise = noise ? 1 : 0;
-  const int64_t tiles = static_cast<int64_t>(ceil_div(d.T, kBM)) * ceil_div(NB, 8);
+  // 128-row tiles, or 64 / 32 while that leaves fewer than 512 blocks
+  int bm = 128;
+  while (bm > 32 && static_cast<int64_t>(ceil_div(d.T, bm)) * ceil_div(NB, 8) < 512) bm >>= 1;
+  const int64_t tiles = static_cast<int64_t>(ceil_div(d.T, bm)) * ceil_div(NB, 8);
   const int grid = static_cast<int>(ceil_div64(tiles, kXcds) * kXcds);
   const bool full = d.D % (d.dtype == MOE_BF16 ? 64 : 32) == 0;
   if (d.dtype == MOE_BF16) {
-    if (full) router_gemm<uint16_t, true><<<grid, kThreads, 0, stream>>>(g);
-    else router_gemm<uint16_t, false><<<grid, kThreads, 0, stream>>>(g);
+    if (full) router_gemm_bm<uint16_t, true>(bm, grid, g, stream);
+    else router_gemm_bm<uint16_t, false>(bm, grid, g, stream);
   } else {
-    if (full) router_gemm<float, true><<<grid, kThreads, 0, stream>>>(g);
-    else router_gemm<float, false><<<grid, kThreads, 0, stream>>>(g);
+    if (full) router_gemm_bm<float, true>(bm, grid, g, stream);
+    else router_gemm_bm<float, false>(bm, grid, g, stream);
   }
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
 
@@ -577,12 +610,14 @@ moe_status route_launch(const Dims& d, const moe_problem* p, const void* X, cons
   sa.E = d.E;
   sa.k = d.k;
   sa.switch_gate = d.gating == MOE_GATE_SWITCH_TOP1 ? 1 : 0;
-  const int sgrid = ceil_div(d.T, kThreads / 8);
+  sa.vec = (d.E % 4 == 0 && reinterpret_cast<uintptr_t>(sa.score) % 16 == 0) ? 1 : 0;
+  // lanes per row: 8, doubled (up to 64) while the grid would hold fewer than 64K threads and
+  // each lane would still see at least 16 scores
+  int lpr = 8;
+  while (lpr < 64 && static_cast<int64_t>(d.T) * lpr < 65536 && d.E >= 32 * lpr) lpr <<= 1;
   const int need = d.k + 1;
-  if (need <= 2) router_select<2><<<sgrid, kThreads, 0, stream>>>(sa);
-  else if (need <= 4) router_select<4><<<sgrid, kThreads, 0, stream>>>(sa);
-  else if (need <= 8) router_select<8><<<sgrid, kThreads, 0, stream>>>(sa);
-  else router_select<16><<<sgrid, kThreads, 0, stream>>>(sa);
+  const int kl = need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
+  select_launch(kl, lpr, sa, stream);
   return launch_status();
 }
 

@@ -53,7 +53,31 @@ def test_route(moe, name):
     log(f"[route] {name}")
     w, inp = workload_inputs(name)
     r, _ = oracle_routing(name)
-    g = _route_gpu(moe, w, inp)
+    _check_route(w, r, _route_gpu(moe, w, inp))
+
+
+# token counts that select the router's 64-row tiles (T = 40000, 96 experts) and its widest
+# selection rows (E = 300 with few tokens: 16 lanes per row)
+ROUTE_SHAPES = [
+    I.Workload("bm64", T=40000, D=64, E=96, k=2, H=16, act="bf16", gating="noisy", noise=True,
+               capacity_factor=0.0, seed=14),
+    I.Workload("lpr16", T=96, D=48, E=300, k=3, H=16, act="f32", gating="noisy", noise=True,
+               capacity_factor=0.0, seed=15),
+    I.Workload("sw64", T=40000, D=40, E=24, k=1, H=16, act="bf16", gating="switch", noise=False,
+               capacity_factor=1.0, seed=16),
+]
+
+
+@pytest.mark.parametrize("w", ROUTE_SHAPES, ids=[w.name for w in ROUTE_SHAPES])
+def test_route_tile_shapes(moe, w):
+    log(f"[route shape] {w}")
+    inp = I.make_inputs(w, experts=False)
+    r = O.route(inp["X"], inp["Wg"], inp["Wnoise"], inp["bias"], w.k, w.gating, w.noise,
+                seed=w.seed)
+    _check_route(w, r, _route_gpu(moe, w, inp))
+
+
+def _check_route(w, r, g):
     assert rel_err(g["clean"], r.clean) < 1e-5
     if r.std is not None:
         assert rel_err(g["std"], r.std) < 1e-5
