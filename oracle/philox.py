@@ -6,7 +6,9 @@ Top-K Gating", Step 1) but fix no generator. The reading used here keys the
 sample by (seed, token t, expert e):
 
   q = e // 4, r = e % 4
-  (r0, r1, r2, r3) = Philox4x64-10(counter = (t, q, 0, 0), key = (seed, 0))
+  (r0, r1, r2, r3) = Philox4x64-10(counter = (t, q, 0, 0), key = (seed, g))
+  with g = 0 for a flat gate (and the primary gate of a hierarchical MoE) and
+  g = 1 + i for the secondary gate of group i
   pair a = (r0, r1) feeds experts 4q+0 (cosine) and 4q+1 (sine),
   pair b = (r2, r3) feeds experts 4q+2 (cosine) and 4q+3 (sine):
      u1 = ((hi >> 11) + 1) * 2^-53        in (0, 1]
@@ -73,13 +75,21 @@ def _box_muller(a, b):
     return rho * np.cos(theta), rho * np.sin(theta)
 
 
-def gaussian_noise(seed: int, T: int, E: int, t0: int = 0) -> np.ndarray:
-    """eps [T, E] fp32 for tokens t0 .. t0+T-1 (counter-keyed; any slice is reproducible)."""
+def gaussian_noise(seed: int, T: int, E: int, t0: int = 0, key1: int = 0,
+                   tokens=None) -> np.ndarray:
+    """eps [T, E] fp32 for tokens t0 .. t0+T-1, or for the listed token indices
+    (counter-keyed; any slice is reproducible). key1 is the second key word: 0
+    for a flat gate and for the primary gate of a hierarchical one, 1 + i for
+    the secondary gate of group i (an independent stream per gate)."""
     Q = (E + 3) // 4
-    t = np.arange(t0, t0 + T, dtype=np.uint64)[:, None]
+    if tokens is None:
+        t = np.arange(t0, t0 + T, dtype=np.uint64)[:, None]
+    else:
+        t = np.asarray(tokens, dtype=np.uint64).reshape(-1, 1)
+        T = t.shape[0]
     q = np.arange(Q, dtype=np.uint64)[None, :]
     zero = np.uint64(0)
-    r0, r1, r2, r3 = philox4x64_10(t, q, zero, zero, np.uint64(seed), zero)
+    r0, r1, r2, r3 = philox4x64_10(t, q, zero, zero, np.uint64(seed), np.uint64(key1))
     ca, sa = _box_muller(r0, r1)
     cb, sb = _box_muller(r2, r3)
     out = np.stack([ca, sa, cb, sb], axis=-1).reshape(T, 4 * Q)[:, :E]

@@ -20,6 +20,12 @@ used or needed, random draws stand in for them):
                  factor 1.25, router bias skewed by a Zipf(1.1) pmf
   top2_bf16      T=65536 D=1024 E=256 k=2 H=4096, bf16, noisy top-2, capacity
                  factor 1.0, 10% of the token rows duplicated
+  hier_bf16      T=16384 D=512 H=1024, bf16, hierarchical: 16 groups of 64
+                 experts (E=1024), k_p=2 groups then k_s=2 experts (k=4), no
+                 capacity (Outrageously Large Neural Networks summary,
+                 "Hierarchical Mixture-of-Experts", with the first-level
+                 branching factor 16 and two choices per level of the paper's
+                 1024-expert hierarchical model)
 
 Recipe. Every tensor comes from its own numpy PCG64 stream keyed by
 SeedSequence([seed, tag]) (expert weights: [seed, tag, expert]; token rows in
@@ -30,6 +36,8 @@ the draws can run in parallel threads.
   W1[e]    ~ N(0, 1/D)  as [D, H]   (fan-in D)
   W2[e]    ~ N(0, 1/H)  as [H, D]   (fan-in H)
   bias[e]  = (e+1)^-1.1 / sum_j j^-1.1   (switch_bf16 only)
+  hierarchical gates: Wpg, Wpn ~ N(0, 1/D) as [D, a]; Wsg[i], Wsn[i] ~ N(0, 1/D)
+  as [D, b] from streams [seed, tag, i]
   duplicates: floor(0.1 T) token rows, chosen without replacement, copy the row
   of a source token drawn uniformly from the remaining rows (top2_bf16 only).
 bf16 tensors are produced by rounding the fp32 draw to nearest-even and are
@@ -44,6 +52,7 @@ import os
 import numpy as np
 
 TAG_X, TAG_WG, TAG_WNOISE, TAG_W1, TAG_W2, TAG_DUP = 1, 2, 3, 4, 5, 6
+TAG_WPG, TAG_WPN, TAG_WSG, TAG_WSN = 7, 8, 9, 10
 
 
 @dataclasses.dataclass(frozen=True)
@@ -62,6 +71,8 @@ class Workload:
     min_capacity: int = 1
     zipf_bias: float = 0.0  # > 0: router bias = Zipf(s) pmf over experts
     dup_frac: float = 0.0   # fraction of token rows that duplicate another row
+    groups: int = 0         # > 0: hierarchical gate over `groups` groups of E/groups experts
+    k_primary: int = 0      # hierarchical: groups kept per token (k / k_primary experts each)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -83,6 +94,13 @@ WORKLOADS = {
                           dup_frac=0.1),
 }
 WORKLOAD_ORDER = ["switch_toy", "noisy_fp32", "shrinking_bf16", "switch_bf16", "top2_bf16"]
+
+HIER_WORKLOADS = {
+    "hier_bf16": Workload("hier_bf16", T=16384, D=512, E=1024, k=4, H=1024, act="bf16",
+                          gating="noisy", noise=True, capacity_factor=0.0, seed=2,
+                          groups=16, k_primary=2),
+}
+WORKLOADS.update(HIER_WORKLOADS)
 
 
 def _rng(*key: int) -> np.random.Generator:
@@ -166,6 +184,18 @@ def make_router(w: Workload):
     return Wg, Wn, bias
 
 
+def make_hier_router(w: Workload):
+    """Primary gate weights [D, a] and per-group secondary weights [a, D, b] (fp32)."""
+    a, b = w.groups, w.E // w.groups
+    sc = 1.0 / np.sqrt(w.D)
+    Wpg = _normal(_rng(w.seed, TAG_WPG), (w.D, a), sc)
+    Wpn = _normal(_rng(w.seed, TAG_WPN), (w.D, a), sc) if w.noise else None
+    Wsg = np.stack([_normal(_rng(w.seed, TAG_WSG, i), (w.D, b), sc) for i in range(a)])
+    Wsn = (np.stack([_normal(_rng(w.seed, TAG_WSN, i), (w.D, b), sc) for i in range(a)])
+           if w.noise else None)
+    return Wpg, Wpn, Wsg, Wsn
+
+
 def make_expert(w: Workload, e: int):
     """(W1[e] as [D,H], W2[e] as [H,D]) for one expert."""
     W1 = _normal(_rng(w.seed, TAG_W1, e), (w.D, w.H), 1.0 / np.sqrt(w.D))
@@ -190,8 +220,12 @@ def make_experts(w: Workload, threads: int | None = None):
 
 def make_inputs(w: Workload, experts: bool = True, threads: int | None = None) -> dict:
     X = make_tokens(w, threads)
-    Wg, Wn, bias = make_router(w)
-    out = dict(X=X, Wg=Wg, Wnoise=Wn, bias=bias)
+    if w.groups > 0:
+        Wpg, Wpn, Wsg, Wsn = make_hier_router(w)
+        out = dict(X=X, Wpg=Wpg, Wpn=Wpn, Wsg=Wsg, Wsn=Wsn)
+    else:
+        Wg, Wn, bias = make_router(w)
+        out = dict(X=X, Wg=Wg, Wnoise=Wn, bias=bias)
     if experts:
         out["W1"], out["W2"] = make_experts(w, threads)
     return out

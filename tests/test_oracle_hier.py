@@ -1,0 +1,188 @@
+"""Pins for the hierarchical-MoE oracle (CPU only): special cases that reduce to
+the flat layer, the double-sum output written from the definition with dense
+gates, invariants of Importance_H, a Monte-Carlo check of Load_H's factors, the
+empty-group reading and the per-group noise streams.
+
+Passages: "Outrageously Large Neural Networks" summary, section 3.4,
+"Hierarchical Mixture-of-Experts" (y_H, Importance_H, Load_H); the
+"Mixture-of-Experts: Sparse Computation" lesson, chapter 5, "Balancing at every
+level" (X^(i), the division by |X^(i)|).
+"""
+import numpy as np
+import pytest
+import scipy.special
+
+from oracle import hier as HO
+from oracle import moe as O
+from oracle import philox as P
+from sparsely_gated_mixture_amd import inputs as I
+
+
+def _wl(T=40, D=6, a=4, b=3, kp=2, ks=2, H=5, noise=True, seed=3, cf=0.0):
+    return I.Workload("hier_pin", T=T, D=D, E=a * b, k=kp * ks, H=H, act="f32", gating="noisy",
+                      noise=noise, capacity_factor=cf, seed=seed, groups=a, k_primary=kp)
+
+
+def _inputs(w):
+    inp = I.make_inputs(w)
+    return inp
+
+
+def _dense_gate(score, k):
+    """Dense gate vector from its definition: softmax over H with every entry outside the
+    k largest set to -inf (the KeepTopK mask form); ties are absent in random draws."""
+    thr = -np.sort(-score.astype(np.float32), axis=1)[:, k - 1:k]
+    masked = np.where(score.astype(np.float32) >= thr, score, -np.inf)
+    return scipy.special.softmax(masked, axis=1)
+
+
+def test_one_group_is_the_flat_gate():
+    """a = 1, k_p = 1: the primary gate is 1 for the only group, so the hierarchy is the
+    flat gate of group 0 (with group 0's noise stream), its load and importance."""
+    w = _wl(a=1, b=7, kp=1, ks=3)
+    inp = _inputs(w)
+    f = HO.forward_hier(inp, w)
+    h = f["hier"]
+    np.testing.assert_allclose(h.primary.gates, 1.0)
+    eps = P.gaussian_noise(w.seed, w.T, 7, key1=1)
+    r = O.route(inp["X"], inp["Wsg"][0], inp["Wsn"][0], None, 3, "noisy", True, eps=eps)
+    np.testing.assert_array_equal(h.ids, r.ids)
+    np.testing.assert_allclose(h.gates, r.gates, rtol=1e-13)
+    flat = O.aux(r, O.dispatch(r.ids, 7, w.T), 3)
+    np.testing.assert_allclose(f["aux"]["importance"], flat["importance"], rtol=1e-12)
+    np.testing.assert_allclose(f["aux"]["load"], flat["load"], rtol=1e-12)
+
+
+def test_one_expert_per_group_is_the_primary_gate():
+    """b = 1, k_s = 1: every secondary gate is 1, so the final gates are the primary's and
+    Load_H = Load_primary (Load_i(X^(i)) = |X^(i)| when k = E)."""
+    w = _wl(a=5, b=1, kp=2, ks=1)
+    inp = _inputs(w)
+    f = HO.forward_hier(inp, w)
+    h = f["hier"]
+    r = O.route(inp["X"], inp["Wpg"], inp["Wpn"], None, 2, "noisy", True, seed=w.seed)
+    np.testing.assert_array_equal(h.ids, r.ids)
+    np.testing.assert_allclose(h.gates, r.gates, rtol=1e-13)
+    np.testing.assert_allclose(f["aux"]["load"], O.load_probs(r, 2).sum(axis=0), rtol=1e-12)
+
+
+def test_output_is_the_double_sum_of_the_definition():
+    """y_H = x + sum_i sum_j Gp(x)_i G_i(x)_j E_ij(x), with both gates built densely from the
+    mask form and every expert evaluated directly, equals the dispatch/combine forward."""
+    w = _wl(T=30, a=3, b=4, kp=2, ks=2)
+    inp = _inputs(w)
+    f = HO.forward_hier(inp, w)
+    h = f["hier"]
+    a, b = 3, 4
+    Gp = _dense_gate(h.primary.score, 2)
+    X = inp["X"].astype(np.float64)
+    for t in range(w.T):
+        y = X[t].copy()
+        for i in range(a):
+            if Gp[t, i] == 0:
+                continue
+            Wg, Wn = inp["Wsg"][i].astype(np.float64), inp["Wsn"][i].astype(np.float64)
+            eps = P.gaussian_noise(w.seed, 0, b, key1=1 + i, tokens=[t]).astype(np.float64)
+            Hs = X[t:t + 1] @ Wg + eps * np.logaddexp(0.0, X[t:t + 1] @ Wn)
+            Gi = _dense_gate(Hs, 2)[0]
+            for j in range(b):
+                if Gi[j] == 0:
+                    continue
+                e = i * b + j
+                W1, W2 = inp["W1"][e].astype(np.float64), inp["W2"][e].astype(np.float64)
+                y += Gp[t, i] * Gi[j] * (np.maximum(X[t] @ W1, 0.0) @ W2)
+        np.testing.assert_allclose(f["Y"][t], y, rtol=1e-10, atol=1e-12)
+
+
+def test_importance_invariants():
+    """Each token's gate products sum to 1 (so sum Importance_H = T), and summing
+    Importance_H over a group's experts gives the primary importance of that group."""
+    w = _wl(T=64, a=4, b=5, kp=2, ks=3)
+    f = HO.forward_hier(_inputs(w), w)
+    imp = f["aux"]["importance"]
+    assert imp.sum() == pytest.approx(w.T, rel=1e-12)
+    np.testing.assert_allclose(imp.reshape(4, 5).sum(axis=1), f["aux"]["importance_primary"],
+                               rtol=1e-12)
+    assert f["aux"]["out"][6] == pytest.approx(w.T, rel=1e-12)
+
+
+def _mc_load(clean, std, score, k, rng, n):
+    """Expected selections per component: for every row and component, redraw only that
+    component's noise n times and count how often it stays among the k largest (the
+    load estimator's definition); returns the column sums and their standard errors."""
+    T, E = clean.shape
+    load, var = np.zeros(E), np.zeros(E)
+    for t in range(T):
+        for i in range(E):
+            Hi = np.repeat(score[t:t + 1], n, axis=0)
+            Hi[:, i] = clean[t, i] + std[t, i] * rng.standard_normal(n)
+            p = ((Hi > Hi[:, i:i + 1]).sum(axis=1) < k).mean()
+            load[i] += p
+            var[i] += max(p * (1 - p), 1e-12) / n
+    return load, np.sqrt(var)
+
+
+def test_load_factors_against_monte_carlo():
+    """Load_H(i,j) = Load_p(X)_i Load_i(X^(i))_j / |X^(i)|: the primary load over all tokens
+    and group i's load over X^(i) (with that gate's own noise and k_s), each checked by
+    redrawing one component's noise at a time."""
+    w = _wl(T=16, D=4, a=3, b=4, kp=1, ks=2, seed=11)
+    inp = _inputs(w)
+    f = HO.forward_hier(inp, w)
+    h = f["hier"]
+    rng = np.random.default_rng(0)
+    n = 4000
+    p = h.primary
+    lp, sp = _mc_load(p.clean, p.std, p.score, 1, rng, n)
+    assert (np.abs(f["aux"]["load_primary"] - lp) < 4 * sp + 1e-9).all()
+    for i in range(3):
+        r = h.secondary[i]
+        if r is None:
+            continue
+        ls, ss = _mc_load(r.clean, r.std, r.score, 2, rng, n)
+        m = h.members[i].size
+        want = f["aux"]["load_primary"][i] * ls / m
+        band = f["aux"]["load_primary"][i] * 4 * ss / m
+        assert (np.abs(f["aux"]["load"][i * 4:(i + 1) * 4] - want) < band + 1e-9).all()
+
+
+def test_empty_group_has_zero_load():
+    """A group that no token reaches: |X^(i)| = 0, read as Load_H = 0 for its experts."""
+    w = _wl(T=20, a=4, b=3, kp=2, ks=2)
+    inp = _inputs(w)
+    eps_p = P.gaussian_noise(w.seed, w.T, 4).astype(np.float64)
+    eps_p[:, 1] = -1e6  # group 1 never wins
+    h = HO.route_hier(inp["X"], inp["Wpg"], inp["Wpn"], inp["Wsg"], inp["Wsn"], 2, 2, True,
+                      seed=w.seed, eps_primary=eps_p)
+    assert h.members[1].size == 0
+    a_ = HO.aux_hier(h, 4, 3, 2, 2)
+    assert (a_["load"][3:6] == 0).all() and (a_["importance"][3:6] == 0).all()
+    assert a_["out"][5] == 1.0
+    assert np.isfinite(a_["out"]).all()
+
+
+def test_secondary_noise_streams():
+    """Group i's secondary noise for token t is the key-(seed, 1+i) stream at counter t;
+    the streams differ between groups and from the primary's."""
+    s = 9
+    full = P.gaussian_noise(s, 50, 12, key1=3)
+    np.testing.assert_array_equal(P.gaussian_noise(s, 0, 12, key1=3, tokens=[4, 17, 49]),
+                                  full[[4, 17, 49]])
+    assert not np.array_equal(full, P.gaussian_noise(s, 50, 12, key1=2))
+    assert not np.array_equal(full, P.gaussian_noise(s, 50, 12))
+
+
+def test_final_assignments_layout():
+    """Final expert ids are i*b + j, listed by primary slot then secondary order, distinct
+    per token; the dispatch then caps them like the flat layer."""
+    w = _wl(T=50, a=4, b=3, kp=2, ks=2, cf=0.6)
+    f = HO.forward_hier(_inputs(w), w)
+    h = f["hier"]
+    for t in range(w.T):
+        for s in range(2):
+            grp = h.primary.ids[t, s]
+            blk = h.ids[t, 2 * s:2 * s + 2]
+            assert (blk // 3 == grp).all()
+        assert len(set(h.ids[t].tolist())) == 4
+    C = O.capacity(w.T, 4, 0.6, 12)
+    assert f["dispatch"].C == C and (f["dispatch"].counts == np.bincount(h.ids.ravel(), minlength=12)).all()

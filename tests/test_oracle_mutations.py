@@ -116,3 +116,46 @@ def test_pins_catch_mutation(monkeypatch, modname, label, old, new):
                 if hasattr(O, name):
                     monkeypatch.setattr(O, name, val)
     assert _run_pins(), f"no pin failed for mutation: {label}"
+
+
+# ------------------------------------------------------------ hierarchical oracle
+
+import oracle.hier as HO  # noqa: E402
+import test_oracle_hier as hier_pins  # noqa: E402
+
+HIER_MUTATIONS = [
+    ("slot ignored in the final layout", "ids[tok, slot * ks + j] = i * b + r.ids[:, j]",
+     "ids[tok, j] = i * b + r.ids[:, j]"),
+    ("final gate without the primary factor",
+     "gates[tok, slot * ks + j] = p.gates[tok, slot] * r.gates[:, j]",
+     "gates[tok, slot * ks + j] = r.gates[:, j]"),
+    ("secondary noise on the primary key", "key1=1 + i, tokens=tok", "key1=0, tokens=tok"),
+    ("secondary noise key off by one", "key1=1 + i, tokens=tok", "key1=i, tokens=tok"),
+    ("Load_H without the primary load", "load[i * b:(i + 1) * b] = lp[i] * ls / n",
+     "load[i * b:(i + 1) * b] = ls / n"),
+    ("Load_H not divided by |X^(i)|", "load[i * b:(i + 1) * b] = lp[i] * ls / n",
+     "load[i * b:(i + 1) * b] = lp[i] * ls"),
+    ("X^(i) from the first primary slot only", "tok = np.nonzero((p.ids == i).any(axis=1))[0]",
+     "tok = np.nonzero((p.ids[:, :1] == i).any(axis=1))[0]"),
+    ("expert id group-minor", "i * b + r.ids[:, j]", "r.ids[:, j] * a + i"),
+    ("secondary keeps k_p experts", "r = O.route(X[tok], Wsg[i], Wsn[i], None, ks,",
+     "r = O.route(X[tok], Wsg[i], Wsn[i], None, kp,"),
+]
+
+HIER_PIN_TESTS = [getattr(hier_pins, n) for n in dir(hier_pins) if n.startswith("test_")]
+
+
+@pytest.mark.parametrize("label,old,new", HIER_MUTATIONS, ids=[m[0] for m in HIER_MUTATIONS])
+def test_hier_pins_catch_mutation(monkeypatch, label, old, new):
+    mut = _mutant("hier", old, new)
+    for name, val in vars(mut).items():
+        if isinstance(val, types.FunctionType) and hasattr(HO, name):
+            monkeypatch.setattr(HO, name, val)
+    failed = []
+    for fn in HIER_PIN_TESTS:
+        try:
+            fn()
+        except Exception:
+            failed.append(fn.__name__)
+            break
+    assert failed, f"no hierarchical pin failed for mutation: {label}"
