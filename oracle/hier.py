@@ -74,7 +74,8 @@ def route_hier(X, Wpg, Wpn, Wsg, Wsn, kp: int, ks: int, noise: bool, seed: int =
         if noise:
             eps = (gaussian_noise(seed, 0, b, key1=1 + i, tokens=tok) if eps_secondary is None
                    else eps_secondary[i])
-        r = O.route(X[tok], Wsg[i], Wsn[i], None, ks, "noisy", noise, eps=eps)
+        r = O.route(X[tok], Wsg[i], Wsn[i] if Wsn is not None else None, None, ks, "noisy",
+                    noise, eps=eps)
         sec.append(r)
         near[tok] |= r.near_tie
         slot = np.argmax(p.ids[tok] == i, axis=1)  # where group i sits in each token's list

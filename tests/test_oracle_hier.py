@@ -94,16 +94,20 @@ def test_output_is_the_double_sum_of_the_definition():
         np.testing.assert_allclose(f["Y"][t], y, rtol=1e-10, atol=1e-12)
 
 
-def test_importance_invariants():
+@pytest.mark.parametrize("noise", [True, False])
+def test_importance_invariants(noise):
     """Each token's gate products sum to 1 (so sum Importance_H = T), and summing
-    Importance_H over a group's experts gives the primary importance of that group."""
-    w = _wl(T=64, a=4, b=5, kp=2, ks=3)
+    Importance_H over a group's experts gives the primary importance of that group
+    (with or without noise; without it Load_H is 0)."""
+    w = _wl(T=64, a=4, b=5, kp=2, ks=3, noise=noise)
     f = HO.forward_hier(_inputs(w), w)
     imp = f["aux"]["importance"]
     assert imp.sum() == pytest.approx(w.T, rel=1e-12)
     np.testing.assert_allclose(imp.reshape(4, 5).sum(axis=1), f["aux"]["importance_primary"],
                                rtol=1e-12)
     assert f["aux"]["out"][6] == pytest.approx(w.T, rel=1e-12)
+    if not noise:
+        assert (f["aux"]["load"] == 0).all()
 
 
 def _mc_load(clean, std, score, k, rng, n):

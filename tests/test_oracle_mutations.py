@@ -138,8 +138,7 @@ HIER_MUTATIONS = [
     ("X^(i) from the first primary slot only", "tok = np.nonzero((p.ids == i).any(axis=1))[0]",
      "tok = np.nonzero((p.ids[:, :1] == i).any(axis=1))[0]"),
     ("expert id group-minor", "i * b + r.ids[:, j]", "r.ids[:, j] * a + i"),
-    ("secondary keeps k_p experts", "r = O.route(X[tok], Wsg[i], Wsn[i], None, ks,",
-     "r = O.route(X[tok], Wsg[i], Wsn[i], None, kp,"),
+    ("secondary keeps k_p experts", "None, None, ks, \"noisy\"", "None, None, kp, \"noisy\""),
 ]
 
 HIER_PIN_TESTS = [getattr(hier_pins, n) for n in dir(hier_pins) if n.startswith("test_")]
