@@ -228,6 +228,80 @@ moe_status moe_aux_loss(const moe_problem* p, const int32_t* ids,
                         float* out, void* workspace, size_t workspace_bytes,
                         void* hip_stream);
 
+/* ------------------------------------------------------ hierarchical MoE */
+
+/* Two-level gating ([OLNN] 3.4 "Hierarchical Mixture-of-Experts"; [LESSON]
+ * ch. 1 "When n gets too large to gate directly", ch. 5 "Balancing at every
+ * level"). The p->E experts form `groups` groups of b = E / groups; a primary
+ * noisy top-k gate over the groups keeps k_primary of them per token, and group
+ * i's own noisy top-k gate keeps k_s = p->k / k_primary of its b experts for the
+ * tokens routed to it (X^(i)). Expert (i, j) is expert i*b + j of p, weighted
+ * by Gp(x)_i * G_i(x)_j; a token's p->k assignments list the primary slots in
+ * the primary's order, each followed by its group's choices in that gate's
+ * order. The final ids / gates then go through moe_dispatch, moe_expert_ffn and
+ * moe_combine with p unchanged (capacity applies to the p->E experts).
+ * Noise: the primary gate draws as moe_route (key (seed, 0)); group i's gate
+ * draws from key (seed, 1 + i), counter (t, j / 4), same Box-Muller pairing.
+ * Requires p->gating == MOE_GATE_NOISY_TOPK (noise on or off) and no bias. */
+typedef struct {
+  int32_t groups;     /* a: 1 <= a <= E, E % a == 0                         */
+  int32_t k_primary;  /* 1 <= k_primary <= a, p->k % k_primary == 0,
+                         p->k / k_primary <= E / a                           */
+} moe_hier;
+
+/* Caller-owned device buffers of both levels (fp32 unless noted). R = T *
+ * k_primary secondary rows, grouped: group i holds rows offsets_p[i] ..
+ * offsets_p[i+1]-1, its tokens in ascending order. std_p / std_s are NULL
+ * when p->noise == 0. Written by moe_route_hier, read by moe_aux_loss_hier. */
+typedef struct {
+  int32_t* ids_p;       /* [T, k_primary] chosen groups, (score desc, index asc) */
+  float*   gates_p;     /* [T, k_primary] softmax over the kept group scores    */
+  float*   clean_p;     /* [T, groups]   X . Wpg                                 */
+  float*   std_p;       /* [T, groups]   Softplus(X . Wpn)                       */
+  float*   row_stats_p; /* [T, 2]        k_primary-th, (k_primary+1)-th score    */
+  int32_t* pos_p;       /* [T, k_primary] row of the token inside its group      */
+  uint8_t* accepted_p;  /* [T, k_primary] all 1: no capacity between the levels  */
+  int32_t* counts_p;    /* [groups]      |X^(i)|                                 */
+  int32_t* offsets_p;   /* [groups + 1]  first row of each group                 */
+  int32_t* row_token_p; /* [R]           token of each secondary row             */
+  float*   clean_s;     /* [R, b]        X[token] . Wsg[group]                   */
+  float*   std_s;       /* [R, b]        Softplus(X[token] . Wsn[group])         */
+  float*   row_stats_s; /* [R, 2]        k_s-th, (k_s+1)-th secondary score      */
+  int32_t* ids_s;       /* [R, k_s]      experts within the group                */
+  float*   gates_s;     /* [R, k_s]      softmax over the kept secondary scores  */
+} moe_hier_state;
+
+/* Workspace bytes for moe_route_hier (which = MOE_WS_ROUTE) or
+ * moe_aux_loss_hier (MOE_WS_AUX); 0 for invalid arguments. */
+size_t moe_hier_workspace_size(const moe_problem* p, const moe_hier* h, int which);
+
+/* moe_route_hier -- both gate levels and the final assignments.
+ *   X [T,D] (p->dtype); Wpg, Wpn [D, groups]; Wsg, Wsn [groups, D, b] (fp32;
+ *   Wpn / Wsn NULL without noise); ids [T, p->k] int32 out; gates [T, p->k] out;
+ *   st: every buffer above (std_p / std_s only with noise). */
+moe_status moe_route_hier(const moe_problem* p, const moe_hier* h, const void* X,
+                          const float* Wpg, const float* Wpn, const float* Wsg,
+                          const float* Wsn, int32_t* ids, float* gates,
+                          const moe_hier_state* st, void* workspace,
+                          size_t workspace_bytes, void* hip_stream);
+
+/* moe_aux_loss_hier -- hierarchical balancing terms, unweighted.
+ *   importance[i*b+j] = sum over x of Gp(x)_i * G_i(x)_j          (Importance_H)
+ *   load[i*b+j]       = Load_p(X)_i * Load_i(X^(i))_j / |X^(i)|  (Load_H), with
+ *                       Load_p the moe_aux_loss load of the primary gate over
+ *                       all tokens and Load_i that of group i's gate over
+ *                       X^(i); 0 for a group no token reached; 0 without noise
+ *   out[0] = CV^2(Importance_H)  out[1] = CV^2(Load_H)
+ *   out[2] = CV^2(primary importance)  out[3] = CV^2(primary load)
+ *   out[4] = max(Load_H) / mean(Load_H)  out[5] = groups with |X^(i)| = 0
+ *   out[6] = sum(Importance_H)  out[7] = 0
+ *   st as written by moe_route_hier; importance, load [E] out (either may be
+ *   NULL); out [8] out; workspace moe_hier_workspace_size(.., MOE_WS_AUX). */
+moe_status moe_aux_loss_hier(const moe_problem* p, const moe_hier* h,
+                             const moe_hier_state* st, float* importance,
+                             float* load, float* out, void* workspace,
+                             size_t workspace_bytes, void* hip_stream);
+
 /* ------------------------------------------------------------------- misc */
 
 /* Synchronises hip_stream, then returns MOE_ERR_NONFINITE if a kernel run with

@@ -10,6 +10,12 @@
 
 namespace moe {
 
+#define MOE_STATUS_TRY(expr)          \
+  do {                                \
+    const moe_status s_ = (expr);     \
+    if (s_ != MOE_OK) return s_;      \
+  } while (0)
+
 // Largest expert count: dispatch and the grouped GEMM keep per-expert tables
 // in LDS (dispatch: 2E+1+512 ints).
 constexpr int kMaxExperts = 4096;
@@ -68,6 +74,18 @@ static int* nonfinite_flag(const moe_problem* p) {
     ptrs[dev] = static_cast<int*>(ptr);
   }
   return ptrs[dev];
+}
+
+// Hierarchical options on top of a valid flat problem.
+static moe_status validate_hier(const moe_problem* p, const moe_hier* h, Dims* d) {
+  MOE_STATUS_TRY(validate(p, d));
+  if (!h) return MOE_ERR_INVALID_ARG;
+  if (p->gating != MOE_GATE_NOISY_TOPK) return MOE_ERR_INVALID_ARG;
+  const int a = h->groups, kp = h->k_primary;
+  if (a < 1 || a > p->E || p->E % a != 0) return MOE_ERR_INVALID_ARG;
+  if (kp < 1 || kp > a || p->k % kp != 0 || p->k / kp > p->E / a) return MOE_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(p->T) * kp * (p->E / a) > (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
 }
 
 }  // namespace moe
@@ -201,6 +219,53 @@ moe_status moe_aux_loss(const moe_problem* p, const int32_t* ids, const float* g
   if (!workspace || workspace_bytes < aux_workspace(d)) return MOE_ERR_WORKSPACE;
   return aux_launch(d, ids, gates, clean, noise_std, row_stats, counts, importance, load, out,
                     workspace, as_stream(hip_stream));
+}
+
+size_t moe_hier_workspace_size(const moe_problem* p, const moe_hier* h, int which) {
+  Dims d;
+  if (validate_hier(p, h, &d) != MOE_OK) return 0;
+  switch (which) {
+    case MOE_WS_ROUTE: return hier_route_workspace(d, h);
+    case MOE_WS_AUX: return hier_aux_workspace(d, h);
+    default: return 0;
+  }
+}
+
+moe_status moe_route_hier(const moe_problem* p, const moe_hier* h, const void* X,
+                          const float* Wpg, const float* Wpn, const float* Wsg, const float* Wsn,
+                          int32_t* ids, float* gates, const moe_hier_state* st, void* workspace,
+                          size_t workspace_bytes, void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate_hier(p, h, &d));
+  const bool noise = d.noise != 0;
+  if (!X || !Wpg || !Wsg || !ids || !gates || !st) return MOE_ERR_INVALID_ARG;
+  if (noise && (!Wpn || !Wsn || !st->std_p || !st->std_s)) return MOE_ERR_INVALID_ARG;
+  if (!st->ids_p || !st->gates_p || !st->clean_p || !st->row_stats_p || !st->pos_p ||
+      !st->accepted_p || !st->counts_p || !st->offsets_p || !st->row_token_p || !st->clean_s ||
+      !st->row_stats_s || !st->ids_s || !st->gates_s)
+    return MOE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < hier_route_workspace(d, h)) return MOE_ERR_WORKSPACE;
+  int* flag;
+  MOE_TRY(flag_for(p, &flag));
+  return hier_route_launch(d, h, p, X, Wpg, Wpn, Wsg, Wsn, ids, gates, st, workspace, flag,
+                           as_stream(hip_stream));
+}
+
+moe_status moe_aux_loss_hier(const moe_problem* p, const moe_hier* h, const moe_hier_state* st,
+                             float* importance,
+                             float* load, float* out, void* workspace, size_t workspace_bytes,
+                             void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate_hier(p, h, &d));
+  const bool noise = d.noise != 0;
+  if (!st || !out) return MOE_ERR_INVALID_ARG;
+  if (noise && (!st->std_p || !st->std_s)) return MOE_ERR_INVALID_ARG;
+  if (!st->ids_p || !st->gates_p || !st->clean_p || !st->row_stats_p || !st->counts_p ||
+      !st->offsets_p || !st->row_token_p || !st->clean_s || !st->row_stats_s || !st->ids_s ||
+      !st->gates_s)
+    return MOE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < hier_aux_workspace(d, h)) return MOE_ERR_WORKSPACE;
+  return hier_aux_launch(d, h, st, importance, load, out, workspace, as_stream(hip_stream));
 }
 
 moe_status moe_check_finite(void* hip_stream) {

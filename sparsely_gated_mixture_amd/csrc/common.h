@@ -94,6 +94,30 @@ __device__ __forceinline__ void note_nonfinite(int* flag, bool bad) {
   if (bad) *flag = 1;
 }
 
+// Exclusive scan of v over a block of N threads (*excl gets this thread's prefix);
+// returns the block total. warp_tot holds N / 64 ints of shared memory.
+template <int N>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* excl, int* warp_tot) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) warp_tot[w] = x;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < N / 64; ++i) {
+    if (i < w) before += warp_tot[i];
+    total += warp_tot[i];
+  }
+  *excl = before + x - v;
+  __syncthreads();
+  return total;
+}
+
 // ----------------------------------------------------------------- host-side checks
 struct Dims {
   int T, D, E, H, k;
@@ -132,5 +156,22 @@ moe_status combine_launch(const Dims& d, const void* Z, const int32_t* ids, cons
 moe_status aux_launch(const Dims& d, const int32_t* ids, const float* gates, const float* clean,
                       const float* noise_std, const float* row_stats, const int32_t* counts,
                       float* importance, float* load, float* out, void* ws, hipStream_t stream);
+
+// Hierarchical MoE (hier.hip, grouped gates in router.hip).
+void hier_dims(const Dims& d, const moe_hier* h, Dims* dp, Dims* ds);
+size_t route_groups_workspace(const Dims& ds, int G);
+moe_status route_groups_launch(const Dims& ds, int G, uint64_t seed, const void* X,
+                               const int32_t* goff, const int32_t* row_token, const float* Wsg,
+                               const float* Wsn, int32_t* ids, float* gates, float* clean,
+                               float* noise_std, float* row_stats, void* ws, int* nonfinite,
+                               hipStream_t stream);
+size_t hier_route_workspace(const Dims& d, const moe_hier* h);
+size_t hier_aux_workspace(const Dims& d, const moe_hier* h);
+moe_status hier_route_launch(const Dims& d, const moe_hier* h, const moe_problem* p, const void* X,
+                             const float* Wpg, const float* Wpn, const float* Wsg, const float* Wsn,
+                             int32_t* ids, float* gates, const moe_hier_state* st, void* ws,
+                             int* nonfinite, hipStream_t stream);
+moe_status hier_aux_launch(const Dims& d, const moe_hier* h, const moe_hier_state* st,
+                           float* importance, float* load, float* out, void* ws, hipStream_t stream);
 
 }  // namespace moe

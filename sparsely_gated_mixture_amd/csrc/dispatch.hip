@@ -40,29 +40,6 @@ __global__ __launch_bounds__(kThreads) void dispatch_count(const int32_t* __rest
     hist[static_cast<int64_t>(e) * nblk + blockIdx.x] = sh[e];
 }
 
-// Exclusive scan of v over a block (kScanThreads threads), returns the total.
-template <int N>
-__device__ __forceinline__ int block_exclusive_scan(int v, int* excl, int* warp_tot) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) warp_tot[w] = x;
-  __syncthreads();
-  int before = 0, total = 0;
-#pragma unroll
-  for (int i = 0; i < N / 64; ++i) {
-    if (i < w) before += warp_tot[i];
-    total += warp_tot[i];
-  }
-  *excl = before + x - v;
-  __syncthreads();
-  return total;
-}
-
 __global__ __launch_bounds__(kScanThreads) void dispatch_scan(int32_t* __restrict__ hist, int nblk,
                                                               int32_t* __restrict__ counts) {
   __shared__ int wt[kScanThreads / 64];
@@ -160,7 +137,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_place(
   }
   __syncthreads();
 
-  // gather: each token row is read once and written to its accepted rows
+  // gather: each token row is read once and written to its accepted rows (none without Xd)
+  if (Xd == nullptr) return;
   constexpr int V = Elem<T>::kVec;
   const bool vec_ok = (D % V) == 0;
   if (vec_ok) {

@@ -46,27 +46,6 @@ struct GemmArgs {
   int KS;  // k-steps per column block in Wp (multiple of 4)
 };
 
-__device__ __forceinline__ int block_exclusive_scan(int v, int* excl, int* wt) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) wt[w] = x;
-  __syncthreads();
-  int before = 0, total = 0;
-#pragma unroll
-  for (int i = 0; i < kThreads / 64; ++i) {
-    if (i < w) before += wt[i];
-    total += wt[i];
-  }
-  *excl = before + x - v;
-  __syncthreads();
-  return total;
-}
-
 // Operands live in native vector registers (the HIP uint4 struct defeats
 // register promotion of arrays).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -108,7 +87,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
     int s = 0;
     for (int e = e0; e < e1; ++e) s += (off[e + 1] - off[e] + BM - 1) / BM;
     int excl;
-    const int total = block_exclusive_scan(s, &excl, wt);
+    const int total = block_exclusive_scan<kThreads>(s, &excl, wt);
     for (int e = e0; e < e1; ++e) {
       sCum[e] = excl;
       excl += (off[e + 1] - off[e] + BM - 1) / BM;

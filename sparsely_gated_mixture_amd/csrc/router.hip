@@ -25,6 +25,8 @@
 //                  (K = next power of two >= k+1) merged by a bitonic
 //                  butterfly; writes ids, gates, row_stats. Switch also sums
 //                  exp(logit - max) for its gate.
+#include <algorithm>
+
 #include "common.h"
 
 namespace moe {
@@ -65,6 +67,14 @@ struct GemmArgs {
   int NB;              // 32-column blocks in wfrag (per piece)
   int KS;              // k-steps per column block (multiple of 4)
   int use_noise;
+  int vec_out;         // E % 4 == 0 and the outputs 16-byte aligned: float4 stores
+  // grouped mode (secondary gates of a hierarchical MoE): rows offsets goff[g] ..
+  // goff[g+1]-1 belong to group g, hold token row_token[r], use group g's weights
+  // (wfrag + g * wgroup) and draw noise from key (seed, 1 + g)
+  const int32_t* goff;
+  const int32_t* row_token;
+  int G;
+  int64_t wgroup;
 };
 
 struct SelectArgs {
@@ -112,10 +122,10 @@ __device__ __forceinline__ void box_muller(uint64_t a, uint64_t b, float& g0, fl
   g1 = static_cast<float>(rho * s);
 }
 
-// eps for experts 4q .. 4q+3 of token t.
-__device__ __forceinline__ void noise4(uint64_t seed, int t, int q, float g[4]) {
+// eps for experts 4q .. 4q+3 of token t; key (seed, key1).
+__device__ __forceinline__ void noise4(uint64_t seed, uint64_t key1, int t, int q, float g[4]) {
   uint64_t c0 = static_cast<uint64_t>(t), c1 = static_cast<uint64_t>(q), c2 = 0, c3 = 0;
-  philox4x64_10(c0, c1, c2, c3, seed, 0);
+  philox4x64_10(c0, c1, c2, c3, seed, key1);
   box_muller(c0, c1, g[0], g[1]);
   box_muller(c2, c3, g[2], g[3]);
 }
@@ -133,11 +143,16 @@ __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
 // One thread per (column block nb, k-step ks, lane). Column n of block nb is
 // expert 32*(nb/2) + lane%32 of Wg (nb even) or Wnoise (nb odd) with noise,
 // else expert 32*nb + lane%32 of Wg. k = ks*2V + (lane/32)*V + i. Zero padded.
+// blockIdx.y selects a gate of a stack (weights wstride floats apart, packed outputs
+// ostride uint4 apart): the secondary gates of a hierarchical MoE.
 template <bool kBf16>
 __global__ void router_pack(const float* __restrict__ Wg, const float* __restrict__ Wn,
                             int D, int E, int with_noise, int NB, int KS,
-                            uint4* __restrict__ out) {
+                            uint4* __restrict__ out, int64_t wstride, int64_t ostride) {
   constexpr int V = kBf16 ? 8 : 4;
+  Wg += blockIdx.y * wstride;
+  if (Wn) Wn += blockIdx.y * wstride;
+  out += blockIdx.y * ostride;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t total = static_cast<int64_t>(NB) * KS * kWave;
   if (idx >= total) return;
@@ -175,8 +190,9 @@ __global__ void router_pack(const float* __restrict__ Wg, const float* __restric
 }
 
 // ------------------------------------------------------------------ router GEMM + epilogue
-// BM token rows per block (128, or 64 / 32 when T is small).
-template <typename XT, bool kFullK, int BM>
+// BM token rows per block (128, or 64 / 32 when T is small). kGrouped: rows grouped by
+// gate (tile table from goff in dynamic LDS, G + 1 ints).
+template <typename XT, bool kFullK, int BM, bool kGrouped>
 __global__ __launch_bounds__(kThreads, 2) void router_gemm(GemmArgs a) {
   constexpr int V = Elem<XT>::kVec;
   constexpr int kPieces = sizeof(XT) == 2 ? 3 : 1;
@@ -188,29 +204,75 @@ __global__ __launch_bounds__(kThreads, 2) void router_gemm(GemmArgs a) {
   constexpr int kStage = BM * kAStride > kEpiHalf ? BM * kAStride : kEpiHalf;
 
   __shared__ __align__(16) unsigned char sA[2][kStage];
+  extern __shared__ int sCum[];  // grouped: G + 1 running row-tile counts
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int T = a.T, D = a.D, E = a.E;
-  const int mtiles = (T + BM - 1) / BM, ntiles = (a.NB + 7) / 8;
-  const int total = mtiles * ntiles;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
-  const int local = blockIdx.x / kXcds;
-  if (local >= per_xcd) return;
-  const int logical = (blockIdx.x % kXcds) * per_xcd + local;
-  if (logical >= total) return;
-  const int m_tile = logical / ntiles, n_tile = logical - m_tile * ntiles;
-  const int r0 = m_tile * BM;
-  const int rows = min(BM, T - r0);
+  const int ntiles = (a.NB + 7) / 8;
+  int g = 0, m_tile, n_tile, r0, rows;
+  if constexpr (kGrouped) {
+    const int G = a.G;
+    const int per = (G + kThreads - 1) / kThreads;
+    const int g0 = tid * per, g1 = min(G, g0 + per);
+    int s = 0;
+    for (int q = g0; q < g1; ++q) s += (a.goff[q + 1] - a.goff[q] + BM - 1) / BM;
+    int excl;
+    __shared__ int wt[kThreads / 64];
+    const int tot = block_exclusive_scan<kThreads>(s, &excl, wt);
+    for (int q = g0; q < g1; ++q) {
+      sCum[q] = excl;
+      excl += (a.goff[q + 1] - a.goff[q] + BM - 1) / BM;
+    }
+    if (tid == 0) sCum[G] = tot;
+    __syncthreads();
+    const int total = sCum[G] * ntiles;
+    const int per_xcd = (total + kXcds - 1) / kXcds;
+    const int local = blockIdx.x / kXcds;
+    if (local >= per_xcd) return;
+    const int logical = (blockIdx.x % kXcds) * per_xcd + local;
+    if (logical >= total) return;
+    const int q = logical / ntiles;  // group-major, then column tile, then row tile
+    int lo = 0, hi = G;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (sCum[mid] > q) hi = mid; else lo = mid + 1;
+    }
+    g = lo - 1;
+    const int mt = sCum[g + 1] - sCum[g];
+    const int loc = logical - sCum[g] * ntiles;
+    n_tile = loc / mt;
+    m_tile = loc - n_tile * mt;
+    r0 = a.goff[g] + m_tile * BM;
+    rows = min(BM, a.goff[g + 1] - r0);
+  } else {
+    const int mtiles = (T + BM - 1) / BM;
+    const int total = mtiles * ntiles;
+    const int per_xcd = (total + kXcds - 1) / kXcds;
+    const int local = blockIdx.x / kXcds;
+    if (local >= per_xcd) return;
+    const int logical = (blockIdx.x % kXcds) * per_xcd + local;
+    if (logical >= total) return;
+    m_tile = logical / ntiles;
+    n_tile = logical - m_tile * ntiles;
+    r0 = m_tile * BM;
+    rows = min(BM, T - r0);
+  }
   const int nst = a.KS / 4;
 
   const XT* X = static_cast<const XT*>(a.X);
   const int aseg = tid & 7, arow0 = tid >> 3;
   const bool vec_ok = (D % V) == 0;
   u32x4 areg[kChunks];
+  int64_t asrc[kChunks];  // X row of each chunk (the row's token when grouped)
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int r = r0 + min(arow0 + i * (kThreads / 8), rows - 1);
+    asrc[i] = static_cast<int64_t>(kGrouped ? a.row_token[r] : r) * D;
+  }
   auto load_a = [&](int st) {
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
-      const XT* row = X + static_cast<int64_t>(r0 + min(arow0 + i * (kThreads / 8), rows - 1)) * D;
+      const XT* row = X + asrc[i];
       if constexpr (kFullK) {
         areg[i] = *reinterpret_cast<const u32x4*>(row + st * kStageElems + aseg * V);
       } else {
@@ -229,8 +291,9 @@ __global__ __launch_bounds__(kThreads, 2) void router_gemm(GemmArgs a) {
   // blocks without); blocks past NB read a valid block and are never stored
   const int cb0 = n_tile * 8 + wave * 2;
   const int64_t piece = static_cast<int64_t>(a.NB) * a.KS * kWave;
-  const u32x4* W0 = a.wfrag + static_cast<int64_t>(min(cb0, a.NB - 1)) * a.KS * kWave + lane;
-  const u32x4* W1 = a.wfrag + static_cast<int64_t>(min(cb0 + 1, a.NB - 1)) * a.KS * kWave + lane;
+  const u32x4* wf = a.wfrag + (kGrouped ? g * a.wgroup : 0);
+  const u32x4* W0 = wf + static_cast<int64_t>(min(cb0, a.NB - 1)) * a.KS * kWave + lane;
+  const u32x4* W1 = wf + static_cast<int64_t>(min(cb0 + 1, a.NB - 1)) * a.KS * kWave + lane;
 
   f32x16 acc[MB][2];
 #pragma unroll
@@ -293,7 +356,8 @@ __global__ __launch_bounds__(kThreads, 2) void router_gemm(GemmArgs a) {
   // ---- epilogue, one 32-row block at a time through a wave-private LDS tile [2][32][kTS]
   float* Ts = reinterpret_cast<float*>(&sA[0][0]) + wave * (2 * 32 * kTS);
   const bool check = a.nonfinite != nullptr;
-  const bool full4 = (E % 4) == 0;
+  const bool full4 = a.vec_out != 0;
+  const uint64_t key1 = kGrouped ? static_cast<uint64_t>(1 + g) : 0;
   bool bad = false;
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
@@ -310,7 +374,7 @@ __global__ __launch_bounds__(kThreads, 2) void router_gemm(GemmArgs a) {
         const int row = it >> 3, g4 = it & 7;
         const int t = r0 + m * 32 + row;
         const int e0 = eb * 32 + 4 * g4;
-        if (t >= T || e0 >= E) continue;
+        if (m * 32 + row >= rows || e0 >= E) continue;
         float cl[4], sd[4], ep[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -325,7 +389,7 @@ __global__ __launch_bounds__(kThreads, 2) void router_gemm(GemmArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) ep[i] = (e0 + i < E) ? a.eps[base + i] : 0.f;
         } else {
-          noise4(a.seed, t, e0 >> 2, ep);
+          noise4(a.seed, key1, kGrouped ? a.row_token[t] : t, e0 >> 2, ep);
         }
         float hv[4];
 #pragma unroll
@@ -353,7 +417,7 @@ __global__ __launch_bounds__(kThreads, 2) void router_gemm(GemmArgs a) {
         const int c = g >> 3, g4 = g & 7;
         const int t = r0 + m * 32 + row;
         const int e0 = (cb0 + c) * 32 + 4 * g4;
-        if (t >= T || e0 >= E) continue;
+        if (m * 32 + row >= rows || e0 >= E) continue;
         float cl[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -522,17 +586,41 @@ static size_t router_wbytes(const Dims& d) {
   return align256(pieces * router_nb(d) * static_cast<size_t>(router_ks(d)) * kWave * 16);
 }
 
+// 128-row tiles, or 64 / 32 while that leaves fewer than 512 blocks
+static int router_bm(int64_t rows, int NB) {
+  int bm = 128;
+  while (bm > 32 && ceil_div64(rows, bm) * ceil_div(NB, 8) < 512) bm >>= 1;
+  return bm;
+}
+static int vec_outputs(int E, const float* a, const float* b, const float* c) {
+  const uintptr_t m = reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
+                      reinterpret_cast<uintptr_t>(c);
+  return (E % 4 == 0 && m % 16 == 0) ? 1 : 0;
+}
+
 size_t route_workspace(const Dims& d) {
   size_t b = router_wbytes(d);
   if (router_noise(d)) b += align256(static_cast<size_t>(d.T) * d.E * sizeof(float));
   return b;
 }
 
-template <typename XT, bool kFullK>
+template <typename XT, bool kFullK, bool kGrouped>
 static void router_gemm_bm(int bm, int grid, const GemmArgs& g, hipStream_t stream) {
-  if (bm == 128) router_gemm<XT, kFullK, 128><<<grid, kThreads, 0, stream>>>(g);
-  else if (bm == 64) router_gemm<XT, kFullK, 64><<<grid, kThreads, 0, stream>>>(g);
-  else router_gemm<XT, kFullK, 32><<<grid, kThreads, 0, stream>>>(g);
+  const size_t lds = kGrouped ? (static_cast<size_t>(g.G) + 1) * sizeof(int) : 0;
+  if (bm == 128) router_gemm<XT, kFullK, 128, kGrouped><<<grid, kThreads, lds, stream>>>(g);
+  else if (bm == 64) router_gemm<XT, kFullK, 64, kGrouped><<<grid, kThreads, lds, stream>>>(g);
+  else router_gemm<XT, kFullK, 32, kGrouped><<<grid, kThreads, lds, stream>>>(g);
+}
+template <bool kGrouped>
+static void router_gemm_launch(const Dims& d, int bm, int grid, const GemmArgs& g, hipStream_t stream) {
+  const bool full = d.D % (d.dtype == MOE_BF16 ? 64 : 32) == 0;
+  if (d.dtype == MOE_BF16) {
+    if (full) router_gemm_bm<uint16_t, true, kGrouped>(bm, grid, g, stream);
+    else router_gemm_bm<uint16_t, false, kGrouped>(bm, grid, g, stream);
+  } else {
+    if (full) router_gemm_bm<float, true, kGrouped>(bm, grid, g, stream);
+    else router_gemm_bm<float, false, kGrouped>(bm, grid, g, stream);
+  }
 }
 
 template <int KL>
@@ -554,6 +642,28 @@ static void select_launch(int kl, int lpr, const SelectArgs& sa, hipStream_t str
   }
 }
 
+// Top-k of every score row: ids, gates, row_stats (v_k, v_{k+1}).
+static void select_rows(const float* score, int T, int E, int k, bool switch_gate, int32_t* ids,
+                        float* gates, float* row_stats, hipStream_t stream) {
+  SelectArgs sa;
+  sa.score = score;
+  sa.ids = ids;
+  sa.gates = gates;
+  sa.row_stats = row_stats;
+  sa.T = T;
+  sa.E = E;
+  sa.k = k;
+  sa.switch_gate = switch_gate ? 1 : 0;
+  sa.vec = (E % 4 == 0 && reinterpret_cast<uintptr_t>(score) % 16 == 0) ? 1 : 0;
+  // lanes per row: 8, doubled (up to 64) while the grid would hold fewer than 64K threads and
+  // each lane would still see at least 16 scores
+  int lpr = 8;
+  while (lpr < 64 && static_cast<int64_t>(T) * lpr < 65536 && E >= 32 * lpr) lpr <<= 1;
+  const int need = k + 1;
+  const int kl = need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
+  select_launch(kl, lpr, sa, stream);
+}
+
 moe_status route_launch(const Dims& d, const moe_problem* p, const void* X, const float* Wg,
                         const float* Wnoise, const float* bias, const float* eps, int32_t* ids,
                         float* gates, float* clean, float* noise_std, float* row_stats,
@@ -565,9 +675,9 @@ moe_status route_launch(const Dims& d, const moe_problem* p, const void* X, cons
   const int64_t items = static_cast<int64_t>(NB) * KS * kWave;
   const int pgrid = static_cast<int>(ceil_div64(items, 256));
   if (d.dtype == MOE_BF16)
-    router_pack<true><<<pgrid, 256, 0, stream>>>(Wg, noise ? Wnoise : nullptr, d.D, d.E, noise, NB, KS, wfrag);
+    router_pack<true><<<pgrid, 256, 0, stream>>>(Wg, noise ? Wnoise : nullptr, d.D, d.E, noise, NB, KS, wfrag, 0, 0);
   else
-    router_pack<false><<<pgrid, 256, 0, stream>>>(Wg, noise ? Wnoise : nullptr, d.D, d.E, noise, NB, KS, wfrag);
+    router_pack<false><<<pgrid, 256, 0, stream>>>(Wg, noise ? Wnoise : nullptr, d.D, d.E, noise, NB, KS, wfrag, 0, 0);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
 
   GemmArgs g;
@@ -586,38 +696,89 @@ moe_status route_launch(const Dims& d, const moe_problem* p, const void* X, cons
   g.NB = NB;
   g.KS = KS;
   g.use_noise = noise ? 1 : 0;
-  // 128-row tiles, or 64 / 32 while that leaves fewer than 512 blocks
-  int bm = 128;
-  while (bm > 32 && static_cast<int64_t>(ceil_div(d.T, bm)) * ceil_div(NB, 8) < 512) bm >>= 1;
+  g.vec_out = vec_outputs(d.E, clean, noise ? noise_std : nullptr, H);
+  g.goff = nullptr;
+  g.row_token = nullptr;
+  g.G = 0;
+  g.wgroup = 0;
+  const int bm = router_bm(d.T, NB);
   const int64_t tiles = static_cast<int64_t>(ceil_div(d.T, bm)) * ceil_div(NB, 8);
   const int grid = static_cast<int>(ceil_div64(tiles, kXcds) * kXcds);
-  const bool full = d.D % (d.dtype == MOE_BF16 ? 64 : 32) == 0;
-  if (d.dtype == MOE_BF16) {
-    if (full) router_gemm_bm<uint16_t, true>(bm, grid, g, stream);
-    else router_gemm_bm<uint16_t, false>(bm, grid, g, stream);
-  } else {
-    if (full) router_gemm_bm<float, true>(bm, grid, g, stream);
-    else router_gemm_bm<float, false>(bm, grid, g, stream);
-  }
+  router_gemm_launch<false>(d, bm, grid, g, stream);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
 
-  SelectArgs sa;
-  sa.score = noise ? H : clean;
-  sa.ids = ids;
-  sa.gates = gates;
-  sa.row_stats = row_stats;
-  sa.T = d.T;
-  sa.E = d.E;
-  sa.k = d.k;
-  sa.switch_gate = d.gating == MOE_GATE_SWITCH_TOP1 ? 1 : 0;
-  sa.vec = (d.E % 4 == 0 && reinterpret_cast<uintptr_t>(sa.score) % 16 == 0) ? 1 : 0;
-  // lanes per row: 8, doubled (up to 64) while the grid would hold fewer than 64K threads and
-  // each lane would still see at least 16 scores
-  int lpr = 8;
-  while (lpr < 64 && static_cast<int64_t>(d.T) * lpr < 65536 && d.E >= 32 * lpr) lpr <<= 1;
-  const int need = d.k + 1;
-  const int kl = need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
-  select_launch(kl, lpr, sa, stream);
+  select_rows(noise ? H : clean, d.T, d.E, d.k, d.gating == MOE_GATE_SWITCH_TOP1, ids, gates,
+              row_stats, stream);
+  return launch_status();
+}
+
+// ------------------------------------------------------------------ grouped gates
+// Secondary gates of a hierarchical MoE. ds: T = R rows (grouped by gate through goff),
+// D, E = experts per group, k = kept per group. Weights [G][D][E] (Wsg, Wsn).
+static int64_t group_pack_stride(const Dims& ds) {  // uint4 per group in the packed stack
+  const int pieces = ds.dtype == MOE_BF16 ? 3 : 1;
+  return static_cast<int64_t>(pieces) * router_nb(ds) * router_ks(ds) * kWave;
+}
+
+size_t route_groups_workspace(const Dims& ds, int G) {
+  size_t b = align256(static_cast<size_t>(G) * group_pack_stride(ds) * 16);
+  if (router_noise(ds)) b += align256(static_cast<size_t>(ds.T) * ds.E * sizeof(float));
+  return b;
+}
+
+moe_status route_groups_launch(const Dims& ds, int G, uint64_t seed, const void* X,
+                               const int32_t* goff, const int32_t* row_token, const float* Wsg,
+                               const float* Wsn, int32_t* ids, float* gates, float* clean,
+                               float* noise_std, float* row_stats, void* ws, int* nonfinite,
+                               hipStream_t stream) {
+  const bool noise = router_noise(ds);
+  const int NB = router_nb(ds), KS = router_ks(ds);
+  const int64_t gstride = group_pack_stride(ds);
+  uint4* wfrag = static_cast<uint4*>(ws);
+  float* H = noise ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                              align256(static_cast<size_t>(G) * gstride * 16))
+                   : nullptr;
+  const int64_t items = static_cast<int64_t>(NB) * KS * kWave;
+  const dim3 pgrid(static_cast<unsigned>(ceil_div64(items, 256)), static_cast<unsigned>(G));
+  const int64_t wstride = static_cast<int64_t>(ds.D) * ds.E;
+  if (ds.dtype == MOE_BF16)
+    router_pack<true><<<pgrid, 256, 0, stream>>>(Wsg, noise ? Wsn : nullptr, ds.D, ds.E, noise, NB,
+                                                 KS, wfrag, wstride, gstride);
+  else
+    router_pack<false><<<pgrid, 256, 0, stream>>>(Wsg, noise ? Wsn : nullptr, ds.D, ds.E, noise, NB,
+                                                  KS, wfrag, wstride, gstride);
+  if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+
+  GemmArgs g;
+  g.X = X;
+  g.wfrag = reinterpret_cast<const u32x4*>(wfrag);
+  g.bias = nullptr;
+  g.eps = nullptr;
+  g.clean = clean;
+  g.std_out = noise ? noise_std : nullptr;
+  g.H = H;
+  g.nonfinite = nonfinite;
+  g.seed = seed;
+  g.T = ds.T;
+  g.D = ds.D;
+  g.E = ds.E;
+  g.NB = NB;
+  g.KS = KS;
+  g.use_noise = noise ? 1 : 0;
+  g.vec_out = vec_outputs(ds.E, clean, noise ? noise_std : nullptr, H);
+  g.goff = goff;
+  g.row_token = row_token;
+  g.G = G;
+  g.wgroup = gstride;
+  const int bm = router_bm(ds.T, NB);
+  // at most (R + G*(bm-1)) / bm row tiles over all groups
+  const int64_t mtiles = (static_cast<int64_t>(ds.T) + static_cast<int64_t>(G) * (bm - 1)) / bm;
+  const int64_t tiles = mtiles * ceil_div(NB, 8);
+  if (tiles > 0x7fff0000LL) return MOE_ERR_UNSUPPORTED;
+  const int grid = static_cast<int>(ceil_div64(std::max<int64_t>(tiles, 1), kXcds) * kXcds);
+  router_gemm_launch<true>(ds, bm, grid, g, stream);
+  if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  select_rows(noise ? H : clean, ds.T, ds.E, ds.k, false, ids, gates, row_stats, stream);
   return launch_status();
 }
 

@@ -29,6 +29,7 @@ ENTRY_POINTS = [
     "moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_packed_weight_bytes",
     "moe_route", "moe_dispatch", "moe_pack_expert_weights", "moe_grouped_gemm",
     "moe_expert_ffn", "moe_combine", "moe_aux_loss", "moe_check_finite", "moe_status_string",
+    "moe_hier_workspace_size", "moe_route_hier", "moe_aux_loss_hier",
 ]
 
 
@@ -48,6 +49,21 @@ class Problem(ctypes.Structure):
         ("seed", ctypes.c_uint64), ("check_finite", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
     ]
+
+
+class Hier(ctypes.Structure):
+    """Mirror of moe_hier."""
+    _fields_ = [("groups", ctypes.c_int32), ("k_primary", ctypes.c_int32)]
+
+
+HIER_STATE_FIELDS = ["ids_p", "gates_p", "clean_p", "std_p", "row_stats_p", "pos_p", "accepted_p",
+                     "counts_p", "offsets_p", "row_token_p", "clean_s", "std_s", "row_stats_s",
+                     "ids_s", "gates_s"]
+
+
+class HierState(ctypes.Structure):
+    """Mirror of moe_hier_state (device pointers)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in HIER_STATE_FIELDS]
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -70,6 +86,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_aux_loss": (ctypes.c_int, [P] + [vp] * 9 + [vp, sz, vp]),
         "moe_check_finite": (ctypes.c_int, [vp]),
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "moe_hier_workspace_size": (sz, [P, ctypes.POINTER(Hier), ctypes.c_int]),
+        "moe_route_hier": (ctypes.c_int, [P, ctypes.POINTER(Hier)] + [vp] * 7 +
+                           [ctypes.POINTER(HierState), vp, sz, vp]),
+        "moe_aux_loss_hier": (ctypes.c_int, [P, ctypes.POINTER(Hier), ctypes.POINTER(HierState)] +
+                              [vp] * 4 + [sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -184,6 +205,36 @@ def moe_aux_loss(p, ids, gates, clean, noise_std, row_stats, counts, importance,
            "moe_aux_loss")
 
 
+def hier(groups: int, k_primary: int) -> Hier:
+    return Hier(groups=int(groups), k_primary=int(k_primary))
+
+
+def hier_state(st: dict) -> HierState:
+    """HierState from a dict of device tensors (missing / None fields are NULL)."""
+    return HierState(**{n: (_ptr(st[n]).value if st.get(n) is not None else None)
+                        for n in HIER_STATE_FIELDS})
+
+
+def moe_hier_workspace_size(p: Problem, h: Hier, which: int) -> int:
+    return _lib.moe_hier_workspace_size(ctypes.byref(p), ctypes.byref(h), which)
+
+
+def moe_route_hier(p, h, X, Wpg, Wpn, Wsg, Wsn, ids, gates, st: dict, ws, stream=None):
+    hs = hier_state(st)
+    _check(_lib.moe_route_hier(ctypes.byref(p), ctypes.byref(h), _ptr(X), _ptr(Wpg), _ptr(Wpn),
+                               _ptr(Wsg), _ptr(Wsn), _ptr(ids), _ptr(gates), ctypes.byref(hs),
+                               _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)),
+           "moe_route_hier")
+
+
+def moe_aux_loss_hier(p, h, st: dict, importance, load, out, ws, stream=None):
+    hs = hier_state(st)
+    _check(_lib.moe_aux_loss_hier(ctypes.byref(p), ctypes.byref(h), ctypes.byref(hs),
+                                  _ptr(importance), _ptr(load), _ptr(out), _ptr(ws),
+                                  ws.numel() if ws is not None else 0, _stream(stream)),
+           "moe_aux_loss_hier")
+
+
 def moe_check_finite(stream=None):
     _check(_lib.moe_check_finite(_stream(stream)), "moe_check_finite")
 
@@ -284,3 +335,40 @@ class Layer:
         if aux:
             self.aux()
         return self.b
+
+
+class HierLayer(Layer):
+    """A hierarchical MoE layer: two-level routing (moe_route_hier), then the flat
+    dispatch, expert FFN and combine over all E experts, and the hierarchical
+    balancing terms (moe_aux_loss_hier)."""
+
+    def __init__(self, p: Problem, h: Hier, Wpg, Wpn, Wsg, Wsn, W1, W2, device="cuda"):
+        super().__init__(p, None, None, None, W1, W2, device=device)
+        self.h = h
+        self.Wpg, self.Wpn, self.Wsg, self.Wsn = Wpg, Wpn, Wsg, Wsn
+        T, a, kp = p.T, h.groups, h.k_primary
+        b, ks = p.E // a, p.k // kp
+        R = T * kp
+        noisy = p.noise == 1
+        e = lambda *s, dtype=torch.float32: torch.empty(*s, dtype=dtype, device=device)
+        self.st = dict(
+            ids_p=e(T, kp, dtype=torch.int32), gates_p=e(T, kp), clean_p=e(T, a),
+            std_p=e(T, a) if noisy else None, row_stats_p=e(T, 2),
+            pos_p=e(T, kp, dtype=torch.int32), accepted_p=e(T, kp, dtype=torch.uint8),
+            counts_p=e(a, dtype=torch.int32), offsets_p=e(a + 1, dtype=torch.int32),
+            row_token_p=e(R, dtype=torch.int32), clean_s=e(R, b),
+            std_s=e(R, b) if noisy else None, row_stats_s=e(R, 2),
+            ids_s=e(R, ks, dtype=torch.int32), gates_s=e(R, ks))
+        self.ws_route_h = e(max(moe_hier_workspace_size(p, h, MOE_WS_ROUTE), 1), dtype=torch.uint8)
+        self.ws_aux_h = e(max(moe_hier_workspace_size(p, h, MOE_WS_AUX), 1), dtype=torch.uint8)
+
+    def route(self, X, eps=None):
+        if eps is not None:
+            raise ValueError("the hierarchical router draws its own noise")
+        b = self.b
+        moe_route_hier(self.p, self.h, X, self.Wpg, self.Wpn, self.Wsg, self.Wsn, b.ids, b.gates,
+                       self.st, self.ws_route_h)
+
+    def aux(self):
+        b = self.b
+        moe_aux_loss_hier(self.p, self.h, self.st, b.importance, b.load, b.aux_out, self.ws_aux_h)

@@ -120,3 +120,28 @@ def test_sizes_scale(m):
     assert m.moe_packed_weight_bytes(p, 3) == 0
     # router: three bf16 pieces of [Wg | Wnoise] plus the fp32 noisy scores [T,E]
     assert m.moe_workspace_size(p, m.MOE_WS_ROUTE) == 3 * 1024 * 512 * 2 + 65536 * 256 * 4
+
+
+def test_hier_validation(m):
+    p = _p(m, T=64, E=12, k=4, noise=True)
+    assert m.moe_hier_workspace_size(p, m.hier(4, 2), m.MOE_WS_ROUTE) > 0
+    assert m.moe_hier_workspace_size(p, m.hier(4, 2), m.MOE_WS_AUX) > 0
+    for h in (m.hier(5, 2), m.hier(4, 3), m.hier(4, 5), m.hier(0, 1), m.hier(12, 1)):
+        # 12 not divisible by 5; 4 % 3 != 0; k_primary > groups; no groups; k_s = 4 > b = 1
+        assert m.moe_hier_workspace_size(p, h, m.MOE_WS_ROUTE) == 0
+    h = m.hier(4, 2)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: rejected on the host
+    st = m.HierState(**{n: 0x1000 for n in m.HIER_STATE_FIELDS})
+    args = [fake] * 7
+    sw = _p(m, T=64, E=12, k=1, gating="switch", noise=False)
+    assert m._lib.moe_route_hier(ctypes.byref(sw), ctypes.byref(m.hier(4, 1)), *args,
+                                 ctypes.byref(st), fake, 1 << 30, None) == -1
+    assert m._lib.moe_route_hier(ctypes.byref(p), ctypes.byref(h), *args, None, fake, 1 << 30,
+                                 None) == -1
+    need = m.moe_hier_workspace_size(p, h, m.MOE_WS_ROUTE)
+    assert m._lib.moe_route_hier(ctypes.byref(p), ctypes.byref(h), *args, ctypes.byref(st), fake,
+                                 need - 1, None) == -5
+    st_nostd = m.HierState(**{n: (None if n in ("std_p", "std_s") else 0x1000)
+                              for n in m.HIER_STATE_FIELDS})
+    assert m._lib.moe_aux_loss_hier(ctypes.byref(p), ctypes.byref(h), ctypes.byref(st_nostd),
+                                    fake, fake, fake, fake, 1 << 30, None) == -1
