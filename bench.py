@@ -68,7 +68,12 @@ def cpu_baseline(w, inp, budget_tokens: int):
         threads = 1
     S = min(budget_tokens, w.T)
     t0 = time.perf_counter()
-    O.forward(inp, w, t_count=S)
+    if w.groups > 0:
+        from oracle import hier as HO
+        # the prefix as a batch of its own (capacity, if any, then follows the prefix size)
+        HO.forward_hier(dict(inp, X=inp["X"][:S]), w.replace(T=S))
+    else:
+        O.forward(inp, w, t_count=S)
     dt = time.perf_counter() - t0
     return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {S} of {w.T} tokens of {w.name}: route, slots, per-token expert "
@@ -85,6 +90,46 @@ def copy_probe(torch, nbytes: int, reps: int):
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def vendor_gemm(torch, workload: str, reps: int):
+    """Library batched GEMMs on the expert shapes: E groups of ceil(T*k/E) rows (capped at the
+    capacity), bf16 in and out, both layers, plus one large square GEMM; median of reps."""
+    from sparsely_gated_mixture_amd import inputs as I
+    w = I.WORKLOADS[workload]
+    dt = torch.bfloat16 if w.act == "bf16" else torch.float32
+    cap = w.T if w.capacity_factor <= 0 else max(w.min_capacity, min(w.T, int(w.k * w.T * w.capacity_factor // w.E)))
+    R = min(cap, -(-w.T * w.k // w.E))
+    g = torch.Generator(device="cuda").manual_seed(0)
+    A = torch.randn(w.E, R, w.D, device="cuda", dtype=dt, generator=g)
+    W1 = torch.randn(w.E, w.D, w.H, device="cuda", dtype=dt, generator=g)
+    W2 = torch.randn(w.E, w.H, w.D, device="cuda", dtype=dt, generator=g)
+    Hh = torch.empty(w.E, R, w.H, device="cuda", dtype=dt)
+    Z = torch.empty(w.E, R, w.D, device="cuda", dtype=dt)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        for i in range(reps):
+            ev[i].record()
+            fn()
+        ev[reps].record()
+        torch.cuda.synchronize()
+        return float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+
+    fl = 2.0 * w.E * R * w.D * w.H
+    m1 = timed(lambda: torch.bmm(A, W1, out=Hh))
+    m2 = timed(lambda: torch.bmm(Hh, W2, out=Z))
+    n = 8192
+    S1 = torch.randn(n, n, device="cuda", dtype=dt, generator=g)
+    S2 = torch.randn(n, n, device="cuda", dtype=dt, generator=g)
+    O = torch.empty_like(S1)
+    m3 = timed(lambda: torch.mm(S1, S2, out=O))
+    print(json.dumps({"vendor_gemm": workload, "rows_per_expert": R, "experts": w.E,
+                      "layer1_ms": m1, "layer1_TFLOPs": fl / m1 / 1e9,
+                      "layer2_ms": m2, "layer2_TFLOPs": fl / m2 / 1e9,
+                      "square_8192_ms": m3, "square_8192_TFLOPs": 2.0 * n ** 3 / m3 / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,6 +139,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--copy-probe", type=int, default=0, help="bytes; run copies only")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time torch.bmm (the ROCm BLAS library) on the workload's expert GEMM "
+                         "shapes with a uniform rows-per-expert split, for context only")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -104,6 +152,9 @@ def main():
     import torch
     if args.copy_probe:
         copy_probe(torch, args.copy_probe, max(args.steps, 1))
+        return
+    if args.vendor_gemm:
+        vendor_gemm(torch, args.workload, max(args.steps, 1))
         return
 
     from sparsely_gated_mixture_amd import inputs as I
@@ -116,8 +167,13 @@ def main():
     p = moe.problem(T=w.T, D=w.D, E=w.E, H=w.H, k=w.k, dtype=w.act, gating=w.gating,
                     noise=w.noise, capacity_factor=w.capacity_factor,
                     min_capacity=w.min_capacity, seed=w.seed)
-    L = moe.Layer(p, _dev(torch, inp["Wg"]), _dev(torch, inp["Wnoise"]), _dev(torch, inp["bias"]),
-                  _dev(torch, inp["W1"]), _dev(torch, inp["W2"]))
+    if w.groups > 0:  # hierarchical gate: route / aux are the two-level stages
+        L = moe.HierLayer(p, moe.hier(w.groups, w.k_primary), _dev(torch, inp["Wpg"]),
+                          _dev(torch, inp["Wpn"]), _dev(torch, inp["Wsg"]),
+                          _dev(torch, inp["Wsn"]), _dev(torch, inp["W1"]), _dev(torch, inp["W2"]))
+    else:
+        L = moe.Layer(p, _dev(torch, inp["Wg"]), _dev(torch, inp["Wnoise"]),
+                      _dev(torch, inp["bias"]), _dev(torch, inp["W1"]), _dev(torch, inp["W2"]))
     X = _dev(torch, inp["X"])
     torch.cuda.synchronize()
 
@@ -191,7 +247,10 @@ def main():
         "dtype": w.act,
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "D": w.D, "E": w.E, "k": w.k, "H": w.H,
-                   "gating": w.gating, "capacity_factor": w.capacity_factor,
+                   "gating": w.gating if w.groups == 0 else
+                   f"hierarchical {w.groups} groups x {w.E // w.groups}, k {w.k_primary} x "
+                   f"{w.k // w.k_primary}",
+                   "capacity_factor": w.capacity_factor,
                    "capacity": moe.moe_capacity(p), "accepted_rows": A,
                    "dropped": w.T * w.k - A, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": "grouped_gemm", "achieved": achieved,

@@ -105,6 +105,7 @@ __global__ __launch_bounds__(kThreads) void hier_group_partial(HierAuxArgs a) {
   __shared__ float sGp[kChunk], sR0[kChunk], sR1[kChunk];
   __shared__ int sId[kChunk * MOE_MAX_K];
   __shared__ float sG[kChunk * MOE_MAX_K];
+  __shared__ float sRedI[kThreads], sRedL[kThreads];
   int g = 0;
   const int c = group_chunk(a.counts_p, a.a, blockIdx.x, cum, wt, &g);
   if (c < 0) return;  // uniform: past the real chunk count
@@ -129,26 +130,44 @@ __global__ __launch_bounds__(kThreads) void hier_group_partial(HierAuxArgs a) {
     }
   }
   __syncthreads();
+  // threads = P row slices x be experts (be = min(b, kThreads)); slice s takes rows s, s+P, ..
+  const int be = min(b, kThreads);
+  const int P = kThreads / be;
+  const int slice = tid / be, el = tid - slice * be;
   const int64_t plane = static_cast<int64_t>(a.nblk) * b;
-  for (int e = tid; e < b; e += kThreads) {
+  for (int e0 = 0; e0 < b; e0 += be) {
+    const int e = e0 + el;
     float imp = 0.f, load = 0.f;
-    for (int r = 0; r < nr; ++r) {
-      bool inside = false;
-      for (int j = 0; j < ks; ++j)
-        if (sId[r * ks + j] == e) {
-          inside = true;
-          imp += sGp[r] * sG[r * ks + j];
+    if (slice < P && e < b) {
+      for (int r = slice; r < nr; r += P) {
+        bool inside = false;
+        for (int j = 0; j < ks; ++j)
+          if (sId[r * ks + j] == e) {
+            inside = true;
+            imp += sGp[r] * sG[r * ks + j];
+          }
+        if (a.use_noise) {
+          const int64_t ix = static_cast<int64_t>(r0 + r) * b + e;
+          const float diff = a.clean_s[ix] - (inside ? sR1[r] : sR0[r]);
+          const float sd = a.std_s[ix];
+          load += sd > 0.f ? phi(diff / sd) : (diff > 0.f ? 1.f : (diff == 0.f ? 0.5f : 0.f));
         }
-      if (a.use_noise) {
-        const int64_t ix = static_cast<int64_t>(r0 + r) * b + e;
-        const float diff = a.clean_s[ix] - (inside ? sR1[r] : sR0[r]);
-        const float sd = a.std_s[ix];
-        load += sd > 0.f ? phi(diff / sd) : (diff > 0.f ? 1.f : (diff == 0.f ? 0.5f : 0.f));
       }
     }
-    const int64_t o = static_cast<int64_t>(blockIdx.x) * b + e;
-    a.partial[o] = imp;
-    a.partial[plane + o] = load;
+    // slices added in fixed order
+    sRedI[tid] = imp;
+    sRedL[tid] = load;
+    __syncthreads();
+    if (slice == 0 && e < b) {
+      for (int q = 1; q < P; ++q) {
+        imp += sRedI[q * be + el];
+        load += sRedL[q * be + el];
+      }
+      const int64_t o = static_cast<int64_t>(blockIdx.x) * b + e;
+      a.partial[o] = imp;
+      a.partial[plane + o] = load;
+    }
+    __syncthreads();
   }
 }
 

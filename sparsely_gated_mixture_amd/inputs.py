@@ -26,6 +26,8 @@ used or needed, random draws stand in for them):
                  "Hierarchical Mixture-of-Experts", with the first-level
                  branching factor 16 and two choices per level of the paper's
                  1024-expert hierarchical model)
+  flat1024_bf16  the same shapes with one flat noisy top-4 gate over the 1024
+                 experts (routing-cost comparison)
 
 Recipe. Every tensor comes from its own numpy PCG64 stream keyed by
 SeedSequence([seed, tag]) (expert weights: [seed, tag, expert]; token rows in
@@ -101,6 +103,11 @@ HIER_WORKLOADS = {
                           groups=16, k_primary=2),
 }
 WORKLOADS.update(HIER_WORKLOADS)
+# the same layer with one flat gate over all 1024 experts (k = 4), for comparing the
+# routing cost of the two gates
+WORKLOADS["flat1024_bf16"] = Workload("flat1024_bf16", T=16384, D=512, E=1024, k=4, H=1024,
+                                      act="bf16", gating="noisy", noise=True,
+                                      capacity_factor=0.0, seed=2)
 
 
 def _rng(*key: int) -> np.random.Generator:

@@ -85,6 +85,18 @@ def test_forward(moe, name):
     _check_forward(moe, w, inp, r, d, b, full_y=w.T <= 4096)
 
 
+def test_forward_flat1024(moe):
+    """The flat gate over 1024 experts at T = 16384 (the hierarchical workload's shapes):
+    routing in full, Y on a seeded token sample."""
+    import torch
+    w, inp = workload_inputs("flat1024_bf16")
+    r, d = oracle_routing("flat1024_bf16")
+    L = _layer(moe, w, inp)
+    b = L.forward(dev(inp["X"]))
+    torch.cuda.synchronize()
+    _check_forward(moe, w, inp, r, d, b, full_y=False)
+
+
 def test_forward_deterministic(moe):
     """Three runs give bitwise-identical outputs (no float atomics anywhere)."""
     import torch
