@@ -28,6 +28,11 @@ used or needed, random draws stand in for them):
                  1024-expert hierarchical model)
   flat1024_bf16  the same shapes with one flat noisy top-4 gate over the 1024
                  experts (routing-cost comparison)
+  batchwise_bf16 T=16384 D=512 E=256 k=2 H=2048, bf16, batchwise (strictly
+                 balanced) mask: every expert keeps m = kT/E = 128 tokens
+                 (Outrageously Large Neural Networks summary, "Strictly Balanced
+                 Gating"; the translation experts' widths s=512, h=2048 of the
+                 Mixture-of-Experts lesson, chapter 4)
 
 Recipe. Every tensor comes from its own numpy PCG64 stream keyed by
 SeedSequence([seed, tag]) (expert weights: [seed, tag, expert]; token rows in
@@ -66,7 +71,7 @@ class Workload:
     k: int
     H: int
     act: str              # "f32" or "bf16": X, expert weights and activations
-    gating: str           # "noisy" or "switch"
+    gating: str           # "noisy", "switch" or "batchwise"
     noise: bool
     capacity_factor: float  # <= 0: no capacity limit
     seed: int
@@ -105,6 +110,9 @@ HIER_WORKLOADS = {
 WORKLOADS.update(HIER_WORKLOADS)
 # the same layer with one flat gate over all 1024 experts (k = 4), for comparing the
 # routing cost of the two gates
+WORKLOADS["batchwise_bf16"] = Workload("batchwise_bf16", T=16384, D=512, E=256, k=2, H=2048,
+                                       act="bf16", gating="batchwise", noise=False,
+                                       capacity_factor=0.0, seed=3)
 WORKLOADS["flat1024_bf16"] = Workload("flat1024_bf16", T=16384, D=512, E=1024, k=4, H=1024,
                                       act="bf16", gating="noisy", noise=True,
                                       capacity_factor=0.0, seed=2)

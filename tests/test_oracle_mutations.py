@@ -158,3 +158,40 @@ def test_hier_pins_catch_mutation(monkeypatch, label, old, new):
             failed.append(fn.__name__)
             break
     assert failed, f"no hierarchical pin failed for mutation: {label}"
+
+
+# ------------------------------------------------------------ batchwise-mask oracle
+
+import oracle.batchwise as BWO  # noqa: E402
+import test_oracle_batchwise as bw_pins  # noqa: E402
+
+BW_MUTATIONS = [
+    ("ties to the higher token", 'order = np.argsort(-key[:, i], kind="stable")',
+     'order = np.argsort(key[:, i], kind="stable")[::-1]'),
+    ("gate not renormalised", "gates = np.where(den > 0, num / den, 0.0)",
+     "gates = np.where(den > 0, num, 0.0)"),
+    ("mask ranks the logits", "key = probs.astype(np.float32)", "key = clean.astype(np.float32)"),
+    ("m rounded up", "return (k * T) // E", "return -(-k * T // E)"),
+    ("loss sign swapped", "(((s > thr).astype(np.float64) - r.mask) * (s - thr))",
+     "((r.mask - (s > thr).astype(np.float64)) * (s - thr))"),
+    ("residual dropped", "y = x.copy() if residual else np.zeros(D)", "y = np.zeros(D)"),
+    ("softmax over kept only", "probs = z / z.sum(axis=1, keepdims=True)", "probs = z"),
+]
+
+BW_PIN_TESTS = [getattr(bw_pins, n) for n in dir(bw_pins) if n.startswith("test_")]
+
+
+@pytest.mark.parametrize("label,old,new", BW_MUTATIONS, ids=[m[0] for m in BW_MUTATIONS])
+def test_batchwise_pins_catch_mutation(monkeypatch, label, old, new):
+    mut = _mutant("batchwise", old, new)
+    for name, val in vars(mut).items():
+        if isinstance(val, types.FunctionType) and hasattr(BWO, name):
+            monkeypatch.setattr(BWO, name, val)
+    failed = []
+    for fn in BW_PIN_TESTS:
+        try:
+            fn()
+        except Exception:
+            failed.append(fn.__name__)
+            break
+    assert failed, f"no batchwise pin failed for mutation: {label}"
