@@ -28,7 +28,9 @@ Readings (listed in the design notes as well):
     residual (0/0 read as 0). A token may be kept by any number of experts.
   * Near-tie: an expert whose m-th and (m+1)-th scores differ by less than
     2e-6 of the m-th (relative) decides inside fp32 resolution; reported, not
-    counted.
+    counted. When the two are exactly equal (identical token rows) the token
+    index decides on any hardware, and the expert is a near-tie only if a
+    distinct score lies within that margin of the tied value.
   * L_batchwise(X, T, m) = sum_j sum_i (1[s_ji > T_i] - M_ji) (s_ji - T_i), with
     s the same dense scores and T the caller's per-expert thresholds.
 """
@@ -80,7 +82,16 @@ def route_batchwise(X, Wg, bias, k: int) -> BatchwiseRouting:
         mask[kept, i] = True
         if m < T:
             a, b = probs[order[m - 1], i], probs[order[m], i]
-            near[i] = abs(a - b) < NEAR_TIE_REL * abs(a)
+            if a != b:
+                near[i] = abs(a - b) < NEAR_TIE_REL * abs(a)
+            else:
+                # an exact tie (identical rows) is decided by the token index on any
+                # hardware; only distinct scores close to it could round into it
+                u = np.unique(probs[:, i])
+                k_ = np.searchsorted(u, a)
+                gaps = [u[k_ + 1] - a] if k_ + 1 < u.size else []
+                gaps += [a - u[k_ - 1]] if k_ > 0 else []
+                near[i] = bool(gaps) and min(gaps) < NEAR_TIE_REL * abs(a)
     num = np.where(mask, probs, 0.0)
     den = num.sum(axis=1, keepdims=True)
     with np.errstate(invalid="ignore", divide="ignore"):

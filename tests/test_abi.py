@@ -145,3 +145,24 @@ def test_hier_validation(m):
                               for n in m.HIER_STATE_FIELDS})
     assert m._lib.moe_aux_loss_hier(ctypes.byref(p), ctypes.byref(h), ctypes.byref(st_nostd),
                                     fake, fake, fake, fake, 1 << 30, None) == -1
+
+
+def test_batchwise_validation(m):
+    p = _p(m, T=64, E=8, k=2, gating="batchwise", noise=False)
+    assert m.moe_batchwise_m(p) == 16
+    assert m.moe_batchwise_workspace_size(p, m.MOE_WS_ROUTE) > 0
+    assert m.moe_workspace_size(p, m.MOE_WS_ROUTE) == 0  # the top-k entry points refuse it
+    fake0 = ctypes.c_void_p(0x1000)
+    assert m._lib.moe_route(ctypes.byref(p), *([fake0] * 10), fake0, 1 << 30, None) == -1
+    assert m._lib.moe_batchwise_m(ctypes.byref(_p(m, T=3, E=8, k=2, gating="batchwise",
+                                                  noise=False))) == -1  # k T < E
+    assert m._lib.moe_batchwise_m(ctypes.byref(_p(m, gating="batchwise", noise=True))) == -1
+    assert m._lib.moe_batchwise_m(ctypes.byref(_p(m))) == -1  # not a batchwise problem
+    fake = ctypes.c_void_p(0x1000)
+    st = m.BatchwiseState(**{n: 0x1000 for n in m.BATCHWISE_STATE_FIELDS})
+    need = m.moe_batchwise_workspace_size(p, m.MOE_WS_ROUTE)
+    assert m._lib.moe_route_batchwise(ctypes.byref(p), fake, fake, None, fake, ctypes.byref(st),
+                                      fake, need - 1, None) == -5
+    st.tok_gate = None
+    assert m._lib.moe_route_batchwise(ctypes.byref(p), fake, fake, None, fake, ctypes.byref(st),
+                                      fake, need, None) == -1
