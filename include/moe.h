@@ -52,7 +52,9 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 typedef enum {
   MOE_GATE_NOISY_TOPK = 0,  /* [OLNN] 3.4 Noisy Top-K Gating                */
-  MOE_GATE_SWITCH_TOP1 = 1  /* [SWITCH] steps 1-2                           */
+  MOE_GATE_SWITCH_TOP1 = 1, /* [SWITCH] steps 1-2                           */
+  MOE_GATE_BATCHWISE = 2    /* [OLNN] 3.4 Strictly Balanced Gating: the
+                               moe_*_batchwise entry points only           */
 } moe_gating;
 
 /* Largest k the kernels support. */
@@ -301,6 +303,70 @@ moe_status moe_aux_loss_hier(const moe_problem* p, const moe_hier* h,
                              const moe_hier_state* st, float* importance,
                              float* load, float* out, void* workspace,
                              size_t workspace_bytes, void* hip_stream);
+
+/* ---------------------------------------------------------- batchwise mask */
+
+/* Strictly balanced gating ([OLNN] 3.4 "Strictly Balanced Gating (Batchwise
+ * Mask)"; [LESSON] ch. 4 "A stricter alternative", ch. 2's mask form), for
+ * p->gating == MOE_GATE_BATCHWISE (p->noise must be 0; capacity does not apply).
+ * Scores s = Softmax(X . Wg (+ bias)) per token (dense, fp32). Each expert e
+ * keeps the m = floor(p->k * T / E) tokens with the highest s[., e] (ties to the
+ * lower token), so every expert receives exactly m rows; token t gets
+ * G(t)_e = s[t,e] / sum of s[t,.] over the experts that kept it, for each of
+ * them (any number, possibly none: then Y[t] = residual[t]). Expert-major row
+ * e*m + j holds the j-th kept token of expert e (ascending), so the expert FFN
+ * runs through moe_expert_ffn with offsets[e] = e*m. */
+typedef struct {
+  float*    probs_t;    /* [E, T]  scores s, expert-major                        */
+  int32_t*  sel;        /* [E*m]   token of expert-major row r                   */
+  int32_t*  offsets;    /* [E+1]   e*m                                           */
+  uint32_t* mask;       /* [T, ceil(E/32)] bit e%32 of word e/32: t kept by e     */
+  int32_t*  tok_count;  /* [T]     experts that kept token t                     */
+  int32_t*  tok_off;    /* [T+1]   token t's entries tok_off[t] .. tok_off[t+1]-1 */
+  int32_t*  tok_row;    /* [E*m]   per entry: expert-major row (experts ascending) */
+  float*    tok_gate;   /* [E*m]   per entry: G(t)_e                             */
+  int32_t*  slot_pair;  /* [E*m]   entry index of expert-major row r             */
+} moe_batchwise_state;
+
+/* m for the problem, or -1 if invalid (m < 1 is invalid). */
+int32_t moe_batchwise_m(const moe_problem* p);
+
+/* Workspace bytes for moe_route_batchwise (MOE_WS_ROUTE) or
+ * moe_aux_loss_batchwise (MOE_WS_AUX); 0 if invalid. */
+size_t moe_batchwise_workspace_size(const moe_problem* p, int which);
+
+/* moe_route_batchwise -- scores, the mask and the gates.
+ *   X [T,D]; Wg [D,E] fp32; bias [E] or NULL; clean [T,E] out (X . Wg + bias);
+ *   st: every buffer above, written. */
+moe_status moe_route_batchwise(const moe_problem* p, const void* X, const float* Wg,
+                               const float* bias, float* clean,
+                               const moe_batchwise_state* st, void* workspace,
+                               size_t workspace_bytes, void* hip_stream);
+
+/* moe_dispatch_batchwise -- Xd[r] = X[sel[r]] for the E*m rows. Xd [E*m, D] out. */
+moe_status moe_dispatch_batchwise(const moe_problem* p, const void* X,
+                                  const moe_batchwise_state* st, void* Xd,
+                                  void* hip_stream);
+
+/* moe_combine_batchwise -- Y[t] = residual[t] + sum over token t's entries
+ * (experts ascending) of tok_gate * Z[tok_row], fp32 accumulation, one rounding.
+ *   Z [E*m, D] (moe_expert_ffn output); residual [T,D] or NULL; Y [T,D] out. */
+moe_status moe_combine_batchwise(const moe_problem* p, const void* Z,
+                                 const moe_batchwise_state* st, const void* residual,
+                                 void* Y, void* hip_stream);
+
+/* moe_aux_loss_batchwise -- importance[e] = sum of the gates e received;
+ *   out[0] = CV^2(importance)
+ *   out[1] = L_batchwise = sum_t sum_e (1[s[t,e] > thresholds[e]] - mask[t,e])
+ *            * (s[t,e] - thresholds[e])   (0 if thresholds is NULL)
+ *   out[2] = mean experts per token (= E*m/T)  out[3] = max experts per token
+ *   out[4] = tokens no expert kept  out[5] = sum(importance)  out[6] = m  out[7] = 0
+ *   thresholds [E] or NULL; importance [E] out or NULL; out [8] out;
+ *   workspace moe_batchwise_workspace_size(p, MOE_WS_AUX). */
+moe_status moe_aux_loss_batchwise(const moe_problem* p, const moe_batchwise_state* st,
+                                  const float* thresholds, float* importance,
+                                  float* out, void* workspace, size_t workspace_bytes,
+                                  void* hip_stream);
 
 /* ------------------------------------------------------------------- misc */
 

@@ -29,11 +29,16 @@ moe_status launch_status() {
 moe_status validate(const moe_problem* p, Dims* d) {
   if (!p) return MOE_ERR_INVALID_ARG;
   if (p->T < 1 || p->D < 1 || p->E < 1 || p->H < 1) return MOE_ERR_INVALID_ARG;
-  if (p->gating != MOE_GATE_NOISY_TOPK && p->gating != MOE_GATE_SWITCH_TOP1) return MOE_ERR_INVALID_ARG;
+  if (p->gating != MOE_GATE_NOISY_TOPK && p->gating != MOE_GATE_SWITCH_TOP1 &&
+      p->gating != MOE_GATE_BATCHWISE)
+    return MOE_ERR_INVALID_ARG;
   if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (p->k < 1 || p->k > p->E) return MOE_ERR_INVALID_ARG;
   if (p->gating == MOE_GATE_SWITCH_TOP1 && p->k != 1) return MOE_ERR_INVALID_ARG;
   if (p->noise != 0 && p->noise != 1) return MOE_ERR_INVALID_ARG;
+  if (p->gating == MOE_GATE_BATCHWISE &&
+      (p->noise != 0 || static_cast<int64_t>(p->k) * p->T < p->E))
+    return MOE_ERR_INVALID_ARG;  // no noise; at least one token per expert
   if (p->check_finite != 0 && p->check_finite != 1) return MOE_ERR_INVALID_ARG;
   if (!isfinite(p->capacity_factor)) return MOE_ERR_INVALID_ARG;
   if (p->min_capacity < 1) return MOE_ERR_INVALID_ARG;
@@ -100,6 +105,13 @@ using namespace moe;
 
 static hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// The per-token top-k entry points (route, dispatch, combine, aux) do not take the
+// batchwise mask, which has entry points of its own.
+static moe_status validate_topk(const moe_problem* p, Dims* d) {
+  MOE_TRY(validate(p, d));
+  return d->gating == MOE_GATE_BATCHWISE ? MOE_ERR_INVALID_ARG : MOE_OK;
+}
+
 static moe_status flag_for(const moe_problem* p, int** flag) {
   *flag = nonfinite_flag(p);
   if (p->check_finite && !*flag) return MOE_ERR_HIP;
@@ -120,7 +132,7 @@ int64_t moe_max_rows(const moe_problem* p) {
 
 size_t moe_workspace_size(const moe_problem* p, int which) {
   Dims d;
-  if (validate(p, &d) != MOE_OK) return 0;
+  if (validate_topk(p, &d) != MOE_OK) return 0;
   switch (which) {
     case MOE_WS_ROUTE: return route_workspace(d);
     case MOE_WS_DISPATCH: return dispatch_workspace(d);
@@ -140,7 +152,7 @@ moe_status moe_route(const moe_problem* p, const void* X, const float* Wg, const
                      float* noise_std, float* row_stats, void* workspace, size_t workspace_bytes,
                      void* hip_stream) {
   Dims d;
-  MOE_TRY(validate(p, &d));
+  MOE_TRY(validate_topk(p, &d));
   const bool noise = d.gating == MOE_GATE_NOISY_TOPK && d.noise;
   if (!X || !Wg || !ids || !gates || !clean) return MOE_ERR_INVALID_ARG;
   if (noise && (!Wnoise || !noise_std)) return MOE_ERR_INVALID_ARG;
@@ -155,7 +167,7 @@ moe_status moe_dispatch(const moe_problem* p, const void* X, const int32_t* ids,
                         uint8_t* accepted, int32_t* counts, int32_t* offsets, int32_t* row_token,
                         void* Xd, void* workspace, size_t workspace_bytes, void* hip_stream) {
   Dims d;
-  MOE_TRY(validate(p, &d));
+  MOE_TRY(validate_topk(p, &d));
   if (!X || !ids || !pos || !accepted || !counts || !offsets || !row_token || !Xd)
     return MOE_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < dispatch_workspace(d)) return MOE_ERR_WORKSPACE;
@@ -199,7 +211,7 @@ moe_status moe_combine(const moe_problem* p, const void* Z, const int32_t* ids, 
                        const int32_t* pos, const uint8_t* accepted, const int32_t* offsets,
                        const void* residual, void* Y, void* hip_stream) {
   Dims d;
-  MOE_TRY(validate(p, &d));
+  MOE_TRY(validate_topk(p, &d));
   if (!Z || !ids || !gates || !pos || !accepted || !offsets || !Y) return MOE_ERR_INVALID_ARG;
   int* flag;
   MOE_TRY(flag_for(p, &flag));
@@ -212,7 +224,7 @@ moe_status moe_aux_loss(const moe_problem* p, const int32_t* ids, const float* g
                         const int32_t* counts, float* importance, float* load, float* out,
                         void* workspace, size_t workspace_bytes, void* hip_stream) {
   Dims d;
-  MOE_TRY(validate(p, &d));
+  MOE_TRY(validate_topk(p, &d));
   const bool noise = d.gating == MOE_GATE_NOISY_TOPK && d.noise;
   if (!ids || !gates || !clean || !counts || !out) return MOE_ERR_INVALID_ARG;
   if (noise && (!noise_std || !row_stats)) return MOE_ERR_INVALID_ARG;
@@ -266,6 +278,72 @@ moe_status moe_aux_loss_hier(const moe_problem* p, const moe_hier* h, const moe_
     return MOE_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < hier_aux_workspace(d, h)) return MOE_ERR_WORKSPACE;
   return hier_aux_launch(d, h, st, importance, load, out, workspace, as_stream(hip_stream));
+}
+
+// --------------------------------------------------------------- batchwise mask
+static moe_status validate_batchwise(const moe_problem* p, Dims* d) {
+  MOE_TRY(validate(p, d));
+  return d->gating == MOE_GATE_BATCHWISE ? MOE_OK : MOE_ERR_INVALID_ARG;
+}
+
+static bool batchwise_state_ok(const moe_batchwise_state* st) {
+  return st && st->probs_t && st->sel && st->offsets && st->mask && st->tok_count && st->tok_off &&
+         st->tok_row && st->tok_gate && st->slot_pair;
+}
+
+int32_t moe_batchwise_m(const moe_problem* p) {
+  Dims d;
+  return validate_batchwise(p, &d) == MOE_OK ? batchwise_m(d) : -1;
+}
+
+size_t moe_batchwise_workspace_size(const moe_problem* p, int which) {
+  Dims d;
+  if (validate_batchwise(p, &d) != MOE_OK) return 0;
+  switch (which) {
+    case MOE_WS_ROUTE: return batchwise_route_workspace(d);
+    case MOE_WS_AUX: return batchwise_aux_workspace(d);
+    default: return 0;
+  }
+}
+
+moe_status moe_route_batchwise(const moe_problem* p, const void* X, const float* Wg,
+                               const float* bias, float* clean, const moe_batchwise_state* st,
+                               void* workspace, size_t workspace_bytes, void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate_batchwise(p, &d));
+  if (!X || !Wg || !clean || !batchwise_state_ok(st)) return MOE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < batchwise_route_workspace(d)) return MOE_ERR_WORKSPACE;
+  int* flag;
+  MOE_TRY(flag_for(p, &flag));
+  return batchwise_route_launch(d, X, Wg, bias, clean, st, workspace, flag, as_stream(hip_stream));
+}
+
+moe_status moe_dispatch_batchwise(const moe_problem* p, const void* X,
+                                  const moe_batchwise_state* st, void* Xd, void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate_batchwise(p, &d));
+  if (!X || !Xd || !batchwise_state_ok(st)) return MOE_ERR_INVALID_ARG;
+  return batchwise_dispatch_launch(d, X, st, Xd, as_stream(hip_stream));
+}
+
+moe_status moe_combine_batchwise(const moe_problem* p, const void* Z, const moe_batchwise_state* st,
+                                 const void* residual, void* Y, void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate_batchwise(p, &d));
+  if (!Z || !Y || !batchwise_state_ok(st)) return MOE_ERR_INVALID_ARG;
+  int* flag;
+  MOE_TRY(flag_for(p, &flag));
+  return batchwise_combine_launch(d, Z, st, residual, Y, flag, as_stream(hip_stream));
+}
+
+moe_status moe_aux_loss_batchwise(const moe_problem* p, const moe_batchwise_state* st,
+                                  const float* thresholds, float* importance, float* out,
+                                  void* workspace, size_t workspace_bytes, void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate_batchwise(p, &d));
+  if (!out || !batchwise_state_ok(st)) return MOE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < batchwise_aux_workspace(d)) return MOE_ERR_WORKSPACE;
+  return batchwise_aux_launch(d, st, thresholds, importance, out, workspace, as_stream(hip_stream));
 }
 
 moe_status moe_check_finite(void* hip_stream) {

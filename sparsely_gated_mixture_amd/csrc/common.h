@@ -174,4 +174,25 @@ moe_status hier_route_launch(const Dims& d, const moe_hier* h, const moe_problem
 moe_status hier_aux_launch(const Dims& d, const moe_hier* h, const moe_hier_state* st,
                            float* importance, float* load, float* out, void* ws, hipStream_t stream);
 
+// Router scores only (router.hip): clean = X . Wg (+ bias), no noise, no selection.
+size_t router_clean_workspace(const Dims& d);
+moe_status router_clean_launch(const Dims& d, const void* X, const float* Wg, const float* bias,
+                               float* clean, void* ws, int* nonfinite, hipStream_t stream);
+
+// Batchwise mask (batchwise.hip).
+int batchwise_m(const Dims& d);
+size_t batchwise_route_workspace(const Dims& d);
+size_t batchwise_aux_workspace(const Dims& d);
+moe_status batchwise_route_launch(const Dims& d, const void* X, const float* Wg, const float* bias,
+                                  float* clean, const moe_batchwise_state* st, void* ws,
+                                  int* nonfinite, hipStream_t stream);
+moe_status batchwise_dispatch_launch(const Dims& d, const void* X, const moe_batchwise_state* st,
+                                     void* Xd, hipStream_t stream);
+moe_status batchwise_combine_launch(const Dims& d, const void* Z, const moe_batchwise_state* st,
+                                    const void* residual, void* Y, int* nonfinite,
+                                    hipStream_t stream);
+moe_status batchwise_aux_launch(const Dims& d, const moe_batchwise_state* st,
+                                const float* thresholds, float* importance, float* out, void* ws,
+                                hipStream_t stream);
+
 }  // namespace moe

@@ -664,10 +664,11 @@ static void select_rows(const float* score, int T, int E, int k, bool switch_gat
   select_launch(kl, lpr, sa, stream);
 }
 
-moe_status route_launch(const Dims& d, const moe_problem* p, const void* X, const float* Wg,
-                        const float* Wnoise, const float* bias, const float* eps, int32_t* ids,
-                        float* gates, float* clean, float* noise_std, float* row_stats,
-                        void* ws, int* nonfinite, hipStream_t stream) {
+// Router weights packed, then the GEMM with its epilogue: clean (+ std and H with noise).
+static moe_status router_scores(const Dims& d, uint64_t seed, const void* X, const float* Wg,
+                                const float* Wnoise, const float* bias, const float* eps,
+                                float* clean, float* noise_std, void* ws, int* nonfinite,
+                                hipStream_t stream) {
   const bool noise = router_noise(d);
   const int NB = router_nb(d), KS = router_ks(d);
   uint4* wfrag = static_cast<uint4*>(ws);
@@ -689,7 +690,7 @@ moe_status route_launch(const Dims& d, const moe_problem* p, const void* X, cons
   g.std_out = noise ? noise_std : nullptr;
   g.H = H;
   g.nonfinite = nonfinite;
-  g.seed = p->seed;
+  g.seed = seed;
   g.T = d.T;
   g.D = d.D;
   g.E = d.E;
@@ -705,11 +706,34 @@ moe_status route_launch(const Dims& d, const moe_problem* p, const void* X, cons
   const int64_t tiles = static_cast<int64_t>(ceil_div(d.T, bm)) * ceil_div(NB, 8);
   const int grid = static_cast<int>(ceil_div64(tiles, kXcds) * kXcds);
   router_gemm_launch<false>(d, bm, grid, g, stream);
-  if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  return launch_status();
+}
 
+moe_status route_launch(const Dims& d, const moe_problem* p, const void* X, const float* Wg,
+                        const float* Wnoise, const float* bias, const float* eps, int32_t* ids,
+                        float* gates, float* clean, float* noise_std, float* row_stats,
+                        void* ws, int* nonfinite, hipStream_t stream) {
+  const moe_status s = router_scores(d, p->seed, X, Wg, Wnoise, bias, eps, clean, noise_std, ws,
+                                     nonfinite, stream);
+  if (s != MOE_OK) return s;
+  const bool noise = router_noise(d);
+  float* H = noise ? reinterpret_cast<float*>(static_cast<char*>(ws) + router_wbytes(d)) : nullptr;
   select_rows(noise ? H : clean, d.T, d.E, d.k, d.gating == MOE_GATE_SWITCH_TOP1, ids, gates,
               row_stats, stream);
   return launch_status();
+}
+
+// clean = X . Wg (+ bias) only (no noise, no selection); workspace router_wbytes(d).
+size_t router_clean_workspace(const Dims& d) {
+  Dims dn = d;
+  dn.noise = 0;
+  return router_wbytes(dn);
+}
+moe_status router_clean_launch(const Dims& d, const void* X, const float* Wg, const float* bias,
+                               float* clean, void* ws, int* nonfinite, hipStream_t stream) {
+  Dims dn = d;
+  dn.noise = 0;
+  return router_scores(dn, 0, X, Wg, nullptr, bias, nullptr, clean, nullptr, ws, nonfinite, stream);
 }
 
 // ------------------------------------------------------------------ grouped gates

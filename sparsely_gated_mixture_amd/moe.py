@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
-MOE_GATE_NOISY_TOPK, MOE_GATE_SWITCH_TOP1 = 0, 1
+MOE_GATE_NOISY_TOPK, MOE_GATE_SWITCH_TOP1, MOE_GATE_BATCHWISE = 0, 1, 2
 MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_AUX = 0, 1, 2
 MOE_MAX_K = 8
 
@@ -30,6 +30,8 @@ ENTRY_POINTS = [
     "moe_route", "moe_dispatch", "moe_pack_expert_weights", "moe_grouped_gemm",
     "moe_expert_ffn", "moe_combine", "moe_aux_loss", "moe_check_finite", "moe_status_string",
     "moe_hier_workspace_size", "moe_route_hier", "moe_aux_loss_hier",
+    "moe_batchwise_m", "moe_batchwise_workspace_size", "moe_route_batchwise",
+    "moe_dispatch_batchwise", "moe_combine_batchwise", "moe_aux_loss_batchwise",
 ]
 
 
@@ -66,6 +68,15 @@ class HierState(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in HIER_STATE_FIELDS]
 
 
+BATCHWISE_STATE_FIELDS = ["probs_t", "sel", "offsets", "mask", "tok_count", "tok_off", "tok_row",
+                          "tok_gate", "slot_pair"]
+
+
+class BatchwiseState(ctypes.Structure):
+    """Mirror of moe_batchwise_state (device pointers)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in BATCHWISE_STATE_FIELDS]
+
+
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"HIP library not built: {path} (run python -m sparsely_gated_mixture_amd.build)")
@@ -91,6 +102,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                            [ctypes.POINTER(HierState), vp, sz, vp]),
         "moe_aux_loss_hier": (ctypes.c_int, [P, ctypes.POINTER(Hier), ctypes.POINTER(HierState)] +
                               [vp] * 4 + [sz, vp]),
+        "moe_batchwise_m": (i32, [P]),
+        "moe_batchwise_workspace_size": (sz, [P, ctypes.c_int]),
+        "moe_route_batchwise": (ctypes.c_int, [P, vp, vp, vp, vp, ctypes.POINTER(BatchwiseState),
+                                               vp, sz, vp]),
+        "moe_dispatch_batchwise": (ctypes.c_int, [P, vp, ctypes.POINTER(BatchwiseState), vp, vp]),
+        "moe_combine_batchwise": (ctypes.c_int, [P, vp, ctypes.POINTER(BatchwiseState), vp, vp, vp]),
+        "moe_aux_loss_batchwise": (ctypes.c_int, [P, ctypes.POINTER(BatchwiseState), vp, vp, vp,
+                                                  vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -130,7 +149,8 @@ def problem(T, D, E, H, k, dtype="bf16", gating="noisy", noise=True, capacity_fa
             min_capacity=1, seed=0, check_finite=False) -> Problem:
     return Problem(T=T, D=D, E=E, H=H, k=k,
                    dtype=MOE_BF16 if dtype == "bf16" else MOE_F32,
-                   gating=MOE_GATE_SWITCH_TOP1 if gating == "switch" else MOE_GATE_NOISY_TOPK,
+                   gating={"switch": MOE_GATE_SWITCH_TOP1,
+                           "batchwise": MOE_GATE_BATCHWISE}.get(gating, MOE_GATE_NOISY_TOPK),
                    noise=1 if noise else 0, capacity_factor=float(capacity_factor),
                    min_capacity=int(min_capacity), seed=int(seed),
                    check_finite=1 if check_finite else 0, reserved=0)
@@ -233,6 +253,49 @@ def moe_aux_loss_hier(p, h, st: dict, importance, load, out, ws, stream=None):
                                   _ptr(importance), _ptr(load), _ptr(out), _ptr(ws),
                                   ws.numel() if ws is not None else 0, _stream(stream)),
            "moe_aux_loss_hier")
+
+
+def batchwise_state(st: dict) -> BatchwiseState:
+    return BatchwiseState(**{n: (_ptr(st[n]).value if st.get(n) is not None else None)
+                             for n in BATCHWISE_STATE_FIELDS})
+
+
+def moe_batchwise_m(p: Problem) -> int:
+    m = _lib.moe_batchwise_m(ctypes.byref(p))
+    if m < 0:
+        raise MoEError(-1, "moe_batchwise_m")
+    return m
+
+
+def moe_batchwise_workspace_size(p: Problem, which: int) -> int:
+    return _lib.moe_batchwise_workspace_size(ctypes.byref(p), which)
+
+
+def moe_route_batchwise(p, X, Wg, bias, clean, st: dict, ws, stream=None):
+    bs = batchwise_state(st)
+    _check(_lib.moe_route_batchwise(ctypes.byref(p), _ptr(X), _ptr(Wg), _ptr(bias), _ptr(clean),
+                                    ctypes.byref(bs), _ptr(ws), ws.numel() if ws is not None else 0,
+                                    _stream(stream)), "moe_route_batchwise")
+
+
+def moe_dispatch_batchwise(p, X, st: dict, Xd, stream=None):
+    bs = batchwise_state(st)
+    _check(_lib.moe_dispatch_batchwise(ctypes.byref(p), _ptr(X), ctypes.byref(bs), _ptr(Xd),
+                                       _stream(stream)), "moe_dispatch_batchwise")
+
+
+def moe_combine_batchwise(p, Z, st: dict, residual, Y, stream=None):
+    bs = batchwise_state(st)
+    _check(_lib.moe_combine_batchwise(ctypes.byref(p), _ptr(Z), ctypes.byref(bs), _ptr(residual),
+                                      _ptr(Y), _stream(stream)), "moe_combine_batchwise")
+
+
+def moe_aux_loss_batchwise(p, st: dict, thresholds, importance, out, ws, stream=None):
+    bs = batchwise_state(st)
+    _check(_lib.moe_aux_loss_batchwise(ctypes.byref(p), ctypes.byref(bs), _ptr(thresholds),
+                                       _ptr(importance), _ptr(out), _ptr(ws),
+                                       ws.numel() if ws is not None else 0, _stream(stream)),
+           "moe_aux_loss_batchwise")
 
 
 def moe_check_finite(stream=None):
@@ -372,3 +435,65 @@ class HierLayer(Layer):
     def aux(self):
         b = self.b
         moe_aux_loss_hier(self.p, self.h, self.st, b.importance, b.load, b.aux_out, self.ws_aux_h)
+
+
+class BatchwiseLayer:
+    """The MoE layer with the batchwise mask: route (scores, mask, gates), dispatch
+    (gather of the E*m rows), expert FFN (grouped GEMMs over offsets e*m), combine,
+    aux; same stage names as Layer."""
+
+    def __init__(self, p: Problem, Wg, bias, W1, W2, device="cuda", thresholds=None):
+        self.p = p
+        dt = torch_dtype(p)
+        T, D, E, H = p.T, p.D, p.E, p.H
+        m = moe_batchwise_m(p)
+        R = E * m
+        W = (E + 31) // 32
+        e = lambda *s, dtype=torch.float32: torch.empty(*s, dtype=dtype, device=device)
+        self.Wg, self.bias, self.thresholds = Wg, bias, thresholds
+        self.W1p = e(moe_packed_weight_bytes(p, 1), dtype=torch.uint8)
+        self.W2p = e(moe_packed_weight_bytes(p, 2), dtype=torch.uint8)
+        moe_pack_expert_weights(p, W1, W2, self.W1p, self.W2p)
+        self.m = m
+        self.st = dict(probs_t=e(E, T), sel=e(R, dtype=torch.int32),
+                       offsets=e(E + 1, dtype=torch.int32), mask=e(T, W, dtype=torch.int32),
+                       tok_count=e(T, dtype=torch.int32), tok_off=e(T + 1, dtype=torch.int32),
+                       tok_row=e(R, dtype=torch.int32), tok_gate=e(R),
+                       slot_pair=e(R, dtype=torch.int32))
+        self.clean = e(T, E)
+        self.Xd, self.Hd, self.Z = e(R, D, dtype=dt), e(R, H, dtype=dt), e(R, D, dtype=dt)
+        self.Y = e(T, D, dtype=dt)
+        self.importance, self.aux_out = e(E), e(8)
+        self.ws_route = e(max(moe_batchwise_workspace_size(p, MOE_WS_ROUTE), 1), dtype=torch.uint8)
+        self.ws_aux = e(max(moe_batchwise_workspace_size(p, MOE_WS_AUX), 1), dtype=torch.uint8)
+
+    def route(self, X):
+        moe_route_batchwise(self.p, X, self.Wg, self.bias, self.clean, self.st, self.ws_route)
+
+    def dispatch(self, X):
+        moe_dispatch_batchwise(self.p, X, self.st, self.Xd)
+
+    def gemm(self, layer):
+        if layer == 1:
+            moe_grouped_gemm(self.p, 1, self.Xd, self.W1p, self.st["offsets"], self.Hd)
+        else:
+            moe_grouped_gemm(self.p, 2, self.Hd, self.W2p, self.st["offsets"], self.Z)
+
+    def ffn(self):
+        moe_expert_ffn(self.p, self.Xd, self.W1p, self.W2p, self.st["offsets"], self.Hd, self.Z)
+
+    def combine(self, X, residual=True):
+        moe_combine_batchwise(self.p, self.Z, self.st, X if residual else None, self.Y)
+
+    def aux(self):
+        moe_aux_loss_batchwise(self.p, self.st, self.thresholds, self.importance, self.aux_out,
+                               self.ws_aux)
+
+    def forward(self, X, residual=True, aux=True):
+        self.route(X)
+        self.dispatch(X)
+        self.ffn()
+        self.combine(X, residual)
+        if aux:
+            self.aux()
+        return self
