@@ -68,7 +68,11 @@ def cpu_baseline(w, inp, budget_tokens: int):
         threads = 1
     S = min(budget_tokens, w.T)
     t0 = time.perf_counter()
-    if w.groups > 0:
+    if w.gating == "batchwise":
+        from oracle import batchwise as BO
+        # the prefix as a batch of its own (m then follows the prefix size)
+        BO.forward_batchwise(dict(inp, X=inp["X"][:S]), w.replace(T=S))
+    elif w.groups > 0:
         from oracle import hier as HO
         # the prefix as a batch of its own (capacity, if any, then follows the prefix size)
         HO.forward_hier(dict(inp, X=inp["X"][:S]), w.replace(T=S))
@@ -167,7 +171,10 @@ def main():
     p = moe.problem(T=w.T, D=w.D, E=w.E, H=w.H, k=w.k, dtype=w.act, gating=w.gating,
                     noise=w.noise, capacity_factor=w.capacity_factor,
                     min_capacity=w.min_capacity, seed=w.seed)
-    if w.groups > 0:  # hierarchical gate: route / aux are the two-level stages
+    if w.gating == "batchwise":  # every expert keeps m = kT/E tokens
+        L = moe.BatchwiseLayer(p, _dev(torch, inp["Wg"]), _dev(torch, inp["bias"]),
+                               _dev(torch, inp["W1"]), _dev(torch, inp["W2"]))
+    elif w.groups > 0:  # hierarchical gate: route / aux are the two-level stages
         L = moe.HierLayer(p, moe.hier(w.groups, w.k_primary), _dev(torch, inp["Wpg"]),
                           _dev(torch, inp["Wpn"]), _dev(torch, inp["Wsg"]),
                           _dev(torch, inp["Wsn"]), _dev(torch, inp["W1"]), _dev(torch, inp["W2"]))
@@ -218,8 +225,7 @@ def main():
                                 for s in range(args.steps)]))
            for i, name in enumerate(stages)}
 
-    b = L.b
-    offs = b.offsets.cpu().numpy()
+    offs = (L.st["offsets"] if w.gating == "batchwise" else L.b.offsets).cpu().numpy()
     A = int(offs[-1])
     U = int(np.count_nonzero(np.diff(offs)))  # experts that received rows
     el = 2 if w.act == "bf16" else 4
@@ -247,7 +253,8 @@ def main():
         "dtype": w.act,
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "D": w.D, "E": w.E, "k": w.k, "H": w.H,
-                   "gating": w.gating if w.groups == 0 else
+                   "gating": (f"batchwise mask, m = {w.k * w.T // w.E} tokens per expert"
+                              if w.gating == "batchwise" else w.gating) if w.groups == 0 else
                    f"hierarchical {w.groups} groups x {w.E // w.groups}, k {w.k_primary} x "
                    f"{w.k // w.k_primary}",
                    "capacity_factor": w.capacity_factor,

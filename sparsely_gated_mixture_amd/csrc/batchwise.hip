@@ -12,8 +12,8 @@
 //
 // Launches (route):
 //   router_pack + router_gemm   clean = X . Wg (+ bias), fp32-exact (router.hip)
-//   bw_softmax    64 tokens per block: row max / sum by wave reductions, then
-//                 64x64 tiles through LDS so the scores leave expert-major
+//   bw_softmax    32 tokens per block: row max / sum by wave reductions, then
+//                 32x64 tiles through LDS so the scores leave expert-major
 //                 (probs_t [E, T]) with coalesced stores; clears the mask rows
 //   bw_select     one block per expert: radix select (4 passes of 8 bits on the
 //                 fp32 bit pattern) of the m-th largest score, then one pass in
@@ -36,7 +36,9 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTileTok = 64;
+constexpr int kTileTok = 32;   // tokens per softmax block
+constexpr int kSelThreads = 512;
+constexpr int kHistCopies = 16;  // radix histogram copies (spreads LDS atomics)
 
 __device__ __forceinline__ float bw_wave_max(float v) {
 #pragma unroll
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void bw_softmax(const float* __restrict__
                                                       int W, float* __restrict__ probs_t,
                                                       uint32_t* __restrict__ mask) {
   __shared__ float sMax[kTileTok], sSum[kTileTok];
-  __shared__ float tile[64][65];
+  __shared__ float tile[kTileTok][65];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int t0 = blockIdx.x * kTileTok;
   const int nt = min(kTileTok, T - t0);
@@ -86,49 +88,59 @@ __global__ __launch_bounds__(kThreads) void bw_softmax(const float* __restrict__
     __syncthreads();
     // store [experts][tokens], coalesced along the tokens
     for (int i = tid; i < 64 * kTileTok; i += kThreads) {
-      const int c = i >> 6, r = i & 63;
+      const int c = i / kTileTok, r = i % kTileTok;
       if (r < nt && e0 + c < E) probs_t[static_cast<int64_t>(e0 + c) * T + t0 + r] = tile[r][c];
     }
     __syncthreads();
   }
 }
 
-__global__ __launch_bounds__(kThreads) void bw_select(const float* __restrict__ probs_t, int T,
-                                                     int E, int m, int W, int32_t* __restrict__ sel,
-                                                     int32_t* __restrict__ offsets,
-                                                     uint32_t* __restrict__ mask) {
-  __shared__ int hist[256];
-  __shared__ int wt[kThreads / 64];
+__global__ __launch_bounds__(kSelThreads) void bw_select(const float* __restrict__ probs_t, int T,
+                                                        int E, int m, int W,
+                                                        int32_t* __restrict__ sel,
+                                                        int32_t* __restrict__ offsets,
+                                                        uint32_t* __restrict__ mask) {
+  __shared__ int hist[kHistCopies][256];
+  __shared__ int wt[kSelThreads / 64];
   __shared__ uint32_t sPrefix;
-  __shared__ int sRemain, sAbove;
+  __shared__ int sRemain;
   const int tid = threadIdx.x;
   const int e = blockIdx.x;
   const uint32_t* key = reinterpret_cast<const uint32_t*>(probs_t + static_cast<int64_t>(e) * T);
+  int* myhist = hist[tid % kHistCopies];
   if (tid == 0) {
     sPrefix = 0u;
     sRemain = m;
-    sAbove = 0;
   }
   uint32_t pmask = 0u;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
+    for (int i = tid; i < kHistCopies * 256; i += kSelThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
     const uint32_t prefix = sPrefix;
-    for (int t = tid; t < T; t += kThreads) {
+    for (int t = tid; t < T; t += kSelThreads) {
       const uint32_t k = key[t];
-      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
+      if ((k & pmask) == prefix) atomicAdd(&myhist[(k >> shift) & 255u], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int rem = sRemain, above = 0;
-      int b = 255;
-      for (; b > 0; --b) {
-        if (above + hist[b] >= rem) break;
-        above += hist[b];
+    for (int b = tid; b < 256; b += kSelThreads) {
+      int c = 0;
+#pragma unroll
+      for (int q = 0; q < kHistCopies; ++q) c += hist[q][b];
+      hist[0][b] = c;
+    }
+    __syncthreads();
+    // bins from the top: thread i holds bin 255 - i; the bin holding the rem-th largest is
+    // where the running count (from the top) first reaches rem
+    {
+      const int rem = sRemain;
+      const int bin = 255 - tid;
+      const int h = tid < 256 ? hist[0][bin] : 0;
+      int excl;
+      block_exclusive_scan<kSelThreads>(h, &excl, wt);
+      if (tid < 256 && excl < rem && excl + h >= rem) {
+        sRemain = rem - excl;
+        sPrefix = prefix | (static_cast<uint32_t>(bin) << shift);
       }
-      sRemain = rem - above;
-      sAbove += above;
-      sPrefix = prefix | (static_cast<uint32_t>(b) << shift);
     }
     __syncthreads();
     pmask |= 255u << shift;
@@ -137,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void bw_select(const float* __restrict__ 
   const int need_eq = sRemain;  // ties at the m-th score to keep, lowest tokens first
   // keep in token order: above kth, or equal with rank < need_eq
   int base_above = 0, base_eq = 0;
-  for (int c0 = 0; c0 < T; c0 += kThreads * 4) {
+  for (int c0 = 0; c0 < T; c0 += kSelThreads * 4) {
     int a[4], q[4];
     int la = 0, lq = 0;
 #pragma unroll
@@ -149,8 +161,8 @@ __global__ __launch_bounds__(kThreads) void bw_select(const float* __restrict__ 
       la += a[u];
       lq += q[u];
     }
-    int excl;
-    const int tot = block_exclusive_scan<kThreads>(la | (lq << 16), &excl, wt);
+    int excl;  // packed pair: low 16 bits above, high 16 bits equal (a chunk has 2048 tokens)
+    const int tot = block_exclusive_scan<kSelThreads>(la | (lq << 16), &excl, wt);
     int ra = base_above + (excl & 0xffff), rq = base_eq + (excl >> 16);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -269,7 +281,8 @@ __global__ void bw_gather_scalar(const T* __restrict__ X, const int32_t* __restr
   Xd[r * D + c] = X[static_cast<int64_t>(sel[r]) * D + c];
 }
 
-// A wave per token: Y = R + sum over the token's experts (ascending) of gate * Z[row].
+// A wave per token: Y = R + sum over the token's experts (ascending) of gate * Z[row];
+// 16-byte vectors when D allows.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bw_combine(const T* __restrict__ Z,
                                                       const int32_t* __restrict__ tok_off,
@@ -277,17 +290,48 @@ __global__ __launch_bounds__(kThreads) void bw_combine(const T* __restrict__ Z,
                                                       const float* __restrict__ tok_gate,
                                                       const T* __restrict__ R, int Tn, int D,
                                                       T* __restrict__ Y, int* nonfinite) {
+  constexpr int V = Elem<T>::kVec;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (t >= Tn) return;
   const int j0 = tok_off[t], j1 = tok_off[t + 1];
   bool bad = false;
-  for (int c = lane; c < D; c += 64) {
-    float y = R ? Elem<T>::to_f32(R[static_cast<int64_t>(t) * D + c]) : 0.f;
-    for (int j = j0; j < j1; ++j)
-      y = fmaf(tok_gate[j], Elem<T>::to_f32(Z[static_cast<int64_t>(tok_row[j]) * D + c]), y);
-    bad |= !isfinite(y);
-    Y[static_cast<int64_t>(t) * D + c] = Elem<T>::from_f32(y);
+  if (D % V == 0) {
+    const int nv = D / V;
+    for (int c = lane; c < nv; c += 64) {
+      float y[V];
+      if (R) {
+        const uint4 rv = reinterpret_cast<const uint4*>(R + static_cast<int64_t>(t) * D)[c];
+        const T* rp = reinterpret_cast<const T*>(&rv);
+#pragma unroll
+        for (int i = 0; i < V; ++i) y[i] = Elem<T>::to_f32(rp[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) y[i] = 0.f;
+      }
+      for (int j = j0; j < j1; ++j) {
+        const float g = tok_gate[j];
+        const uint4 zv = reinterpret_cast<const uint4*>(Z + static_cast<int64_t>(tok_row[j]) * D)[c];
+        const T* zp = reinterpret_cast<const T*>(&zv);
+#pragma unroll
+        for (int i = 0; i < V; ++i) y[i] = fmaf(g, Elem<T>::to_f32(zp[i]), y[i]);
+      }
+      T out[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        bad |= !isfinite(y[i]);
+        out[i] = Elem<T>::from_f32(y[i]);
+      }
+      reinterpret_cast<uint4*>(Y + static_cast<int64_t>(t) * D)[c] = *reinterpret_cast<const uint4*>(out);
+    }
+  } else {
+    for (int c = lane; c < D; c += 64) {
+      float y = R ? Elem<T>::to_f32(R[static_cast<int64_t>(t) * D + c]) : 0.f;
+      for (int j = j0; j < j1; ++j)
+        y = fmaf(tok_gate[j], Elem<T>::to_f32(Z[static_cast<int64_t>(tok_row[j]) * D + c]), y);
+      bad |= !isfinite(y);
+      Y[static_cast<int64_t>(t) * D + c] = Elem<T>::from_f32(y);
+    }
   }
   if (nonfinite) note_nonfinite(nonfinite, bad);
 }
@@ -299,7 +343,7 @@ struct BwAuxArgs {
   const float* tok_gate;
   const int32_t* slot_pair;
   const float* thresholds;
-  double* per_expert;  // [2][E]: importance, loss
+  double* per_expert;  // [5][E]: importance, loss; token count sum, max, zero count per slice
   float* importance;
   float* out;
   int T, E, m, W;
@@ -348,9 +392,24 @@ __global__ __launch_bounds__(kThreads) void bw_aux_expert(BwAuxArgs a) {
     }
     loss = bw_block_sum(loss, sh);
   }
+  // experts-per-token statistics of token slice e (the E blocks split the tokens)
+  const int64_t t0 = static_cast<int64_t>(a.T) * e / a.E, t1 = static_cast<int64_t>(a.T) * (e + 1) / a.E;
+  double ct = 0, mx = 0, none = 0;
+  for (int64_t t = t0 + threadIdx.x; t < t1; t += kThreads) {
+    const int c = a.tok_count[t];
+    ct += c;
+    mx = fmax(mx, static_cast<double>(c));
+    none += c == 0 ? 1.0 : 0.0;
+  }
+  ct = bw_block_sum(ct, sh);
+  mx = bw_block_max(mx, sh);
+  none = bw_block_sum(none, sh);
   if (threadIdx.x == 0) {
     a.per_expert[e] = imp;
     a.per_expert[a.E + e] = loss;
+    a.per_expert[2 * a.E + e] = ct;
+    a.per_expert[3 * a.E + e] = mx;
+    a.per_expert[4 * a.E + e] = none;
     if (a.importance) a.importance[e] = static_cast<float>(imp);
   }
 }
@@ -371,11 +430,10 @@ __global__ __launch_bounds__(kThreads) void bw_aux_final(BwAuxArgs a) {
   for (int e = threadIdx.x; e < a.E; e += kThreads) vi += (imp[e] - mi) * (imp[e] - mi);
   vi = bw_block_sum(vi, sh) / a.E;
   double ct = 0, mx = 0, none = 0;
-  for (int t = threadIdx.x; t < a.T; t += kThreads) {
-    const int c = a.tok_count[t];
-    ct += c;
-    mx = fmax(mx, static_cast<double>(c));
-    none += c == 0 ? 1.0 : 0.0;
+  for (int e = threadIdx.x; e < a.E; e += kThreads) {
+    ct += a.per_expert[2 * a.E + e];
+    mx = fmax(mx, a.per_expert[3 * a.E + e]);
+    none += a.per_expert[4 * a.E + e];
   }
   ct = bw_block_sum(ct, sh);
   mx = bw_block_max(mx, sh);
@@ -405,7 +463,7 @@ size_t batchwise_route_workspace(const Dims& d) {
          align256(static_cast<size_t>(ceil_div(d.T, kThreads)) * sizeof(int32_t));
 }
 size_t batchwise_aux_workspace(const Dims& d) {
-  return align256(2 * static_cast<size_t>(d.E) * sizeof(double));
+  return align256(5 * static_cast<size_t>(d.E) * sizeof(double));
 }
 
 moe_status batchwise_route_launch(const Dims& d, const void* X, const float* Wg, const float* bias,
@@ -419,8 +477,8 @@ moe_status batchwise_route_launch(const Dims& d, const void* X, const float* Wg,
   bw_softmax<<<ceil_div(d.T, kTileTok), kThreads, 0, stream>>>(clean, d.T, d.E, W, st->probs_t,
                                                                  st->mask);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
-  bw_select<<<d.E, kThreads, 0, stream>>>(st->probs_t, d.T, d.E, m, W, st->sel, st->offsets,
-                                          st->mask);
+  bw_select<<<d.E, kSelThreads, 0, stream>>>(st->probs_t, d.T, d.E, m, W, st->sel, st->offsets,
+                                             st->mask);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   const int nblk = ceil_div(d.T, kThreads);
   bw_tok_count<<<nblk, kThreads, 0, stream>>>(st->mask, d.T, W, st->tok_count, block_sum);
