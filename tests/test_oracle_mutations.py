@@ -195,3 +195,47 @@ def test_batchwise_pins_catch_mutation(monkeypatch, label, old, new):
             failed.append(fn.__name__)
             break
     assert failed, f"no batchwise pin failed for mutation: {label}"
+
+
+# ------------------------------------------------------------ backward oracle
+
+import oracle.backward as OBW  # noqa: E402
+import test_oracle_backward as bwd_pins  # noqa: E402
+
+BWD_MUTATIONS = [
+    ("load threshold detached", "thr = torch.where(inside, vk1[:, None], vk[:, None])",
+     "thr = torch.where(inside, vk1[:, None], vk[:, None]).detach()"),
+    ("noise scale detached", "H = clean + torch.from_numpy(O.widen(eps)) * std",
+     "H = clean + torch.from_numpy(O.widen(eps)) * std.detach()"),
+    ("dropped assignments contribute", "tt, jj = np.nonzero((r.ids == e) & d.accepted)",
+     "tt, jj = np.nonzero(r.ids == e)"),
+    ("gate detached", "G = torch.softmax(Hk, dim=1)", "G = torch.softmax(Hk.detach(), dim=1)"),
+    ("residual dropped", "Y = X * 1.0 if residual else torch.zeros_like(X)",
+     "Y = torch.zeros_like(X)"),
+    ("CV with ddof 1", "return ((v - m) ** 2).mean() / (m * m)",
+     "return ((v - m) ** 2).sum() / (v.numel() - 1) / (m * m)"),
+]
+
+BWD_PIN_TESTS = [getattr(bwd_pins, n) for n in dir(bwd_pins) if n.startswith("test_")]
+
+
+@pytest.mark.parametrize("label,old,new", BWD_MUTATIONS, ids=[m[0] for m in BWD_MUTATIONS])
+def test_backward_pins_catch_mutation(monkeypatch, label, old, new):
+    mut = _mutant("backward", old, new)
+    for name, val in vars(mut).items():
+        if isinstance(val, types.FunctionType) and hasattr(OBW, name):
+            monkeypatch.setattr(OBW, name, val)
+    failed = []
+    for fn in BWD_PIN_TESTS:
+        marks = getattr(fn, "pytestmark", [])
+        params = [m_ for m_ in marks if m_.name == "parametrize"]
+        cases = [()]
+        if params:
+            cases = [v if isinstance(v, tuple) else (v,) for v in params[0].args[1]]
+        try:
+            for c in cases:
+                fn(*c)
+        except Exception:
+            failed.append(fn.__name__)
+            break
+    assert failed, f"no backward pin failed for mutation: {label}"
