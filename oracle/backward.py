@@ -99,10 +99,11 @@ def layer_grads(inp: dict, w, r: O.Routing, d: O.Dispatch, eps, dY, w_imp=0.0, w
             ik1 = torch.from_numpy(order[:, k].astype(np.int64))
             vk1 = H[torch.arange(T), ik1]
             thr = torch.where(inside, vk1[:, None], vk[:, None])
+            P = torch.special.ndtr((clean - thr) / std)
         else:
-            thr = torch.full((T, E), -float("inf"), dtype=torch.float64)
-        z = (clean - thr) / std
-        P = torch.special.ndtr(z)
+            # k = E: every expert is kept and no (k+1)-th score exists, so each expert is kept
+            # under every noise draw; P = 1 is a constant and the term has no gradient
+            P = torch.ones(T, E, dtype=torch.float64)
         obj = obj + w_load * _cv2(P.sum(dim=0))
     obj.backward()
     out = dict(dX=X.grad.numpy(), dWg=Wg.grad.numpy(),

@@ -38,11 +38,13 @@ def _objective(inp, w, eps, dY, ids_ref, w_imp, w_load):
     return float((Y * dY).sum() + w_imp * O.cv2(a["importance"]) + w_load * O.cv2(a["load"]))
 
 
-@pytest.mark.parametrize("w_imp,w_load,noise", [(0.0, 0.0, True), (0.3, 0.0, True),
-                                                (0.0, 0.7, True), (0.2, 0.5, True),
-                                                (0.4, 0.0, False)])
-def test_gradients_match_finite_differences(w_imp, w_load, noise):
-    w, inp, eps, dY = _setup(noise=noise)
+@pytest.mark.parametrize("w_imp,w_load,noise,k", [(0.0, 0.0, True, 2), (0.3, 0.0, True, 2),
+                                                  (0.0, 0.7, True, 2), (0.2, 0.5, True, 2),
+                                                  (0.4, 0.0, False, 2), (0.2, 0.5, True, 4)])
+def test_gradients_match_finite_differences(w_imp, w_load, noise, k):
+    """k = 4 = E keeps every expert: the load term is constant there (no finite gradient
+    may leak from a threshold that does not exist)."""
+    w, inp, eps, dY = _setup(noise=noise, k=k)
     r = O.route(inp["X"], inp["Wg"], inp["Wnoise"], inp["bias"], w.k, "noisy", w.noise, eps=eps)
     assert not r.near_tie.any()
     C = O.capacity(w.T, w.k, w.capacity_factor, w.E)
