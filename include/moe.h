@@ -368,6 +368,59 @@ moe_status moe_aux_loss_batchwise(const moe_problem* p, const moe_batchwise_stat
                                   float* out, void* workspace, size_t workspace_bytes,
                                   void* hip_stream);
 
+/* -------------------------------------------------------------- backward */
+
+/* Gradients of the noisy top-k layer ([OLNN] 3.4: the gate trains through the
+ * softmax over the kept experts and through the importance and load losses;
+ * [LESSON] ch. 2 "trace it forward, then backward"). The selection, the
+ * capacity mask and the noise are those of the forward and are held fixed (the
+ * selection is piecewise constant); the load estimator's threshold is the k-th
+ * or (k+1)-th score of the row and passes its gradient to that expert. The
+ * objective is <Y, dY> + w_imp CV^2(importance) + w_load CV^2(load). Order:
+ * moe_combine_backward -> moe_expert_ffn_backward -> moe_route_backward, on the
+ * forward's buffers. p->gating must be MOE_GATE_NOISY_TOPK (Switch:
+ * MOE_ERR_UNSUPPORTED). Weight gradients are fp32 and overwrite their outputs. */
+
+/* W1^T and W2^T in MFMA fragment order (layers 4 and 3 of moe_packed_weight_bytes). */
+moe_status moe_pack_expert_weights_t(const moe_problem* p, const void* W1, const void* W2,
+                                     void* W1t_packed, void* W2t_packed, void* hip_stream);
+
+/* dZ[row] = gate * dY[t] for every accepted assignment (p->dtype); dgates[t,j] =
+ * <dY[t], Z[row]> (fp32; 0 for dropped assignments). dY [T,D]; Z, dZ [rows, D]. */
+moe_status moe_combine_backward(const moe_problem* p, const void* dY, const void* Z,
+                                const int32_t* ids, const float* gates, const int32_t* pos,
+                                const uint8_t* accepted, const int32_t* offsets, void* dZ,
+                                float* dgates, void* hip_stream);
+
+/* dHp = (dZ W2_e^T) masked where Hd <= 0 (the ReLU derivative) [rows, H];
+ * dXd = dHp W1_e^T [rows, D]; dW2_e = Hd_e^T dZ_e [E,H,D] and dW1_e = Xd_e^T dHp_e
+ * [E,D,H] (fp32; either may be NULL). Xd, Hd from the forward. */
+moe_status moe_expert_ffn_backward(const moe_problem* p, const void* Xd, const void* Hd,
+                                   const void* dZ, const void* W1t_packed,
+                                   const void* W2t_packed, const int32_t* offsets, void* dHp,
+                                   void* dXd, float* dW1, float* dW2, void* hip_stream);
+
+/* The gate and router: dclean and d raw from the softmax over the kept scores, the
+ * importance term (importance [E] from moe_aux_loss, needed if w_imp != 0) and the
+ * load term (load [E], needed if w_load != 0; noise only); then
+ *   dX = dY (if dY_residual, the forward used residual = X) + the accepted rows
+ *        of dXd + [dclean | d raw] [Wg | Wnoise]^T          [T,D] p->dtype
+ *   dWg = X^T dclean, dWnoise = X^T d raw  [D,E] fp32; dbias = sum_t dclean [E]
+ *   (dWnoise NULL without noise; dbias may be NULL).
+ * eps: the external noise given to moe_route, or NULL if the router drew it.
+ * workspace moe_backward_workspace_size(p) bytes. */
+moe_status moe_route_backward(const moe_problem* p, const void* X, const float* Wg,
+                              const float* Wnoise, const float* eps, const int32_t* ids,
+                              const float* gates, const float* clean, const float* noise_std,
+                              const float* row_stats, const float* dgates,
+                              const float* importance, const float* load, float w_imp,
+                              float w_load, const void* dY_residual, const void* dXd,
+                              const int32_t* pos, const uint8_t* accepted,
+                              const int32_t* offsets, void* dX, float* dWg, float* dWnoise,
+                              float* dbias, void* workspace, size_t workspace_bytes,
+                              void* hip_stream);
+size_t moe_backward_workspace_size(const moe_problem* p);
+
 /* ------------------------------------------------------------------- misc */
 
 /* Synchronises hip_stream, then returns MOE_ERR_NONFINITE if a kernel run with

@@ -143,7 +143,7 @@ size_t moe_workspace_size(const moe_problem* p, int which) {
 
 size_t moe_packed_weight_bytes(const moe_problem* p, int layer) {
   Dims d;
-  if (validate(p, &d) != MOE_OK || (layer != 1 && layer != 2)) return 0;
+  if (validate(p, &d) != MOE_OK || layer < 1 || layer > 4) return 0;
   return packed_weight_bytes(d, layer);
 }
 
@@ -344,6 +344,78 @@ moe_status moe_aux_loss_batchwise(const moe_problem* p, const moe_batchwise_stat
   if (!out || !batchwise_state_ok(st)) return MOE_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < batchwise_aux_workspace(d)) return MOE_ERR_WORKSPACE;
   return batchwise_aux_launch(d, st, thresholds, importance, out, workspace, as_stream(hip_stream));
+}
+
+// --------------------------------------------------------------- backward
+static moe_status validate_backward(const moe_problem* p, Dims* d) {
+  MOE_TRY(validate(p, d));
+  if (d->gating == MOE_GATE_SWITCH_TOP1) return MOE_ERR_UNSUPPORTED;
+  return d->gating == MOE_GATE_NOISY_TOPK ? MOE_OK : MOE_ERR_INVALID_ARG;
+}
+
+moe_status moe_pack_expert_weights_t(const moe_problem* p, const void* W1, const void* W2,
+                                     void* W1t, void* W2t, void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate(p, &d));
+  if ((W1 && !W1t) || (W2 && !W2t) || (!W1 && !W2)) return MOE_ERR_INVALID_ARG;
+  if (W2) MOE_TRY(pack_launch(d, 3, W2, W2t, as_stream(hip_stream)));
+  if (W1) MOE_TRY(pack_launch(d, 4, W1, W1t, as_stream(hip_stream)));
+  return MOE_OK;
+}
+
+moe_status moe_combine_backward(const moe_problem* p, const void* dY, const void* Z,
+                                const int32_t* ids, const float* gates, const int32_t* pos,
+                                const uint8_t* accepted, const int32_t* offsets, void* dZ,
+                                float* dgates, void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate_backward(p, &d));
+  if (!dY || !Z || !ids || !gates || !pos || !accepted || !offsets || !dZ || !dgates)
+    return MOE_ERR_INVALID_ARG;
+  return combine_backward_launch(d, dY, Z, ids, gates, pos, accepted, offsets, dZ, dgates,
+                                 as_stream(hip_stream));
+}
+
+moe_status moe_expert_ffn_backward(const moe_problem* p, const void* Xd, const void* Hd,
+                                   const void* dZ, const void* W1t, const void* W2t,
+                                   const int32_t* offsets, void* dHp, void* dXd, float* dW1,
+                                   float* dW2, void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate_backward(p, &d));
+  if (!Xd || !Hd || !dZ || !W1t || !W2t || !offsets || !dHp || !dXd) return MOE_ERR_INVALID_ARG;
+  return ffn_backward_launch(d, Xd, Hd, dZ, W1t, W2t, offsets, dHp, dXd, dW1, dW2,
+                             as_stream(hip_stream));
+}
+
+size_t moe_backward_workspace_size(const moe_problem* p) {
+  Dims d;
+  if (validate_backward(p, &d) != MOE_OK) return 0;
+  return route_backward_workspace(d);
+}
+
+moe_status moe_route_backward(const moe_problem* p, const void* X, const float* Wg,
+                              const float* Wnoise, const float* eps, const int32_t* ids,
+                              const float* gates, const float* clean, const float* noise_std,
+                              const float* row_stats, const float* dgates, const float* importance,
+                              const float* load, float w_imp, float w_load,
+                              const void* dY_residual, const void* dXd, const int32_t* pos,
+                              const uint8_t* accepted, const int32_t* offsets, void* dX,
+                              float* dWg, float* dWnoise, float* dbias, void* workspace,
+                              size_t workspace_bytes, void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate_backward(p, &d));
+  const bool noise = d.noise != 0;
+  if (!isfinite(w_imp) || !isfinite(w_load)) return MOE_ERR_INVALID_ARG;
+  if (!X || !Wg || !ids || !gates || !clean || !row_stats || !dgates || !dXd || !pos ||
+      !accepted || !offsets || !dX || !dWg)
+    return MOE_ERR_INVALID_ARG;
+  if (noise && (!Wnoise || !noise_std || !dWnoise)) return MOE_ERR_INVALID_ARG;
+  if (w_imp != 0.f && !importance) return MOE_ERR_INVALID_ARG;
+  if (w_load != 0.f && noise && !load) return MOE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < route_backward_workspace(d)) return MOE_ERR_WORKSPACE;
+  return route_backward_launch(d, p->seed, X, Wg, Wnoise, eps, ids, gates, clean, noise_std,
+                               row_stats, dgates, importance, load, w_imp, w_load, dY_residual,
+                               dXd, pos, accepted, offsets, dX, dWg, dWnoise, dbias, workspace,
+                               as_stream(hip_stream));
 }
 
 moe_status moe_check_finite(void* hip_stream) {

@@ -1,0 +1,664 @@
+// Backward pass of the noisy top-k MoE layer.
+//
+// The pages' purpose is training: "Outrageously Large Neural Networks" summary,
+// section 3.4 (k > 1 so the gate receives gradient through the softmax over the
+// kept experts; the importance and load losses train the gate towards balance);
+// the "Mixture-of-Experts: Sparse Computation" lesson, chapter 2, traces the
+// backward pass: an incoming gradient splits over the kept experts in
+// proportion to their gates, and masked experts are absent from it. The
+// selection and the capacity mask are piecewise constant and held fixed, as is
+// the noise sample (H = clean + eps * Softplus(raw)); the load estimator's
+// threshold is another expert's score and passes its gradient to it.
+//
+// Objective: <Y, dY> + w_imp CV^2(Importance) + w_load CV^2(Load).
+//
+// Kernels:
+//   cb_backward      a wave per token: dZ[row] = g * dY[t] for each accepted
+//                    assignment and dg = <dY[t], Z[row]> (fp32)
+//   cv2_grad         d CV^2 / d v for the importance and load vectors
+//   gate_backward    a wave per token row: softmax backward over the kept
+//                    scores (plus the importance term), the load term of every
+//                    expert through Phi (with the threshold's share going to the
+//                    k-th / (k+1)-th expert), noise redrawn by Philox, then
+//                    d raw = d std * sigmoid(raw); writes [dclean | draw] [T, 2E]
+//                    and per-block partial sums of dclean (the bias gradient)
+//   wgrad_gemm       per group, C = A^T B over the group's rows (fp32 output):
+//                    8x8 (bf16) / 4x4 (fp32) register transposes put both
+//                    operands k-contiguous in LDS, then MFMA; one block per
+//                    (group, 128 x 128 tile), fixed row order
+//   dx_final         a wave per token: dX = dY + sum of the accepted rows of dXd
+//                    + the router's share, fp32 accumulation, one rounding
+// The dense GEMMs of the backward (dZ W2^T with the ReLU mask, dH W1^T and the
+// router's [dclean | draw] [Wg | Wnoise]^T) run on the forward's grouped GEMM
+// kernel with transposed packed weights.
+#include <algorithm>
+
+#include "common.h"
+#include "noise.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// ------------------------------------------------------------------ combine backward
+template <typename T>
+__global__ __launch_bounds__(kThreads) void cb_backward(
+    const T* __restrict__ dY, const T* __restrict__ Z, const int32_t* __restrict__ ids,
+    const float* __restrict__ gates, const int32_t* __restrict__ pos,
+    const uint8_t* __restrict__ accepted, const int32_t* __restrict__ offsets, int Tn, int D, int k,
+    T* __restrict__ dZ, float* __restrict__ dgates) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  for (int j = 0; j < k; ++j) {
+    const int64_t gi = static_cast<int64_t>(t) * k + j;
+    if (!accepted[gi]) {
+      if (lane == 0) dgates[gi] = 0.f;
+      continue;
+    }
+    const int64_t row = static_cast<int64_t>(offsets[ids[gi]]) + pos[gi];
+    const float g = gates[gi];
+    float dot = 0.f;
+    for (int c = lane; c < D; c += 64) {
+      const float dy = Elem<T>::to_f32(dY[static_cast<int64_t>(t) * D + c]);
+      dot = fmaf(dy, Elem<T>::to_f32(Z[row * D + c]), dot);
+      dZ[row * D + c] = Elem<T>::from_f32(g * dy);
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) dgates[gi] = dot;
+  }
+}
+
+// ------------------------------------------------------------------ d CV^2 / d v
+// CV^2 = var / mean^2 (population variance): d/dv_e = 2 / (E mean^2) * ((v_e - mean) - var / mean)
+__global__ __launch_bounds__(kThreads) void cv2_grad(const float* __restrict__ v, int E, float w,
+                                                    float* __restrict__ dv) {
+  __shared__ double sh[kThreads];
+  double s = 0;
+  for (int e = threadIdx.x; e < E; e += kThreads) s += v[e];
+  sh[threadIdx.x] = s;
+  __syncthreads();
+  for (int n = kThreads / 2; n >= 1; n >>= 1) {
+    if (threadIdx.x < n) sh[threadIdx.x] += sh[threadIdx.x + n];
+    __syncthreads();
+  }
+  const double mean = sh[0] / E;
+  __syncthreads();
+  double q = 0;
+  for (int e = threadIdx.x; e < E; e += kThreads) q += (v[e] - mean) * (v[e] - mean);
+  sh[threadIdx.x] = q;
+  __syncthreads();
+  for (int n = kThreads / 2; n >= 1; n >>= 1) {
+    if (threadIdx.x < n) sh[threadIdx.x] += sh[threadIdx.x + n];
+    __syncthreads();
+  }
+  const double var = sh[0] / E;
+  for (int e = threadIdx.x; e < E; e += kThreads)
+    dv[e] = (w == 0.f || mean == 0.0) ? 0.f
+                                      : static_cast<float>(w * 2.0 / (E * mean * mean) *
+                                                           ((v[e] - mean) - var / mean));
+}
+
+// ------------------------------------------------------------------ gate backward
+struct GateArgs {
+  const int32_t* ids;
+  const float* gates;
+  const float* clean;
+  const float* std_in;
+  const float* row_stats;
+  const float* dgates;
+  const float* dimp;   // [E] importance term or NULL
+  const float* dload;  // [E] load term or NULL (needs noise)
+  const float* eps;    // [T, E] the noise the forward was given, or NULL (redrawn by Philox)
+  void* dcat;          // [T, 2E] act dtype: dclean | draw (draw only with noise)
+  float* dbias_part;   // [nblk][E] or NULL
+  uint64_t seed;
+  int T, E, k, noise, dtype;
+};
+
+__device__ __forceinline__ float phi_pdf(float z) { return 0.3989422804014327f * expf(-0.5f * z * z); }
+
+// One wave per row; the row's per-expert values live in LDS (4 waves x E floats x 3). Every
+// wave runs every phase (rows past T only skip their memory accesses), so the phases can be
+// separated by block barriers.
+__global__ __launch_bounds__(kThreads) void gate_backward(GateArgs a) {
+  extern __shared__ float sh[];  // [4][3][E]: dclean, dstd, eps
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int E = a.E, k = a.k;
+  float* dcl = sh + wave * 3 * E;
+  float* dsd = dcl + E;
+  float* eps = dsd + E;
+  const int rows_per_block = kThreads / 64;
+  const int t = blockIdx.x * rows_per_block + wave;
+  const bool live = t < a.T;
+  const int64_t base = static_cast<int64_t>(live ? t : 0) * E;
+  const int32_t* rid = a.ids + static_cast<int64_t>(live ? t : 0) * k;
+  const bool load_term = a.noise && a.dload;
+  for (int e = lane; e < E; e += 64) {
+    dcl[e] = 0.f;
+    dsd[e] = 0.f;
+    eps[e] = 0.f;
+  }
+  __syncthreads();
+  // redraw the forward's noise: every group of 4 experts for the load term, else the kept ones
+  if (live && a.noise && a.eps) {
+    for (int e = lane; e < E; e += 64) eps[e] = a.eps[base + e];
+  } else if (live && a.noise) {
+    if (load_term) {
+      for (int q = lane; q < (E + 3) / 4; q += 64) {
+        float g4[4];
+        noise4(a.seed, 0, t, q, g4);
+        for (int i = 0; i < 4 && 4 * q + i < E; ++i) eps[4 * q + i] = g4[i];
+      }
+    } else if (lane < k) {
+      const int e = rid[lane];
+      float g4[4];
+      noise4(a.seed, 0, t, e >> 2, g4);
+      eps[e] = g4[e & 3];
+    }
+  }
+  __syncthreads();
+  // softmax backward over the kept scores (plus the importance term)
+  {
+    float gj = 0.f, dgj = 0.f;
+    int ej = 0;
+    if (live && lane < k) {
+      const int64_t gi = static_cast<int64_t>(t) * k + lane;
+      ej = a.ids[gi];
+      gj = a.gates[gi];
+      dgj = a.dgates[gi] + (a.dimp ? a.dimp[ej] : 0.f);
+    }
+    const float s = wave_sum(gj * dgj);
+    if (live && lane < k) {
+      const float dh = gj * (dgj - s);
+      dcl[ej] += dh;  // a row's experts are distinct: no two lanes share ej
+      if (a.noise) dsd[ej] += dh * eps[ej];
+    }
+  }
+  __syncthreads();
+  // load term: P(t,e) = Phi((clean - thr) / std) for every expert; the threshold is v_{k+1}
+  // for the kept experts and v_k for the others
+  float s_in = 0.f, s_out = 0.f;
+  int bi = 0x7fffffff;
+  if (load_term) {
+    float best = -INFINITY;
+    if (live) {
+      const float vk = a.row_stats[2 * static_cast<int64_t>(t)];
+      const float vk1 = a.row_stats[2 * static_cast<int64_t>(t) + 1];
+      for (int e = lane; e < E; e += 64) {
+        bool inside = false;
+        for (int j = 0; j < k; ++j) inside |= rid[j] == e;
+        const float cl = a.clean[base + e], sd = a.std_in[base + e];
+        if (!inside) {  // candidate for v_{k+1}: H exactly as the router formed it
+          const float h = fmaf(sd, eps[e], cl);
+          if (h > best || (h == best && e < bi)) {
+            best = h;
+            bi = e;
+          }
+        }
+        const float thr = inside ? vk1 : vk;
+        if (!(sd > 0.f) || thr == -INFINITY) continue;
+        const float z = (cl - thr) / sd;
+        const float dz = a.dload[e] * phi_pdf(z);
+        dcl[e] += dz / sd;
+        dsd[e] -= dz * z / sd;
+        if (inside) s_in += dz / sd;
+        else s_out += dz / sd;
+      }
+    }
+    s_in = wave_sum(s_in);
+    s_out = wave_sum(s_out);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ob = __shfl_xor(best, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ob > best || (ob == best && oi < bi)) {
+        best = ob;
+        bi = oi;
+      }
+    }
+  }
+  __syncthreads();
+  if (load_term && live && lane == 0) {
+    const int ik = rid[k - 1];  // v_k: the last kept expert
+    dcl[ik] -= s_out;
+    dsd[ik] -= s_out * eps[ik];
+    if (k < E && bi < E) {  // v_{k+1}: the best other expert
+      dcl[bi] -= s_in;
+      dsd[bi] -= s_in * eps[bi];
+    }
+  }
+  __syncthreads();
+  // write [dclean | draw]; d raw = d std * sigmoid(raw) = d std * (1 - exp(-std))
+  if (live) {
+    const int64_t o = static_cast<int64_t>(t) * 2 * E;
+    for (int e = lane; e < E; e += 64) {
+      const float dr = a.noise ? dsd[e] * (1.f - expf(-a.std_in[base + e])) : 0.f;
+      if (a.dtype == MOE_BF16) {
+        uint16_t* d = static_cast<uint16_t*>(a.dcat);
+        d[o + e] = f32_to_bf16(dcl[e]);
+        d[o + E + e] = f32_to_bf16(dr);
+      } else {
+        float* d = static_cast<float*>(a.dcat);
+        d[o + e] = dcl[e];
+        d[o + E + e] = dr;
+      }
+    }
+  }
+  // bias gradient partials: the block's rows summed in row order
+  if (a.dbias_part) {
+    const int r0 = blockIdx.x * rows_per_block;
+    const int nr = min(rows_per_block, a.T - r0);
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+      float s2 = 0.f;
+      for (int r = 0; r < nr; ++r) s2 += sh[r * 3 * E + e];
+      a.dbias_part[static_cast<int64_t>(blockIdx.x) * E + e] = s2;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void bias_reduce(const float* __restrict__ part, int nblk,
+                                                       int E, float* __restrict__ dbias) {
+  const int e = blockIdx.x * kThreads + threadIdx.x;
+  if (e >= E) return;
+  double s = 0;
+  for (int b = 0; b < nblk; ++b) s += part[static_cast<int64_t>(b) * E + e];
+  dbias[e] = static_cast<float>(s);
+}
+
+// [Wg | Wnoise]^T packed for the router's input gradient: B[k][n] = Wg[n][k] (k < E) or
+// Wnoise[n][k - E], cast to the activation dtype; one thread per (column block, k-step, lane).
+template <typename T>
+__global__ void router_pack_t(const float* __restrict__ Wg, const float* __restrict__ Wn, int D,
+                              int E, int NB, int KS, uint4* __restrict__ out) {
+  constexpr int V = Elem<T>::kVec;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<int64_t>(NB) * KS * kWave) return;
+  const int lane = static_cast<int>(idx % kWave);
+  const int ks = static_cast<int>((idx / kWave) % KS);
+  const int nb = static_cast<int>(idx / (static_cast<int64_t>(kWave) * KS));
+  const int n = nb * 32 + (lane & 31);
+  const int k0 = ks * 2 * V + (lane >> 5) * V;
+  T v[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int kk = k0 + i;
+    float x = 0.f;
+    if (n < D && kk < 2 * E) x = kk < E ? Wg[static_cast<int64_t>(n) * E + kk]
+                                        : (Wn ? Wn[static_cast<int64_t>(n) * E + kk - E] : 0.f);
+    v[i] = Elem<T>::from_f32(x);
+  }
+  out[idx] = *reinterpret_cast<const uint4*>(v);
+}
+
+__global__ void set_offsets(int32_t* off, int T) {
+  if (threadIdx.x == 0) {
+    off[0] = 0;
+    off[1] = T;
+  }
+}
+
+// ------------------------------------------------------------------ weight-gradient GEMM
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> __device__ __forceinline__ f32x16 wmma(u32x4 a, u32x4 b, f32x16 c);
+template <> __device__ __forceinline__ f32x16 wmma<uint16_t>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x16 wmma<float>(u32x4 a, u32x4 b, f32x16 c) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[s]), __uint_as_float(b[s]), c, 0, 0, 0);
+  return c;
+}
+
+// VB x VB block transpose of 16-byte rows (VB = 16 / sizeof(T)): in[r] holds row r,
+// out[c] holds column c.
+template <typename T> __device__ __forceinline__ void transpose_block(const u32x4 (&in)[16 / sizeof(T)],
+                                                                       u32x4 (&out)[16 / sizeof(T)]);
+template <> __device__ __forceinline__ void transpose_block<float>(const u32x4 (&in)[4], u32x4 (&out)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) out[c] = u32x4{in[0][c], in[1][c], in[2][c], in[3][c]};
+}
+template <> __device__ __forceinline__ void transpose_block<uint16_t>(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+  // step 1: within each pair of rows (2a, 2a+1), pair up the 16-bit halves of each dword:
+  // p[2a][j] = (row 2a col 2j, row 2a+1 col 2j), p[2a+1][j] = (row 2a col 2j+1, row 2a+1 col 2j+1)
+  unsigned p[8][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const unsigned x = in[2 * a][j], y = in[2 * a + 1][j];
+      p[2 * a][j] = (x & 0xffffu) | (y << 16);
+      p[2 * a + 1][j] = (x >> 16) | (y & 0xffff0000u);
+    }
+  // step 2: column c (rows 0..7) is the dwords of row pairs 0..3 for that column
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    out[c] = u32x4{p[0 + (c & 1)][c >> 1], p[2 + (c & 1)][c >> 1], p[4 + (c & 1)][c >> 1],
+                   p[6 + (c & 1)][c >> 1]};
+}
+
+struct WgradArgs {
+  const void* A;   // [rows, M]
+  const void* B;   // [rows, N]
+  const int32_t* offsets;  // [G + 1]
+  float* C;        // [G][M][N]
+  int G, M, N;
+};
+
+constexpr int kWT = 128;            // tile M and N
+constexpr int kWRows = 64;          // rows (the reduction) per stage
+constexpr int kWStride = kWRows * 2 + 16;  // bytes per LDS column line (64 bf16 + pad) for bf16
+
+// One block per (group, m tile, n tile): C_g[m, n] = sum over the group's rows r of
+// A[r, m] B[r, n]; 4 waves in a 2 x 2 layout, each 64 x 64.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void wgrad_gemm(WgradArgs a) {
+  constexpr int VB = 16 / static_cast<int>(sizeof(T));   // elements per 16 bytes
+  constexpr int kLine = kWRows * static_cast<int>(sizeof(T)) + 16;  // LDS bytes per column line
+  // per stage: A tile [kWRows][kWT] and B tile [kWRows][kWT] -> transposed into
+  // lines [kWT][kWRows] (k contiguous)
+  __shared__ __align__(16) unsigned char sA[kWT * kLine];
+  __shared__ __align__(16) unsigned char sB[kWT * kLine];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int mt = (a.M + kWT - 1) / kWT, nt = (a.N + kWT - 1) / kWT;
+  const int g = blockIdx.x / (mt * nt);
+  const int rem = blockIdx.x - g * mt * nt;
+  const int m0 = (rem / nt) * kWT, n0 = (rem % nt) * kWT;
+  const int r_begin = a.offsets[g], r_end = a.offsets[g + 1];
+  const T* A = static_cast<const T*>(a.A);
+  const T* B = static_cast<const T*>(a.B);
+  // loader: blocks of VB rows x VB columns; (kWRows / VB) x (kWT / VB) per operand
+  constexpr int kBR = kWRows / VB, kBC = kWT / VB, kBlocks = kBR * kBC;  // per operand
+  const int wm = wave >> 1, wn = wave & 1;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  for (int rs = r_begin; rs < r_end; rs += kWRows) {
+    // load + transpose both operands (2 * kBlocks blocks over kThreads threads)
+    for (int bidx = tid; bidx < 2 * kBlocks; bidx += kThreads) {
+      const bool isA = bidx < kBlocks;
+      const int b2 = isA ? bidx : bidx - kBlocks;
+      const int rb = b2 / kBC, cb = b2 - rb * kBC;
+      const T* src = isA ? A : B;
+      const int ld = isA ? a.M : a.N;
+      const int c0 = (isA ? m0 : n0) + cb * VB;
+      u32x4 in[VB], out[VB];
+#pragma unroll
+      for (int i = 0; i < VB; ++i) {
+        const int r = rs + rb * VB + i;
+        if (r < r_end && c0 + VB <= ld && ld % VB == 0) {  // 16-byte aligned row segment
+          in[i] = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(r) * ld + c0);
+        } else {
+          T tmp[VB];
+#pragma unroll
+          for (int q = 0; q < VB; ++q)
+            tmp[q] = (r < r_end && c0 + q < ld) ? src[static_cast<int64_t>(r) * ld + c0 + q] : T(0);
+          in[i] = *reinterpret_cast<const u32x4*>(tmp);
+        }
+      }
+      transpose_block<T>(in, out);
+      unsigned char* dst = isA ? sA : sB;
+#pragma unroll
+      for (int c = 0; c < VB; ++c)
+        *reinterpret_cast<u32x4*>(dst + (cb * VB + c) * kLine + rb * 16) = out[c];
+    }
+    __syncthreads();
+    // MFMA over the stage: k-steps of 2*VB rows (one 16-byte fragment per lane half)
+#pragma unroll
+    for (int ks = 0; ks < kWRows / (2 * VB); ++ks) {
+      u32x4 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int m = wm * 64 + i * 32 + (lane & 31);
+        fa[i] = *reinterpret_cast<const u32x4*>(sA + m * kLine + (ks * 2 + (lane >> 5)) * 16);
+        const int n = wn * 64 + i * 32 + (lane & 31);
+        fb[i] = *reinterpret_cast<const u32x4*>(sB + n * kLine + (ks * 2 + (lane >> 5)) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = wmma<T>(fa[i], fb[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  // fp32 output tile
+  float* C = a.C + static_cast<int64_t>(g) * a.M * a.N;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = m0 + wm * 64 + i * 32 + acc_row(lane, q);
+        if (m < a.M && n < a.N) C[static_cast<int64_t>(m) * a.N + n] = acc[i][j][q];
+      }
+    }
+}
+
+// ------------------------------------------------------------------ input gradient
+template <typename T>
+__global__ __launch_bounds__(kThreads) void dx_final(
+    const T* __restrict__ dY, const T* __restrict__ dXd, const T* __restrict__ dXr,
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ pos,
+    const uint8_t* __restrict__ accepted, const int32_t* __restrict__ offsets, int Tn, int D, int k,
+    int residual, T* __restrict__ dX) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  int64_t row[MOE_MAX_K];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_K; ++j) {
+    row[j] = -1;
+    if (j < k) {
+      const int64_t gi = static_cast<int64_t>(t) * k + j;
+      if (accepted[gi]) row[j] = static_cast<int64_t>(offsets[ids[gi]]) + pos[gi];
+    }
+  }
+  for (int c = lane; c < D; c += 64) {
+    const int64_t o = static_cast<int64_t>(t) * D + c;
+    float v = residual ? Elem<T>::to_f32(dY[o]) : 0.f;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_K; ++j)
+      if (row[j] >= 0) v += Elem<T>::to_f32(dXd[row[j] * D + c]);
+    if (dXr) v += Elem<T>::to_f32(dXr[o]);
+    dX[o] = Elem<T>::from_f32(v);
+  }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ host side
+moe_status combine_backward_launch(const Dims& d, const void* dY, const void* Z, const int32_t* ids,
+                                   const float* gates, const int32_t* pos, const uint8_t* accepted,
+                                   const int32_t* offsets, void* dZ, float* dgates,
+                                   hipStream_t stream) {
+  const int grid = ceil_div(d.T, kThreads / 64);
+  if (d.dtype == MOE_BF16)
+    cb_backward<uint16_t><<<grid, kThreads, 0, stream>>>(
+        static_cast<const uint16_t*>(dY), static_cast<const uint16_t*>(Z), ids, gates, pos,
+        accepted, offsets, d.T, d.D, d.k, static_cast<uint16_t*>(dZ), dgates);
+  else
+    cb_backward<float><<<grid, kThreads, 0, stream>>>(
+        static_cast<const float*>(dY), static_cast<const float*>(Z), ids, gates, pos, accepted,
+        offsets, d.T, d.D, d.k, static_cast<float*>(dZ), dgates);
+  return launch_status();
+}
+
+moe_status wgrad_launch(const Dims& d, const void* A, const void* B, const int32_t* offsets, int G,
+                        int M, int N, float* C, hipStream_t stream) {
+  WgradArgs a{A, B, offsets, C, G, M, N};
+  const int64_t blocks = static_cast<int64_t>(G) * ceil_div(M, kWT) * ceil_div(N, kWT);
+  if (blocks > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  if (d.dtype == MOE_BF16)
+    wgrad_gemm<uint16_t><<<static_cast<int>(blocks), kThreads, 0, stream>>>(a);
+  else
+    wgrad_gemm<float><<<static_cast<int>(blocks), kThreads, 0, stream>>>(a);
+  return launch_status();
+}
+
+static int router_bwd_ks(const Dims& d) {  // k-steps over the 2E inputs of the router GEMM
+  const int stage = d.dtype == MOE_BF16 ? 64 : 32;
+  return ceil_div(2 * d.E, stage) * 4;
+}
+
+// Workspace of moe_route_backward: dimp, dload [E]; dbias partials; dcat [T, 2E]; the packed
+// [Wg | Wnoise]^T; offsets {0, T}; the router's input-gradient share [T, D]; dWcat [D, 2E].
+struct RouteBwdLayout {
+  size_t dimp, dload, dbias, dcat, wpack, off, dxr, dwcat, total;
+};
+static RouteBwdLayout route_bwd_layout(const Dims& d) {
+  RouteBwdLayout L;
+  const size_t el = d.dtype == MOE_BF16 ? 2 : 4;
+  const int nblk = ceil_div(d.T, kThreads / 64);
+  size_t o = 0;
+  L.dimp = o; o += align256(d.E * sizeof(float));
+  L.dload = o; o += align256(d.E * sizeof(float));
+  L.dbias = o; o += align256(static_cast<size_t>(nblk) * d.E * sizeof(float));
+  L.dcat = o; o += align256(static_cast<size_t>(d.T) * 2 * d.E * el);
+  L.wpack = o; o += align256(static_cast<size_t>(ceil_div(d.D, 32)) * router_bwd_ks(d) * kWave * 16);
+  L.off = o; o += 256;
+  L.dxr = o; o += align256(static_cast<size_t>(d.T) * d.D * el);
+  L.dwcat = o; o += align256(static_cast<size_t>(d.D) * 2 * d.E * sizeof(float));
+  L.total = o;
+  return L;
+}
+size_t route_backward_workspace(const Dims& d) { return route_bwd_layout(d).total; }
+
+__global__ void split_dw(const float* __restrict__ dwcat, int D, int E, float* __restrict__ dWg,
+                         float* __restrict__ dWn) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(D) * E) return;
+  const int64_t dd = i / E;
+  const int e = static_cast<int>(i - dd * E);
+  dWg[i] = dwcat[dd * 2 * E + e];
+  if (dWn) dWn[i] = dwcat[dd * 2 * E + E + e];
+}
+
+moe_status route_backward_launch(const Dims& d, uint64_t seed, const void* X, const float* Wg,
+                                 const float* Wnoise, const float* eps, const int32_t* ids,
+                                 const float* gates,
+                                 const float* clean, const float* noise_std, const float* row_stats,
+                                 const float* dgates, const float* importance, const float* load,
+                                 float w_imp, float w_load, const void* dY, const void* dXd,
+                                 const int32_t* pos, const uint8_t* accepted, const int32_t* offsets,
+                                 void* dX, float* dWg, float* dWnoise, float* dbias, void* ws,
+                                 hipStream_t stream) {
+  const RouteBwdLayout L = route_bwd_layout(d);
+  char* base = static_cast<char*>(ws);
+  float* dimp = reinterpret_cast<float*>(base + L.dimp);
+  float* dload = reinterpret_cast<float*>(base + L.dload);
+  float* dbias_part = reinterpret_cast<float*>(base + L.dbias);
+  void* dcat = base + L.dcat;
+  uint4* wpack = reinterpret_cast<uint4*>(base + L.wpack);
+  int32_t* off = reinterpret_cast<int32_t*>(base + L.off);
+  void* dxr = base + L.dxr;
+  float* dwcat = reinterpret_cast<float*>(base + L.dwcat);
+  const bool noise = d.noise != 0;
+  if (w_imp != 0.f) {
+    cv2_grad<<<1, kThreads, 0, stream>>>(importance, d.E, w_imp, dimp);
+    if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  }
+  const bool use_load = noise && w_load != 0.f;
+  if (use_load) {
+    cv2_grad<<<1, kThreads, 0, stream>>>(load, d.E, w_load, dload);
+    if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  }
+  GateArgs ga;
+  ga.ids = ids;
+  ga.gates = gates;
+  ga.clean = clean;
+  ga.std_in = noise ? noise_std : nullptr;
+  ga.row_stats = row_stats;
+  ga.dgates = dgates;
+  ga.dimp = w_imp != 0.f ? dimp : nullptr;
+  ga.dload = use_load ? dload : nullptr;
+  ga.eps = noise ? eps : nullptr;
+  ga.dcat = dcat;
+  ga.dbias_part = dbias ? dbias_part : nullptr;
+  ga.seed = seed;
+  ga.T = d.T;
+  ga.E = d.E;
+  ga.k = d.k;
+  ga.noise = noise ? 1 : 0;
+  ga.dtype = d.dtype;
+  const int nblk = ceil_div(d.T, kThreads / 64);
+  const size_t lds = static_cast<size_t>(kThreads / 64) * 3 * d.E * sizeof(float);
+  gate_backward<<<nblk, kThreads, lds, stream>>>(ga);
+  if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  if (dbias) {
+    bias_reduce<<<ceil_div(d.E, kThreads), kThreads, 0, stream>>>(dbias_part, nblk, d.E, dbias);
+    if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  }
+  // the router's share of dX: [dclean | draw] [Wg | Wnoise]^T as a one-group GEMM
+  Dims dr = d;
+  dr.E = 1;
+  dr.k = 1;
+  dr.D = 2 * d.E;  // K
+  dr.H = d.D;      // N
+  dr.C = d.T;
+  dr.max_rows = d.T;
+  const int NB = ceil_div(d.D, 32), KS = router_bwd_ks(d);
+  const int64_t items = static_cast<int64_t>(NB) * KS * kWave;
+  if (d.dtype == MOE_BF16)
+    router_pack_t<uint16_t><<<static_cast<int>(ceil_div64(items, 256)), 256, 0, stream>>>(
+        Wg, noise ? Wnoise : nullptr, d.D, d.E, NB, KS, wpack);
+  else
+    router_pack_t<float><<<static_cast<int>(ceil_div64(items, 256)), 256, 0, stream>>>(
+        Wg, noise ? Wnoise : nullptr, d.D, d.E, NB, KS, wpack);
+  if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  set_offsets<<<1, 64, 0, stream>>>(off, d.T);
+  moe_status s = gemm_launch(dr, 3, dcat, wpack, off, dxr, nullptr, stream);
+  if (s != MOE_OK) return s;
+  // dWcat = X^T [dclean | draw]
+  s = wgrad_launch(d, X, dcat, off, 1, d.D, 2 * d.E, dwcat, stream);
+  if (s != MOE_OK) return s;
+  split_dw<<<static_cast<int>(ceil_div64(static_cast<int64_t>(d.D) * d.E, 256)), 256, 0, stream>>>(
+      dwcat, d.D, d.E, dWg, noise ? dWnoise : nullptr);
+  if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  // dX = dY (residual) + the experts' rows + the router's share
+  const int grid = ceil_div(d.T, kThreads / 64);
+  if (d.dtype == MOE_BF16)
+    dx_final<uint16_t><<<grid, kThreads, 0, stream>>>(
+        static_cast<const uint16_t*>(dY), static_cast<const uint16_t*>(dXd),
+        static_cast<const uint16_t*>(dxr), ids, pos, accepted, offsets, d.T, d.D, d.k, dY ? 1 : 0,
+        static_cast<uint16_t*>(dX));
+  else
+    dx_final<float><<<grid, kThreads, 0, stream>>>(
+        static_cast<const float*>(dY), static_cast<const float*>(dXd),
+        static_cast<const float*>(dxr), ids, pos, accepted, offsets, d.T, d.D, d.k, dY ? 1 : 0,
+        static_cast<float*>(dX));
+  return launch_status();
+}
+
+moe_status ffn_backward_launch(const Dims& d, const void* Xd, const void* Hd, const void* dZ,
+                               const void* W1t, const void* W2t, const int32_t* offsets, void* dHp,
+                               void* dXd, float* dW1, float* dW2, hipStream_t stream) {
+  // dH (pre-activation) = (dZ W2^T) masked by Hd > 0; dXd = dH W1^T
+  moe_status s = gemm_launch(d, 3, dZ, W2t, offsets, dHp, nullptr, stream, Hd);
+  if (s != MOE_OK) return s;
+  s = gemm_launch(d, 4, dHp, W1t, offsets, dXd, nullptr, stream);
+  if (s != MOE_OK) return s;
+  if (dW2) {
+    s = wgrad_launch(d, Hd, dZ, offsets, d.E, d.H, d.D, dW2, stream);
+    if (s != MOE_OK) return s;
+  }
+  if (dW1) s = wgrad_launch(d, Xd, dHp, offsets, d.E, d.D, d.H, dW1, stream);
+  return s;
+}
+
+}  // namespace moe

@@ -149,7 +149,8 @@ moe_status dispatch_launch(const Dims& d, const void* X, const int32_t* ids, int
                            int32_t* row_token, void* Xd, void* ws, hipStream_t stream);
 moe_status pack_launch(const Dims& d, int layer, const void* W, void* Wp, hipStream_t stream);
 moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp,
-                       const int32_t* offsets, void* C, int* nonfinite, hipStream_t stream);
+                       const int32_t* offsets, void* C, int* nonfinite, hipStream_t stream,
+                       const void* mask = nullptr);
 moe_status combine_launch(const Dims& d, const void* Z, const int32_t* ids, const float* gates,
                           const int32_t* pos, const uint8_t* accepted, const int32_t* offsets,
                           const void* residual, void* Y, int* nonfinite, hipStream_t stream);
@@ -194,5 +195,26 @@ moe_status batchwise_combine_launch(const Dims& d, const void* Z, const moe_batc
 moe_status batchwise_aux_launch(const Dims& d, const moe_batchwise_state* st,
                                 const float* thresholds, float* importance, float* out, void* ws,
                                 hipStream_t stream);
+
+// Backward pass (backward.hip).
+size_t route_backward_workspace(const Dims& d);
+moe_status combine_backward_launch(const Dims& d, const void* dY, const void* Z, const int32_t* ids,
+                                   const float* gates, const int32_t* pos, const uint8_t* accepted,
+                                   const int32_t* offsets, void* dZ, float* dgates,
+                                   hipStream_t stream);
+moe_status wgrad_launch(const Dims& d, const void* A, const void* B, const int32_t* offsets, int G,
+                        int M, int N, float* C, hipStream_t stream);
+moe_status ffn_backward_launch(const Dims& d, const void* Xd, const void* Hd, const void* dZ,
+                               const void* W1t, const void* W2t, const int32_t* offsets, void* dHp,
+                               void* dXd, float* dW1, float* dW2, hipStream_t stream);
+moe_status route_backward_launch(const Dims& d, uint64_t seed, const void* X, const float* Wg,
+                                 const float* Wnoise, const float* eps, const int32_t* ids,
+                                 const float* gates, const float* clean, const float* noise_std,
+                                 const float* row_stats, const float* dgates,
+                                 const float* importance, const float* load, float w_imp,
+                                 float w_load, const void* dY, const void* dXd, const int32_t* pos,
+                                 const uint8_t* accepted, const int32_t* offsets, void* dX,
+                                 float* dWg, float* dWnoise, float* dbias, void* ws,
+                                 hipStream_t stream);
 
 }  // namespace moe

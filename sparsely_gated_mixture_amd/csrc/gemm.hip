@@ -41,6 +41,7 @@ struct GemmArgs {
   const int32_t* offsets;
   void* C;
   int* nonfinite;
+  const void* mask;  // epilogue mode 2: output zeroed where mask[row, col] <= 0 ([rows, N])
   int E, K, N;
   int NB;  // 32-column blocks per expert in Wp
   int KS;  // k-steps per column block in Wp (multiple of 4)
@@ -62,9 +63,11 @@ template <> __device__ __forceinline__ f32x16 mma<float>(u32x4 a, u32x4 b, f32x1
   return c;
 }
 
+// kEpi: 0 plain, 1 ReLU, 2 masked by a second tensor of the output's shape (the ReLU
+// derivative in the backward pass: zero where the forward's hidden value is not positive).
 // kFullK: K is a multiple of the 128-byte k stage (no tail, no bounds checks on A).
 // kVecOut: N * sizeof(T) is a multiple of 16 (row-contiguous 16-byte output stores).
-template <typename T, int BM, bool kRelu, bool kFullK, bool kVecOut>
+template <typename T, int BM, int kEpi, bool kFullK, bool kVecOut>
 __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
   constexpr int V = Elem<T>::kVec;
   constexpr int kStageElems = 128 / static_cast<int>(sizeof(T));
@@ -221,7 +224,14 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float v = acc[m][j][i];
-          if (kRelu) v = fmaxf(v, 0.f);
+          if (kEpi == 1) v = fmaxf(v, 0.f);
+          if (kEpi == 2) {
+            const int row = m * 32 + acc_row(lane, i);
+            const T* M = static_cast<const T*>(g.mask);
+            if (col_ok && row < rows &&
+                !(Elem<T>::to_f32(M[static_cast<int64_t>(r0 + row) * g.N + cbase + (lane & 31)]) > 0.f))
+              v = 0.f;
+          }
           bad |= col_ok && m * 32 + acc_row(lane, i) < rows && !isfinite(v);
           Ts[acc_row(lane, i) * kTStride + (lane & 31)] = Elem<T>::from_f32(v);
         }
@@ -247,7 +257,10 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
           const int row = m * 32 + acc_row(lane, i);
           if (row < rows) {
             float v = acc[m][j][i];
-            if (kRelu) v = fmaxf(v, 0.f);
+            if (kEpi == 1) v = fmaxf(v, 0.f);
+            if (kEpi == 2 &&
+                !(Elem<T>::to_f32(static_cast<const T*>(g.mask)[static_cast<int64_t>(r0 + row) * g.N + col]) > 0.f))
+              v = 0.f;
             bad |= !isfinite(v);
             C[static_cast<int64_t>(r0 + row) * g.N + col] = Elem<T>::from_f32(v);
           }
@@ -258,8 +271,9 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
 }
 
 // One thread per (expert, column block, k-step, lane): lane's 16-byte B operand.
-// Column n = nb*32 + lane%32, k = ks*2V + (lane/32)*V + i; zero padded.
-template <typename T>
+// Column n = nb*32 + lane%32, k = ks*2V + (lane/32)*V + i; zero padded. kTrans: the
+// source is stored [E, N, K] (B = the transpose of a weight, for the backward pass).
+template <typename T, bool kTrans>
 __global__ void pack_weights(const T* __restrict__ W, int E, int K, int N, int NB, int KS,
                              uint4* __restrict__ out) {
   constexpr int V = Elem<T>::kVec;
@@ -278,7 +292,9 @@ __global__ void pack_weights(const T* __restrict__ W, int E, int K, int N, int N
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     const int k = k0 + i;
-    v[i] = (n < N && k < K) ? W[(static_cast<int64_t>(e) * K + k) * N + n] : T(0);
+    v[i] = (n < N && k < K) ? W[kTrans ? (static_cast<int64_t>(e) * N + n) * K + k
+                                        : (static_cast<int64_t>(e) * K + k) * N + n]
+                            : T(0);
   }
   out[idx] = *reinterpret_cast<const uint4*>(v);
 }
@@ -288,9 +304,12 @@ constexpr int kBM = 128;
 }  // namespace
 
 // ------------------------------------------------------------------ host side
+// layer 1: W1 (K = D, N = H); 2: W2 (K = H, N = D); 3: W2 transposed (K = D, N = H);
+// 4: W1 transposed (K = H, N = D).
 static void layer_dims(const Dims& d, int layer, int* K, int* N) {
-  *K = layer == 1 ? d.D : d.H;
-  *N = layer == 1 ? d.H : d.D;
+  const bool to_h = layer == 1 || layer == 3;
+  *K = to_h ? d.D : d.H;
+  *N = to_h ? d.H : d.D;
 }
 static int gemm_ks(const Dims& d, int K) {
   const int stage = d.dtype == MOE_BF16 ? 64 : 32;
@@ -309,34 +328,39 @@ moe_status pack_launch(const Dims& d, int layer, const void* W, void* Wp, hipStr
   const int NB = ceil_div(N, 32), KS = gemm_ks(d, K);
   const int64_t total = static_cast<int64_t>(d.E) * NB * KS * kWave;
   const int grid = static_cast<int>(ceil_div64(total, 256));
-  if (d.dtype == MOE_BF16)
-    pack_weights<uint16_t><<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(W), d.E, K, N, NB, KS,
-                                                     static_cast<uint4*>(Wp));
-  else
-    pack_weights<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(W), d.E, K, N, NB, KS,
-                                                  static_cast<uint4*>(Wp));
+  const bool tr = layer >= 3;
+  if (d.dtype == MOE_BF16) {
+    const auto* w = static_cast<const uint16_t*>(W);
+    if (tr) pack_weights<uint16_t, true><<<grid, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
+    else pack_weights<uint16_t, false><<<grid, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
+  } else {
+    const auto* w = static_cast<const float*>(W);
+    if (tr) pack_weights<float, true><<<grid, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
+    else pack_weights<float, false><<<grid, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
+  }
   return launch_status();
 }
 
-template <typename T, bool kRelu>
+template <typename T, int kEpi>
 static void launch_k(const GemmArgs& g, int grid, size_t lds, hipStream_t stream) {
   constexpr int V = Elem<T>::kVec;
   const bool full = g.K % (128 / static_cast<int>(sizeof(T))) == 0;
   const bool vout = g.N % V == 0;
-  if (full && vout) grouped_gemm<T, kBM, kRelu, true, true><<<grid, kThreads, lds, stream>>>(g);
-  else if (full) grouped_gemm<T, kBM, kRelu, true, false><<<grid, kThreads, lds, stream>>>(g);
-  else if (vout) grouped_gemm<T, kBM, kRelu, false, true><<<grid, kThreads, lds, stream>>>(g);
-  else grouped_gemm<T, kBM, kRelu, false, false><<<grid, kThreads, lds, stream>>>(g);
+  if (full && vout) grouped_gemm<T, kBM, kEpi, true, true><<<grid, kThreads, lds, stream>>>(g);
+  else if (full) grouped_gemm<T, kBM, kEpi, true, false><<<grid, kThreads, lds, stream>>>(g);
+  else if (vout) grouped_gemm<T, kBM, kEpi, false, true><<<grid, kThreads, lds, stream>>>(g);
+  else grouped_gemm<T, kBM, kEpi, false, false><<<grid, kThreads, lds, stream>>>(g);
 }
 
 template <typename T>
 static void launch_typed(const GemmArgs& g, int layer, int grid, size_t lds, hipStream_t stream) {
-  if (layer == 1) launch_k<T, true>(g, grid, lds, stream);
-  else launch_k<T, false>(g, grid, lds, stream);
+  if (layer == 1) launch_k<T, 1>(g, grid, lds, stream);
+  else if (g.mask) launch_k<T, 2>(g, grid, lds, stream);
+  else launch_k<T, 0>(g, grid, lds, stream);
 }
 
 moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp, const int32_t* offsets,
-                       void* C, int* nonfinite, hipStream_t stream) {
+                       void* C, int* nonfinite, hipStream_t stream, const void* mask) {
   int K, N;
   layer_dims(d, layer, &K, &N);
   GemmArgs g;
@@ -345,6 +369,7 @@ moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp, 
   g.offsets = offsets;
   g.C = C;
   g.nonfinite = nonfinite;
+  g.mask = mask;
   g.E = d.E;
   g.K = K;
   g.N = N;

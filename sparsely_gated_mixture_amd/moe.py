@@ -32,6 +32,8 @@ ENTRY_POINTS = [
     "moe_hier_workspace_size", "moe_route_hier", "moe_aux_loss_hier",
     "moe_batchwise_m", "moe_batchwise_workspace_size", "moe_route_batchwise",
     "moe_dispatch_batchwise", "moe_combine_batchwise", "moe_aux_loss_batchwise",
+    "moe_pack_expert_weights_t", "moe_combine_backward", "moe_expert_ffn_backward",
+    "moe_route_backward", "moe_backward_workspace_size",
 ]
 
 
@@ -102,6 +104,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                            [ctypes.POINTER(HierState), vp, sz, vp]),
         "moe_aux_loss_hier": (ctypes.c_int, [P, ctypes.POINTER(Hier), ctypes.POINTER(HierState)] +
                               [vp] * 4 + [sz, vp]),
+        "moe_pack_expert_weights_t": (ctypes.c_int, [P, vp, vp, vp, vp, vp]),
+        "moe_combine_backward": (ctypes.c_int, [P] + [vp] * 9 + [vp]),
+        "moe_expert_ffn_backward": (ctypes.c_int, [P] + [vp] * 10 + [vp]),
+        "moe_route_backward": (ctypes.c_int, [P] + [vp] * 12 + [ctypes.c_float, ctypes.c_float] +
+                               [vp] * 9 + [vp, sz, vp]),
+        "moe_backward_workspace_size": (sz, [P]),
         "moe_batchwise_m": (i32, [P]),
         "moe_batchwise_workspace_size": (sz, [P, ctypes.c_int]),
         "moe_route_batchwise": (ctypes.c_int, [P, vp, vp, vp, vp, ctypes.POINTER(BatchwiseState),
@@ -298,6 +306,40 @@ def moe_aux_loss_batchwise(p, st: dict, thresholds, importance, out, ws, stream=
            "moe_aux_loss_batchwise")
 
 
+def moe_pack_expert_weights_t(p, W1, W2, W1t, W2t, stream=None):
+    _check(_lib.moe_pack_expert_weights_t(ctypes.byref(p), _ptr(W1), _ptr(W2), _ptr(W1t),
+                                          _ptr(W2t), _stream(stream)), "moe_pack_expert_weights_t")
+
+
+def moe_combine_backward(p, dY, Z, ids, gates, pos, accepted, offsets, dZ, dgates, stream=None):
+    _check(_lib.moe_combine_backward(ctypes.byref(p), _ptr(dY), _ptr(Z), _ptr(ids), _ptr(gates),
+                                     _ptr(pos), _ptr(accepted), _ptr(offsets), _ptr(dZ),
+                                     _ptr(dgates), _stream(stream)), "moe_combine_backward")
+
+
+def moe_expert_ffn_backward(p, Xd, Hd, dZ, W1t, W2t, offsets, dHp, dXd, dW1, dW2, stream=None):
+    _check(_lib.moe_expert_ffn_backward(ctypes.byref(p), _ptr(Xd), _ptr(Hd), _ptr(dZ), _ptr(W1t),
+                                        _ptr(W2t), _ptr(offsets), _ptr(dHp), _ptr(dXd), _ptr(dW1),
+                                        _ptr(dW2), _stream(stream)), "moe_expert_ffn_backward")
+
+
+def moe_backward_workspace_size(p: Problem) -> int:
+    return _lib.moe_backward_workspace_size(ctypes.byref(p))
+
+
+def moe_route_backward(p, X, Wg, Wnoise, eps, ids, gates, clean, noise_std, row_stats, dgates,
+                       importance, load, w_imp, w_load, dY_residual, dXd, pos, accepted, offsets,
+                       dX, dWg, dWnoise, dbias, ws, stream=None):
+    _check(_lib.moe_route_backward(ctypes.byref(p), _ptr(X), _ptr(Wg), _ptr(Wnoise), _ptr(eps),
+                                   _ptr(ids), _ptr(gates), _ptr(clean), _ptr(noise_std),
+                                   _ptr(row_stats), _ptr(dgates), _ptr(importance), _ptr(load),
+                                   float(w_imp), float(w_load), _ptr(dY_residual), _ptr(dXd),
+                                   _ptr(pos), _ptr(accepted), _ptr(offsets), _ptr(dX), _ptr(dWg),
+                                   _ptr(dWnoise), _ptr(dbias), _ptr(ws),
+                                   ws.numel() if ws is not None else 0, _stream(stream)),
+           "moe_route_backward")
+
+
 def moe_check_finite(stream=None):
     _check(_lib.moe_check_finite(_stream(stream)), "moe_check_finite")
 
@@ -343,6 +385,8 @@ class Layer:
         noisy = p.gating == MOE_GATE_NOISY_TOPK and p.noise == 1
         e = lambda *s, dtype=torch.float32: torch.empty(*s, dtype=dtype, device=device)
         self.Wg, self.Wnoise, self.bias = Wg, Wnoise, bias
+        self.W1, self.W2 = W1, W2
+        self.grads = None
         self.W1p = e(moe_packed_weight_bytes(p, 1), dtype=torch.uint8)
         self.W2p = e(moe_packed_weight_bytes(p, 2), dtype=torch.uint8)
         moe_pack_expert_weights(p, W1, W2, self.W1p, self.W2p)
@@ -389,6 +433,38 @@ class Layer:
         b = self.b
         moe_aux_loss(self.p, b.ids, b.gates, b.clean, b.noise_std, b.row_stats, b.counts,
                      b.importance, b.load, b.aux_out, b.ws_aux)
+
+    def backward(self, X, dY, w_imp=0.0, w_load=0.0, residual=True, eps=None,
+                 weight_grads=True) -> dict:
+        """Gradients after forward(X): dX, dWg, dWnoise, dbias, dW1, dW2 (fp32 weights),
+        for the objective <Y, dY> + w_imp CV^2(importance) + w_load CV^2(load)."""
+        p, b = self.p, self.b
+        dev = dY.device
+        e = lambda *s, dtype=torch.float32: torch.empty(*s, dtype=dtype, device=dev)
+        if self.grads is None:
+            dt = torch_dtype(p)
+            rows = max(moe_max_rows(p), 1)
+            noisy = p.noise == 1
+            self.W1t = e(moe_packed_weight_bytes(p, 4), dtype=torch.uint8)
+            self.W2t = e(moe_packed_weight_bytes(p, 3), dtype=torch.uint8)
+            moe_pack_expert_weights_t(p, self.W1, self.W2, self.W1t, self.W2t)
+            self.grads = dict(
+                dZ=e(rows, p.D, dtype=dt), dgates=e(p.T, p.k), dHp=e(rows, p.H, dtype=dt),
+                dXd=e(rows, p.D, dtype=dt), dX=e(p.T, p.D, dtype=dt), dWg=e(p.D, p.E),
+                dWnoise=e(p.D, p.E) if noisy else None, dbias=e(p.E),
+                dW1=e(p.E, p.D, p.H) if weight_grads else None,
+                dW2=e(p.E, p.H, p.D) if weight_grads else None,
+                ws=e(max(moe_backward_workspace_size(p), 1), dtype=torch.uint8))
+        g = self.grads
+        moe_combine_backward(p, dY, b.Z, b.ids, b.gates, b.pos, b.accepted, b.offsets, g["dZ"],
+                             g["dgates"])
+        moe_expert_ffn_backward(p, b.Xd, b.Hd, g["dZ"], self.W1t, self.W2t, b.offsets, g["dHp"],
+                                g["dXd"], g["dW1"], g["dW2"])
+        moe_route_backward(p, X, self.Wg, self.Wnoise, eps, b.ids, b.gates, b.clean, b.noise_std,
+                           b.row_stats, g["dgates"], b.importance, b.load, w_imp, w_load,
+                           dY if residual else None, g["dXd"], b.pos, b.accepted, b.offsets,
+                           g["dX"], g["dWg"], g["dWnoise"], g["dbias"], g["ws"])
+        return g
 
     def forward(self, X, eps=None, residual=True, aux=True) -> Buffers:
         self.route(X, eps)

@@ -117,7 +117,10 @@ def test_sizes_scale(m):
     # packed expert weights: zero padding only to 32 columns / 64-deep k stages
     assert m.moe_packed_weight_bytes(p, 1) == 256 * 1024 * 4096 * 2
     assert m.moe_packed_weight_bytes(p, 2) == 256 * 4096 * 1024 * 2
-    assert m.moe_packed_weight_bytes(p, 3) == 0
+    # transposed layers for the backward pass: W2^T (3) and W1^T (4)
+    assert m.moe_packed_weight_bytes(p, 3) == 256 * 1024 * 4096 * 2
+    assert m.moe_packed_weight_bytes(p, 4) == 256 * 4096 * 1024 * 2
+    assert m.moe_packed_weight_bytes(p, 5) == 0
     # router: three bf16 pieces of [Wg | Wnoise] plus the fp32 noisy scores [T,E]
     assert m.moe_workspace_size(p, m.MOE_WS_ROUTE) == 3 * 1024 * 512 * 2 + 65536 * 256 * 4
 
@@ -166,3 +169,18 @@ def test_batchwise_validation(m):
     st.tok_gate = None
     assert m._lib.moe_route_batchwise(ctypes.byref(p), fake, fake, None, fake, ctypes.byref(st),
                                       fake, need, None) == -1
+
+
+def test_backward_validation(m):
+    p = _p(m, T=64, E=8, k=2)
+    assert m.moe_backward_workspace_size(p) > 0
+    sw = _p(m, T=64, E=8, k=1, gating="switch", noise=False)
+    assert m.moe_backward_workspace_size(sw) == 0
+    fake = ctypes.c_void_p(0x1000)
+    assert m._lib.moe_combine_backward(ctypes.byref(sw), *([fake] * 9), None) == -2
+    assert m._lib.moe_combine_backward(ctypes.byref(p), fake, None, *([fake] * 7), None) == -1
+    args = [fake] * 12 + [ctypes.c_float(0.0), ctypes.c_float(0.0)] + [fake] * 9
+    need = m.moe_backward_workspace_size(p)
+    assert m._lib.moe_route_backward(ctypes.byref(p), *args, fake, need - 1, None) == -5
+    args_nan = [fake] * 12 + [ctypes.c_float(float("nan")), ctypes.c_float(0.0)] + [fake] * 9
+    assert m._lib.moe_route_backward(ctypes.byref(p), *args_nan, fake, need, None) == -1
