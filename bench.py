@@ -12,6 +12,12 @@ roofline kernel.
 
 Prints one JSON line. The CPU baseline is the fp64 oracle, timed on a bounded
 prefix of the same workload's tokens on the host cores.
+
+    python bench.py --backward [--workload top2_bf16]
+
+times a training step instead (forward, then backward: combine, expert FFN data
+and weight gradients, gate and router), with the weight-gradient GEMM as the
+roofline kernel.
 """
 from __future__ import annotations
 
@@ -134,6 +140,113 @@ def vendor_gemm(torch, workload: str, reps: int):
                       "square_8192_ms": m3, "square_8192_TFLOPs": 2.0 * n ** 3 / m3 / 1e9}), flush=True)
 
 
+def cpu_baseline_backward(w, inp, dY, budget_tokens: int, w_imp: float, w_load: float):
+    """The gradient oracle as it stands on the first `budget_tokens` tokens, taken as a batch
+    of their own (route, slots, fp64 autograd of the objective)."""
+    from oracle import backward as OB
+    from oracle import moe as O
+    from oracle import philox as P
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    S = min(budget_tokens, w.T)
+    ws = w.replace(T=S)
+    sub = dict(inp, X=inp["X"][:S])
+    t0 = time.perf_counter()
+    eps = P.gaussian_noise(w.seed, S, w.E)
+    r = O.route(sub["X"], sub["Wg"], sub["Wnoise"], sub["bias"], w.k, "noisy", w.noise, eps=eps)
+    d = O.dispatch(r.ids, w.E, O.capacity(S, w.k, w.capacity_factor, w.E))
+    OB.layer_grads(sub, ws, r, d, eps, O.widen(dY[:S]), w_imp=w_imp, w_load=w_load)
+    dt = time.perf_counter() - t0
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {S} of {w.T} tokens of {w.name} as a batch of their own: route, "
+                      f"slots, fp64 torch autograd of the objective (the experts those tokens "
+                      f"reach); {dt:.1f} s"}
+
+
+def bench_backward(args, torch, w, inp, p, L, X, t_gen):
+    """A training step: the forward stages, then the backward stages, HIP events between
+    them on the one stream; the weight-gradient GEMM is the roofline kernel."""
+    from sparsely_gated_mixture_amd import inputs as I
+    from sparsely_gated_mixture_amd import moe
+    w_imp = w_load = 0.1
+    dY_h = I.make_output_grad(w)
+    dY = _dev(torch, dY_h)
+    g = L.backward_buffers(weight_grads=True)
+    b = L.b
+    stages = ["route", "dispatch", "gemm1", "gemm2", "combine", "aux", "combine_bwd",
+              "ffn_bwd_data", "wgrad_W2", "wgrad_W1", "route_bwd"]
+
+    def step(ev=None):
+        calls = [lambda: L.route(X), lambda: L.dispatch(X), lambda: L.gemm(1),
+                 lambda: L.gemm(2), lambda: L.combine(X), lambda: L.aux(),
+                 lambda: L.backward_combine(dY),
+                 lambda: moe.moe_expert_ffn_backward(p, b.Xd, b.Hd, g["dZ"], L.W1t, L.W2t,
+                                                     b.offsets, g["dHp"], g["dXd"], None, None),
+                 lambda: moe.moe_expert_weight_grad(p, 2, b.Hd, g["dZ"], b.offsets, g["dW2"]),
+                 lambda: moe.moe_expert_weight_grad(p, 1, b.Xd, g["dHp"], b.offsets, g["dW1"]),
+                 lambda: L.backward_route(X, dY, w_imp, w_load)]
+        for i, c in enumerate(calls):
+            if ev is not None:
+                ev[i].record()
+            c()
+        if ev is not None:
+            ev[len(calls)].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(events[s_])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    per = {name: float(np.mean([events[s_][i].elapsed_time(events[s_][i + 1])
+                                for s_ in range(args.steps)]))
+           for i, name in enumerate(stages)}
+    offs = b.offsets.cpu().numpy()
+    A = int(offs[-1])
+    U = int(np.count_nonzero(np.diff(offs)))
+    el = 2 if w.act == "bf16" else 4
+    flops = 2.0 * A * w.D * w.H  # per launch, either weight gradient
+    wg_ms = 0.5 * (per["wgrad_W2"] + per["wgrad_W1"])
+    achieved = flops / (wg_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.act]
+    # per launch: both operands' rows once, the fp32 gradient of every expert written once
+    wg_bytes = A * (w.D + w.H) * el + w.E * w.D * w.H * 4
+    fwd_ms = sum(per[k] for k in stages[:6])
+    bwd_ms = sum(per[k] for k in stages[6:])
+    out = {
+        "metric": "MoE layer fwd+bwd tokens/s at 1 GPU; weight-gradient GEMM % MFMA peak",
+        "value": w.T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.act,
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "D": w.D, "E": w.E, "k": w.k, "H": w.H,
+                   "gating": w.gating, "capacity_factor": w.capacity_factor,
+                   "capacity": moe.moe_capacity(p), "accepted_rows": A, "used_experts": U,
+                   "w_importance": w_imp, "w_load": w_load, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "wgrad_gemm", "achieved": achieved,
+                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "flops_per_launch": flops, "avg_launch_ms": wg_ms,
+                     "alg_bytes_per_launch": wg_bytes,
+                     "hbm_frac_alg": wg_bytes / (wg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "forward_ms": fwd_ms, "backward_ms": bwd_ms, "stages_ms": per,
+        "input_gen_s": t_gen,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_backward(w, inp, dY_h, args.cpu_tokens_backward,
+                                                    w_imp, w_load)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,7 +255,12 @@ def main():
     ap.add_argument("--workload", default="top2_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-tokens-backward", type=int, default=16)
     ap.add_argument("--copy-probe", type=int, default=0, help="bytes; run copies only")
+    ap.add_argument("--backward", action="store_true",
+                    help="time a training step of the layer instead: the forward, then the "
+                         "backward (combine, expert FFN data and weight gradients, gate and "
+                         "router) with w_importance = w_load = 0.1")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="time torch.bmm (the ROCm BLAS library) on the workload's expert GEMM "
                          "shapes with a uniform rows-per-expert split, for context only")
@@ -183,6 +301,12 @@ def main():
                       _dev(torch, inp["bias"]), _dev(torch, inp["W1"]), _dev(torch, inp["W2"]))
     X = _dev(torch, inp["X"])
     torch.cuda.synchronize()
+    if args.backward:
+        if w.gating != "noisy" or w.groups > 0:
+            print("--backward covers the flat noisy top-k gate only", file=sys.stderr, flush=True)
+            sys.exit(2)
+        bench_backward(args, torch, w, inp, p, L, X, t_gen)
+        return
 
     stages = ["route", "dispatch", "gemm1", "gemm2", "combine", "aux"]
 

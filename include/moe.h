@@ -400,6 +400,14 @@ moe_status moe_expert_ffn_backward(const moe_problem* p, const void* Xd, const v
                                    const void* W2t_packed, const int32_t* offsets, void* dHp,
                                    void* dXd, float* dW1, float* dW2, void* hip_stream);
 
+/* One weight gradient of moe_expert_ffn_backward on its own (the same kernel):
+ * which = 1: C_e = A_e^T B_e with A = Xd [rows, D], B = dHp [rows, H], C = dW1 [E,D,H];
+ * which = 2: A = Hd [rows, H], B = dZ [rows, D], C = dW2 [E,H,D]. fp32 C, overwritten;
+ * experts with no rows get zeros. */
+moe_status moe_expert_weight_grad(const moe_problem* p, int32_t which, const void* A,
+                                  const void* B, const int32_t* offsets, float* C,
+                                  void* hip_stream);
+
 /* The gate and router: dclean and d raw from the softmax over the kept scores, the
  * importance term (importance [E] from moe_aux_loss, needed if w_imp != 0) and the
  * load term (load [E], needed if w_load != 0; noise only); then

@@ -386,6 +386,17 @@ moe_status moe_expert_ffn_backward(const moe_problem* p, const void* Xd, const v
                              as_stream(hip_stream));
 }
 
+moe_status moe_expert_weight_grad(const moe_problem* p, int32_t which, const void* A,
+                                  const void* B, const int32_t* offsets, float* C,
+                                  void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate_backward(p, &d));
+  if (which != 1 && which != 2) return MOE_ERR_INVALID_ARG;
+  if (!A || !B || !offsets || !C) return MOE_ERR_INVALID_ARG;
+  return which == 1 ? wgrad_launch(d, A, B, offsets, d.E, d.D, d.H, C, as_stream(hip_stream))
+                    : wgrad_launch(d, A, B, offsets, d.E, d.H, d.D, C, as_stream(hip_stream));
+}
+
 size_t moe_backward_workspace_size(const moe_problem* p) {
   Dims d;
   if (validate_backward(p, &d) != MOE_OK) return 0;

@@ -16,16 +16,20 @@
 //   cb_backward      a wave per token: dZ[row] = g * dY[t] for each accepted
 //                    assignment and dg = <dY[t], Z[row]> (fp32)
 //   cv2_grad         d CV^2 / d v for the importance and load vectors
-//   gate_backward    a wave per token row: softmax backward over the kept
-//                    scores (plus the importance term), the load term of every
-//                    expert through Phi (with the threshold's share going to the
-//                    k-th / (k+1)-th expert), noise redrawn by Philox, then
+//   gate_backward    4 token rows per wave, one at a time: softmax backward over
+//                    the kept scores (plus the importance term), the load term of
+//                    every expert through Phi (with the threshold's share going to
+//                    the k-th / (k+1)-th expert), noise redrawn by Philox, then
 //                    d raw = d std * sigmoid(raw); writes [dclean | draw] [T, 2E]
-//                    and per-block partial sums of dclean (the bias gradient)
-//   wgrad_gemm       per group, C = A^T B over the group's rows (fp32 output):
-//                    8x8 (bf16) / 4x4 (fp32) register transposes put both
-//                    operands k-contiguous in LDS, then MFMA; one block per
-//                    (group, 128 x 128 tile), fixed row order
+//                    and per-block sums of dclean (the bias gradient)
+//   column_sums      the per-block sums, in two passes, in a fixed order
+//   wgrad_gemm       per group (and row split), C = A^T B over the group's rows
+//                    (fp32 output): 8x8 (bf16) / 4x4 (fp32) register transposes put
+//                    both operands k-contiguous in LDS, then MFMA; the next stage's
+//                    loads are in flight during the current stage's MFMAs; one block
+//                    per (group, split, 128 x 128 tile), fixed row order. The router's
+//                    weight gradient (one group of T rows) is split over rows and the
+//                    splits summed in order (split_dw)
 //   dx_final         a wave per token: dX = dY + sum of the accepted rows of dXd
 //                    + the router's share, fp32 accumulation, one rounding
 // The dense GEMMs of the backward (dZ W2^T with the ReLU mask, dH W1^T and the
@@ -125,152 +129,173 @@ struct GateArgs {
 
 __device__ __forceinline__ float phi_pdf(float z) { return 0.3989422804014327f * expf(-0.5f * z * z); }
 
-// One wave per row; the row's per-expert values live in LDS (4 waves x E floats x 3). Every
-// wave runs every phase (rows past T only skip their memory accesses), so the phases can be
+constexpr int kGateRowsPerWave = 4;
+
+// The forward's noise sample for (t, e): the given eps, else the same Philox draw.
+__device__ __forceinline__ float noise_at(const GateArgs& a, int t, int64_t base, int e) {
+  if (a.eps) return a.eps[base + e];
+  float g4[4];
+  noise4(a.seed, 0, t, e >> 2, g4);
+  return g4[e & 3];
+}
+
+// W waves per block (blockDim.x / 64: 4, or 2 when E is large) take rows
+// (blockIdx.x * kGateRowsPerWave + i) * W + wave, i < kGateRowsPerWave. A wave keeps its row's
+// dclean and dstd in LDS, plus its running sum of dclean (the bias gradient). Every wave runs
+// every phase of every row (rows past T only skip their memory accesses), so the phases can be
 // separated by block barriers.
 __global__ __launch_bounds__(kThreads) void gate_backward(GateArgs a) {
-  extern __shared__ float sh[];  // [4][3][E]: dclean, dstd, eps
+  extern __shared__ float sh[];  // [W][3][E]: dclean, dstd, sum of dclean
+  const int W = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int E = a.E, k = a.k;
   float* dcl = sh + wave * 3 * E;
   float* dsd = dcl + E;
-  float* eps = dsd + E;
-  const int rows_per_block = kThreads / 64;
-  const int t = blockIdx.x * rows_per_block + wave;
-  const bool live = t < a.T;
-  const int64_t base = static_cast<int64_t>(live ? t : 0) * E;
-  const int32_t* rid = a.ids + static_cast<int64_t>(live ? t : 0) * k;
+  float* acc = dsd + E;
   const bool load_term = a.noise && a.dload;
-  for (int e = lane; e < E; e += 64) {
-    dcl[e] = 0.f;
-    dsd[e] = 0.f;
-    eps[e] = 0.f;
-  }
-  __syncthreads();
-  // redraw the forward's noise: every group of 4 experts for the load term, else the kept ones
-  if (live && a.noise && a.eps) {
-    for (int e = lane; e < E; e += 64) eps[e] = a.eps[base + e];
-  } else if (live && a.noise) {
-    if (load_term) {
-      for (int q = lane; q < (E + 3) / 4; q += 64) {
-        float g4[4];
-        noise4(a.seed, 0, t, q, g4);
-        for (int i = 0; i < 4 && 4 * q + i < E; ++i) eps[4 * q + i] = g4[i];
+  for (int e = lane; e < E; e += 64) acc[e] = 0.f;
+  for (int it = 0; it < kGateRowsPerWave; ++it) {
+    const int t = (blockIdx.x * kGateRowsPerWave + it) * W + wave;
+    const bool live = t < a.T;
+    const int64_t base = static_cast<int64_t>(live ? t : 0) * E;
+    const int32_t* rid = a.ids + static_cast<int64_t>(live ? t : 0) * k;
+    for (int e = lane; e < E; e += 64) {
+      dcl[e] = 0.f;
+      dsd[e] = 0.f;
+    }
+    __syncthreads();
+    // softmax backward over the kept scores (plus the importance term)
+    {
+      float gj = 0.f, dgj = 0.f;
+      int ej = 0;
+      if (live && lane < k) {
+        const int64_t gi = static_cast<int64_t>(t) * k + lane;
+        ej = a.ids[gi];
+        gj = a.gates[gi];
+        dgj = a.dgates[gi] + (a.dimp ? a.dimp[ej] : 0.f);
       }
-    } else if (lane < k) {
-      const int e = rid[lane];
-      float g4[4];
-      noise4(a.seed, 0, t, e >> 2, g4);
-      eps[e] = g4[e & 3];
+      const float s = wave_sum(gj * dgj);
+      if (live && lane < k) {
+        const float dh = gj * (dgj - s);
+        dcl[ej] += dh;  // a row's experts are distinct: no two lanes share ej
+        if (a.noise) dsd[ej] += dh * noise_at(a, t, base, ej);
+      }
     }
-  }
-  __syncthreads();
-  // softmax backward over the kept scores (plus the importance term)
-  {
-    float gj = 0.f, dgj = 0.f;
-    int ej = 0;
-    if (live && lane < k) {
-      const int64_t gi = static_cast<int64_t>(t) * k + lane;
-      ej = a.ids[gi];
-      gj = a.gates[gi];
-      dgj = a.dgates[gi] + (a.dimp ? a.dimp[ej] : 0.f);
-    }
-    const float s = wave_sum(gj * dgj);
-    if (live && lane < k) {
-      const float dh = gj * (dgj - s);
-      dcl[ej] += dh;  // a row's experts are distinct: no two lanes share ej
-      if (a.noise) dsd[ej] += dh * eps[ej];
-    }
-  }
-  __syncthreads();
-  // load term: P(t,e) = Phi((clean - thr) / std) for every expert; the threshold is v_{k+1}
-  // for the kept experts and v_k for the others
-  float s_in = 0.f, s_out = 0.f;
-  int bi = 0x7fffffff;
-  if (load_term) {
-    float best = -INFINITY;
-    if (live) {
-      const float vk = a.row_stats[2 * static_cast<int64_t>(t)];
-      const float vk1 = a.row_stats[2 * static_cast<int64_t>(t) + 1];
-      for (int e = lane; e < E; e += 64) {
-        bool inside = false;
-        for (int j = 0; j < k; ++j) inside |= rid[j] == e;
-        const float cl = a.clean[base + e], sd = a.std_in[base + e];
-        if (!inside) {  // candidate for v_{k+1}: H exactly as the router formed it
-          const float h = fmaf(sd, eps[e], cl);
-          if (h > best || (h == best && e < bi)) {
-            best = h;
-            bi = e;
+    __syncthreads();
+    // load term: P(t,e) = Phi((clean - thr) / std) for every expert; the threshold is v_{k+1}
+    // for the kept experts and v_k for the others. A lane takes 4 consecutive experts (one
+    // Philox draw) at a time.
+    float s_in = 0.f, s_out = 0.f;
+    int bi = 0x7fffffff;
+    if (load_term) {
+      float best = -INFINITY;
+      if (live) {
+        const float vk = a.row_stats[2 * static_cast<int64_t>(t)];
+        const float vk1 = a.row_stats[2 * static_cast<int64_t>(t) + 1];
+        for (int q = lane; 4 * q < E; q += 64) {
+          float g4[4];
+          if (a.eps) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) g4[i] = 4 * q + i < E ? a.eps[base + 4 * q + i] : 0.f;
+          } else {
+            noise4(a.seed, 0, t, q, g4);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * q + i;
+            if (e >= E) break;
+            bool inside = false;
+            for (int j = 0; j < k; ++j) inside |= rid[j] == e;
+            const float cl = a.clean[base + e], sd = a.std_in[base + e];
+            if (!inside) {  // candidate for v_{k+1}: H exactly as the router formed it
+              const float h = fmaf(sd, g4[i], cl);
+              if (h > best || (h == best && e < bi)) {
+                best = h;
+                bi = e;
+              }
+            }
+            const float thr = inside ? vk1 : vk;
+            if (!(sd > 0.f) || thr == -INFINITY) continue;
+            const float z = (cl - thr) / sd;
+            const float dz = a.dload[e] * phi_pdf(z);
+            dcl[e] += dz / sd;
+            dsd[e] -= dz * z / sd;
+            if (inside) s_in += dz / sd;
+            else s_out += dz / sd;
           }
         }
-        const float thr = inside ? vk1 : vk;
-        if (!(sd > 0.f) || thr == -INFINITY) continue;
-        const float z = (cl - thr) / sd;
-        const float dz = a.dload[e] * phi_pdf(z);
-        dcl[e] += dz / sd;
-        dsd[e] -= dz * z / sd;
-        if (inside) s_in += dz / sd;
-        else s_out += dz / sd;
       }
-    }
-    s_in = wave_sum(s_in);
-    s_out = wave_sum(s_out);
+      s_in = wave_sum(s_in);
+      s_out = wave_sum(s_out);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ob = __shfl_xor(best, off);
-      const int oi = __shfl_xor(bi, off);
-      if (ob > best || (ob == best && oi < bi)) {
-        best = ob;
-        bi = oi;
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ob = __shfl_xor(best, off);
+        const int oi = __shfl_xor(bi, off);
+        if (ob > best || (ob == best && oi < bi)) {
+          best = ob;
+          bi = oi;
+        }
       }
     }
-  }
-  __syncthreads();
-  if (load_term && live && lane == 0) {
-    const int ik = rid[k - 1];  // v_k: the last kept expert
-    dcl[ik] -= s_out;
-    dsd[ik] -= s_out * eps[ik];
-    if (k < E && bi < E) {  // v_{k+1}: the best other expert
-      dcl[bi] -= s_in;
-      dsd[bi] -= s_in * eps[bi];
-    }
-  }
-  __syncthreads();
-  // write [dclean | draw]; d raw = d std * sigmoid(raw) = d std * (1 - exp(-std))
-  if (live) {
-    const int64_t o = static_cast<int64_t>(t) * 2 * E;
-    for (int e = lane; e < E; e += 64) {
-      const float dr = a.noise ? dsd[e] * (1.f - expf(-a.std_in[base + e])) : 0.f;
-      if (a.dtype == MOE_BF16) {
-        uint16_t* d = static_cast<uint16_t*>(a.dcat);
-        d[o + e] = f32_to_bf16(dcl[e]);
-        d[o + E + e] = f32_to_bf16(dr);
-      } else {
-        float* d = static_cast<float*>(a.dcat);
-        d[o + e] = dcl[e];
-        d[o + E + e] = dr;
+    __syncthreads();
+    if (load_term && live && lane == 0) {
+      const int ik = rid[k - 1];  // v_k: the last kept expert
+      dcl[ik] -= s_out;
+      dsd[ik] -= s_out * noise_at(a, t, base, ik);
+      if (k < E && bi < E) {  // v_{k+1}: the best other expert
+        dcl[bi] -= s_in;
+        dsd[bi] -= s_in * noise_at(a, t, base, bi);
       }
     }
+    __syncthreads();
+    // write [dclean | draw]; d raw = d std * sigmoid(raw) = d std * (1 - exp(-std))
+    if (live) {
+      const int64_t o = static_cast<int64_t>(t) * 2 * E;
+      for (int e = lane; e < E; e += 64) {
+        const float dr = a.noise ? dsd[e] * (1.f - expf(-a.std_in[base + e])) : 0.f;
+        if (a.dtype == MOE_BF16) {
+          uint16_t* d = static_cast<uint16_t*>(a.dcat);
+          d[o + e] = f32_to_bf16(dcl[e]);
+          d[o + E + e] = f32_to_bf16(dr);
+        } else {
+          float* d = static_cast<float*>(a.dcat);
+          d[o + e] = dcl[e];
+          d[o + E + e] = dr;
+        }
+        acc[e] += dcl[e];
+      }
+    }
+    // the next row clears this lane's own entries before its first barrier
   }
-  // bias gradient partials: the block's rows summed in row order
+  // bias gradient partial: each wave's rows in order, then the waves in order
   if (a.dbias_part) {
-    const int r0 = blockIdx.x * rows_per_block;
-    const int nr = min(rows_per_block, a.T - r0);
-    for (int e = threadIdx.x; e < E; e += kThreads) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
       float s2 = 0.f;
-      for (int r = 0; r < nr; ++r) s2 += sh[r * 3 * E + e];
+      for (int w = 0; w < W; ++w) s2 += sh[w * 3 * E + 2 * E + e];
       a.dbias_part[static_cast<int64_t>(blockIdx.x) * E + e] = s2;
     }
   }
 }
 
-__global__ __launch_bounds__(kThreads) void bias_reduce(const float* __restrict__ part, int nblk,
-                                                       int E, float* __restrict__ dbias) {
-  const int e = blockIdx.x * kThreads + threadIdx.x;
-  if (e >= E) return;
+// Column sums of a [R, E] fp32 matrix over row slices: out[slice][e] = sum of rows
+// slice*per .. min(R, (slice+1)*per) - 1, with per = ceil(R / gridDim.y); four interleaved row
+// sets of the slice, each in row order, then the four in order (deterministic).
+__global__ __launch_bounds__(kThreads) void column_sums(const float* __restrict__ part, int R,
+                                                       int E, float* __restrict__ out) {
+  __shared__ double sh[4][64];
+  const int el = threadIdx.x & 63, r = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + el;
+  const int per = (R + gridDim.y - 1) / gridDim.y;
+  const int b0 = blockIdx.y * per, b1 = min(R, b0 + per);
   double s = 0;
-  for (int b = 0; b < nblk; ++b) s += part[static_cast<int64_t>(b) * E + e];
-  dbias[e] = static_cast<float>(s);
+  if (e < E)
+    for (int b = b0 + r; b < b1; b += 4) s += part[static_cast<int64_t>(b) * E + e];
+  sh[r][el] = s;
+  __syncthreads();
+  if (r == 0 && e < E)
+    out[static_cast<int64_t>(blockIdx.y) * E + e] =
+        static_cast<float>(sh[0][el] + sh[1][el] + sh[2][el] + sh[3][el]);
 }
 
 // [Wg | Wnoise]^T packed for the router's input gradient: B[k][n] = Wg[n][k] (k < E) or
@@ -351,34 +376,52 @@ struct WgradArgs {
   const void* A;   // [rows, M]
   const void* B;   // [rows, N]
   const int32_t* offsets;  // [G + 1]
-  float* C;        // [G][M][N]
-  int G, M, N;
+  float* C;        // [G][S][M][N]: split s of group g's rows
+  int G, M, N, S;
 };
 
 constexpr int kWT = 128;            // tile M and N
 constexpr int kWRows = 64;          // rows (the reduction) per stage
-constexpr int kWStride = kWRows * 2 + 16;  // bytes per LDS column line (64 bf16 + pad) for bf16
+constexpr int kXcds = 8;
 
-// One block per (group, m tile, n tile): C_g[m, n] = sum over the group's rows r of
-// A[r, m] B[r, n]; 4 waves in a 2 x 2 layout, each 64 x 64.
-template <typename T>
+// One block per (group, row split, m tile, n tile): C_gs[m, n] = sum over the split's rows r
+// of A[r, m] B[r, n]; 4 waves in a 2 x 2 layout, each 64 x 64. The next stage's global loads
+// are issued before the current stage's MFMAs. Blocks are remapped so that each XCD (blocks
+// are dealt round-robin over the 8 XCDs) takes a contiguous run of (group, split, tile): a
+// group's operands then stay in one XCD's L2.
+template <typename T, bool kAligned>
 __global__ __launch_bounds__(kThreads) void wgrad_gemm(WgradArgs a) {
   constexpr int VB = 16 / static_cast<int>(sizeof(T));   // elements per 16 bytes
-  constexpr int kLine = kWRows * static_cast<int>(sizeof(T)) + 16;  // LDS bytes per column line
+  constexpr int kLine = kWRows * static_cast<int>(sizeof(T));  // LDS bytes per column line
+  constexpr int kQ = kLine / 16;                                   // 16-byte quads per line
+  // quad q of line l sits at quad (q + l + l / VB) % kQ, so that neighbouring lanes of one
+  // stash write (lines VB apart) and of one fragment read (consecutive lines) hit distinct
+  // quads (LDS banks)
+  auto qaddr = [](int line, int q) { return line * kLine + ((q + line + line / VB) % kQ) * 16; };
   // per stage: A tile [kWRows][kWT] and B tile [kWRows][kWT] -> transposed into
   // lines [kWT][kWRows] (k contiguous)
   __shared__ __align__(16) unsigned char sA[kWT * kLine];
   __shared__ __align__(16) unsigned char sB[kWT * kLine];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int mt = (a.M + kWT - 1) / kWT, nt = (a.N + kWT - 1) / kWT;
-  const int g = blockIdx.x / (mt * nt);
-  const int rem = blockIdx.x - g * mt * nt;
+  const int tiles = mt * nt;
+  const int total = a.G * a.S * tiles;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int logical = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (logical >= total) return;
+  const int gs = logical / tiles;  // group * S + split
+  const int g = gs / a.S, sp = gs - g * a.S;
+  const int rem = logical - gs * tiles;
   const int m0 = (rem / nt) * kWT, n0 = (rem % nt) * kWT;
-  const int r_begin = a.offsets[g], r_end = a.offsets[g + 1];
+  const int gb = a.offsets[g], ge = a.offsets[g + 1];
+  const int chunk = ((ge - gb + a.S - 1) / a.S + kWRows - 1) / kWRows * kWRows;
+  const int r_begin = min(ge, gb + sp * chunk), r_end = min(ge, r_begin + chunk);
   const T* A = static_cast<const T*>(a.A);
   const T* B = static_cast<const T*>(a.B);
   // loader: blocks of VB rows x VB columns; (kWRows / VB) x (kWT / VB) per operand
   constexpr int kBR = kWRows / VB, kBC = kWT / VB, kBlocks = kBR * kBC;  // per operand
+  constexpr int kPer = 2 * kBlocks / kThreads;                            // per thread
+  static_assert(kPer * kThreads == 2 * kBlocks, "loader blocks must split evenly");
   const int wm = wave >> 1, wn = wave & 1;
   f32x16 acc[2][2];
 #pragma unroll
@@ -387,36 +430,69 @@ __global__ __launch_bounds__(kThreads) void wgrad_gemm(WgradArgs a) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-  for (int rs = r_begin; rs < r_end; rs += kWRows) {
-    // load + transpose both operands (2 * kBlocks blocks over kThreads threads)
-    for (int bidx = tid; bidx < 2 * kBlocks; bidx += kThreads) {
+  u32x4 in[kPer][VB];
+  // kAligned (M and N multiples of VB): every lane issues its loads unconditionally from a
+  // clamped in-bounds address, and the rows / columns past the edge are zeroed in stash, so
+  // the loads of a stage are all in flight together.
+  unsigned vmask[kPer];  // bit i: row i of the lane's block is inside the split and the tile
+  auto load = [&](int rs) {
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int bidx = tid + p * kThreads;
       const bool isA = bidx < kBlocks;
       const int b2 = isA ? bidx : bidx - kBlocks;
       const int rb = b2 / kBC, cb = b2 - rb * kBC;
       const T* src = isA ? A : B;
       const int ld = isA ? a.M : a.N;
       const int c0 = (isA ? m0 : n0) + cb * VB;
-      u32x4 in[VB], out[VB];
+      if constexpr (kAligned) {
+        const int cc = min(c0, ld - VB);
+        unsigned m = 0;
 #pragma unroll
-      for (int i = 0; i < VB; ++i) {
-        const int r = rs + rb * VB + i;
-        if (r < r_end && c0 + VB <= ld && ld % VB == 0) {  // 16-byte aligned row segment
-          in[i] = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(r) * ld + c0);
-        } else {
+        for (int i = 0; i < VB; ++i) {
+          const int r = rs + rb * VB + i;
+          m |= (r < r_end && c0 < ld) ? (1u << i) : 0u;
+          in[p][i] = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(min(r, r_end - 1)) * ld + cc);
+        }
+        vmask[p] = m;
+      } else {
+#pragma unroll
+        for (int i = 0; i < VB; ++i) {
+          const int r = rs + rb * VB + i;
           T tmp[VB];
 #pragma unroll
           for (int q = 0; q < VB; ++q)
             tmp[q] = (r < r_end && c0 + q < ld) ? src[static_cast<int64_t>(r) * ld + c0 + q] : T(0);
-          in[i] = *reinterpret_cast<const u32x4*>(tmp);
+          in[p][i] = *reinterpret_cast<const u32x4*>(tmp);
         }
       }
-      transpose_block<T>(in, out);
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int bidx = tid + p * kThreads;
+      const bool isA = bidx < kBlocks;
+      const int b2 = isA ? bidx : bidx - kBlocks;
+      const int rb = b2 / kBC, cb = b2 - rb * kBC;
+      if constexpr (kAligned) {
+#pragma unroll
+        for (int i = 0; i < VB; ++i)
+          if (!((vmask[p] >> i) & 1u)) in[p][i] = u32x4{0u, 0u, 0u, 0u};
+      }
+      u32x4 out[VB];
+      transpose_block<T>(in[p], out);
       unsigned char* dst = isA ? sA : sB;
 #pragma unroll
       for (int c = 0; c < VB; ++c)
-        *reinterpret_cast<u32x4*>(dst + (cb * VB + c) * kLine + rb * 16) = out[c];
+        *reinterpret_cast<u32x4*>(dst + qaddr(cb * VB + c, rb)) = out[c];
     }
+  };
+  if (r_begin < r_end) load(r_begin);
+  for (int rs = r_begin; rs < r_end; rs += kWRows) {
+    stash();
     __syncthreads();
+    if (rs + kWRows < r_end) load(rs + kWRows);
     // MFMA over the stage: k-steps of 2*VB rows (one 16-byte fragment per lane half)
 #pragma unroll
     for (int ks = 0; ks < kWRows / (2 * VB); ++ks) {
@@ -424,9 +500,9 @@ __global__ __launch_bounds__(kThreads) void wgrad_gemm(WgradArgs a) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int m = wm * 64 + i * 32 + (lane & 31);
-        fa[i] = *reinterpret_cast<const u32x4*>(sA + m * kLine + (ks * 2 + (lane >> 5)) * 16);
+        fa[i] = *reinterpret_cast<const u32x4*>(sA + qaddr(m, ks * 2 + (lane >> 5)));
         const int n = wn * 64 + i * 32 + (lane & 31);
-        fb[i] = *reinterpret_cast<const u32x4*>(sB + n * kLine + (ks * 2 + (lane >> 5)) * 16);
+        fb[i] = *reinterpret_cast<const u32x4*>(sB + qaddr(n, ks * 2 + (lane >> 5)));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -436,7 +512,7 @@ __global__ __launch_bounds__(kThreads) void wgrad_gemm(WgradArgs a) {
     __syncthreads();
   }
   // fp32 output tile
-  float* C = a.C + static_cast<int64_t>(g) * a.M * a.N;
+  float* C = a.C + static_cast<int64_t>(gs) * a.M * a.N;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -500,14 +576,19 @@ moe_status combine_backward_launch(const Dims& d, const void* dY, const void* Z,
 }
 
 moe_status wgrad_launch(const Dims& d, const void* A, const void* B, const int32_t* offsets, int G,
-                        int M, int N, float* C, hipStream_t stream) {
-  WgradArgs a{A, B, offsets, C, G, M, N};
-  const int64_t blocks = static_cast<int64_t>(G) * ceil_div(M, kWT) * ceil_div(N, kWT);
-  if (blocks > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
-  if (d.dtype == MOE_BF16)
-    wgrad_gemm<uint16_t><<<static_cast<int>(blocks), kThreads, 0, stream>>>(a);
-  else
-    wgrad_gemm<float><<<static_cast<int>(blocks), kThreads, 0, stream>>>(a);
+                        int M, int N, float* C, hipStream_t stream, int splits) {
+  WgradArgs a{A, B, offsets, C, G, M, N, splits};
+  const int64_t blocks = static_cast<int64_t>(G) * splits * ceil_div(M, kWT) * ceil_div(N, kWT);
+  if (blocks > 0x7fffffffLL - kXcds) return MOE_ERR_UNSUPPORTED;
+  const int grid = static_cast<int>(ceil_div64(blocks, kXcds) * kXcds);
+  const bool aligned = M % 8 == 0 && N % 8 == 0;  // multiples of 16 bytes for either dtype
+  if (d.dtype == MOE_BF16) {
+    if (aligned) wgrad_gemm<uint16_t, true><<<grid, kThreads, 0, stream>>>(a);
+    else wgrad_gemm<uint16_t, false><<<grid, kThreads, 0, stream>>>(a);
+  } else {
+    if (aligned) wgrad_gemm<float, true><<<grid, kThreads, 0, stream>>>(a);
+    else wgrad_gemm<float, false><<<grid, kThreads, 0, stream>>>(a);
+  }
   return launch_status();
 }
 
@@ -519,34 +600,55 @@ static int router_bwd_ks(const Dims& d) {  // k-steps over the 2E inputs of the 
 // Workspace of moe_route_backward: dimp, dload [E]; dbias partials; dcat [T, 2E]; the packed
 // [Wg | Wnoise]^T; offsets {0, T}; the router's input-gradient share [T, D]; dWcat [D, 2E].
 struct RouteBwdLayout {
-  size_t dimp, dload, dbias, dcat, wpack, off, dxr, dwcat, total;
+  size_t dimp, dload, dbias, dbias2, dcat, wpack, off, dxr, dwcat, total;
 };
+// Row splits of the router's weight gradient X^T [dclean | draw] (one group of T rows): enough
+// blocks to fill the chip, at least 256 rows a split.
+static int router_splits(const Dims& d) {
+  const int tiles = ceil_div(d.D, kWT) * ceil_div(2 * d.E, kWT);
+  return std::max(1, std::min(ceil_div(2048, tiles), ceil_div(d.T, 256)));
+}
+
+// Row slices of the first pass over the bias partials (about 32 rows a slice, at most 64).
+static int bias_slices(int nblk) { return std::max(1, std::min(64, nblk / 32)); }
+
+static int gate_waves(const Dims& d) { return d.E > 2048 ? 2 : 4; }
+static int gate_blocks(const Dims& d) { return ceil_div(d.T, gate_waves(d) * kGateRowsPerWave); }
+
 static RouteBwdLayout route_bwd_layout(const Dims& d) {
   RouteBwdLayout L;
   const size_t el = d.dtype == MOE_BF16 ? 2 : 4;
-  const int nblk = ceil_div(d.T, kThreads / 64);
+  const int nblk = gate_blocks(d);
   size_t o = 0;
   L.dimp = o; o += align256(d.E * sizeof(float));
   L.dload = o; o += align256(d.E * sizeof(float));
   L.dbias = o; o += align256(static_cast<size_t>(nblk) * d.E * sizeof(float));
+  L.dbias2 = o; o += align256(static_cast<size_t>(bias_slices(nblk)) * d.E * sizeof(float));
   L.dcat = o; o += align256(static_cast<size_t>(d.T) * 2 * d.E * el);
   L.wpack = o; o += align256(static_cast<size_t>(ceil_div(d.D, 32)) * router_bwd_ks(d) * kWave * 16);
   L.off = o; o += 256;
   L.dxr = o; o += align256(static_cast<size_t>(d.T) * d.D * el);
-  L.dwcat = o; o += align256(static_cast<size_t>(d.D) * 2 * d.E * sizeof(float));
+  L.dwcat = o; o += align256(static_cast<size_t>(router_splits(d)) * d.D * 2 * d.E * sizeof(float));
   L.total = o;
   return L;
 }
 size_t route_backward_workspace(const Dims& d) { return route_bwd_layout(d).total; }
 
-__global__ void split_dw(const float* __restrict__ dwcat, int D, int E, float* __restrict__ dWg,
-                         float* __restrict__ dWn) {
+// dWg / dWnoise from the router's split partials [S][D][2E], summed over the splits in order.
+__global__ void split_dw(const float* __restrict__ dwcat, int S, int D, int E,
+                         float* __restrict__ dWg, float* __restrict__ dWn) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= static_cast<int64_t>(D) * E) return;
   const int64_t dd = i / E;
   const int e = static_cast<int>(i - dd * E);
-  dWg[i] = dwcat[dd * 2 * E + e];
-  if (dWn) dWn[i] = dwcat[dd * 2 * E + E + e];
+  const int64_t plane = static_cast<int64_t>(D) * 2 * E;
+  float g = 0.f, n = 0.f;
+  for (int s = 0; s < S; ++s) {
+    g += dwcat[s * plane + dd * 2 * E + e];
+    if (dWn) n += dwcat[s * plane + dd * 2 * E + E + e];
+  }
+  dWg[i] = g;
+  if (dWn) dWn[i] = n;
 }
 
 moe_status route_backward_launch(const Dims& d, uint64_t seed, const void* X, const float* Wg,
@@ -596,12 +698,20 @@ moe_status route_backward_launch(const Dims& d, uint64_t seed, const void* X, co
   ga.k = d.k;
   ga.noise = noise ? 1 : 0;
   ga.dtype = d.dtype;
-  const int nblk = ceil_div(d.T, kThreads / 64);
-  const size_t lds = static_cast<size_t>(kThreads / 64) * 3 * d.E * sizeof(float);
-  gate_backward<<<nblk, kThreads, lds, stream>>>(ga);
+  const int nblk = gate_blocks(d), gw = gate_waves(d);
+  const size_t lds = static_cast<size_t>(gw) * 3 * d.E * sizeof(float);
+  if (lds > 65536 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_backward),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess)
+    return MOE_ERR_HIP;
+  gate_backward<<<nblk, 64 * gw, lds, stream>>>(ga);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   if (dbias) {
-    bias_reduce<<<ceil_div(d.E, kThreads), kThreads, 0, stream>>>(dbias_part, nblk, d.E, dbias);
+    const int sl = bias_slices(nblk);
+    float* dbias2 = reinterpret_cast<float*>(base + L.dbias2);
+    column_sums<<<dim3(ceil_div(d.E, 64), sl), kThreads, 0, stream>>>(dbias_part, nblk, d.E, dbias2);
+    if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+    column_sums<<<dim3(ceil_div(d.E, 64), 1), kThreads, 0, stream>>>(dbias2, sl, d.E, dbias);
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   }
   // the router's share of dX: [dclean | draw] [Wg | Wnoise]^T as a one-group GEMM
@@ -625,10 +735,11 @@ moe_status route_backward_launch(const Dims& d, uint64_t seed, const void* X, co
   moe_status s = gemm_launch(dr, 3, dcat, wpack, off, dxr, nullptr, stream);
   if (s != MOE_OK) return s;
   // dWcat = X^T [dclean | draw]
-  s = wgrad_launch(d, X, dcat, off, 1, d.D, 2 * d.E, dwcat, stream);
+  const int S = router_splits(d);
+  s = wgrad_launch(d, X, dcat, off, 1, d.D, 2 * d.E, dwcat, stream, S);
   if (s != MOE_OK) return s;
   split_dw<<<static_cast<int>(ceil_div64(static_cast<int64_t>(d.D) * d.E, 256)), 256, 0, stream>>>(
-      dwcat, d.D, d.E, dWg, noise ? dWnoise : nullptr);
+      dwcat, S, d.D, d.E, dWg, noise ? dWnoise : nullptr);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   // dX = dY (residual) + the experts' rows + the router's share
   const int grid = ceil_div(d.T, kThreads / 64);

@@ -203,7 +203,7 @@ moe_status combine_backward_launch(const Dims& d, const void* dY, const void* Z,
                                    const int32_t* offsets, void* dZ, float* dgates,
                                    hipStream_t stream);
 moe_status wgrad_launch(const Dims& d, const void* A, const void* B, const int32_t* offsets, int G,
-                        int M, int N, float* C, hipStream_t stream);
+                        int M, int N, float* C, hipStream_t stream, int splits = 1);
 moe_status ffn_backward_launch(const Dims& d, const void* Xd, const void* Hd, const void* dZ,
                                const void* W1t, const void* W2t, const int32_t* offsets, void* dHp,
                                void* dXd, float* dW1, float* dW2, hipStream_t stream);

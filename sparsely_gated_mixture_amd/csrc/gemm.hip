@@ -225,24 +225,29 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
         for (int i = 0; i < 16; ++i) {
           float v = acc[m][j][i];
           if (kEpi == 1) v = fmaxf(v, 0.f);
-          if (kEpi == 2) {
-            const int row = m * 32 + acc_row(lane, i);
-            const T* M = static_cast<const T*>(g.mask);
-            if (col_ok && row < rows &&
-                !(Elem<T>::to_f32(M[static_cast<int64_t>(r0 + row) * g.N + cbase + (lane & 31)]) > 0.f))
-              v = 0.f;
-          }
-          bad |= col_ok && m * 32 + acc_row(lane, i) < rows && !isfinite(v);
+          if (kEpi != 2) bad |= col_ok && m * 32 + acc_row(lane, i) < rows && !isfinite(v);
           Ts[acc_row(lane, i) * kTStride + (lane & 31)] = Elem<T>::from_f32(v);
         }
 #pragma unroll
         for (int h = 0; h < 32 * kSegs / 64; ++h) {
           const int qd = lane + 64 * h;
           const int row = qd / kSegs, seg = qd % kSegs;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(&Ts[row * kTStride + seg * V]);
+          u32x4 v = *reinterpret_cast<const u32x4*>(&Ts[row * kTStride + seg * V]);
           const int grow = m * 32 + row, gcol = cbase + seg * V;
-          if (grow < rows && gcol < g.N)
-            *reinterpret_cast<u32x4*>(&C[static_cast<int64_t>(r0 + grow) * g.N + gcol]) = v;
+          if (grow < rows && gcol < g.N) {
+            const int64_t o = static_cast<int64_t>(r0 + grow) * g.N + gcol;
+            if constexpr (kEpi == 2) {  // the mask's 16 bytes at the same place: zero where <= 0
+              const u32x4 mk = *reinterpret_cast<const u32x4*>(static_cast<const T*>(g.mask) + o);
+              T* ve = reinterpret_cast<T*>(&v);
+              const T* me = reinterpret_cast<const T*>(&mk);
+#pragma unroll
+              for (int q = 0; q < V; ++q) {
+                if (!(Elem<T>::to_f32(me[q]) > 0.f)) ve[q] = T(0);
+                bad |= !isfinite(Elem<T>::to_f32(ve[q]));
+              }
+            }
+            *reinterpret_cast<u32x4*>(&C[o]) = v;
+          }
         }
       }
   } else {

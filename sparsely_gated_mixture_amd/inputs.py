@@ -60,6 +60,7 @@ import numpy as np
 
 TAG_X, TAG_WG, TAG_WNOISE, TAG_W1, TAG_W2, TAG_DUP = 1, 2, 3, 4, 5, 6
 TAG_WPG, TAG_WPN, TAG_WSG, TAG_WSN = 7, 8, 9, 10
+TAG_DY = 11
 
 
 @dataclasses.dataclass(frozen=True)
@@ -108,11 +109,11 @@ HIER_WORKLOADS = {
                           groups=16, k_primary=2),
 }
 WORKLOADS.update(HIER_WORKLOADS)
-# the same layer with one flat gate over all 1024 experts (k = 4), for comparing the
-# routing cost of the two gates
 WORKLOADS["batchwise_bf16"] = Workload("batchwise_bf16", T=16384, D=512, E=256, k=2, H=2048,
                                        act="bf16", gating="batchwise", noise=False,
                                        capacity_factor=0.0, seed=3)
+# the hierarchical layer's shape with one flat gate over all 1024 experts (k = 4), for
+# comparing the routing cost of the two gates
 WORKLOADS["flat1024_bf16"] = Workload("flat1024_bf16", T=16384, D=512, E=1024, k=4, H=1024,
                                       act="bf16", gating="noisy", noise=True,
                                       capacity_factor=0.0, seed=2)
@@ -244,3 +245,16 @@ def make_inputs(w: Workload, experts: bool = True, threads: int | None = None) -
     if experts:
         out["W1"], out["W2"] = make_experts(w, threads)
     return out
+
+
+def make_output_grad(w: Workload, threads: int | None = None) -> np.ndarray:
+    """dY [T, D]: an incoming gradient for the layer output, N(0, 1/D), in the activation
+    dtype (bf16 as uint16 bits); chunk c of ROW_CHUNK rows from stream [seed, TAG_DY, c]."""
+    dY = np.empty((w.T, w.D), dtype=np.float32)
+
+    def one(c):
+        r0, r1 = c * ROW_CHUNK, min(w.T, (c + 1) * ROW_CHUNK)
+        dY[r0:r1] = _normal(_rng(w.seed, TAG_DY, c), (r1 - r0, w.D), 1.0 / np.sqrt(w.D))
+
+    _run(one, range((w.T + ROW_CHUNK - 1) // ROW_CHUNK), threads)
+    return _cast(dY, w.act)

@@ -33,7 +33,7 @@ ENTRY_POINTS = [
     "moe_batchwise_m", "moe_batchwise_workspace_size", "moe_route_batchwise",
     "moe_dispatch_batchwise", "moe_combine_batchwise", "moe_aux_loss_batchwise",
     "moe_pack_expert_weights_t", "moe_combine_backward", "moe_expert_ffn_backward",
-    "moe_route_backward", "moe_backward_workspace_size",
+    "moe_route_backward", "moe_backward_workspace_size", "moe_expert_weight_grad",
 ]
 
 
@@ -110,6 +110,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_route_backward": (ctypes.c_int, [P] + [vp] * 12 + [ctypes.c_float, ctypes.c_float] +
                                [vp] * 9 + [vp, sz, vp]),
         "moe_backward_workspace_size": (sz, [P]),
+        "moe_expert_weight_grad": (ctypes.c_int, [P, i32, vp, vp, vp, vp, vp]),
         "moe_batchwise_m": (i32, [P]),
         "moe_batchwise_workspace_size": (sz, [P, ctypes.c_int]),
         "moe_route_batchwise": (ctypes.c_int, [P, vp, vp, vp, vp, ctypes.POINTER(BatchwiseState),
@@ -323,6 +324,12 @@ def moe_expert_ffn_backward(p, Xd, Hd, dZ, W1t, W2t, offsets, dHp, dXd, dW1, dW2
                                         _ptr(dW2), _stream(stream)), "moe_expert_ffn_backward")
 
 
+def moe_expert_weight_grad(p, which, A, B, offsets, C, stream=None):
+    _check(_lib.moe_expert_weight_grad(ctypes.byref(p), int(which), _ptr(A), _ptr(B),
+                                       _ptr(offsets), _ptr(C), _stream(stream)),
+           "moe_expert_weight_grad")
+
+
 def moe_backward_workspace_size(p: Problem) -> int:
     return _lib.moe_backward_workspace_size(ctypes.byref(p))
 
@@ -434,20 +441,18 @@ class Layer:
         moe_aux_loss(self.p, b.ids, b.gates, b.clean, b.noise_std, b.row_stats, b.counts,
                      b.importance, b.load, b.aux_out, b.ws_aux)
 
-    def backward(self, X, dY, w_imp=0.0, w_load=0.0, residual=True, eps=None,
-                 weight_grads=True) -> dict:
-        """Gradients after forward(X): dX, dWg, dWnoise, dbias, dW1, dW2 (fp32 weights),
-        for the objective <Y, dY> + w_imp CV^2(importance) + w_load CV^2(load)."""
-        p, b = self.p, self.b
-        dev = dY.device
-        e = lambda *s, dtype=torch.float32: torch.empty(*s, dtype=dtype, device=dev)
-        if self.grads is None:
+    def backward_buffers(self, weight_grads=True) -> dict:
+        """Gradient buffers (allocated on first use) and the transposed packed weights."""
+        p = self.p
+        if self.grads is None or (weight_grads and self.grads["dW1"] is None):
+            e = lambda *s, dtype=torch.float32: torch.empty(*s, dtype=dtype, device=self.b.Y.device)
             dt = torch_dtype(p)
             rows = max(moe_max_rows(p), 1)
             noisy = p.noise == 1
-            self.W1t = e(moe_packed_weight_bytes(p, 4), dtype=torch.uint8)
-            self.W2t = e(moe_packed_weight_bytes(p, 3), dtype=torch.uint8)
-            moe_pack_expert_weights_t(p, self.W1, self.W2, self.W1t, self.W2t)
+            if self.grads is None:
+                self.W1t = e(moe_packed_weight_bytes(p, 4), dtype=torch.uint8)
+                self.W2t = e(moe_packed_weight_bytes(p, 3), dtype=torch.uint8)
+                moe_pack_expert_weights_t(p, self.W1, self.W2, self.W1t, self.W2t)
             self.grads = dict(
                 dZ=e(rows, p.D, dtype=dt), dgates=e(p.T, p.k), dHp=e(rows, p.H, dtype=dt),
                 dXd=e(rows, p.D, dtype=dt), dX=e(p.T, p.D, dtype=dt), dWg=e(p.D, p.E),
@@ -455,16 +460,36 @@ class Layer:
                 dW1=e(p.E, p.D, p.H) if weight_grads else None,
                 dW2=e(p.E, p.H, p.D) if weight_grads else None,
                 ws=e(max(moe_backward_workspace_size(p), 1), dtype=torch.uint8))
-        g = self.grads
-        moe_combine_backward(p, dY, b.Z, b.ids, b.gates, b.pos, b.accepted, b.offsets, g["dZ"],
-                             g["dgates"])
-        moe_expert_ffn_backward(p, b.Xd, b.Hd, g["dZ"], self.W1t, self.W2t, b.offsets, g["dHp"],
-                                g["dXd"], g["dW1"], g["dW2"])
-        moe_route_backward(p, X, self.Wg, self.Wnoise, eps, b.ids, b.gates, b.clean, b.noise_std,
-                           b.row_stats, g["dgates"], b.importance, b.load, w_imp, w_load,
-                           dY if residual else None, g["dXd"], b.pos, b.accepted, b.offsets,
-                           g["dX"], g["dWg"], g["dWnoise"], g["dbias"], g["ws"])
-        return g
+        return self.grads
+
+    def backward_combine(self, dY):
+        b, g = self.b, self.grads
+        moe_combine_backward(self.p, dY, b.Z, b.ids, b.gates, b.pos, b.accepted, b.offsets,
+                             g["dZ"], g["dgates"])
+
+    def backward_ffn(self, weight_grads=True):
+        b, g = self.b, self.grads
+        moe_expert_ffn_backward(self.p, b.Xd, b.Hd, g["dZ"], self.W1t, self.W2t, b.offsets,
+                                g["dHp"], g["dXd"], g["dW1"] if weight_grads else None,
+                                g["dW2"] if weight_grads else None)
+
+    def backward_route(self, X, dY, w_imp=0.0, w_load=0.0, residual=True, eps=None):
+        b, g = self.b, self.grads
+        moe_route_backward(self.p, X, self.Wg, self.Wnoise, eps, b.ids, b.gates, b.clean,
+                           b.noise_std, b.row_stats, g["dgates"], b.importance, b.load, w_imp,
+                           w_load, dY if residual else None, g["dXd"], b.pos, b.accepted,
+                           b.offsets, g["dX"], g["dWg"], g["dWnoise"], g["dbias"], g["ws"])
+
+    def backward(self, X, dY, w_imp=0.0, w_load=0.0, residual=True, eps=None,
+                 weight_grads=True) -> dict:
+        """Gradients after forward(X) (with aux, whose importance and load the balancing
+        terms use): dX, dWg, dWnoise, dbias, dW1, dW2 (fp32 weight gradients) of the
+        objective <Y, dY> + w_imp CV^2(importance) + w_load CV^2(load)."""
+        self.backward_buffers(weight_grads)
+        self.backward_combine(dY)
+        self.backward_ffn(weight_grads)
+        self.backward_route(X, dY, w_imp, w_load, residual, eps)
+        return self.grads
 
     def forward(self, X, eps=None, residual=True, aux=True) -> Buffers:
         self.route(X, eps)

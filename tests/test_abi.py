@@ -184,3 +184,12 @@ def test_backward_validation(m):
     assert m._lib.moe_route_backward(ctypes.byref(p), *args, fake, need - 1, None) == -5
     args_nan = [fake] * 12 + [ctypes.c_float(float("nan")), ctypes.c_float(0.0)] + [fake] * 9
     assert m._lib.moe_route_backward(ctypes.byref(p), *args_nan, fake, need, None) == -1
+
+
+def test_weight_grad_validation(m):
+    p = _p(m, T=64, E=8, k=2)
+    fake = ctypes.c_void_p(0x1000)
+    assert m._lib.moe_expert_weight_grad(ctypes.byref(p), 3, *([fake] * 4), None) == -1
+    assert m._lib.moe_expert_weight_grad(ctypes.byref(p), 1, fake, None, fake, fake, None) == -1
+    sw = _p(m, T=64, E=8, k=1, gating="switch", noise=False)
+    assert m._lib.moe_expert_weight_grad(ctypes.byref(sw), 1, *([fake] * 4), None) == -2

@@ -117,3 +117,44 @@ def test_gate_share_of_the_gradient():
         G = r.gates[t]
         dclean[t, r.ids[t]] = G * (gg - (G * gg).sum())
     np.testing.assert_allclose(g["dWg"], inp["X"].T @ dclean, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("w_imp,w_load,noise,k,bias", [(0.3, 0.6, True, 2, True),
+                                                       (0.0, 0.0, True, 3, False),
+                                                       (0.5, 0.0, False, 2, True),
+                                                       (0.2, 0.4, True, 4, False)])
+def test_sampled_closed_form_matches_autograd(w_imp, w_load, noise, k, bias):
+    """The hand-written sampled gradients (used at sizes the autograd graph cannot
+    hold) agree with the autograd gradients on every output of a small layer."""
+    w, inp, eps, dY = _setup(T=30, D=6, E=4 if k == 4 else 6, k=k, H=7, cf=0.8, seed=19,
+                             noise=noise)
+    if bias:
+        inp["bias"] = np.random.default_rng(3).normal(0, 0.5, w.E)
+    r = O.route(inp["X"], inp["Wg"], inp["Wnoise"], inp["bias"], w.k, "noisy", w.noise, eps=eps)
+    d = O.dispatch(r.ids, w.E, O.capacity(w.T, w.k, w.capacity_factor, w.E))
+    ref = OB.layer_grads(inp, w, r, d, eps, dY, w_imp=w_imp, w_load=w_load)
+    s = OB.SampledGrads(inp, w, r, d, eps, dY, w_imp=w_imp, w_load=w_load)
+    np.testing.assert_allclose(s.dX(np.arange(w.T)), ref["dX"], rtol=1e-9, atol=1e-11)
+    for e in range(w.E):
+        g1, g2 = s.expert_grads(e)
+        if e in ref["dW1"]:
+            np.testing.assert_allclose(g1, ref["dW1"][e], rtol=1e-9, atol=1e-11)
+            np.testing.assert_allclose(g2, ref["dW2"][e], rtol=1e-9, atol=1e-11)
+    gw, nw, bw = s.router_columns(range(w.E))
+    np.testing.assert_allclose(gw, ref["dWg"], rtol=1e-9, atol=1e-11)
+    if noise:
+        np.testing.assert_allclose(nw, ref["dWnoise"], rtol=1e-9, atol=1e-11)
+    if bias:
+        np.testing.assert_allclose(bw, ref["dbias"], rtol=1e-9, atol=1e-11)
+
+
+def test_cv2_grad_closed_form():
+    """d CV^2 / dv against central differences of CV^2 itself."""
+    v = np.random.default_rng(5).uniform(0.5, 2.0, 9)
+    g = OB.cv2_grad(v)
+    for i in range(v.size):
+        h = 1e-6
+        a, b = v.copy(), v.copy()
+        a[i] += h
+        b[i] -= h
+        assert (O.cv2(a) - O.cv2(b)) / (2 * h) == pytest.approx(g[i], rel=1e-6, abs=1e-10)
