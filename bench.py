@@ -35,24 +35,51 @@ if ROOT not in sys.path:
 
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_top2_bf16_traffic.json")
-GEMM_SOURCES = [os.path.join(ROOT, "sparsely_gated_mixture_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
+CSRC = os.path.join(ROOT, "sparsely_gated_mixture_amd", "csrc")
+TRAFFIC = {  # kernel -> (committed counter summary, the sources the kernel is built from)
+    "grouped_gemm": (os.path.join(ROOT, "profiles", "grouped_gemm_top2_bf16_traffic.json"),
+                     [os.path.join(CSRC, f) for f in ("gemm.hip", "common.h")]),
+    "wgrad_gemm": (os.path.join(ROOT, "profiles", "wgrad_gemm_top2_bf16_traffic.json"),
+                   [os.path.join(CSRC, f) for f in ("backward.hip", "common.h")]),
+}
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per grouped-GEMM launch from the committed rocprofv3 counter summary
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, copy-calibrated); None if absent, for another workload,
-    or taken on a different version of the kernel source."""
+    or taken on a different version of the kernel's source."""
     import hashlib
+    path, sources = TRAFFIC[kernel]
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
-        src = b"".join(open(p, "rb").read() for p in GEMM_SOURCES)
+        src = b"".join(open(p, "rb").read() for p in sources)
     except OSError:
         return None
     if t.get("workload") != workload or t.get("source_sha256") != hashlib.sha256(src).hexdigest():
         return None
     return float(t["bytes_per_launch"])
+
+
+def roofline(kernel: str, flops: float, alg_bytes: float, ms: float, peak_tflops: float,
+             traffic) -> dict:
+    """The binding roof of a kernel: the larger of its MFMA time (flops at the dtype's
+    dense peak) and its HBM time (algorithmic bytes at 8 TB/s). `achieved` and `frac`
+    are against that roof; the other roof's fraction is reported beside it."""
+    t_mfma = flops / (peak_tflops * 1e12)
+    t_hbm = alg_bytes / (PEAK_HBM_GBS * 1e9)
+    s = ms * 1e-3
+    mfma = {"achieved": flops / s / 1e12, "peak": peak_tflops, "unit": "TFLOP/s"}
+    hbm = {"achieved": alg_bytes / s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    bound, main, other = ("mfma", mfma, "hbm") if t_mfma >= t_hbm else ("hbm", hbm, "mfma")
+    return {"bound": bound, "kernel": kernel, **main, "frac": main["achieved"] / main["peak"],
+            "traffic": traffic, "traffic_unit": "bytes per launch",
+            "flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": ms,
+            f"{other}_frac": (mfma if other == "mfma" else hbm)["achieved"] /
+                             (mfma if other == "mfma" else hbm)["peak"],
+            "mfma_ms_at_peak": t_mfma * 1e3, "hbm_ms_at_peak": t_hbm * 1e3,
+            "hbm_frac_measured": (None if traffic is None else
+                                  traffic / s / 1e9 / PEAK_HBM_GBS)}
 
 
 def _dev(torch, a):
@@ -216,10 +243,10 @@ def bench_backward(args, torch, w, inp, p, L, X, t_gen):
     el = 2 if w.act == "bf16" else 4
     flops = 2.0 * A * w.D * w.H  # per launch, either weight gradient
     wg_ms = 0.5 * (per["wgrad_W2"] + per["wgrad_W1"])
-    achieved = flops / (wg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.act]
     # per launch: both operands' rows once, the fp32 gradient of every expert written once
     wg_bytes = A * (w.D + w.H) * el + w.E * w.D * w.H * 4
+    traffic = measured_traffic("wgrad_gemm", w.name)
     fwd_ms = sum(per[k] for k in stages[:6])
     bwd_ms = sum(per[k] for k in stages[6:])
     out = {
@@ -233,11 +260,7 @@ def bench_backward(args, torch, w, inp, p, L, X, t_gen):
                    "gating": w.gating, "capacity_factor": w.capacity_factor,
                    "capacity": moe.moe_capacity(p), "accepted_rows": A, "used_experts": U,
                    "w_importance": w_imp, "w_load": w_load, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": "wgrad_gemm", "achieved": achieved,
-                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
-                     "flops_per_launch": flops, "avg_launch_ms": wg_ms,
-                     "alg_bytes_per_launch": wg_bytes,
-                     "hbm_frac_alg": wg_bytes / (wg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "roofline": roofline("wgrad_gemm", flops, wg_bytes, wg_ms, peak, traffic),
         "forward_ms": fwd_ms, "backward_ms": bwd_ms, "stages_ms": per,
         "input_gen_s": t_gen,
     }
@@ -255,7 +278,7 @@ def main():
     ap.add_argument("--workload", default="top2_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
-    ap.add_argument("--cpu-tokens-backward", type=int, default=16)
+    ap.add_argument("--cpu-tokens-backward", type=int, default=256)
     ap.add_argument("--copy-probe", type=int, default=0, help="bytes; run copies only")
     ap.add_argument("--backward", action="store_true",
                     help="time a training step of the layer instead: the forward, then the "
@@ -358,9 +381,8 @@ def main():
     # the output rows once
     gemm_bytes = U * w.D * w.H * el + A * (w.D + w.H) * el
     gemm_ms = 0.5 * (per["gemm1"] + per["gemm2"])
-    achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.act]
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic("grouped_gemm", w.name)
     disp_bytes = w.T * w.D * el + A * w.D * el + w.T * w.k * (4 + 4 + 1) + A * 4
     comb_bytes = A * w.D * el + 2 * w.T * w.D * el + w.T * w.k * 13
     out = {
@@ -384,14 +406,7 @@ def main():
                    "capacity_factor": w.capacity_factor,
                    "capacity": moe.moe_capacity(p), "accepted_rows": A,
                    "dropped": w.T * w.k - A, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": "grouped_gemm", "achieved": achieved,
-                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": traffic, "traffic_unit": "bytes per launch",
-                     "flops_per_launch": gemm_flops, "avg_launch_ms": gemm_ms,
-                     "alg_bytes_per_launch": gemm_bytes,
-                     "hbm_frac_alg": gemm_bytes / (gemm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                     "hbm_frac_measured": (None if traffic is None else
-                                           traffic / (gemm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS)},
+        "roofline": roofline("grouped_gemm", gemm_flops, gemm_bytes, gemm_ms, peak, traffic),
         "tokens_per_s_without_aux": w.T / ((ms_per_step - per["aux"]) * 1e-3),
         "stages_ms": per,
         "dispatch_GBps": disp_bytes / (per["dispatch"] * 1e-3) / 1e9,

@@ -389,7 +389,7 @@ constexpr int kXcds = 8;
 // are issued before the current stage's MFMAs. Blocks are remapped so that each XCD (blocks
 // are dealt round-robin over the 8 XCDs) takes a contiguous run of (group, split, tile): a
 // group's operands then stay in one XCD's L2.
-template <typename T, bool kAligned>
+template <typename T, bool kAligned, bool kRowSplit>
 __global__ __launch_bounds__(kThreads) void wgrad_gemm(WgradArgs a) {
   constexpr int VB = 16 / static_cast<int>(sizeof(T));   // elements per 16 bytes
   constexpr int kLine = kWRows * static_cast<int>(sizeof(T));  // LDS bytes per column line
@@ -405,16 +405,17 @@ __global__ __launch_bounds__(kThreads) void wgrad_gemm(WgradArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int mt = (a.M + kWT - 1) / kWT, nt = (a.N + kWT - 1) / kWT;
   const int tiles = mt * nt;
-  const int total = a.G * a.S * tiles;
+  const int S = kRowSplit ? a.S : 1;  // the row-split instance serves the router's gradient
+  const int total = a.G * S * tiles;
   const int per_xcd = (total + kXcds - 1) / kXcds;
   const int logical = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
   if (logical >= total) return;
   const int gs = logical / tiles;  // group * S + split
-  const int g = gs / a.S, sp = gs - g * a.S;
+  const int g = gs / S, sp = gs - g * S;
   const int rem = logical - gs * tiles;
   const int m0 = (rem / nt) * kWT, n0 = (rem % nt) * kWT;
   const int gb = a.offsets[g], ge = a.offsets[g + 1];
-  const int chunk = ((ge - gb + a.S - 1) / a.S + kWRows - 1) / kWRows * kWRows;
+  const int chunk = ((ge - gb + S - 1) / S + kWRows - 1) / kWRows * kWRows;
   const int r_begin = min(ge, gb + sp * chunk), r_end = min(ge, r_begin + chunk);
   const T* A = static_cast<const T*>(a.A);
   const T* B = static_cast<const T*>(a.B);
@@ -582,13 +583,16 @@ moe_status wgrad_launch(const Dims& d, const void* A, const void* B, const int32
   if (blocks > 0x7fffffffLL - kXcds) return MOE_ERR_UNSUPPORTED;
   const int grid = static_cast<int>(ceil_div64(blocks, kXcds) * kXcds);
   const bool aligned = M % 8 == 0 && N % 8 == 0;  // multiples of 16 bytes for either dtype
+  const bool split = splits > 1;
+#define MOE_WGRAD(TY, AL, SP) wgrad_gemm<TY, AL, SP><<<grid, kThreads, 0, stream>>>(a)
   if (d.dtype == MOE_BF16) {
-    if (aligned) wgrad_gemm<uint16_t, true><<<grid, kThreads, 0, stream>>>(a);
-    else wgrad_gemm<uint16_t, false><<<grid, kThreads, 0, stream>>>(a);
+    if (aligned) { if (split) MOE_WGRAD(uint16_t, true, true); else MOE_WGRAD(uint16_t, true, false); }
+    else { if (split) MOE_WGRAD(uint16_t, false, true); else MOE_WGRAD(uint16_t, false, false); }
   } else {
-    if (aligned) wgrad_gemm<float, true><<<grid, kThreads, 0, stream>>>(a);
-    else wgrad_gemm<float, false><<<grid, kThreads, 0, stream>>>(a);
+    if (aligned) { if (split) MOE_WGRAD(float, true, true); else MOE_WGRAD(float, true, false); }
+    else { if (split) MOE_WGRAD(float, false, true); else MOE_WGRAD(float, false, false); }
   }
+#undef MOE_WGRAD
   return launch_status();
 }
 
