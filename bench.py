@@ -203,6 +203,8 @@ def bench_backward(args, torch, w, inp, p, L, X, t_gen):
     dY = _dev(torch, dY_h)
     g = L.backward_buffers(weight_grads=True)
     b = L.b
+    Hs = torch.empty_like(b.Hd) if args.recompute else None  # the recomputed activations
+    hd_src = Hs if args.recompute else b.Hd
     stages = ["route", "dispatch", "gemm1", "gemm2", "combine", "aux", "combine_bwd",
               "ffn_bwd_data", "wgrad_W2", "wgrad_W1", "route_bwd"]
 
@@ -210,9 +212,12 @@ def bench_backward(args, torch, w, inp, p, L, X, t_gen):
         calls = [lambda: L.route(X), lambda: L.dispatch(X), lambda: L.gemm(1),
                  lambda: L.gemm(2), lambda: L.combine(X), lambda: L.aux(),
                  lambda: L.backward_combine(dY),
-                 lambda: moe.moe_expert_ffn_backward(p, b.Xd, b.Hd, g["dZ"], L.W1t, L.W2t,
-                                                     b.offsets, g["dHp"], g["dXd"], None, None),
-                 lambda: moe.moe_expert_weight_grad(p, 2, b.Hd, g["dZ"], b.offsets, g["dW2"]),
+                 (lambda: moe.moe_expert_ffn_backward_recompute(
+                     p, b.Xd, L.W1p, g["dZ"], L.W1t, L.W2t, b.offsets, Hs, g["dHp"], g["dXd"],
+                     None, None)) if args.recompute else
+                 (lambda: moe.moe_expert_ffn_backward(p, b.Xd, b.Hd, g["dZ"], L.W1t, L.W2t,
+                                                      b.offsets, g["dHp"], g["dXd"], None, None)),
+                 lambda: moe.moe_expert_weight_grad(p, 2, hd_src, g["dZ"], b.offsets, g["dW2"]),
                  lambda: moe.moe_expert_weight_grad(p, 1, b.Xd, g["dHp"], b.offsets, g["dW1"]),
                  lambda: L.backward_route(X, dY, w_imp, w_load)]
         for i, c in enumerate(calls):
@@ -259,7 +264,9 @@ def bench_backward(args, torch, w, inp, p, L, X, t_gen):
         "config": {"workload": w.name, "T": w.T, "D": w.D, "E": w.E, "k": w.k, "H": w.H,
                    "gating": w.gating, "capacity_factor": w.capacity_factor,
                    "capacity": moe.moe_capacity(p), "accepted_rows": A, "used_experts": U,
-                   "w_importance": w_imp, "w_load": w_load, "parallelism": "none (1 GPU)"},
+                   "w_importance": w_imp, "w_load": w_load,
+                   "hidden": "recomputed in the backward" if args.recompute else "stored",
+                   "parallelism": "none (1 GPU)"},
         "roofline": roofline("wgrad_gemm", flops, wg_bytes, wg_ms, peak, traffic),
         "forward_ms": fwd_ms, "backward_ms": bwd_ms, "stages_ms": per,
         "input_gen_s": t_gen,
@@ -278,12 +285,15 @@ def main():
     ap.add_argument("--workload", default="top2_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
-    ap.add_argument("--cpu-tokens-backward", type=int, default=256)
+    ap.add_argument("--cpu-tokens-backward", type=int, default=2048)
     ap.add_argument("--copy-probe", type=int, default=0, help="bytes; run copies only")
     ap.add_argument("--backward", action="store_true",
                     help="time a training step of the layer instead: the forward, then the "
                          "backward (combine, expert FFN data and weight gradients, gate and "
                          "router) with w_importance = w_load = 0.1")
+    ap.add_argument("--recompute", action="store_true",
+                    help="with --backward: recompute the experts' hidden activations in the "
+                         "backward instead of reading the forward's")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="time torch.bmm (the ROCm BLAS library) on the workload's expert GEMM "
                          "shapes with a uniform rows-per-expert split, for context only")

@@ -372,7 +372,7 @@ moe_status moe_aux_loss_batchwise(const moe_problem* p, const moe_batchwise_stat
 
 /* Gradients of the noisy top-k layer ([OLNN] 3.4: the gate trains through the
  * softmax over the kept experts and through the importance and load losses;
- * [LESSON] ch. 2 "trace it forward, then backward"). The selection, the
+ * [LESSON] ch. 3 "trace it forward, then backward"). The selection, the
  * capacity mask and the noise are those of the forward and are held fixed (the
  * selection is piecewise constant); the load estimator's threshold is the k-th
  * or (k+1)-th score of the row and passes its gradient to that expert. The
@@ -399,6 +399,19 @@ moe_status moe_expert_ffn_backward(const moe_problem* p, const void* Xd, const v
                                    const void* dZ, const void* W1t_packed,
                                    const void* W2t_packed, const int32_t* offsets, void* dHp,
                                    void* dXd, float* dW1, float* dW2, void* hip_stream);
+
+/* moe_expert_ffn_backward without a stored hidden layer ([LESSON] ch. 4, "recompute
+ * instead of store": the experts' hidden activations are not kept from the forward but
+ * recomputed in the backward, a second layer-1 pass traded for their memory): first
+ * Hd = ReLU(Xd_e W1_e) into the caller's Hd_scratch [rows, H] (p->dtype; overwritten;
+ * bitwise equal to the forward's Hd) from W1_packed (moe_pack_expert_weights layout),
+ * then exactly moe_expert_ffn_backward on it. */
+moe_status moe_expert_ffn_backward_recompute(const moe_problem* p, const void* Xd,
+                                             const void* W1_packed, const void* dZ,
+                                             const void* W1t_packed, const void* W2t_packed,
+                                             const int32_t* offsets, void* Hd_scratch,
+                                             void* dHp, void* dXd, float* dW1, float* dW2,
+                                             void* hip_stream);
 
 /* One weight gradient of moe_expert_ffn_backward on its own (the same kernel):
  * which = 1: C_e = A_e^T B_e with A = Xd [rows, D], B = dHp [rows, H], C = dW1 [E,D,H];

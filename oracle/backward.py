@@ -9,7 +9,7 @@ Pages cited:
            output, Noisy Top-K Gating steps 1-3, the importance and load
            losses); the paper's purpose is training, and k > 1 is chosen so the
            gate receives gradient through the softmax over the kept experts.
-  [LESSON] "Mixture-of-Experts: Sparse Computation", chapter 2 ("trace it
+  [LESSON] "Mixture-of-Experts: Sparse Computation", chapter 3 ("trace it
            forward, then backward": the kept experts share an incoming gradient
            in proportion to their gates; masked experts are absent from the
            backward pass) and chapter 5 (the losses).

@@ -386,6 +386,20 @@ moe_status moe_expert_ffn_backward(const moe_problem* p, const void* Xd, const v
                              as_stream(hip_stream));
 }
 
+moe_status moe_expert_ffn_backward_recompute(const moe_problem* p, const void* Xd,
+                                             const void* W1p, const void* dZ, const void* W1t,
+                                             const void* W2t, const int32_t* offsets,
+                                             void* Hd_scratch, void* dHp, void* dXd, float* dW1,
+                                             float* dW2, void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate_backward(p, &d));
+  if (!Xd || !W1p || !dZ || !W1t || !W2t || !offsets || !Hd_scratch || !dHp || !dXd)
+    return MOE_ERR_INVALID_ARG;
+  const hipStream_t s = as_stream(hip_stream);
+  MOE_TRY(gemm_launch(d, 1, Xd, W1p, offsets, Hd_scratch, nullptr, s));
+  return ffn_backward_launch(d, Xd, Hd_scratch, dZ, W1t, W2t, offsets, dHp, dXd, dW1, dW2, s);
+}
+
 moe_status moe_expert_weight_grad(const moe_problem* p, int32_t which, const void* A,
                                   const void* B, const int32_t* offsets, float* C,
                                   void* hip_stream) {

@@ -3,7 +3,7 @@
 // The pages' purpose is training: "Outrageously Large Neural Networks" summary,
 // section 3.4 (k > 1 so the gate receives gradient through the softmax over the
 // kept experts; the importance and load losses train the gate towards balance);
-// the "Mixture-of-Experts: Sparse Computation" lesson, chapter 2, traces the
+// the "Mixture-of-Experts: Sparse Computation" lesson, chapter 3, traces the
 // backward pass: an incoming gradient splits over the kept experts in
 // proportion to their gates, and masked experts are absent from it. The
 // selection and the capacity mask are piecewise constant and held fixed, as is

@@ -34,6 +34,7 @@ ENTRY_POINTS = [
     "moe_dispatch_batchwise", "moe_combine_batchwise", "moe_aux_loss_batchwise",
     "moe_pack_expert_weights_t", "moe_combine_backward", "moe_expert_ffn_backward",
     "moe_route_backward", "moe_backward_workspace_size", "moe_expert_weight_grad",
+    "moe_expert_ffn_backward_recompute",
 ]
 
 
@@ -111,6 +112,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                [vp] * 9 + [vp, sz, vp]),
         "moe_backward_workspace_size": (sz, [P]),
         "moe_expert_weight_grad": (ctypes.c_int, [P, i32, vp, vp, vp, vp, vp]),
+        "moe_expert_ffn_backward_recompute": (ctypes.c_int, [P] + [vp] * 11 + [vp]),
         "moe_batchwise_m": (i32, [P]),
         "moe_batchwise_workspace_size": (sz, [P, ctypes.c_int]),
         "moe_route_batchwise": (ctypes.c_int, [P, vp, vp, vp, vp, ctypes.POINTER(BatchwiseState),
@@ -324,6 +326,14 @@ def moe_expert_ffn_backward(p, Xd, Hd, dZ, W1t, W2t, offsets, dHp, dXd, dW1, dW2
                                         _ptr(dW2), _stream(stream)), "moe_expert_ffn_backward")
 
 
+def moe_expert_ffn_backward_recompute(p, Xd, W1p, dZ, W1t, W2t, offsets, Hd_scratch, dHp, dXd,
+                                      dW1, dW2, stream=None):
+    _check(_lib.moe_expert_ffn_backward_recompute(
+        ctypes.byref(p), _ptr(Xd), _ptr(W1p), _ptr(dZ), _ptr(W1t), _ptr(W2t), _ptr(offsets),
+        _ptr(Hd_scratch), _ptr(dHp), _ptr(dXd), _ptr(dW1), _ptr(dW2), _stream(stream)),
+        "moe_expert_ffn_backward_recompute")
+
+
 def moe_expert_weight_grad(p, which, A, B, offsets, C, stream=None):
     _check(_lib.moe_expert_weight_grad(ctypes.byref(p), int(which), _ptr(A), _ptr(B),
                                        _ptr(offsets), _ptr(C), _stream(stream)),
@@ -467,11 +477,20 @@ class Layer:
         moe_combine_backward(self.p, dY, b.Z, b.ids, b.gates, b.pos, b.accepted, b.offsets,
                              g["dZ"], g["dgates"])
 
-    def backward_ffn(self, weight_grads=True):
+    def backward_ffn(self, weight_grads=True, recompute=False):
+        """recompute: Hd is recomputed from Xd into a scratch buffer instead of read from
+        the forward's (the memory-for-compute trade of not storing it)."""
         b, g = self.b, self.grads
-        moe_expert_ffn_backward(self.p, b.Xd, b.Hd, g["dZ"], self.W1t, self.W2t, b.offsets,
-                                g["dHp"], g["dXd"], g["dW1"] if weight_grads else None,
-                                g["dW2"] if weight_grads else None)
+        dW1 = g["dW1"] if weight_grads else None
+        dW2 = g["dW2"] if weight_grads else None
+        if recompute:
+            if "Hs" not in g:
+                g["Hs"] = torch.empty_like(b.Hd)
+            moe_expert_ffn_backward_recompute(self.p, b.Xd, self.W1p, g["dZ"], self.W1t, self.W2t,
+                                              b.offsets, g["Hs"], g["dHp"], g["dXd"], dW1, dW2)
+        else:
+            moe_expert_ffn_backward(self.p, b.Xd, b.Hd, g["dZ"], self.W1t, self.W2t, b.offsets,
+                                    g["dHp"], g["dXd"], dW1, dW2)
 
     def backward_route(self, X, dY, w_imp=0.0, w_load=0.0, residual=True, eps=None):
         b, g = self.b, self.grads
@@ -481,13 +500,13 @@ class Layer:
                            b.offsets, g["dX"], g["dWg"], g["dWnoise"], g["dbias"], g["ws"])
 
     def backward(self, X, dY, w_imp=0.0, w_load=0.0, residual=True, eps=None,
-                 weight_grads=True) -> dict:
+                 weight_grads=True, recompute=False) -> dict:
         """Gradients after forward(X) (with aux, whose importance and load the balancing
         terms use): dX, dWg, dWnoise, dbias, dW1, dW2 (fp32 weight gradients) of the
         objective <Y, dY> + w_imp CV^2(importance) + w_load CV^2(load)."""
         self.backward_buffers(weight_grads)
         self.backward_combine(dY)
-        self.backward_ffn(weight_grads)
+        self.backward_ffn(weight_grads, recompute)
         self.backward_route(X, dY, w_imp, w_load, residual, eps)
         return self.grads
 

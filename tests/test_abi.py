@@ -193,3 +193,14 @@ def test_weight_grad_validation(m):
     assert m._lib.moe_expert_weight_grad(ctypes.byref(p), 1, fake, None, fake, fake, None) == -1
     sw = _p(m, T=64, E=8, k=1, gating="switch", noise=False)
     assert m._lib.moe_expert_weight_grad(ctypes.byref(sw), 1, *([fake] * 4), None) == -2
+
+
+def test_recompute_validation(m):
+    p = _p(m, T=64, E=8, k=2)
+    fake = ctypes.c_void_p(0x1000)
+    args = [fake] * 11
+    args_missing = list(args)
+    args_missing[6] = None  # Hd scratch
+    assert m._lib.moe_expert_ffn_backward_recompute(ctypes.byref(p), *args_missing, None) == -1
+    sw = _p(m, T=64, E=8, k=1, gating="switch", noise=False)
+    assert m._lib.moe_expert_ffn_backward_recompute(ctypes.byref(sw), *args, None) == -2

@@ -150,3 +150,30 @@ def test_backward_full_top2(moe):
     log(f"  router columns {cols.tolist()}: dWg {eg:.2e} dWnoise {en:.2e} dbias {eb:.2e} "
         f"({time.time() - t0:.1f}s)")
     assert eg < tol and en < tol and eb < tol
+
+
+@pytest.mark.parametrize("w", [CASES[2][0], CASES[-1][0], CASES[5][0]], ids=lambda w: w.name)
+def test_recompute_hidden_matches_stored(moe, w):
+    """Recomputing Hd in the backward (instead of keeping the forward's) gives bitwise the
+    same gradients: the same kernel on the same inputs."""
+    import torch
+    inp = I.make_inputs(w)
+    p = problem_for(moe, w)
+    L = moe.Layer(p, dev(inp["Wg"]), dev(inp["Wnoise"]), dev(inp["bias"]), dev(inp["W1"]),
+                  dev(inp["W2"]))
+    X = dev(inp["X"])
+    dY = dev(I.make_output_grad(w))
+    b = L.forward(X)
+    g = L.backward(X, dY, w_imp=0.1, w_load=0.1)
+    ref = {k: host(v).copy() for k, v in g.items() if k in ("dHp", "dXd", "dW1", "dW2", "dX")}
+    Hd = host(b.Hd).copy()
+    b.Hd.zero_()  # the stored activations are gone
+    g = L.backward(X, dY, w_imp=0.1, w_load=0.1, recompute=True)
+    torch.cuda.synchronize()
+    rows = int(host(b.offsets)[-1])
+    assert (host(g["Hs"])[:rows] == Hd[:rows]).all()
+    for k, v in ref.items():
+        got = host(g[k])
+        if k in ("dHp", "dXd"):
+            got, v = got[:rows], v[:rows]
+        assert (got == v).all(), k

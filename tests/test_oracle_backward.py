@@ -5,7 +5,7 @@ against the oracle's gradients; plus closed forms for one expert and for the
 gate's share of an incoming gradient.
 
 Passages: "Outrageously Large Neural Networks" summary, section 3.4; the
-"Mixture-of-Experts: Sparse Computation" lesson, chapter 2 ("trace it forward,
+"Mixture-of-Experts: Sparse Computation" lesson, chapter 3 ("trace it forward,
 then backward") and chapter 5.
 """
 import numpy as np
@@ -103,7 +103,7 @@ def test_single_expert_closed_form():
 
 
 def test_gate_share_of_the_gradient():
-    """Lesson ch. 2: with the expert outputs z_j held fixed, dL/dH_j = G_j (g_j - sum_l G_l g_l)
+    """Lesson ch. 3: with the expert outputs z_j held fixed, dL/dH_j = G_j (g_j - sum_l G_l g_l)
     where g_j = <dY, z_j> (softmax backward); dropped assignments still pass gradient to the
     scores through the normalisation. Checked on the router gradient dWg = X^T dclean."""
     w, inp, eps, dY = _setup(T=10, D=4, E=5, k=3, H=4, cf=0.0, seed=12)
