@@ -44,10 +44,15 @@ def _cv2(v):
 
 
 def layer_grads(inp: dict, w, r: O.Routing, d: O.Dispatch, eps, dY, w_imp=0.0, w_load=0.0,
-                residual=True, experts=None) -> dict:
+                residual=True, experts=None, w_switch=0.0) -> dict:
     """Gradients of <Y, dY> + w_imp CV^2(Imp) + w_load CV^2(Load) w.r.t. X, Wg, Wnoise,
     bias, W1 and W2 (expert weights only for `experts`, default all), with the routing
-    r / d and the noise eps held fixed."""
+    r / d and the noise eps held fixed.
+
+    Switch gate ([SWITCH] steps 2 and 8): the gate is the selected expert's probability
+    under the full softmax of the clean logits (not renormalised); the balancing term
+    w_switch * E * sum_e f_e * Pbar_e adds its gradient through the mean probabilities
+    Pbar, the hard fractions f = count / T (before capacity) held fixed."""
     X = _t(inp["X"])
     Wg = _t(inp["Wg"])
     noisy = w.noise and inp.get("Wnoise") is not None
@@ -63,8 +68,11 @@ def layer_grads(inp: dict, w, r: O.Routing, d: O.Dispatch, eps, dY, w_imp=0.0, w
         H = clean + torch.from_numpy(O.widen(eps)) * std
     else:
         std, H = None, clean
-    Hk = torch.gather(H, 1, ids)
-    G = torch.softmax(Hk, dim=1)
+    if w.gating == "switch":
+        probs = torch.softmax(clean, dim=1)
+        G = torch.gather(probs, 1, ids)
+    else:
+        G = torch.softmax(torch.gather(H, 1, ids), dim=1)
     ex = sorted(set(np.unique(r.ids).tolist())) if experts is None else list(experts)
     W1 = {e: _t(inp["W1"][e]) for e in ex}
     W2 = {e: _t(inp["W2"][e]) for e in ex}
@@ -88,6 +96,9 @@ def layer_grads(inp: dict, w, r: O.Routing, d: O.Dispatch, eps, dY, w_imp=0.0, w
     if w_imp:
         imp = torch.zeros(E, dtype=torch.float64).index_add(0, ids.reshape(-1), G.reshape(-1))
         obj = obj + w_imp * _cv2(imp)
+    if w_switch and w.gating == "switch":
+        f = torch.from_numpy(d.counts.astype(np.float64) / T)
+        obj = obj + w_switch * E * (f * probs.mean(dim=0)).sum()
     if w_load and noisy:
         # thresholds: the k-th and (k+1)-th scores of the row, by index (the forward's order)
         order = np.argsort(-r.score.astype(np.float32), axis=1, kind="stable")
@@ -162,9 +173,13 @@ class SampledGrads:
     """
 
     def __init__(self, inp: dict, w, r: O.Routing, d: O.Dispatch, eps, dY, w_imp=0.0,
-                 w_load=0.0, residual=True, bank: O.ExpertBank | None = None):
+                 w_load=0.0, residual=True, bank: O.ExpertBank | None = None, w_switch=0.0):
         self.inp, self.w, self.r, self.d = inp, w, r, d
-        self.noisy = w.noise and inp.get("Wnoise") is not None
+        self.switch = w.gating == "switch"
+        # Switch: dPbar_e = w_switch * E * f_e, so every probability p[t, e] gets that / T
+        self.dprob = (w_switch * w.E * d.counts.astype(np.float64) / w.T / w.T
+                      if (self.switch and w_switch) else None)
+        self.noisy = w.noise and inp.get("Wnoise") is not None and not self.switch
         self.eps = O.widen(eps) if self.noisy else None
         self.dY = dY
         self.residual = residual
@@ -208,8 +223,16 @@ class SampledGrads:
         ids = r.ids[tokens]
         G = r.gates[tokens]
         dG = self._dgates(tokens) + self.dimp[ids]
-        dH = G * (dG - (G * dG).sum(axis=1, keepdims=True))
         rows = np.arange(n)[:, None]
+        if self.switch:
+            # p = softmax(clean) over all E; G = p[e*]: dclean = p * (dp - <p, dp>)
+            z = r.clean[tokens] - r.clean[tokens].max(axis=1, keepdims=True)
+            p = np.exp(z)
+            p /= p.sum(axis=1, keepdims=True)
+            dp = np.zeros((n, E)) if self.dprob is None else np.repeat(self.dprob[None, :], n, 0)
+            dp[rows, ids] += dG
+            return p * (dp - (p * dp).sum(axis=1, keepdims=True)), np.zeros((n, E))
+        dH = G * (dG - (G * dG).sum(axis=1, keepdims=True))
         dcl[rows, ids] += dH
         if self.noisy:
             dsd[rows, ids] += dH * self.eps[tokens[:, None], ids]
@@ -281,7 +304,8 @@ class SampledGrads:
         gw, nw, bw = [], [], []
         for e in cols:
             # tokens whose row reaches e beyond its own load term: e kept, or e a threshold
-            touch = (r.ids == e).any(axis=1)
+            # (Switch: every row, through the full softmax)
+            touch = (r.ids == e).any(axis=1) | self.switch
             if self.dload is not None:
                 touch |= self.order[:, k - 1] == e
                 if k < E:

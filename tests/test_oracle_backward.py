@@ -158,3 +158,81 @@ def test_cv2_grad_closed_form():
         a[i] += h
         b[i] -= h
         assert (O.cv2(a) - O.cv2(b)) / (2 * h) == pytest.approx(g[i], rel=1e-6, abs=1e-10)
+
+
+def _setup_switch(T=14, D=5, E=4, H=6, cf=0.8, seed=23, bias=True):
+    w = I.Workload("bwd_switch", T=T, D=D, E=E, k=1, H=H, act="f32", gating="switch",
+                   noise=False, capacity_factor=cf, seed=seed)
+    inp = {kk: (v.astype(np.float64) if isinstance(v, np.ndarray) else v)
+           for kk, v in I.make_inputs(w).items()}
+    if bias:
+        inp["bias"] = np.random.default_rng(seed).normal(0, 0.5, E)
+    dY = np.random.default_rng(seed + 1).standard_normal((T, D))
+    return w, inp, dY
+
+
+def _objective_switch(inp, w, dY, ids_ref, w_switch):
+    r = O.route(inp["X"], inp["Wg"], None, inp["bias"], 1, "switch", False)
+    assert (r.ids == ids_ref).all(), "a perturbation flipped the routing"
+    d = O.dispatch(r.ids, w.E, O.capacity(w.T, 1, w.capacity_factor, w.E))
+    Y = O.combine_tokens(inp["X"], r, d, O.ExpertBank(inp["W1"], inp["W2"]), np.arange(w.T))
+    return float((Y * dY).sum() + w_switch * O.aux(r, d, 1)["out"][2])
+
+
+@pytest.mark.parametrize("w_switch", [0.0, 0.7])
+def test_switch_gradients_match_finite_differences(w_switch):
+    """Switch gate ([SWITCH] step 8): the gate is the selected full-softmax probability and the
+    balancing term E * sum f * Pbar trains the router through Pbar only (f is a hard count).
+    Finite differences of the forward oracle's objective (its aux out[2] is E * sum f * Pbar)."""
+    w, inp, dY = _setup_switch()
+    r = O.route(inp["X"], inp["Wg"], None, inp["bias"], 1, "switch", False)
+    d = O.dispatch(r.ids, w.E, O.capacity(w.T, 1, w.capacity_factor, w.E))
+    assert (~d.accepted).any()
+    g = OB.layer_grads(inp, w, r, d, None, dY, w_switch=w_switch)
+    rng = np.random.default_rng(2)
+    for name, grad in (("X", g["dX"]), ("Wg", g["dWg"]), ("bias", g["dbias"])):
+        base = inp[name]
+        for _ in range(8):
+            idx = tuple(rng.integers(0, s) for s in base.shape)
+            h = 1e-6 * max(1.0, abs(base[idx]))
+            vals = []
+            for sgn in (1, -1):
+                pert = dict(inp)
+                a = base.copy()
+                a[idx] += sgn * h
+                pert[name] = a
+                vals.append(_objective_switch(pert, w, dY, r.ids, w_switch))
+            fd = (vals[0] - vals[1]) / (2 * h)
+            assert fd == pytest.approx(grad[idx], rel=1e-5, abs=1e-7), (name, idx, fd, grad[idx])
+
+
+def test_switch_balancing_term_alone():
+    """dY = 0: only E * sum f * Pbar remains; its clean-logit gradient is, per token,
+    p * (c - <p, c>) with c_e = E f_e / T (closed form of the softmax Jacobian)."""
+    w, inp, dY = _setup_switch(bias=False)
+    r = O.route(inp["X"], inp["Wg"], None, None, 1, "switch", False)
+    d = O.dispatch(r.ids, w.E, O.capacity(w.T, 1, w.capacity_factor, w.E))
+    g = OB.layer_grads(inp, w, r, d, None, np.zeros_like(dY), w_switch=1.0)
+    c = w.E * d.counts / w.T / w.T
+    p = np.exp(r.clean - r.clean.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    dclean = p * (c[None, :] - (p * c[None, :]).sum(axis=1, keepdims=True))
+    np.testing.assert_allclose(g["dWg"], inp["X"].T @ dclean, rtol=1e-10, atol=1e-13)
+
+
+@pytest.mark.parametrize("w_imp,w_switch", [(0.0, 0.5), (0.3, 0.0), (0.2, 0.6)])
+def test_switch_sampled_closed_form_matches_autograd(w_imp, w_switch):
+    w, inp, dY = _setup_switch(T=30, E=5, seed=29)
+    r = O.route(inp["X"], inp["Wg"], None, inp["bias"], 1, "switch", False)
+    d = O.dispatch(r.ids, w.E, O.capacity(w.T, 1, w.capacity_factor, w.E))
+    ref = OB.layer_grads(inp, w, r, d, None, dY, w_imp=w_imp, w_switch=w_switch)
+    s = OB.SampledGrads(inp, w, r, d, None, dY, w_imp=w_imp, w_switch=w_switch)
+    np.testing.assert_allclose(s.dX(np.arange(w.T)), ref["dX"], rtol=1e-9, atol=1e-11)
+    gw, nw, bw = s.router_columns(range(w.E))
+    assert nw is None
+    np.testing.assert_allclose(gw, ref["dWg"], rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(bw, ref["dbias"], rtol=1e-9, atol=1e-11)
+    for e in ref["dW1"]:
+        g1, g2 = s.expert_grads(e)
+        np.testing.assert_allclose(g1, ref["dW1"][e], rtol=1e-9, atol=1e-11)
+        np.testing.assert_allclose(g2, ref["dW2"][e], rtol=1e-9, atol=1e-11)

@@ -209,7 +209,17 @@ BWD_MUTATIONS = [
      "H = clean + torch.from_numpy(O.widen(eps)) * std.detach()"),
     ("dropped assignments contribute", "tt, jj = np.nonzero((r.ids == e) & d.accepted)",
      "tt, jj = np.nonzero(r.ids == e)"),
-    ("gate detached", "G = torch.softmax(Hk, dim=1)", "G = torch.softmax(Hk.detach(), dim=1)"),
+    ("gate detached", "G = torch.softmax(torch.gather(H, 1, ids), dim=1)",
+     "G = torch.softmax(torch.gather(H, 1, ids).detach(), dim=1)"),
+    ("Switch gate renormalised over the kept expert", "G = torch.gather(probs, 1, ids)",
+     "G = torch.softmax(torch.gather(clean, 1, ids), dim=1)"),
+    ("Switch fractions differentiable", "f = torch.from_numpy(d.counts.astype(np.float64) / T)",
+     "f = probs.mean(dim=0)"),
+    ("sampled Switch Jacobian sign", "return p * (dp - (p * dp).sum(axis=1, keepdims=True)), np.zeros((n, E))",
+     "return p * (dp + (p * dp).sum(axis=1, keepdims=True)), np.zeros((n, E))"),
+    ("sampled threshold share to the wrong expert", "dcl[np.arange(n), ik] -= s_out",
+     "dcl[np.arange(n), ik] -= s_in"),
+    ("sampled d softplus", "return 1.0 / (1.0 + np.exp(-raw))", "return 1.0 / (1.0 + np.exp(raw))"),
     ("residual dropped", "Y = X * 1.0 if residual else torch.zeros_like(X)",
      "Y = torch.zeros_like(X)"),
     ("CV with ddof 1", "return ((v - m) ** 2).mean() / (m * m)",
@@ -223,7 +233,8 @@ BWD_PIN_TESTS = [getattr(bwd_pins, n) for n in dir(bwd_pins) if n.startswith("te
 def test_backward_pins_catch_mutation(monkeypatch, label, old, new):
     mut = _mutant("backward", old, new)
     for name, val in vars(mut).items():
-        if isinstance(val, types.FunctionType) and hasattr(OBW, name):
+        if isinstance(val, (types.FunctionType, type)) and hasattr(OBW, name) and \
+                getattr(val, "__module__", None) == mut.__name__:
             monkeypatch.setattr(OBW, name, val)
     failed = []
     for fn in BWD_PIN_TESTS:
