@@ -167,7 +167,8 @@ def vendor_gemm(torch, workload: str, reps: int):
                       "square_8192_ms": m3, "square_8192_TFLOPs": 2.0 * n ** 3 / m3 / 1e9}), flush=True)
 
 
-def cpu_baseline_backward(w, inp, dY, budget_tokens: int, w_imp: float, w_load: float):
+def cpu_baseline_backward(w, inp, dY, budget_tokens: int, w_imp: float, w_load: float,
+                          w_switch: float = 0.0):
     """The gradient oracle as it stands on the first `budget_tokens` tokens, taken as a batch
     of their own (route, slots, fp64 autograd of the objective)."""
     from oracle import backward as OB
@@ -182,10 +183,11 @@ def cpu_baseline_backward(w, inp, dY, budget_tokens: int, w_imp: float, w_load: 
     ws = w.replace(T=S)
     sub = dict(inp, X=inp["X"][:S])
     t0 = time.perf_counter()
-    eps = P.gaussian_noise(w.seed, S, w.E)
-    r = O.route(sub["X"], sub["Wg"], sub["Wnoise"], sub["bias"], w.k, "noisy", w.noise, eps=eps)
-    d = O.dispatch(r.ids, w.E, O.capacity(S, w.k, w.capacity_factor, w.E))
-    OB.layer_grads(sub, ws, r, d, eps, O.widen(dY[:S]), w_imp=w_imp, w_load=w_load)
+    eps = P.gaussian_noise(w.seed, S, w.E) if w.noise else None
+    r = O.route(sub["X"], sub["Wg"], sub["Wnoise"], sub["bias"], w.k, w.gating, w.noise, eps=eps)
+    d = O.dispatch(r.ids, w.E, O.capacity(S, w.k, w.capacity_factor, w.E, w.min_capacity))
+    OB.layer_grads(sub, ws, r, d, eps, O.widen(dY[:S]), w_imp=w_imp, w_load=w_load,
+                   w_switch=w_switch)
     dt = time.perf_counter() - t0
     return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {S} of {w.T} tokens of {w.name} as a batch of their own: route, "
@@ -198,7 +200,10 @@ def bench_backward(args, torch, w, inp, p, L, X, t_gen):
     them on the one stream; the weight-gradient GEMM is the roofline kernel."""
     from sparsely_gated_mixture_amd import inputs as I
     from sparsely_gated_mixture_amd import moe
-    w_imp = w_load = 0.1
+    # the pages' loss weights: 0.1 for both noisy top-k terms (language models), alpha = 0.01
+    # for the Switch balancing term
+    sw = w.gating == "switch"
+    w_imp, w_load, w_switch = (0.0, 0.0, 0.01) if sw else (0.1, 0.1, 0.0)
     dY_h = I.make_output_grad(w)
     dY = _dev(torch, dY_h)
     g = L.backward_buffers(weight_grads=True)
@@ -219,7 +224,7 @@ def bench_backward(args, torch, w, inp, p, L, X, t_gen):
                                                       b.offsets, g["dHp"], g["dXd"], None, None)),
                  lambda: moe.moe_expert_weight_grad(p, 2, hd_src, g["dZ"], b.offsets, g["dW2"]),
                  lambda: moe.moe_expert_weight_grad(p, 1, b.Xd, g["dHp"], b.offsets, g["dW1"]),
-                 lambda: L.backward_route(X, dY, w_imp, w_load)]
+                 lambda: L.backward_route(X, dY, w_imp, w_load, w_switch=w_switch)]
         for i, c in enumerate(calls):
             if ev is not None:
                 ev[i].record()
@@ -264,7 +269,7 @@ def bench_backward(args, torch, w, inp, p, L, X, t_gen):
         "config": {"workload": w.name, "T": w.T, "D": w.D, "E": w.E, "k": w.k, "H": w.H,
                    "gating": w.gating, "capacity_factor": w.capacity_factor,
                    "capacity": moe.moe_capacity(p), "accepted_rows": A, "used_experts": U,
-                   "w_importance": w_imp, "w_load": w_load,
+                   "w_importance": w_imp, "w_load": w_load, "w_switch": w_switch,
                    "hidden": "recomputed in the backward" if args.recompute else "stored",
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline("wgrad_gemm", flops, wg_bytes, wg_ms, peak, traffic),
@@ -273,7 +278,7 @@ def bench_backward(args, torch, w, inp, p, L, X, t_gen):
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_backward(w, inp, dY_h, args.cpu_tokens_backward,
-                                                    w_imp, w_load)
+                                                    w_imp, w_load, w_switch)
     print(json.dumps(out), flush=True)
 
 
@@ -335,8 +340,9 @@ def main():
     X = _dev(torch, inp["X"])
     torch.cuda.synchronize()
     if args.backward:
-        if w.gating != "noisy" or w.groups > 0:
-            print("--backward covers the flat noisy top-k gate only", file=sys.stderr, flush=True)
+        if w.gating not in ("noisy", "switch") or w.groups > 0:
+            print("--backward covers the flat noisy top-k and Switch gates", file=sys.stderr,
+                  flush=True)
             sys.exit(2)
         bench_backward(args, torch, w, inp, p, L, X, t_gen)
         return

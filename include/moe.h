@@ -378,8 +378,12 @@ moe_status moe_aux_loss_batchwise(const moe_problem* p, const moe_batchwise_stat
  * or (k+1)-th score of the row and passes its gradient to that expert. The
  * objective is <Y, dY> + w_imp CV^2(importance) + w_load CV^2(load). Order:
  * moe_combine_backward -> moe_expert_ffn_backward -> moe_route_backward, on the
- * forward's buffers. p->gating must be MOE_GATE_NOISY_TOPK (Switch:
- * MOE_ERR_UNSUPPORTED). Weight gradients are fp32 and overwrite their outputs. */
+ * forward's buffers. The Switch gate ([SWITCH] steps 2 and 8: the gate is the
+ * selected full-softmax probability; the balancing term E * sum f * Pbar trains
+ * the router through Pbar, the hard fractions f held fixed) uses the same first
+ * two calls, then moe_route_backward_switch. The batchwise mask has no backward
+ * here (MOE_ERR_INVALID_ARG). Weight gradients are fp32 and overwrite their
+ * outputs. */
 
 /* W1^T and W2^T in MFMA fragment order (layers 4 and 3 of moe_packed_weight_bytes). */
 moe_status moe_pack_expert_weights_t(const moe_problem* p, const void* W1, const void* W2,
@@ -440,6 +444,23 @@ moe_status moe_route_backward(const moe_problem* p, const void* X, const float* 
                               const int32_t* offsets, void* dX, float* dWg, float* dWnoise,
                               float* dbias, void* workspace, size_t workspace_bytes,
                               void* hip_stream);
+
+/* The Switch gate and router: p = softmax(clean) over all E, g = p[e*];
+ *   dp[t,e] = (dgates[t] + w_imp dCV^2(importance)/d importance[e*]) 1[e = e*]
+ *             + w_switch E counts[e] / T^2
+ *   dclean = p (dp - <p, dp>); then dX, dWg, dbias as moe_route_backward (no noise).
+ * ids [T] (k = 1), clean [T,E] = X Wg + bias from moe_route; counts [E] the
+ * pre-capacity counts from moe_dispatch (needed if w_switch != 0); importance [E]
+ * from moe_aux_loss (needed if w_imp != 0). The objective's balancing term is
+ * w_switch * E * sum_e f_e Pbar_e (moe_aux_loss out[2] times w_switch).
+ * workspace moe_backward_workspace_size(p) bytes. */
+moe_status moe_route_backward_switch(const moe_problem* p, const void* X, const float* Wg,
+                                     const int32_t* ids, const float* clean, const float* dgates,
+                                     const float* importance, const int32_t* counts, float w_imp,
+                                     float w_switch, const void* dY_residual, const void* dXd,
+                                     const int32_t* pos, const uint8_t* accepted,
+                                     const int32_t* offsets, void* dX, float* dWg, float* dbias,
+                                     void* workspace, size_t workspace_bytes, void* hip_stream);
 size_t moe_backward_workspace_size(const moe_problem* p);
 
 /* ------------------------------------------------------------------- misc */

@@ -347,10 +347,11 @@ moe_status moe_aux_loss_batchwise(const moe_problem* p, const moe_batchwise_stat
 }
 
 // --------------------------------------------------------------- backward
+// The backward covers the per-token gates (noisy top-k and Switch top-1); the gate-specific
+// entry points check which one they were given.
 static moe_status validate_backward(const moe_problem* p, Dims* d) {
   MOE_TRY(validate(p, d));
-  if (d->gating == MOE_GATE_SWITCH_TOP1) return MOE_ERR_UNSUPPORTED;
-  return d->gating == MOE_GATE_NOISY_TOPK ? MOE_OK : MOE_ERR_INVALID_ARG;
+  return d->gating == MOE_GATE_BATCHWISE ? MOE_ERR_INVALID_ARG : MOE_OK;
 }
 
 moe_status moe_pack_expert_weights_t(const moe_problem* p, const void* W1, const void* W2,
@@ -428,6 +429,7 @@ moe_status moe_route_backward(const moe_problem* p, const void* X, const float* 
                               size_t workspace_bytes, void* hip_stream) {
   Dims d;
   MOE_TRY(validate_backward(p, &d));
+  if (d.gating != MOE_GATE_NOISY_TOPK) return MOE_ERR_INVALID_ARG;  // Switch: its own entry point
   const bool noise = d.noise != 0;
   if (!isfinite(w_imp) || !isfinite(w_load)) return MOE_ERR_INVALID_ARG;
   if (!X || !Wg || !ids || !gates || !clean || !row_stats || !dgates || !dXd || !pos ||
@@ -438,9 +440,32 @@ moe_status moe_route_backward(const moe_problem* p, const void* X, const float* 
   if (w_load != 0.f && noise && !load) return MOE_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < route_backward_workspace(d)) return MOE_ERR_WORKSPACE;
   return route_backward_launch(d, p->seed, X, Wg, Wnoise, eps, ids, gates, clean, noise_std,
-                               row_stats, dgates, importance, load, w_imp, w_load, dY_residual,
-                               dXd, pos, accepted, offsets, dX, dWg, dWnoise, dbias, workspace,
-                               as_stream(hip_stream));
+                               row_stats, dgates, importance, load, nullptr, w_imp, w_load, 0.f,
+                               dY_residual, dXd, pos, accepted, offsets, dX, dWg, dWnoise, dbias,
+                               workspace, as_stream(hip_stream));
+}
+
+moe_status moe_route_backward_switch(const moe_problem* p, const void* X, const float* Wg,
+                                     const int32_t* ids, const float* clean, const float* dgates,
+                                     const float* importance, const int32_t* counts, float w_imp,
+                                     float w_switch, const void* dY_residual, const void* dXd,
+                                     const int32_t* pos, const uint8_t* accepted,
+                                     const int32_t* offsets, void* dX, float* dWg, float* dbias,
+                                     void* workspace, size_t workspace_bytes, void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate_backward(p, &d));
+  if (d.gating != MOE_GATE_SWITCH_TOP1) return MOE_ERR_INVALID_ARG;
+  if (!isfinite(w_imp) || !isfinite(w_switch)) return MOE_ERR_INVALID_ARG;
+  if (!X || !Wg || !ids || !clean || !dgates || !dXd || !pos || !accepted || !offsets || !dX ||
+      !dWg)
+    return MOE_ERR_INVALID_ARG;
+  if (w_imp != 0.f && !importance) return MOE_ERR_INVALID_ARG;
+  if (w_switch != 0.f && !counts) return MOE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < route_backward_workspace(d)) return MOE_ERR_WORKSPACE;
+  return route_backward_launch(d, p->seed, X, Wg, nullptr, nullptr, ids, nullptr, clean, nullptr,
+                               nullptr, dgates, importance, nullptr, counts, w_imp, 0.f, w_switch,
+                               dY_residual, dXd, pos, accepted, offsets, dX, dWg, nullptr, dbias,
+                               workspace, as_stream(hip_stream));
 }
 
 moe_status moe_check_finite(void* hip_stream) {

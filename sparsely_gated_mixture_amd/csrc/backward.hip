@@ -121,7 +121,8 @@ struct GateArgs {
   const float* dimp;   // [E] importance term or NULL
   const float* dload;  // [E] load term or NULL (needs noise)
   const float* eps;    // [T, E] the noise the forward was given, or NULL (redrawn by Philox)
-  void* dcat;          // [T, 2E] act dtype: dclean | draw (draw only with noise)
+  void* dcat;          // [T, ldc] act dtype: dclean | draw (draw only with noise)
+  int ldc;             // 2E with noise, else E
   float* dbias_part;   // [nblk][E] or NULL
   uint64_t seed;
   int T, E, k, noise, dtype;
@@ -250,17 +251,16 @@ __global__ __launch_bounds__(kThreads) void gate_backward(GateArgs a) {
     __syncthreads();
     // write [dclean | draw]; d raw = d std * sigmoid(raw) = d std * (1 - exp(-std))
     if (live) {
-      const int64_t o = static_cast<int64_t>(t) * 2 * E;
+      const int64_t o = static_cast<int64_t>(t) * a.ldc;
       for (int e = lane; e < E; e += 64) {
-        const float dr = a.noise ? dsd[e] * (1.f - expf(-a.std_in[base + e])) : 0.f;
         if (a.dtype == MOE_BF16) {
           uint16_t* d = static_cast<uint16_t*>(a.dcat);
           d[o + e] = f32_to_bf16(dcl[e]);
-          d[o + E + e] = f32_to_bf16(dr);
+          if (a.noise) d[o + E + e] = f32_to_bf16(dsd[e] * (1.f - expf(-a.std_in[base + e])));
         } else {
           float* d = static_cast<float*>(a.dcat);
           d[o + e] = dcl[e];
-          d[o + E + e] = dr;
+          if (a.noise) d[o + E + e] = dsd[e] * (1.f - expf(-a.std_in[base + e]));
         }
         acc[e] += dcl[e];
       }
@@ -273,6 +273,81 @@ __global__ __launch_bounds__(kThreads) void gate_backward(GateArgs a) {
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
       float s2 = 0.f;
       for (int w = 0; w < W; ++w) s2 += sh[w * 3 * E + 2 * E + e];
+      a.dbias_part[static_cast<int64_t>(blockIdx.x) * E + e] = s2;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ Switch gate backward
+// The gate is the selected expert's probability under the full softmax of the clean logits
+// (not renormalised); the balancing term w * E * sum f * Pbar reaches every probability as
+// dprob[e] = w * E * f_e / T with f = count / T held fixed. Per row: dp = dprob + dG at the
+// selected expert, dclean = p * (dp - <p, dp>).
+struct SwitchGateArgs {
+  const int32_t* ids;    // [T] (k = 1)
+  const float* clean;    // [T, E]
+  const float* dgates;   // [T]
+  const float* dimp;     // [E] importance term or NULL
+  const float* dprob;    // [E] balancing term or NULL
+  void* dcat;            // [T, E] act dtype: dclean
+  float* dbias_part;     // [nblk][E] or NULL
+  int T, E, dtype;
+};
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+__global__ void switch_dprob(const int32_t* __restrict__ counts, int T, int E, float w,
+                             float* __restrict__ dprob) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < E)
+    dprob[e] = static_cast<float>(static_cast<double>(w) * E * counts[e] /
+                                  (static_cast<double>(T) * T));
+}
+
+// Rows as gate_backward (W waves, kGateRowsPerWave rows each); a wave keeps the running sum of
+// its rows' dclean in LDS for the bias gradient.
+__global__ __launch_bounds__(kThreads) void switch_gate_backward(SwitchGateArgs a) {
+  extern __shared__ float sh[];  // [W][E]
+  const int W = blockDim.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int E = a.E;
+  float* acc = sh + wave * E;
+  for (int e = lane; e < E; e += 64) acc[e] = 0.f;
+  for (int it = 0; it < kGateRowsPerWave; ++it) {
+    const int t = (blockIdx.x * kGateRowsPerWave + it) * W + wave;
+    if (t >= a.T) continue;  // wave-uniform; no barrier inside the loop
+    const float* cl = a.clean + static_cast<int64_t>(t) * E;
+    float m = -INFINITY;
+    for (int e = lane; e < E; e += 64) m = fmaxf(m, cl[e]);
+    m = wave_max(m);
+    float z = 0.f;
+    for (int e = lane; e < E; e += 64) z += expf(cl[e] - m);
+    z = wave_sum(z);
+    const int es = a.ids[t];
+    const float dG = a.dgates[t] + (a.dimp ? a.dimp[es] : 0.f);
+    float pd = 0.f;
+    if (a.dprob)
+      for (int e = lane; e < E; e += 64) pd += expf(cl[e] - m) / z * a.dprob[e];
+    const float dot = wave_sum(pd) + expf(cl[es] - m) / z * dG;
+    const int64_t o = static_cast<int64_t>(t) * E;
+    for (int e = lane; e < E; e += 64) {
+      const float pe = expf(cl[e] - m) / z;
+      const float dp = (a.dprob ? a.dprob[e] : 0.f) + (e == es ? dG : 0.f);
+      const float dc = pe * (dp - dot);
+      if (a.dtype == MOE_BF16) static_cast<uint16_t*>(a.dcat)[o + e] = f32_to_bf16(dc);
+      else static_cast<float*>(a.dcat)[o + e] = dc;
+      acc[e] += dc;
+    }
+  }
+  if (a.dbias_part) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      float s2 = 0.f;
+      for (int w = 0; w < W; ++w) s2 += sh[w * E + e];
       a.dbias_part[static_cast<int64_t>(blockIdx.x) * E + e] = s2;
     }
   }
@@ -596,9 +671,14 @@ moe_status wgrad_launch(const Dims& d, const void* A, const void* B, const int32
   return launch_status();
 }
 
-static int router_bwd_ks(const Dims& d) {  // k-steps over the 2E inputs of the router GEMM
+// Columns of [dclean | draw]: 2E for the noisy gate with noise, E otherwise (no draw).
+static int router_cols(const Dims& d) {
+  return d.gating == MOE_GATE_NOISY_TOPK && d.noise ? 2 * d.E : d.E;
+}
+
+static int router_bwd_ks(const Dims& d) {  // k-steps over the router GEMM's inputs
   const int stage = d.dtype == MOE_BF16 ? 64 : 32;
-  return ceil_div(2 * d.E, stage) * 4;
+  return ceil_div(router_cols(d), stage) * 4;
 }
 
 // Workspace of moe_route_backward: dimp, dload [E]; dbias partials; dcat [T, 2E]; the packed
@@ -609,7 +689,7 @@ struct RouteBwdLayout {
 // Row splits of the router's weight gradient X^T [dclean | draw] (one group of T rows): enough
 // blocks to fill the chip, at least 256 rows a split.
 static int router_splits(const Dims& d) {
-  const int tiles = ceil_div(d.D, kWT) * ceil_div(2 * d.E, kWT);
+  const int tiles = ceil_div(d.D, kWT) * ceil_div(router_cols(d), kWT);
   return std::max(1, std::min(ceil_div(2048, tiles), ceil_div(d.T, 256)));
 }
 
@@ -628,28 +708,29 @@ static RouteBwdLayout route_bwd_layout(const Dims& d) {
   L.dload = o; o += align256(d.E * sizeof(float));
   L.dbias = o; o += align256(static_cast<size_t>(nblk) * d.E * sizeof(float));
   L.dbias2 = o; o += align256(static_cast<size_t>(bias_slices(nblk)) * d.E * sizeof(float));
-  L.dcat = o; o += align256(static_cast<size_t>(d.T) * 2 * d.E * el);
+  L.dcat = o; o += align256(static_cast<size_t>(d.T) * router_cols(d) * el);
   L.wpack = o; o += align256(static_cast<size_t>(ceil_div(d.D, 32)) * router_bwd_ks(d) * kWave * 16);
   L.off = o; o += 256;
   L.dxr = o; o += align256(static_cast<size_t>(d.T) * d.D * el);
-  L.dwcat = o; o += align256(static_cast<size_t>(router_splits(d)) * d.D * 2 * d.E * sizeof(float));
+  L.dwcat = o; o += align256(static_cast<size_t>(router_splits(d)) * d.D * router_cols(d) * sizeof(float));
   L.total = o;
   return L;
 }
 size_t route_backward_workspace(const Dims& d) { return route_bwd_layout(d).total; }
 
-// dWg / dWnoise from the router's split partials [S][D][2E], summed over the splits in order.
-__global__ void split_dw(const float* __restrict__ dwcat, int S, int D, int E,
+// dWg / dWnoise from the router's split partials [S][D][KC], summed over the splits in order
+// (KC = E, or 2E with the noise columns after the clean ones).
+__global__ void split_dw(const float* __restrict__ dwcat, int S, int D, int E, int KC,
                          float* __restrict__ dWg, float* __restrict__ dWn) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= static_cast<int64_t>(D) * E) return;
   const int64_t dd = i / E;
   const int e = static_cast<int>(i - dd * E);
-  const int64_t plane = static_cast<int64_t>(D) * 2 * E;
+  const int64_t plane = static_cast<int64_t>(D) * KC;
   float g = 0.f, n = 0.f;
   for (int s = 0; s < S; ++s) {
-    g += dwcat[s * plane + dd * 2 * E + e];
-    if (dWn) n += dwcat[s * plane + dd * 2 * E + E + e];
+    g += dwcat[s * plane + dd * KC + e];
+    if (dWn) n += dwcat[s * plane + dd * KC + E + e];
   }
   dWg[i] = g;
   if (dWn) dWn[i] = n;
@@ -660,56 +741,83 @@ moe_status route_backward_launch(const Dims& d, uint64_t seed, const void* X, co
                                  const float* gates,
                                  const float* clean, const float* noise_std, const float* row_stats,
                                  const float* dgates, const float* importance, const float* load,
-                                 float w_imp, float w_load, const void* dY, const void* dXd,
+                                 const int32_t* counts, float w_imp, float w_load, float w_switch,
+                                 const void* dY, const void* dXd,
                                  const int32_t* pos, const uint8_t* accepted, const int32_t* offsets,
                                  void* dX, float* dWg, float* dWnoise, float* dbias, void* ws,
                                  hipStream_t stream) {
   const RouteBwdLayout L = route_bwd_layout(d);
   char* base = static_cast<char*>(ws);
   float* dimp = reinterpret_cast<float*>(base + L.dimp);
-  float* dload = reinterpret_cast<float*>(base + L.dload);
+  float* dload = reinterpret_cast<float*>(base + L.dload);  // Switch: dprob
   float* dbias_part = reinterpret_cast<float*>(base + L.dbias);
   void* dcat = base + L.dcat;
   uint4* wpack = reinterpret_cast<uint4*>(base + L.wpack);
   int32_t* off = reinterpret_cast<int32_t*>(base + L.off);
   void* dxr = base + L.dxr;
   float* dwcat = reinterpret_cast<float*>(base + L.dwcat);
-  const bool noise = d.noise != 0;
+  const bool sw = d.gating == MOE_GATE_SWITCH_TOP1;
+  const bool noise = !sw && d.noise != 0;
+  const int KC = router_cols(d);
   if (w_imp != 0.f) {
     cv2_grad<<<1, kThreads, 0, stream>>>(importance, d.E, w_imp, dimp);
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   }
-  const bool use_load = noise && w_load != 0.f;
-  if (use_load) {
-    cv2_grad<<<1, kThreads, 0, stream>>>(load, d.E, w_load, dload);
+  const int nblk = gate_blocks(d), gw = gate_waves(d);
+  if (sw) {
+    const bool use_bal = w_switch != 0.f;
+    if (use_bal) {
+      switch_dprob<<<ceil_div(d.E, kThreads), kThreads, 0, stream>>>(counts, d.T, d.E, w_switch,
+                                                                     dload);
+      if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+    }
+    SwitchGateArgs sa;
+    sa.ids = ids;
+    sa.clean = clean;
+    sa.dgates = dgates;
+    sa.dimp = w_imp != 0.f ? dimp : nullptr;
+    sa.dprob = use_bal ? dload : nullptr;
+    sa.dcat = dcat;
+    sa.dbias_part = dbias ? dbias_part : nullptr;
+    sa.T = d.T;
+    sa.E = d.E;
+    sa.dtype = d.dtype;
+    const size_t lds = static_cast<size_t>(gw) * d.E * sizeof(float);
+    switch_gate_backward<<<nblk, 64 * gw, lds, stream>>>(sa);
+    if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  } else {
+    const bool use_load = noise && w_load != 0.f;
+    if (use_load) {
+      cv2_grad<<<1, kThreads, 0, stream>>>(load, d.E, w_load, dload);
+      if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+    }
+    GateArgs ga;
+    ga.ids = ids;
+    ga.gates = gates;
+    ga.clean = clean;
+    ga.std_in = noise ? noise_std : nullptr;
+    ga.row_stats = row_stats;
+    ga.dgates = dgates;
+    ga.dimp = w_imp != 0.f ? dimp : nullptr;
+    ga.dload = use_load ? dload : nullptr;
+    ga.eps = noise ? eps : nullptr;
+    ga.dcat = dcat;
+    ga.ldc = KC;
+    ga.dbias_part = dbias ? dbias_part : nullptr;
+    ga.seed = seed;
+    ga.T = d.T;
+    ga.E = d.E;
+    ga.k = d.k;
+    ga.noise = noise ? 1 : 0;
+    ga.dtype = d.dtype;
+    const size_t lds = static_cast<size_t>(gw) * 3 * d.E * sizeof(float);
+    if (lds > 65536 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_backward),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess)
+      return MOE_ERR_HIP;
+    gate_backward<<<nblk, 64 * gw, lds, stream>>>(ga);
     if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   }
-  GateArgs ga;
-  ga.ids = ids;
-  ga.gates = gates;
-  ga.clean = clean;
-  ga.std_in = noise ? noise_std : nullptr;
-  ga.row_stats = row_stats;
-  ga.dgates = dgates;
-  ga.dimp = w_imp != 0.f ? dimp : nullptr;
-  ga.dload = use_load ? dload : nullptr;
-  ga.eps = noise ? eps : nullptr;
-  ga.dcat = dcat;
-  ga.dbias_part = dbias ? dbias_part : nullptr;
-  ga.seed = seed;
-  ga.T = d.T;
-  ga.E = d.E;
-  ga.k = d.k;
-  ga.noise = noise ? 1 : 0;
-  ga.dtype = d.dtype;
-  const int nblk = gate_blocks(d), gw = gate_waves(d);
-  const size_t lds = static_cast<size_t>(gw) * 3 * d.E * sizeof(float);
-  if (lds > 65536 &&
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_backward),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess)
-    return MOE_ERR_HIP;
-  gate_backward<<<nblk, 64 * gw, lds, stream>>>(ga);
-  if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   if (dbias) {
     const int sl = bias_slices(nblk);
     float* dbias2 = reinterpret_cast<float*>(base + L.dbias2);
@@ -722,8 +830,8 @@ moe_status route_backward_launch(const Dims& d, uint64_t seed, const void* X, co
   Dims dr = d;
   dr.E = 1;
   dr.k = 1;
-  dr.D = 2 * d.E;  // K
-  dr.H = d.D;      // N
+  dr.D = KC;   // K
+  dr.H = d.D;  // N
   dr.C = d.T;
   dr.max_rows = d.T;
   const int NB = ceil_div(d.D, 32), KS = router_bwd_ks(d);
@@ -740,10 +848,10 @@ moe_status route_backward_launch(const Dims& d, uint64_t seed, const void* X, co
   if (s != MOE_OK) return s;
   // dWcat = X^T [dclean | draw]
   const int S = router_splits(d);
-  s = wgrad_launch(d, X, dcat, off, 1, d.D, 2 * d.E, dwcat, stream, S);
+  s = wgrad_launch(d, X, dcat, off, 1, d.D, KC, dwcat, stream, S);
   if (s != MOE_OK) return s;
   split_dw<<<static_cast<int>(ceil_div64(static_cast<int64_t>(d.D) * d.E, 256)), 256, 0, stream>>>(
-      dwcat, S, d.D, d.E, dWg, noise ? dWnoise : nullptr);
+      dwcat, S, d.D, d.E, KC, dWg, noise ? dWnoise : nullptr);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   // dX = dY (residual) + the experts' rows + the router's share
   const int grid = ceil_div(d.T, kThreads / 64);

@@ -211,8 +211,9 @@ moe_status route_backward_launch(const Dims& d, uint64_t seed, const void* X, co
                                  const float* Wnoise, const float* eps, const int32_t* ids,
                                  const float* gates, const float* clean, const float* noise_std,
                                  const float* row_stats, const float* dgates,
-                                 const float* importance, const float* load, float w_imp,
-                                 float w_load, const void* dY, const void* dXd, const int32_t* pos,
+                                 const float* importance, const float* load,
+                                 const int32_t* counts, float w_imp, float w_load, float w_switch,
+                                 const void* dY, const void* dXd, const int32_t* pos,
                                  const uint8_t* accepted, const int32_t* offsets, void* dX,
                                  float* dWg, float* dWnoise, float* dbias, void* ws,
                                  hipStream_t stream);

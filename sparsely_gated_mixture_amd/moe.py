@@ -34,7 +34,7 @@ ENTRY_POINTS = [
     "moe_dispatch_batchwise", "moe_combine_batchwise", "moe_aux_loss_batchwise",
     "moe_pack_expert_weights_t", "moe_combine_backward", "moe_expert_ffn_backward",
     "moe_route_backward", "moe_backward_workspace_size", "moe_expert_weight_grad",
-    "moe_expert_ffn_backward_recompute",
+    "moe_expert_ffn_backward_recompute", "moe_route_backward_switch",
 ]
 
 
@@ -113,6 +113,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_backward_workspace_size": (sz, [P]),
         "moe_expert_weight_grad": (ctypes.c_int, [P, i32, vp, vp, vp, vp, vp]),
         "moe_expert_ffn_backward_recompute": (ctypes.c_int, [P] + [vp] * 11 + [vp]),
+        "moe_route_backward_switch": (ctypes.c_int, [P] + [vp] * 7 + [ctypes.c_float] * 2 +
+                                      [vp] * 9 + [sz, vp]),
         "moe_batchwise_m": (i32, [P]),
         "moe_batchwise_workspace_size": (sz, [P, ctypes.c_int]),
         "moe_route_batchwise": (ctypes.c_int, [P, vp, vp, vp, vp, ctypes.POINTER(BatchwiseState),
@@ -340,6 +342,17 @@ def moe_expert_weight_grad(p, which, A, B, offsets, C, stream=None):
            "moe_expert_weight_grad")
 
 
+def moe_route_backward_switch(p, X, Wg, ids, clean, dgates, importance, counts, w_imp, w_switch,
+                              dY_residual, dXd, pos, accepted, offsets, dX, dWg, dbias, ws,
+                              stream=None):
+    _check(_lib.moe_route_backward_switch(
+        ctypes.byref(p), _ptr(X), _ptr(Wg), _ptr(ids), _ptr(clean), _ptr(dgates),
+        _ptr(importance), _ptr(counts), float(w_imp), float(w_switch), _ptr(dY_residual),
+        _ptr(dXd), _ptr(pos), _ptr(accepted), _ptr(offsets), _ptr(dX), _ptr(dWg), _ptr(dbias),
+        _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)),
+        "moe_route_backward_switch")
+
+
 def moe_backward_workspace_size(p: Problem) -> int:
     return _lib.moe_backward_workspace_size(ctypes.byref(p))
 
@@ -458,7 +471,7 @@ class Layer:
             e = lambda *s, dtype=torch.float32: torch.empty(*s, dtype=dtype, device=self.b.Y.device)
             dt = torch_dtype(p)
             rows = max(moe_max_rows(p), 1)
-            noisy = p.noise == 1
+            noisy = p.gating == MOE_GATE_NOISY_TOPK and p.noise == 1
             if self.grads is None:
                 self.W1t = e(moe_packed_weight_bytes(p, 4), dtype=torch.uint8)
                 self.W2t = e(moe_packed_weight_bytes(p, 3), dtype=torch.uint8)
@@ -492,22 +505,34 @@ class Layer:
             moe_expert_ffn_backward(self.p, b.Xd, b.Hd, g["dZ"], self.W1t, self.W2t, b.offsets,
                                     g["dHp"], g["dXd"], dW1, dW2)
 
-    def backward_route(self, X, dY, w_imp=0.0, w_load=0.0, residual=True, eps=None):
+    def backward_route(self, X, dY, w_imp=0.0, w_load=0.0, residual=True, eps=None,
+                       w_switch=0.0):
+        """Noisy top-k: w_imp, w_load; Switch: w_imp, w_switch (the E * sum f * Pbar term)."""
         b, g = self.b, self.grads
+        if self.p.gating == MOE_GATE_SWITCH_TOP1:
+            if w_load or eps is not None:
+                raise ValueError("the Switch gate has no load term and no noise")
+            moe_route_backward_switch(self.p, X, self.Wg, b.ids, b.clean, g["dgates"],
+                                      b.importance, b.counts, w_imp, w_switch,
+                                      dY if residual else None, g["dXd"], b.pos, b.accepted,
+                                      b.offsets, g["dX"], g["dWg"], g["dbias"], g["ws"])
+            return
+        if w_switch:
+            raise ValueError("w_switch applies to the Switch gate")
         moe_route_backward(self.p, X, self.Wg, self.Wnoise, eps, b.ids, b.gates, b.clean,
                            b.noise_std, b.row_stats, g["dgates"], b.importance, b.load, w_imp,
                            w_load, dY if residual else None, g["dXd"], b.pos, b.accepted,
                            b.offsets, g["dX"], g["dWg"], g["dWnoise"], g["dbias"], g["ws"])
 
     def backward(self, X, dY, w_imp=0.0, w_load=0.0, residual=True, eps=None,
-                 weight_grads=True, recompute=False) -> dict:
+                 weight_grads=True, recompute=False, w_switch=0.0) -> dict:
         """Gradients after forward(X) (with aux, whose importance and load the balancing
         terms use): dX, dWg, dWnoise, dbias, dW1, dW2 (fp32 weight gradients) of the
         objective <Y, dY> + w_imp CV^2(importance) + w_load CV^2(load)."""
         self.backward_buffers(weight_grads)
         self.backward_combine(dY)
         self.backward_ffn(weight_grads, recompute)
-        self.backward_route(X, dY, w_imp, w_load, residual, eps)
+        self.backward_route(X, dY, w_imp, w_load, residual, eps, w_switch)
         return self.grads
 
     def forward(self, X, eps=None, residual=True, aux=True) -> Buffers:

@@ -175,15 +175,29 @@ def test_backward_validation(m):
     p = _p(m, T=64, E=8, k=2)
     assert m.moe_backward_workspace_size(p) > 0
     sw = _p(m, T=64, E=8, k=1, gating="switch", noise=False)
-    assert m.moe_backward_workspace_size(sw) == 0
+    assert m.moe_backward_workspace_size(sw) > 0
+    bw = _p(m, T=64, E=8, k=2, gating="batchwise", noise=False)
+    assert m.moe_backward_workspace_size(bw) == 0
     fake = ctypes.c_void_p(0x1000)
-    assert m._lib.moe_combine_backward(ctypes.byref(sw), *([fake] * 9), None) == -2
+    # every call below is rejected by the host checks before anything is enqueued
+    assert m._lib.moe_combine_backward(ctypes.byref(bw), *([fake] * 9), None) == -1
     assert m._lib.moe_combine_backward(ctypes.byref(p), fake, None, *([fake] * 7), None) == -1
     args = [fake] * 12 + [ctypes.c_float(0.0), ctypes.c_float(0.0)] + [fake] * 9
     need = m.moe_backward_workspace_size(p)
     assert m._lib.moe_route_backward(ctypes.byref(p), *args, fake, need - 1, None) == -5
     args_nan = [fake] * 12 + [ctypes.c_float(float("nan")), ctypes.c_float(0.0)] + [fake] * 9
     assert m._lib.moe_route_backward(ctypes.byref(p), *args_nan, fake, need, None) == -1
+    # each gate has its own route-backward entry point
+    assert m._lib.moe_route_backward(ctypes.byref(sw), *args, fake, need, None) == -1
+    sargs = [fake] * 7 + [ctypes.c_float(0.0), ctypes.c_float(0.1)] + [fake] * 8
+    need_sw = m.moe_backward_workspace_size(sw)
+    assert m._lib.moe_route_backward_switch(ctypes.byref(p), *sargs, fake, need, None) == -1
+    assert m._lib.moe_route_backward_switch(ctypes.byref(sw), *sargs, fake, need_sw - 1,
+                                            None) == -5
+    no_counts = list(sargs)
+    no_counts[6] = None  # counts, needed for w_switch != 0
+    assert m._lib.moe_route_backward_switch(ctypes.byref(sw), *no_counts, fake, need_sw,
+                                            None) == -1
 
 
 def test_weight_grad_validation(m):
@@ -191,8 +205,8 @@ def test_weight_grad_validation(m):
     fake = ctypes.c_void_p(0x1000)
     assert m._lib.moe_expert_weight_grad(ctypes.byref(p), 3, *([fake] * 4), None) == -1
     assert m._lib.moe_expert_weight_grad(ctypes.byref(p), 1, fake, None, fake, fake, None) == -1
-    sw = _p(m, T=64, E=8, k=1, gating="switch", noise=False)
-    assert m._lib.moe_expert_weight_grad(ctypes.byref(sw), 1, *([fake] * 4), None) == -2
+    bw = _p(m, T=64, E=8, k=2, gating="batchwise", noise=False)
+    assert m._lib.moe_expert_weight_grad(ctypes.byref(bw), 1, *([fake] * 4), None) == -1
 
 
 def test_recompute_validation(m):
@@ -202,5 +216,5 @@ def test_recompute_validation(m):
     args_missing = list(args)
     args_missing[6] = None  # Hd scratch
     assert m._lib.moe_expert_ffn_backward_recompute(ctypes.byref(p), *args_missing, None) == -1
-    sw = _p(m, T=64, E=8, k=1, gating="switch", noise=False)
-    assert m._lib.moe_expert_ffn_backward_recompute(ctypes.byref(sw), *args, None) == -2
+    bw = _p(m, T=64, E=8, k=2, gating="batchwise", noise=False)
+    assert m._lib.moe_expert_ffn_backward_recompute(ctypes.byref(bw), *args, None) == -1
