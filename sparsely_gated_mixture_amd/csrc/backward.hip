@@ -23,13 +23,14 @@
 //                    d raw = d std * sigmoid(raw); writes [dclean | draw] [T, 2E]
 //                    and per-block sums of dclean (the bias gradient)
 //   column_sums      the per-block sums, in two passes, in a fixed order
-//   wgrad_gemm       per group (and row split), C = A^T B over the group's rows
-//                    (fp32 output): 8x8 (bf16) / 4x4 (fp32) register transposes put
-//                    both operands k-contiguous in LDS, then MFMA; the next stage's
-//                    loads are in flight during the current stage's MFMAs; one block
-//                    per (group, split, 128 x 128 tile), fixed row order. The router's
-//                    weight gradient (one group of T rows) is split over rows and the
-//                    splits summed in order (split_dw)
+//   wgrad_gemm_tr    per group (and row split), C = A^T B over the group's rows (fp32
+//                    output), bf16: operands row-major in LDS, transposed by the LDS
+//                    transpose read into MFMA fragments; 128 x 256 tiles; fixed row order
+//   wgrad_gemm       the same for fp32 and for widths that are not multiples of 8:
+//                    4x4 / 8x8 register transposes put both operands k-contiguous in
+//                    LDS; 128 x 128 tiles. Either way the router's weight gradient (one
+//                    group of T rows) is split over rows and the splits summed in order
+//                    (split_dw)
 //   dx_final         a wave per token: dX = dY + sum of the accepted rows of dXd
 //                    + the router's share, fp32 accumulation, one rounding
 // The dense GEMMs of the backward (dZ W2^T with the ReLU mask, dH W1^T and the
@@ -602,6 +603,136 @@ __global__ __launch_bounds__(kThreads) void wgrad_gemm(WgradArgs a) {
     }
 }
 
+// bf16 weight gradient (M and N multiples of 8): both operands are copied row-major into LDS
+// as they come from memory, and transposed on the way out by gfx950's LDS transpose read
+// (ds_read_b64_tr_b16): in a group of 16 lanes whose lane 4j + q points at row k0 + j,
+// columns c0 + 4q .. c0 + 4q + 3, lane i receives column c0 + i of rows k0 .. k0 + 3. Two
+// such reads give a lane the 8 k-values of its MFMA operand, with no VALU transposes. A block
+// computes a 128 x 256 tile (waves 2 x 2, each 64 x 128); the next 64-row stage's loads are in
+// flight during the current stage's MFMAs. Rows past the end of the split are zeroed in A
+// only (a zero in either factor removes the product); columns past M / N are clamped reads
+// that only feed outputs never stored. LDS rows are padded by 32 bytes so that the four rows
+// of one transpose read fall in different banks.
+typedef short v4s16 __attribute__((ext_vector_type(4)));
+constexpr int kTrRow = kWT * 2 + 32;  // LDS bytes per k row: 128 bf16 + 32 pad (bank rotation)
+
+__device__ __forceinline__ unsigned long long tr_read(const unsigned char* lds_base, int byte_off) {
+  typedef __attribute__((address_space(3))) v4s16* lptr;
+  typedef __attribute__((address_space(3))) unsigned char* lbyte;
+  const v4s16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lptr)((lbyte)(lds_base) + byte_off));
+  return __builtin_bit_cast(unsigned long long, v);
+}
+
+constexpr int kTN2 = 256;                // tile N of the transpose-read kernel
+constexpr int kTrRowB = kTN2 * 2 + 32;   // LDS bytes per k row of B
+
+template <bool kRowSplit>
+__global__ __launch_bounds__(kThreads) void wgrad_gemm_tr(WgradArgs a) {
+  __shared__ __align__(16) unsigned char sA[kWRows * kTrRow];
+  __shared__ __align__(16) unsigned char sB[kWRows * kTrRowB];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int mt = (a.M + kWT - 1) / kWT, nt = (a.N + kTN2 - 1) / kTN2;
+  const int tiles = mt * nt;
+  const int S = kRowSplit ? a.S : 1;
+  const int total = a.G * S * tiles;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int logical = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (logical >= total) return;
+  const int gs = logical / tiles;
+  const int g = gs / S, sp = gs - g * S;
+  const int rem = logical - gs * tiles;
+  const int m0 = (rem / nt) * kWT, n0 = (rem % nt) * kTN2;
+  const int gb = a.offsets[g], ge = a.offsets[g + 1];
+  const int chunk = ((ge - gb + S - 1) / S + kWRows - 1) / kWRows * kWRows;
+  const int r_begin = min(ge, gb + sp * chunk), r_end = min(ge, r_begin + chunk);
+  const uint16_t* A = static_cast<const uint16_t*>(a.A);
+  const uint16_t* B = static_cast<const uint16_t*>(a.B);
+  // loader: A 64 rows x 16 segments (4 per thread), B 64 rows x 32 segments (8 per thread)
+  constexpr int kSA = kWRows * 16 / kThreads, kSB = kWRows * 32 / kThreads;
+  u32x4 ina[kSA], inb[kSB];
+  const int csa = tid & 15, csb = tid & 31;
+  const int ca = min(m0 + csa * 8, a.M - 8), cb = min(n0 + csb * 8, a.N - 8);
+  auto load = [&](int rs) {
+#pragma unroll
+    for (int p = 0; p < kSA; ++p) {
+      const int row = (tid >> 4) + p * 16;
+      ina[p] = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(min(rs + row, r_end - 1)) * a.M + ca);
+    }
+#pragma unroll
+    for (int p = 0; p < kSB; ++p) {
+      const int row = (tid >> 5) + p * 8;
+      inb[p] = *reinterpret_cast<const u32x4*>(B + static_cast<int64_t>(min(rs + row, r_end - 1)) * a.N + cb);
+    }
+  };
+  auto stash = [&](int rs) {
+    const bool tail = rs + kWRows > r_end;
+#pragma unroll
+    for (int p = 0; p < kSA; ++p) {
+      const int row = (tid >> 4) + p * 16;
+      u32x4 v = ina[p];
+      if (tail && rs + row >= r_end) v = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sA + row * kTrRow + csa * 16) = v;
+    }
+#pragma unroll
+    for (int p = 0; p < kSB; ++p) {
+      const int row = (tid >> 5) + p * 8;
+      *reinterpret_cast<u32x4*>(sB + row * kTrRowB + csb * 16) = inb[p];
+    }
+  };
+  const int wm = wave >> 1, wn = wave & 1;  // wave tile 64 (m) x 128 (n)
+  const int gq = lane >> 4, jr = (lane >> 2) & 3, qc = lane & 3;
+  const int rowq = 8 * (gq >> 1) + jr, colq = 16 * (gq & 1) + 4 * qc;
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) acc[i][j][t] = 0.f;
+  if (r_begin < r_end) load(r_begin);
+  for (int rs = r_begin; rs < r_end; rs += kWRows) {
+    stash(rs);
+    __syncthreads();
+    if (rs + kWRows < r_end) load(rs + kWRows);
+#pragma unroll
+    for (int ks = 0; ks < kWRows / 16; ++ks) {
+      u32x4 fa[2], fb[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int oa = (ks * 16 + rowq) * kTrRow + (wm * 64 + i * 32 + colq) * 2;
+        const unsigned long long a0 = tr_read(sA, oa), a1 = tr_read(sA, oa + 4 * kTrRow);
+        fa[i] = u32x4{static_cast<unsigned>(a0), static_cast<unsigned>(a0 >> 32),
+                      static_cast<unsigned>(a1), static_cast<unsigned>(a1 >> 32)};
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ob = (ks * 16 + rowq) * kTrRowB + (wn * 128 + j * 32 + colq) * 2;
+        const unsigned long long b0 = tr_read(sB, ob), b1 = tr_read(sB, ob + 4 * kTrRowB);
+        fb[j] = u32x4{static_cast<unsigned>(b0), static_cast<unsigned>(b0 >> 32),
+                      static_cast<unsigned>(b1), static_cast<unsigned>(b1 >> 32)};
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = wmma<uint16_t>(fa[i], fb[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  float* C = a.C + static_cast<int64_t>(gs) * a.M * a.N;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn * 128 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int m = m0 + wm * 64 + i * 32 + acc_row(lane, t);
+        if (m < a.M && n < a.N) C[static_cast<int64_t>(m) * a.N + n] = acc[i][j][t];
+      }
+    }
+}
+
 // ------------------------------------------------------------------ input gradient
 template <typename T>
 __global__ __launch_bounds__(kThreads) void dx_final(
@@ -654,14 +785,18 @@ moe_status combine_backward_launch(const Dims& d, const void* dY, const void* Z,
 moe_status wgrad_launch(const Dims& d, const void* A, const void* B, const int32_t* offsets, int G,
                         int M, int N, float* C, hipStream_t stream, int splits) {
   WgradArgs a{A, B, offsets, C, G, M, N, splits};
-  const int64_t blocks = static_cast<int64_t>(G) * splits * ceil_div(M, kWT) * ceil_div(N, kWT);
+  const bool tr = d.dtype == MOE_BF16 && M % 8 == 0 && N % 8 == 0;  // the transpose-read kernel
+  const int64_t blocks = static_cast<int64_t>(G) * splits * ceil_div(M, kWT) * ceil_div(N, tr ? kTN2 : kWT);
   if (blocks > 0x7fffffffLL - kXcds) return MOE_ERR_UNSUPPORTED;
   const int grid = static_cast<int>(ceil_div64(blocks, kXcds) * kXcds);
   const bool aligned = M % 8 == 0 && N % 8 == 0;  // multiples of 16 bytes for either dtype
   const bool split = splits > 1;
 #define MOE_WGRAD(TY, AL, SP) wgrad_gemm<TY, AL, SP><<<grid, kThreads, 0, stream>>>(a)
   if (d.dtype == MOE_BF16) {
-    if (aligned) { if (split) MOE_WGRAD(uint16_t, true, true); else MOE_WGRAD(uint16_t, true, false); }
+    if (aligned) {
+      if (split) wgrad_gemm_tr<true><<<grid, kThreads, 0, stream>>>(a);
+      else wgrad_gemm_tr<false><<<grid, kThreads, 0, stream>>>(a);
+    }
     else { if (split) MOE_WGRAD(uint16_t, false, true); else MOE_WGRAD(uint16_t, false, false); }
   } else {
     if (aligned) { if (split) MOE_WGRAD(float, true, true); else MOE_WGRAD(float, true, false); }
