@@ -247,6 +247,7 @@ def bench_backward(args, torch, w, inp, p, L, X, t_gen):
     per = {name: float(np.mean([events[s_][i].elapsed_time(events[s_][i + 1])
                                 for s_ in range(args.steps)]))
            for i, name in enumerate(stages)}
+    step_ev = [events[s_][0].elapsed_time(events[s_][-1]) for s_ in range(args.steps)]
     offs = b.offsets.cpu().numpy()
     A = int(offs[-1])
     U = int(np.count_nonzero(np.diff(offs)))
@@ -274,6 +275,9 @@ def bench_backward(args, torch, w, inp, p, L, X, t_gen):
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline("wgrad_gemm", flops, wg_bytes, wg_ms, peak, traffic),
         "forward_ms": fwd_ms, "backward_ms": bwd_ms, "stages_ms": per,
+        "step_ms_events": {"p10": float(np.percentile(step_ev, 10)),
+                           "p50": float(np.median(step_ev)),
+                           "p90": float(np.percentile(step_ev, 90))},
         "input_gen_s": t_gen,
     }
     if not args.no_cpu_baseline:
@@ -296,6 +300,9 @@ def main():
                     help="time a training step of the layer instead: the forward, then the "
                          "backward (combine, expert FFN data and weight gradients, gate and "
                          "router) with w_importance = w_load = 0.1")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time K steps each after a 512 MiB scrub write (L2 and MALL "
+                         "cold), reported under 'cold'")
     ap.add_argument("--recompute", action="store_true",
                     help="with --backward: recompute the experts' hidden activations in the "
                          "backward instead of reading the forward's")
@@ -387,6 +394,24 @@ def main():
     per = {name: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
                                 for s in range(args.steps)]))
            for i, name in enumerate(stages)}
+    step_ev = [events[s][0].elapsed_time(events[s][-1]) for s in range(args.steps)]
+    cold = None
+    if args.cold:
+        # each step after a 512 MiB write that evicts the L2s and the MALL: weights, tokens
+        # and routing state then come from HBM (event-timed steps; the scrub is not counted)
+        scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+               for _ in range(args.steps)]
+        for s in range(args.steps):
+            scrub.fill_(s & 0xff)
+            step(cev[s])
+        torch.cuda.synchronize()
+        cstep = [cev[s][0].elapsed_time(cev[s][-1]) for s in range(args.steps)]
+        cold = {"scrub_bytes": 512 << 20, "step_ms_p50": float(np.median(cstep)),
+                "tokens_per_s_p50": w.T / (float(np.median(cstep)) * 1e-3),
+                "stages_ms": {name: float(np.mean([cev[s][i].elapsed_time(cev[s][i + 1])
+                                                   for s in range(args.steps)]))
+                              for i, name in enumerate(stages)}}
 
     offs = (L.st["offsets"] if w.gating == "batchwise" else L.b.offsets).cpu().numpy()
     A = int(offs[-1])
@@ -423,6 +448,9 @@ def main():
                    "capacity": moe.moe_capacity(p), "accepted_rows": A,
                    "dropped": w.T * w.k - A, "parallelism": "none (1 GPU)"},
         "roofline": roofline("grouped_gemm", gemm_flops, gemm_bytes, gemm_ms, peak, traffic),
+        "step_ms_events": {"p10": float(np.percentile(step_ev, 10)),
+                           "p50": float(np.median(step_ev)),
+                           "p90": float(np.percentile(step_ev, 90))},
         "tokens_per_s_without_aux": w.T / ((ms_per_step - per["aux"]) * 1e-3),
         "stages_ms": per,
         "dispatch_GBps": disp_bytes / (per["dispatch"] * 1e-3) / 1e9,
@@ -431,6 +459,8 @@ def main():
         "combine_hbm_frac": comb_bytes / (per["combine"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "input_gen_s": t_gen,
     }
+    if cold is not None:
+        out["cold"] = cold
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_tokens)
     print(json.dumps(out), flush=True)
