@@ -53,15 +53,19 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ------------------------------------------------------------------ combine backward
+// 16-byte vectors along D when D is a multiple of the vector width, else one element a lane.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void cb_backward(
     const T* __restrict__ dY, const T* __restrict__ Z, const int32_t* __restrict__ ids,
     const float* __restrict__ gates, const int32_t* __restrict__ pos,
     const uint8_t* __restrict__ accepted, const int32_t* __restrict__ offsets, int Tn, int D, int k,
     T* __restrict__ dZ, float* __restrict__ dgates) {
+  constexpr int V = Elem<T>::kVec;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (t >= Tn) return;
+  const bool vec = (D % V) == 0;
+  const T* dy = dY + static_cast<int64_t>(t) * D;
   for (int j = 0; j < k; ++j) {
     const int64_t gi = static_cast<int64_t>(t) * k + j;
     if (!accepted[gi]) {
@@ -70,11 +74,30 @@ __global__ __launch_bounds__(kThreads) void cb_backward(
     }
     const int64_t row = static_cast<int64_t>(offsets[ids[gi]]) + pos[gi];
     const float g = gates[gi];
+    const T* z = Z + row * D;
+    T* dz = dZ + row * D;
     float dot = 0.f;
-    for (int c = lane; c < D; c += 64) {
-      const float dy = Elem<T>::to_f32(dY[static_cast<int64_t>(t) * D + c]);
-      dot = fmaf(dy, Elem<T>::to_f32(Z[row * D + c]), dot);
-      dZ[row * D + c] = Elem<T>::from_f32(g * dy);
+    if (vec) {
+      for (int c = lane; c < D / V; c += 64) {
+        const uint4 yv = reinterpret_cast<const uint4*>(dy)[c];
+        const uint4 zv = reinterpret_cast<const uint4*>(z)[c];
+        const T* yp = reinterpret_cast<const T*>(&yv);
+        const T* zp = reinterpret_cast<const T*>(&zv);
+        T out[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const float y = Elem<T>::to_f32(yp[i]);
+          dot = fmaf(y, Elem<T>::to_f32(zp[i]), dot);
+          out[i] = Elem<T>::from_f32(g * y);
+        }
+        reinterpret_cast<uint4*>(dz)[c] = *reinterpret_cast<const uint4*>(out);
+      }
+    } else {
+      for (int c = lane; c < D; c += 64) {
+        const float y = Elem<T>::to_f32(dy[c]);
+        dot = fmaf(y, Elem<T>::to_f32(z[c]), dot);
+        dz[c] = Elem<T>::from_f32(g * y);
+      }
     }
     dot = wave_sum(dot);
     if (lane == 0) dgates[gi] = dot;
@@ -740,6 +763,7 @@ __global__ __launch_bounds__(kThreads) void dx_final(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ pos,
     const uint8_t* __restrict__ accepted, const int32_t* __restrict__ offsets, int Tn, int D, int k,
     int residual, T* __restrict__ dX) {
+  constexpr int V = Elem<T>::kVec;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (t >= Tn) return;
@@ -752,14 +776,37 @@ __global__ __launch_bounds__(kThreads) void dx_final(
       if (accepted[gi]) row[j] = static_cast<int64_t>(offsets[ids[gi]]) + pos[gi];
     }
   }
-  for (int c = lane; c < D; c += 64) {
-    const int64_t o = static_cast<int64_t>(t) * D + c;
-    float v = residual ? Elem<T>::to_f32(dY[o]) : 0.f;
+  const int64_t o = static_cast<int64_t>(t) * D;
+  if ((D % V) == 0) {
+    for (int c = lane; c < D / V; c += 64) {
+      float v[V];
+      auto add = [&](const T* src) {
+        const uint4 u = reinterpret_cast<const uint4*>(src)[c];
+        const T* up = reinterpret_cast<const T*>(&u);
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_K; ++j)
-      if (row[j] >= 0) v += Elem<T>::to_f32(dXd[row[j] * D + c]);
-    if (dXr) v += Elem<T>::to_f32(dXr[o]);
-    dX[o] = Elem<T>::from_f32(v);
+        for (int i = 0; i < V; ++i) v[i] += Elem<T>::to_f32(up[i]);
+      };
+#pragma unroll
+      for (int i = 0; i < V; ++i) v[i] = 0.f;
+      if (residual) add(dY + o);
+#pragma unroll
+      for (int j = 0; j < MOE_MAX_K; ++j)
+        if (row[j] >= 0) add(dXd + row[j] * D);
+      if (dXr) add(dXr + o);
+      T out[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) out[i] = Elem<T>::from_f32(v[i]);
+      reinterpret_cast<uint4*>(dX + o)[c] = *reinterpret_cast<const uint4*>(out);
+    }
+  } else {
+    for (int c = lane; c < D; c += 64) {
+      float v = residual ? Elem<T>::to_f32(dY[o + c]) : 0.f;
+#pragma unroll
+      for (int j = 0; j < MOE_MAX_K; ++j)
+        if (row[j] >= 0) v += Elem<T>::to_f32(dXd[row[j] * D + c]);
+      if (dXr) v += Elem<T>::to_f32(dXr[o + c]);
+      dX[o + c] = Elem<T>::from_f32(v);
+    }
   }
 }
 
