@@ -136,6 +136,12 @@ moe_status moe_route(const moe_problem* p, const void* X, const float* Wg,
                      float* row_stats, void* workspace, size_t workspace_bytes,
                      void* hip_stream);
 
+/* The noisy scores H = clean + eps * noise_std [T,E] fp32 that the last moe_route
+ * selected on live in its workspace; this returns their device address inside
+ * route_workspace (NULL for a gate without noise or an invalid problem). They
+ * stay valid until the workspace is used again; moe_route_backward can take them. */
+const float* moe_route_scores(const moe_problem* p, const void* route_workspace);
+
 /* --------------------------------------------------------------- dispatch */
 
 /* moe_dispatch -- capacity-bounded, stable dispatch ([SWITCH] steps 3-5).
@@ -433,9 +439,13 @@ moe_status moe_expert_weight_grad(const moe_problem* p, int32_t which, const voi
  *   dWg = X^T dclean, dWnoise = X^T d raw  [D,E] fp32; dbias = sum_t dclean [E]
  *   (dWnoise NULL without noise; dbias may be NULL).
  * eps: the external noise given to moe_route, or NULL if the router drew it.
+ * scores: the noisy scores H [T,E] the forward selected on (moe_route_scores), or
+ *   NULL: they are then formed again from clean, noise_std and the noise, which
+ *   for the load term means redrawing the noise of every expert.
  * workspace moe_backward_workspace_size(p) bytes. */
 moe_status moe_route_backward(const moe_problem* p, const void* X, const float* Wg,
-                              const float* Wnoise, const float* eps, const int32_t* ids,
+                              const float* Wnoise, const float* eps, const float* scores,
+                              const int32_t* ids,
                               const float* gates, const float* clean, const float* noise_std,
                               const float* row_stats, const float* dgates,
                               const float* importance, const float* load, float w_imp,

@@ -418,8 +418,15 @@ size_t moe_backward_workspace_size(const moe_problem* p) {
   return route_backward_workspace(d);
 }
 
+const float* moe_route_scores(const moe_problem* p, const void* route_workspace) {
+  Dims d;
+  if (validate_topk(p, &d) != MOE_OK) return nullptr;
+  return route_scores(d, route_workspace);
+}
+
 moe_status moe_route_backward(const moe_problem* p, const void* X, const float* Wg,
-                              const float* Wnoise, const float* eps, const int32_t* ids,
+                              const float* Wnoise, const float* eps, const float* scores,
+                              const int32_t* ids,
                               const float* gates, const float* clean, const float* noise_std,
                               const float* row_stats, const float* dgates, const float* importance,
                               const float* load, float w_imp, float w_load,
@@ -439,10 +446,10 @@ moe_status moe_route_backward(const moe_problem* p, const void* X, const float* 
   if (w_imp != 0.f && !importance) return MOE_ERR_INVALID_ARG;
   if (w_load != 0.f && noise && !load) return MOE_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < route_backward_workspace(d)) return MOE_ERR_WORKSPACE;
-  return route_backward_launch(d, p->seed, X, Wg, Wnoise, eps, ids, gates, clean, noise_std,
-                               row_stats, dgates, importance, load, nullptr, w_imp, w_load, 0.f,
-                               dY_residual, dXd, pos, accepted, offsets, dX, dWg, dWnoise, dbias,
-                               workspace, as_stream(hip_stream));
+  return route_backward_launch(d, p->seed, X, Wg, Wnoise, eps, scores, ids, gates, clean,
+                               noise_std, row_stats, dgates, importance, load, nullptr, w_imp,
+                               w_load, 0.f, dY_residual, dXd, pos, accepted, offsets, dX, dWg,
+                               dWnoise, dbias, workspace, as_stream(hip_stream));
 }
 
 moe_status moe_route_backward_switch(const moe_problem* p, const void* X, const float* Wg,
@@ -462,8 +469,9 @@ moe_status moe_route_backward_switch(const moe_problem* p, const void* X, const 
   if (w_imp != 0.f && !importance) return MOE_ERR_INVALID_ARG;
   if (w_switch != 0.f && !counts) return MOE_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < route_backward_workspace(d)) return MOE_ERR_WORKSPACE;
-  return route_backward_launch(d, p->seed, X, Wg, nullptr, nullptr, ids, nullptr, clean, nullptr,
-                               nullptr, dgates, importance, nullptr, counts, w_imp, 0.f, w_switch,
+  return route_backward_launch(d, p->seed, X, Wg, nullptr, nullptr, nullptr, ids, nullptr, clean,
+                               nullptr, nullptr, dgates, importance, nullptr, counts, w_imp, 0.f,
+                               w_switch,
                                dY_residual, dXd, pos, accepted, offsets, dX, dWg, nullptr, dbias,
                                workspace, as_stream(hip_stream));
 }

@@ -145,6 +145,7 @@ struct GateArgs {
   const float* dimp;   // [E] importance term or NULL
   const float* dload;  // [E] load term or NULL (needs noise)
   const float* eps;    // [T, E] the noise the forward was given, or NULL (redrawn by Philox)
+  const float* scores; // [T, E] the forward's noisy scores H, or NULL (formed again)
   void* dcat;          // [T, ldc] act dtype: dclean | draw (draw only with noise)
   int ldc;             // 2E with noise, else E
   float* dbias_part;   // [nblk][E] or NULL
@@ -218,8 +219,10 @@ __global__ __launch_bounds__(kThreads) void gate_backward(GateArgs a) {
         const float vk = a.row_stats[2 * static_cast<int64_t>(t)];
         const float vk1 = a.row_stats[2 * static_cast<int64_t>(t) + 1];
         for (int q = lane; 4 * q < E; q += 64) {
-          float g4[4];
-          if (a.eps) {
+          float g4[4] = {0.f, 0.f, 0.f, 0.f};
+          if (a.scores) {
+            // H comes from the forward: no noise is needed for the non-kept experts
+          } else if (a.eps) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) g4[i] = 4 * q + i < E ? a.eps[base + 4 * q + i] : 0.f;
           } else {
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void gate_backward(GateArgs a) {
             for (int j = 0; j < k; ++j) inside |= rid[j] == e;
             const float cl = a.clean[base + e], sd = a.std_in[base + e];
             if (!inside) {  // candidate for v_{k+1}: H exactly as the router formed it
-              const float h = fmaf(sd, g4[i], cl);
+              const float h = a.scores ? a.scores[base + e] : fmaf(sd, g4[i], cl);
               if (h > best || (h == best && e < bi)) {
                 best = h;
                 bi = e;
@@ -919,7 +922,8 @@ __global__ void split_dw(const float* __restrict__ dwcat, int S, int D, int E, i
 }
 
 moe_status route_backward_launch(const Dims& d, uint64_t seed, const void* X, const float* Wg,
-                                 const float* Wnoise, const float* eps, const int32_t* ids,
+                                 const float* Wnoise, const float* eps, const float* scores,
+                                 const int32_t* ids,
                                  const float* gates,
                                  const float* clean, const float* noise_std, const float* row_stats,
                                  const float* dgates, const float* importance, const float* load,
@@ -983,6 +987,7 @@ moe_status route_backward_launch(const Dims& d, uint64_t seed, const void* X, co
     ga.dimp = w_imp != 0.f ? dimp : nullptr;
     ga.dload = use_load ? dload : nullptr;
     ga.eps = noise ? eps : nullptr;
+    ga.scores = noise ? scores : nullptr;
     ga.dcat = dcat;
     ga.ldc = KC;
     ga.dbias_part = dbias ? dbias_part : nullptr;

@@ -135,6 +135,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace sizes of the individual stages.
 size_t route_workspace(const Dims& d);
+const float* route_scores(const Dims& d, const void* ws);
 size_t dispatch_workspace(const Dims& d);
 size_t aux_workspace(const Dims& d);
 size_t packed_weight_bytes(const Dims& d, int layer);
@@ -208,7 +209,8 @@ moe_status ffn_backward_launch(const Dims& d, const void* Xd, const void* Hd, co
                                const void* W1t, const void* W2t, const int32_t* offsets, void* dHp,
                                void* dXd, float* dW1, float* dW2, hipStream_t stream);
 moe_status route_backward_launch(const Dims& d, uint64_t seed, const void* X, const float* Wg,
-                                 const float* Wnoise, const float* eps, const int32_t* ids,
+                                 const float* Wnoise, const float* eps, const float* scores,
+                                 const int32_t* ids,
                                  const float* gates, const float* clean, const float* noise_std,
                                  const float* row_stats, const float* dgates,
                                  const float* importance, const float* load,

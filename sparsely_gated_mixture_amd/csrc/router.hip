@@ -560,6 +560,13 @@ size_t route_workspace(const Dims& d) {
   return b;
 }
 
+// The noisy scores H [T,E] that the selection used: after the packed weights in the route
+// workspace (NULL without noise).
+const float* route_scores(const Dims& d, const void* ws) {
+  if (!router_noise(d) || !ws) return nullptr;
+  return reinterpret_cast<const float*>(static_cast<const char*>(ws) + router_wbytes(d));
+}
+
 template <typename XT, bool kFullK, bool kGrouped>
 static void router_gemm_bm(int bm, int grid, const GemmArgs& g, hipStream_t stream) {
   const size_t lds = kGrouped ? (static_cast<size_t>(g.G) + 1) * sizeof(int) : 0;

@@ -34,7 +34,7 @@ ENTRY_POINTS = [
     "moe_dispatch_batchwise", "moe_combine_batchwise", "moe_aux_loss_batchwise",
     "moe_pack_expert_weights_t", "moe_combine_backward", "moe_expert_ffn_backward",
     "moe_route_backward", "moe_backward_workspace_size", "moe_expert_weight_grad",
-    "moe_expert_ffn_backward_recompute", "moe_route_backward_switch",
+    "moe_expert_ffn_backward_recompute", "moe_route_backward_switch", "moe_route_scores",
 ]
 
 
@@ -108,7 +108,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_pack_expert_weights_t": (ctypes.c_int, [P, vp, vp, vp, vp, vp]),
         "moe_combine_backward": (ctypes.c_int, [P] + [vp] * 9 + [vp]),
         "moe_expert_ffn_backward": (ctypes.c_int, [P] + [vp] * 10 + [vp]),
-        "moe_route_backward": (ctypes.c_int, [P] + [vp] * 12 + [ctypes.c_float, ctypes.c_float] +
+        "moe_route_scores": (vp, [P, vp]),
+        "moe_route_backward": (ctypes.c_int, [P] + [vp] * 13 + [ctypes.c_float, ctypes.c_float] +
                                [vp] * 9 + [vp, sz, vp]),
         "moe_backward_workspace_size": (sz, [P]),
         "moe_expert_weight_grad": (ctypes.c_int, [P, i32, vp, vp, vp, vp, vp]),
@@ -357,11 +358,17 @@ def moe_backward_workspace_size(p: Problem) -> int:
     return _lib.moe_backward_workspace_size(ctypes.byref(p))
 
 
+def moe_route_scores(p, route_ws) -> int:
+    """Device address (int, 0 if none) of the noisy scores in a route workspace."""
+    return _lib.moe_route_scores(ctypes.byref(p), _ptr(route_ws)) or 0
+
+
 def moe_route_backward(p, X, Wg, Wnoise, eps, ids, gates, clean, noise_std, row_stats, dgates,
                        importance, load, w_imp, w_load, dY_residual, dXd, pos, accepted, offsets,
-                       dX, dWg, dWnoise, dbias, ws, stream=None):
+                       dX, dWg, dWnoise, dbias, ws, stream=None, scores=None):
+    """scores: a device address from moe_route_scores (or None)."""
     _check(_lib.moe_route_backward(ctypes.byref(p), _ptr(X), _ptr(Wg), _ptr(Wnoise), _ptr(eps),
-                                   _ptr(ids), _ptr(gates), _ptr(clean), _ptr(noise_std),
+                                   ctypes.c_void_p(scores) if scores else None, _ptr(ids), _ptr(gates), _ptr(clean), _ptr(noise_std),
                                    _ptr(row_stats), _ptr(dgates), _ptr(importance), _ptr(load),
                                    float(w_imp), float(w_load), _ptr(dY_residual), _ptr(dXd),
                                    _ptr(pos), _ptr(accepted), _ptr(offsets), _ptr(dX), _ptr(dWg),
@@ -519,10 +526,13 @@ class Layer:
             return
         if w_switch:
             raise ValueError("w_switch applies to the Switch gate")
+        # the noisy scores the forward selected on (still in the route workspace)
+        scores = moe_route_scores(self.p, b.ws_route)
         moe_route_backward(self.p, X, self.Wg, self.Wnoise, eps, b.ids, b.gates, b.clean,
                            b.noise_std, b.row_stats, g["dgates"], b.importance, b.load, w_imp,
                            w_load, dY if residual else None, g["dXd"], b.pos, b.accepted,
-                           b.offsets, g["dX"], g["dWg"], g["dWnoise"], g["dbias"], g["ws"])
+                           b.offsets, g["dX"], g["dWg"], g["dWnoise"], g["dbias"], g["ws"],
+                           scores=scores)
 
     def backward(self, X, dY, w_imp=0.0, w_load=0.0, residual=True, eps=None,
                  weight_grads=True, recompute=False, w_switch=0.0) -> dict:
@@ -580,6 +590,9 @@ class HierLayer(Layer):
     def aux(self):
         b = self.b
         moe_aux_loss_hier(self.p, self.h, self.st, b.importance, b.load, b.aux_out, self.ws_aux_h)
+
+    def backward(self, *args, **kw):
+        raise NotImplementedError("the hierarchical gate has no backward pass here")
 
 
 class BatchwiseLayer:

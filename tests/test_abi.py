@@ -182,10 +182,10 @@ def test_backward_validation(m):
     # every call below is rejected by the host checks before anything is enqueued
     assert m._lib.moe_combine_backward(ctypes.byref(bw), *([fake] * 9), None) == -1
     assert m._lib.moe_combine_backward(ctypes.byref(p), fake, None, *([fake] * 7), None) == -1
-    args = [fake] * 12 + [ctypes.c_float(0.0), ctypes.c_float(0.0)] + [fake] * 9
+    args = [fake] * 13 + [ctypes.c_float(0.0), ctypes.c_float(0.0)] + [fake] * 9
     need = m.moe_backward_workspace_size(p)
     assert m._lib.moe_route_backward(ctypes.byref(p), *args, fake, need - 1, None) == -5
-    args_nan = [fake] * 12 + [ctypes.c_float(float("nan")), ctypes.c_float(0.0)] + [fake] * 9
+    args_nan = [fake] * 13 + [ctypes.c_float(float("nan")), ctypes.c_float(0.0)] + [fake] * 9
     assert m._lib.moe_route_backward(ctypes.byref(p), *args_nan, fake, need, None) == -1
     # each gate has its own route-backward entry point
     assert m._lib.moe_route_backward(ctypes.byref(sw), *args, fake, need, None) == -1
@@ -218,3 +218,18 @@ def test_recompute_validation(m):
     assert m._lib.moe_expert_ffn_backward_recompute(ctypes.byref(p), *args_missing, None) == -1
     bw = _p(m, T=64, E=8, k=2, gating="batchwise", noise=False)
     assert m._lib.moe_expert_ffn_backward_recompute(ctypes.byref(bw), *args, None) == -1
+
+
+def test_route_scores_address(m):
+    """The noisy scores sit after the packed router weights in the route workspace; a gate
+    without noise has none (no device access: pure address arithmetic)."""
+    p = _p(m, T=64, E=8, k=2)
+    base = 0x10000000
+    a = m._lib.moe_route_scores(ctypes.byref(p), ctypes.c_void_p(base))
+    assert a is not None and base < a < base + m.moe_workspace_size(p, m.MOE_WS_ROUTE)
+    assert (a - base) % 256 == 0
+    assert a + 64 * 8 * 4 <= base + m.moe_workspace_size(p, m.MOE_WS_ROUTE)
+    off = _p(m, T=64, E=8, k=2, noise=False)
+    assert m._lib.moe_route_scores(ctypes.byref(off), ctypes.c_void_p(base)) is None
+    sw = _p(m, T=64, E=8, k=1, gating="switch", noise=False)
+    assert m._lib.moe_route_scores(ctypes.byref(sw), ctypes.c_void_p(base)) is None

@@ -271,3 +271,27 @@ def test_backward_full_switch(moe):
     eb = rel_err(host(g["dbias"])[cols], bw)
     log(f"  router columns {cols.tolist()}: dWg {eg:.2e} dbias {eb:.2e} ({time.time() - t0:.1f}s)")
     assert eg < tol and eb < tol
+
+
+@pytest.mark.parametrize("w", [CASES[1][0], CASES[2][0]], ids=lambda w: w.name)
+def test_route_backward_scores_or_redraw(moe, w):
+    """moe_route_backward given the forward's noisy scores (moe_route_scores) and given none
+    (the noise redrawn for every expert) agree bitwise: the same H either way."""
+    import torch
+    inp = I.make_inputs(w)
+    p = problem_for(moe, w)
+    L = moe.Layer(p, dev(inp["Wg"]), dev(inp["Wnoise"]), dev(inp["bias"]), dev(inp["W1"]),
+                  dev(inp["W2"]))
+    X = dev(inp["X"])
+    dY = dev(I.make_output_grad(w))
+    b = L.forward(X)
+    g = L.backward(X, dY, w_imp=0.3, w_load=0.6)
+    assert moe.moe_route_scores(p, b.ws_route) != 0
+    ref = {k: host(g[k]).copy() for k in ("dX", "dWg", "dWnoise", "dbias")}
+    moe.moe_route_backward(p, X, L.Wg, L.Wnoise, None, b.ids, b.gates, b.clean, b.noise_std,
+                           b.row_stats, g["dgates"], b.importance, b.load, 0.3, 0.6, dY, g["dXd"],
+                           b.pos, b.accepted, b.offsets, g["dX"], g["dWg"], g["dWnoise"],
+                           g["dbias"], g["ws"], scores=None)
+    torch.cuda.synchronize()
+    for k, v in ref.items():
+        assert (host(g[k]) == v).all(), k
