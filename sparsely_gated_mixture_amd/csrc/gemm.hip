@@ -215,6 +215,25 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
     // each 32x32 tile goes through a wave-private LDS tile so rows leave as 16-byte stores
     T* Ts = reinterpret_cast<T*>(&sA[0][0]) + wave * (32 * kTStride);
     constexpr int kSegs = 32 / V;  // 16-byte segments per tile row
+    constexpr int kH = 32 * kSegs / 64;  // 16-byte stores per lane per 32x32 tile
+    // mode 2: every mask vector this lane needs is requested before the first store, so the
+    // loads overlap each other instead of each waiting in turn
+    u32x4 mk[kEpi == 2 ? MB : 1][2][kH];
+    if constexpr (kEpi == 2) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int h = 0; h < kH; ++h) {
+            const int qd = lane + 64 * h;
+            const int grow = m * 32 + qd / kSegs, gcol = n0 + wave * 64 + j * 32 + (qd % kSegs) * V;
+            mk[m][j][h] = (grow < rows && gcol < g.N)
+                              ? *reinterpret_cast<const u32x4*>(static_cast<const T*>(g.mask) +
+                                                                static_cast<int64_t>(r0 + grow) * g.N + gcol)
+                              : u32x4{0u, 0u, 0u, 0u};
+          }
+    }
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -229,7 +248,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
           Ts[acc_row(lane, i) * kTStride + (lane & 31)] = Elem<T>::from_f32(v);
         }
 #pragma unroll
-        for (int h = 0; h < 32 * kSegs / 64; ++h) {
+        for (int h = 0; h < kH; ++h) {
           const int qd = lane + 64 * h;
           const int row = qd / kSegs, seg = qd % kSegs;
           u32x4 v = *reinterpret_cast<const u32x4*>(&Ts[row * kTStride + seg * V]);
@@ -237,9 +256,8 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
           if (grow < rows && gcol < g.N) {
             const int64_t o = static_cast<int64_t>(r0 + grow) * g.N + gcol;
             if constexpr (kEpi == 2) {  // the mask's 16 bytes at the same place: zero where <= 0
-              const u32x4 mk = *reinterpret_cast<const u32x4*>(static_cast<const T*>(g.mask) + o);
               T* ve = reinterpret_cast<T*>(&v);
-              const T* me = reinterpret_cast<const T*>(&mk);
+              const T* me = reinterpret_cast<const T*>(&mk[m][j][h]);
 #pragma unroll
               for (int q = 0; q < V; ++q) {
                 if (!(Elem<T>::to_f32(me[q]) > 0.f)) ve[q] = T(0);
