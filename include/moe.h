@@ -1,6 +1,7 @@
 /*
  * moe.h -- C ABI of the MI355X (gfx950) sparsely-gated Mixture-of-Experts
- * layer, forward pass.
+ * layer: forward pass (flat, hierarchical and batchwise gates) and backward pass
+ * (noisy top-k and Switch gates).
  *
  * Pages cited (by title; sections as the pages name them):
  *   [OLNN]   "Outrageously Large Neural Networks: The Sparsely-Gated

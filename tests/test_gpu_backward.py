@@ -38,6 +38,7 @@ CASES = [
     (_w("b_ragged", 133, 37, 5, 2, 21, "f32", 1.0, 46), 0.2, 0.3, False),
     (_w("b_split_f32", 1500, 48, 8, 2, 32, "f32", 1.0, 47), 0.2, 0.3, True),
     (_w("b_wideE", 300, 32, 3000, 2, 16, "f32", 0.0, 48), 0.1, 0.1, False),
+    (_w("b_emax_kmax", 200, 32, 4096, 8, 16, "f32", 1.5, 49), 0.1, 0.1, True),
     (_w("b_medium", 2048, 256, 16, 2, 512, "bf16", 1.0, 45), 0.01, 0.01, False),
 ]
 

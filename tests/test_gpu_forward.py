@@ -143,6 +143,9 @@ EDGE = [
     # E above 1024 (a multiple of 4): the per-expert column aux pass
     I.Workload("e1100", T=40, D=32, E=1100, k=2, H=16, act="f32", gating="noisy", noise=True,
                capacity_factor=0.0, seed=13),
+    # the largest E and k the library takes (E = 4096, k = 8) together, with capacity
+    I.Workload("emax_kmax", T=600, D=64, E=4096, k=8, H=32, act="bf16", gating="noisy",
+               noise=True, capacity_factor=2.0, seed=14),
 ]
 
 
