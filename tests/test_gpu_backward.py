@@ -296,3 +296,27 @@ def test_route_backward_scores_or_redraw(moe, w):
     torch.cuda.synchronize()
     for k, v in ref.items():
         assert (host(g[k]) == v).all(), k
+
+
+def test_backward_deterministic(moe):
+    """Three training steps at the full top2_bf16 size give bitwise-identical gradients:
+    every sum in the backward has a fixed order (no atomics)."""
+    import torch
+    from gpu_helpers import workload_inputs
+    w, inp = workload_inputs("top2_bf16")
+    p = problem_for(moe, w)
+    L = moe.Layer(p, dev(inp["Wg"]), dev(inp["Wnoise"]), dev(inp["bias"]), dev(inp["W1"]),
+                  dev(inp["W2"]))
+    X = dev(inp["X"])
+    dY = dev(I.make_output_grad(w))
+    first = None
+    for _ in range(3):
+        L.forward(X)
+        g = L.backward(X, dY, w_imp=0.1, w_load=0.1)
+        torch.cuda.synchronize()
+        keys = ("dX", "dWg", "dWnoise", "dbias", "dW1", "dW2")
+        if first is None:
+            first = {k: g[k].clone() for k in keys}  # compared on the device (dW1, dW2: 8.6 GB)
+        else:
+            for k in keys:
+                assert torch.equal(g[k], first[k]), k
