@@ -36,6 +36,8 @@ CASES = [
     (_w("b_nonoise", 150, 32, 8, 2, 40, "f32", 0.0, 43, noise=False), 0.5, 0.0, True),
     (_w("b_kE", 96, 32, 4, 4, 16, "f32", 0.0, 44), 0.1, 0.2, False),
     (_w("b_ragged", 133, 37, 5, 2, 21, "f32", 1.0, 46), 0.2, 0.3, False),
+    # bf16 widths that are not multiples of 8: the register-transpose weight-gradient kernel
+    (_w("b_bf16_ragged", 203, 36, 13, 3, 52, "bf16", 0.7, 50), 0.2, 0.3, True),
     (_w("b_split_f32", 1500, 48, 8, 2, 32, "f32", 1.0, 47), 0.2, 0.3, True),
     (_w("b_wideE", 300, 32, 3000, 2, 16, "f32", 0.0, 48), 0.1, 0.1, False),
     (_w("b_emax_kmax", 200, 32, 4096, 8, 16, "f32", 1.5, 49), 0.1, 0.1, True),
