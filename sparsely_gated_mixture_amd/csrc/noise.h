@@ -34,15 +34,74 @@ __device__ __forceinline__ void philox4x64_10(uint64_t& c0, uint64_t& c1, uint64
   }
 }
 
-// Box and Muller (1958): two independent N(0,1) from two uniforms, in fp64,
-// each rounded once to fp32. u1 in (0,1], u2 in [0,1).
+// sin(2 pi u) and cos(2 pi u) in fp64 for u = m 2^-53 in [0, 1). The argument needs no
+// general range reduction: 4u is exact, q = the nearest integer (the quadrant) and r = 4u - q
+// in [-1/2, 1/2] are exact, and x = r pi/2 (pi/2 split in two parts) lies in [-pi/4, pi/4],
+// where the Taylor series of sin to x^17 and of cos to x^18 leave a remainder below 1e-19.
+__device__ __forceinline__ void sincos_2pi(double u, double& s, double& c) {
+  const double u4 = u * 4.0;
+  const double q = rint(u4);
+  const double r = u4 - q;
+  const double x = fma(r, 1.5707963267948966, r * 6.123233995736766e-17);
+  const double x2 = x * x;
+  double ps = -1.0 / 355687428096000.0;  // -1/17!
+  ps = fma(ps, x2, 1.0 / 1307674368000.0);
+  ps = fma(ps, x2, -1.0 / 6227020800.0);
+  ps = fma(ps, x2, 1.0 / 39916800.0);
+  ps = fma(ps, x2, -1.0 / 362880.0);
+  ps = fma(ps, x2, 1.0 / 5040.0);
+  ps = fma(ps, x2, -1.0 / 120.0);
+  ps = fma(ps, x2, 1.0 / 6.0);
+  const double sx = fma(-x * x2, ps, x);
+  double pc = 1.0 / 6402373705728000.0;  // 1/18!
+  pc = fma(pc, x2, -1.0 / 20922789888000.0);
+  pc = fma(pc, x2, 1.0 / 87178291200.0);
+  pc = fma(pc, x2, -1.0 / 479001600.0);
+  pc = fma(pc, x2, 1.0 / 3628800.0);
+  pc = fma(pc, x2, -1.0 / 40320.0);
+  pc = fma(pc, x2, 1.0 / 720.0);
+  pc = fma(pc, x2, -1.0 / 24.0);
+  pc = fma(pc, x2, 0.5);
+  const double cx = fma(-x2, pc, 1.0);
+  const int qi = static_cast<int>(q) & 3;  // angle = q pi/2 + x
+  s = qi == 0 ? sx : qi == 1 ? cx : qi == 2 ? -sx : -cx;
+  c = qi == 0 ? cx : qi == 1 ? -sx : qi == 2 ? -cx : sx;
+}
+
+// log(n 2^-53) in fp64 for an integer n in [1, 2^53]: n = 2^e m with m in [sqrt(1/2),
+// sqrt(2)) (exact), and log m = 2 atanh(s) with s = (m - 1) / (m + 1), |s| < 0.1716: the
+// odd series of atanh to s^23 leaves a remainder below 1e-19; ln 2 in two parts.
+__device__ __forceinline__ double log_u53(uint64_t n) {
+  int e = 63 - __builtin_clzll(n);
+  double m = static_cast<double>(n) * __builtin_ldexp(1.0, -e);
+  if (m > 1.4142135623730951) {
+    m *= 0.5;
+    ++e;
+  }
+  const double sv = (m - 1.0) / (m + 1.0);
+  const double s2 = sv * sv;
+  double p = 1.0 / 23.0;
+  p = fma(p, s2, 1.0 / 21.0);
+  p = fma(p, s2, 1.0 / 19.0);
+  p = fma(p, s2, 1.0 / 17.0);
+  p = fma(p, s2, 1.0 / 15.0);
+  p = fma(p, s2, 1.0 / 13.0);
+  p = fma(p, s2, 1.0 / 11.0);
+  p = fma(p, s2, 1.0 / 9.0);
+  p = fma(p, s2, 1.0 / 7.0);
+  p = fma(p, s2, 1.0 / 5.0);
+  p = fma(p, s2, 1.0 / 3.0);
+  const double lm = fma(2.0 * sv * s2, p, 2.0 * sv);
+  const double k = static_cast<double>(e - 53);
+  return fma(k, 0.6931471805599453, fma(k, 2.3190468138462996e-17, lm));
+}
+
+// Box and Muller (1958): two independent N(0,1) from two uniforms, in fp64, each rounded
+// once to fp32. u1 = (a / 2^11 + 1) 2^-53 in (0,1], u2 = (b / 2^11) 2^-53 in [0,1).
 __device__ __forceinline__ void box_muller(uint64_t a, uint64_t b, float& g0, float& g1) {
-  const double u1 = (static_cast<double>(a >> 11) + 1.0) * 0x1p-53;
-  const double u2 = static_cast<double>(b >> 11) * 0x1p-53;
-  const double rho = sqrt(-2.0 * log(u1));
-  const double th = 6.283185307179586 * u2;
+  const double rho = sqrt(-2.0 * log_u53((a >> 11) + 1));
   double s, c;
-  sincos(th, &s, &c);
+  sincos_2pi(static_cast<double>(b >> 11) * 0x1p-53, s, c);
   g0 = static_cast<float>(rho * c);
   g1 = static_cast<float>(rho * s);
 }
