@@ -490,7 +490,10 @@ constexpr int kXcds = 8;
 // of A[r, m] B[r, n]; 4 waves in a 2 x 2 layout, each 64 x 64. The next stage's global loads
 // are issued before the current stage's MFMAs. Blocks are remapped so that each XCD (blocks
 // are dealt round-robin over the 8 XCDs) takes a contiguous run of (group, split, tile): a
-// group's operands then stay in one XCD's L2.
+// group's operands then stay in one XCD's L2. Within a group the tiles run along the
+// smaller output dimension first, so that the blocks in flight together cover all of the
+// smaller operand and a contiguous part of the larger one (each then comes from memory about
+// once, instead of the larger one once per sweep along the other dimension).
 template <typename T, bool kAligned, bool kRowSplit>
 __global__ __launch_bounds__(kThreads) void wgrad_gemm(WgradArgs a) {
   constexpr int VB = 16 / static_cast<int>(sizeof(T));   // elements per 16 bytes
@@ -515,7 +518,7 @@ __global__ __launch_bounds__(kThreads) void wgrad_gemm(WgradArgs a) {
   const int gs = logical / tiles;  // group * S + split
   const int g = gs / S, sp = gs - g * S;
   const int rem = logical - gs * tiles;
-  const int m0 = (rem / nt) * kWT, n0 = (rem % nt) * kWT;
+  const int m0 = (a.N > a.M ? rem % mt : rem / nt) * kWT, n0 = (a.N > a.M ? rem / mt : rem % nt) * kWT;
   const int gb = a.offsets[g], ge = a.offsets[g + 1];
   const int chunk = ((ge - gb + S - 1) / S + kWRows - 1) / kWRows * kWRows;
   const int r_begin = min(ge, gb + sp * chunk), r_end = min(ge, r_begin + chunk);
@@ -634,11 +637,13 @@ __global__ __launch_bounds__(kThreads) void wgrad_gemm(WgradArgs a) {
 // (ds_read_b64_tr_b16): in a group of 16 lanes whose lane 4j + q points at row k0 + j,
 // columns c0 + 4q .. c0 + 4q + 3, lane i receives column c0 + i of rows k0 .. k0 + 3. Two
 // such reads give a lane the 8 k-values of its MFMA operand, with no VALU transposes. A block
-// computes a 128 x 256 tile (waves 2 x 2, each 64 x 128); the next 64-row stage's loads are in
-// flight during the current stage's MFMAs. Rows past the end of the split are zeroed in A
-// only (a zero in either factor removes the product); columns past M / N are clamped reads
-// that only feed outputs never stored. LDS rows are padded by 32 bytes so that the four rows
-// of one transpose read fall in different banks.
+// computes a 128 x 256 tile (waves 2 x 2, each 64 x 128); the next 64-row stage's loads are
+// in flight during the current stage's MFMAs, and within a stage the transpose reads of the
+// next 16-row k-step are interleaved with the current one's MFMAs. Rows past the end of the
+// split are zeroed in A only (a zero in either factor removes the product); columns past
+// M / N are clamped reads that only feed outputs never stored. Tiles are ordered as in
+// wgrad_gemm. LDS rows are padded by 32 bytes so that the four rows of one transpose read
+// fall in different banks.
 typedef short v4s16 __attribute__((ext_vector_type(4)));
 constexpr int kTrRow = kWT * 2 + 32;  // LDS bytes per k row: 128 bf16 + 32 pad (bank rotation)
 
@@ -668,7 +673,7 @@ __global__ __launch_bounds__(kThreads) void wgrad_gemm_tr(WgradArgs a) {
   const int gs = logical / tiles;
   const int g = gs / S, sp = gs - g * S;
   const int rem = logical - gs * tiles;
-  const int m0 = (rem / nt) * kWT, n0 = (rem % nt) * kTN2;
+  const int m0 = (a.N > a.M ? rem % mt : rem / nt) * kWT, n0 = (a.N > a.M ? rem / mt : rem % nt) * kTN2;
   const int gb = a.offsets[g], ge = a.offsets[g + 1];
   const int chunk = ((ge - gb + S - 1) / S + kWRows - 1) / kWRows * kWRows;
   const int r_begin = min(ge, gb + sp * chunk), r_end = min(ge, r_begin + chunk);
@@ -709,6 +714,23 @@ __global__ __launch_bounds__(kThreads) void wgrad_gemm_tr(WgradArgs a) {
   const int wm = wave >> 1, wn = wave & 1;  // wave tile 64 (m) x 128 (n)
   const int gq = lane >> 4, jr = (lane >> 2) & 3, qc = lane & 3;
   const int rowq = 8 * (gq >> 1) + jr, colq = 16 * (gq & 1) + 4 * qc;
+  // the wave's operand fragments of k-step ks (16 rows of the stage)
+  auto frags = [&](int ks, u32x4 (&fa)[2], u32x4 (&fb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int oa = (ks * 16 + rowq) * kTrRow + (wm * 64 + i * 32 + colq) * 2;
+      const unsigned long long a0 = tr_read(sA, oa), a1 = tr_read(sA, oa + 4 * kTrRow);
+      fa[i] = u32x4{static_cast<unsigned>(a0), static_cast<unsigned>(a0 >> 32),
+                    static_cast<unsigned>(a1), static_cast<unsigned>(a1 >> 32)};
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ob = (ks * 16 + rowq) * kTrRowB + (wn * 128 + j * 32 + colq) * 2;
+      const unsigned long long b0 = tr_read(sB, ob), b1 = tr_read(sB, ob + 4 * kTrRowB);
+      fb[j] = u32x4{static_cast<unsigned>(b0), static_cast<unsigned>(b0 >> 32),
+                    static_cast<unsigned>(b1), static_cast<unsigned>(b1 >> 32)};
+    }
+  };
   f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -721,40 +743,48 @@ __global__ __launch_bounds__(kThreads) void wgrad_gemm_tr(WgradArgs a) {
     stash(rs);
     __syncthreads();
     if (rs + kWRows < r_end) load(rs + kWRows);
+    // two fragment sets: the reads of k-step ks + 1 are issued between k-step ks's MFMAs
+    u32x4 fa[2][2], fb[2][4];
+    frags(0, fa[0], fb[0]);
 #pragma unroll
     for (int ks = 0; ks < kWRows / 16; ++ks) {
-      u32x4 fa[2], fb[4];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int oa = (ks * 16 + rowq) * kTrRow + (wm * 64 + i * 32 + colq) * 2;
-        const unsigned long long a0 = tr_read(sA, oa), a1 = tr_read(sA, oa + 4 * kTrRow);
-        fa[i] = u32x4{static_cast<unsigned>(a0), static_cast<unsigned>(a0 >> 32),
-                      static_cast<unsigned>(a1), static_cast<unsigned>(a1 >> 32)};
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ob = (ks * 16 + rowq) * kTrRowB + (wn * 128 + j * 32 + colq) * 2;
-        const unsigned long long b0 = tr_read(sB, ob), b1 = tr_read(sB, ob + 4 * kTrRowB);
-        fb[j] = u32x4{static_cast<unsigned>(b0), static_cast<unsigned>(b0 >> 32),
-                      static_cast<unsigned>(b1), static_cast<unsigned>(b1 >> 32)};
-      }
+      const int c = ks & 1;
+      if (ks + 1 < kWRows / 16) frags(ks + 1, fa[c ^ 1], fb[c ^ 1]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = wmma<uint16_t>(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = wmma<uint16_t>(fb[c][j], fa[c][i], acc[i][j]);
     }
+    // the order the scheduler keeps: the first k-step's 12 transpose reads, then per k-step
+    // one MFMA after each pair of the next k-step's reads, and the last k-step's MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+    for (int ks = 0; ks < kWRows / 16 - 1; ++ks) {
+#pragma unroll
+      for (int x = 0; x < 6; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __syncthreads();
   }
+  // fp32 output tile: the MFMAs take B's fragment as their first operand, so the accumulator
+  // holds the tile transposed: lane l has C[m = .. + l % 32][n = .. + 8 (t / 4) + 4 (l / 32)
+  // + t % 4], four consecutive n per register quad, stored as one 16-byte vector
   float* C = a.C + static_cast<int64_t>(gs) * a.M * a.N;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 128 + j * 32 + (lane & 31);
+      const int m = m0 + wm * 64 + i * 32 + (lane & 31);
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int m = m0 + wm * 64 + i * 32 + acc_row(lane, t);
-        if (m < a.M && n < a.N) C[static_cast<int64_t>(m) * a.N + n] = acc[i][j][t];
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
+        if (m < a.M && n < a.N)
+          *reinterpret_cast<f32x4*>(C + static_cast<int64_t>(m) * a.N + n) =
+              f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
       }
     }
 }
@@ -835,11 +865,15 @@ moe_status combine_backward_launch(const Dims& d, const void* dY, const void* Z,
 moe_status wgrad_launch(const Dims& d, const void* A, const void* B, const int32_t* offsets, int G,
                         int M, int N, float* C, hipStream_t stream, int splits) {
   WgradArgs a{A, B, offsets, C, G, M, N, splits};
-  const bool tr = d.dtype == MOE_BF16 && M % 8 == 0 && N % 8 == 0;  // the transpose-read kernel
+  // rows of 16-byte multiples from 16-byte aligned bases: vector loads and stores
+  const bool vec = M % 8 == 0 && N % 8 == 0 &&
+                   (reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B) |
+                    reinterpret_cast<uintptr_t>(C)) % 16 == 0;
+  const bool tr = d.dtype == MOE_BF16 && vec;  // the transpose-read kernel
   const int64_t blocks = static_cast<int64_t>(G) * splits * ceil_div(M, kWT) * ceil_div(N, tr ? kTN2 : kWT);
   if (blocks > 0x7fffffffLL - kXcds) return MOE_ERR_UNSUPPORTED;
   const int grid = static_cast<int>(ceil_div64(blocks, kXcds) * kXcds);
-  const bool aligned = M % 8 == 0 && N % 8 == 0;  // multiples of 16 bytes for either dtype
+  const bool aligned = vec;
   const bool split = splits > 1;
 #define MOE_WGRAD(TY, AL, SP) wgrad_gemm<TY, AL, SP><<<grid, kThreads, 0, stream>>>(a)
   if (d.dtype == MOE_BF16) {
