@@ -20,6 +20,10 @@
  *   - All tensor pointers are DEVICE pointers, row-major, densely packed, owned
  *     by the caller. The library never allocates device memory; scratch comes
  *     from the caller as `workspace` (size from moe_workspace_size).
+ *   - Every tensor and workspace pointer (also those inside moe_hier_state and
+ *     moe_batchwise_state) is 16-byte aligned, or NULL where NULL is allowed:
+ *     rows move as 16-byte vectors. hipMalloc and the PyTorch allocator give
+ *     256-byte alignment; a misaligned pointer is MOE_ERR_INVALID_ARG.
  *   - `hip_stream` is a hipStream_t passed as void* (NULL = default stream).
  *     Every entry point only enqueues work on that stream and returns; it never
  *     synchronises. Counts and offsets stay on the device.

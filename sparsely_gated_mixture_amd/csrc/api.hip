@@ -81,6 +81,25 @@ static int* nonfinite_flag(const moe_problem* p) {
   return ptrs[dev];
 }
 
+// Every tensor and workspace pointer given to an entry point must be 16-byte aligned (NULL
+// passes): the kernels move rows and packed weights as 16-byte vectors. hipMalloc and the
+// PyTorch allocator return 256-byte aligned memory; a view at an odd element offset is
+// rejected here instead of being read unaligned.
+template <typename... P>
+static bool aligned16(P... ptrs) {
+  return ((reinterpret_cast<uintptr_t>(ptrs) % 16 == 0) && ...);
+}
+#define MOE_ALIGNED(...)                                     \
+  do {                                                       \
+    if (!aligned16(__VA_ARGS__)) return MOE_ERR_INVALID_ARG; \
+  } while (0)
+
+static bool hier_state_aligned(const moe_hier_state* st) {
+  return aligned16(st->ids_p, st->gates_p, st->clean_p, st->std_p, st->row_stats_p, st->pos_p,
+                   st->accepted_p, st->counts_p, st->offsets_p, st->row_token_p, st->clean_s,
+                   st->std_s, st->row_stats_s, st->ids_s, st->gates_s);
+}
+
 // Hierarchical options on top of a valid flat problem.
 static moe_status validate_hier(const moe_problem* p, const moe_hier* h, Dims* d) {
   MOE_STATUS_TRY(validate(p, d));
@@ -155,6 +174,7 @@ moe_status moe_route(const moe_problem* p, const void* X, const float* Wg, const
   MOE_TRY(validate_topk(p, &d));
   const bool noise = d.gating == MOE_GATE_NOISY_TOPK && d.noise;
   if (!X || !Wg || !ids || !gates || !clean) return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(X, Wg, Wnoise, bias, eps, ids, gates, clean, noise_std, row_stats, workspace);
   if (noise && (!Wnoise || !noise_std)) return MOE_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < route_workspace(d)) return MOE_ERR_WORKSPACE;
   int* flag;
@@ -170,6 +190,7 @@ moe_status moe_dispatch(const moe_problem* p, const void* X, const int32_t* ids,
   MOE_TRY(validate_topk(p, &d));
   if (!X || !ids || !pos || !accepted || !counts || !offsets || !row_token || !Xd)
     return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(X, ids, pos, accepted, counts, offsets, row_token, Xd, workspace);
   if (!workspace || workspace_bytes < dispatch_workspace(d)) return MOE_ERR_WORKSPACE;
   return dispatch_launch(d, X, ids, pos, accepted, counts, offsets, row_token, Xd, workspace,
                          as_stream(hip_stream));
@@ -180,6 +201,7 @@ moe_status moe_pack_expert_weights(const moe_problem* p, const void* W1, const v
   Dims d;
   MOE_TRY(validate(p, &d));
   if ((W1 && !W1p) || (W2 && !W2p) || (!W1 && !W2)) return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(W1, W2, W1p, W2p);
   if (W1) MOE_TRY(pack_launch(d, 1, W1, W1p, as_stream(hip_stream)));
   if (W2) MOE_TRY(pack_launch(d, 2, W2, W2p, as_stream(hip_stream)));
   return MOE_OK;
@@ -191,6 +213,7 @@ moe_status moe_grouped_gemm(const moe_problem* p, int layer, const void* A, cons
   MOE_TRY(validate(p, &d));
   if (layer != 1 && layer != 2) return MOE_ERR_INVALID_ARG;
   if (!A || !Wp || !offsets || !C) return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(A, Wp, offsets, C);
   int* flag = nullptr;
   if (layer == 2) MOE_TRY(flag_for(p, &flag));
   return gemm_launch(d, layer, A, Wp, offsets, C, flag, as_stream(hip_stream));
@@ -201,6 +224,7 @@ moe_status moe_expert_ffn(const moe_problem* p, const void* Xd, const void* W1p,
   Dims d;
   MOE_TRY(validate(p, &d));
   if (!Xd || !W1p || !W2p || !offsets || !Hd || !Z) return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(Xd, W1p, W2p, offsets, Hd, Z);
   int* flag;
   MOE_TRY(flag_for(p, &flag));
   MOE_TRY(gemm_launch(d, 1, Xd, W1p, offsets, Hd, nullptr, as_stream(hip_stream)));
@@ -213,6 +237,7 @@ moe_status moe_combine(const moe_problem* p, const void* Z, const int32_t* ids, 
   Dims d;
   MOE_TRY(validate_topk(p, &d));
   if (!Z || !ids || !gates || !pos || !accepted || !offsets || !Y) return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(Z, ids, gates, pos, accepted, offsets, residual, Y);
   int* flag;
   MOE_TRY(flag_for(p, &flag));
   return combine_launch(d, Z, ids, gates, pos, accepted, offsets, residual, Y, flag,
@@ -227,6 +252,7 @@ moe_status moe_aux_loss(const moe_problem* p, const int32_t* ids, const float* g
   MOE_TRY(validate_topk(p, &d));
   const bool noise = d.gating == MOE_GATE_NOISY_TOPK && d.noise;
   if (!ids || !gates || !clean || !counts || !out) return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(ids, gates, clean, noise_std, row_stats, counts, importance, load, out, workspace);
   if (noise && (!noise_std || !row_stats)) return MOE_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < aux_workspace(d)) return MOE_ERR_WORKSPACE;
   return aux_launch(d, ids, gates, clean, noise_std, row_stats, counts, importance, load, out,
@@ -251,6 +277,8 @@ moe_status moe_route_hier(const moe_problem* p, const moe_hier* h, const void* X
   MOE_TRY(validate_hier(p, h, &d));
   const bool noise = d.noise != 0;
   if (!X || !Wpg || !Wsg || !ids || !gates || !st) return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(X, Wpg, Wpn, Wsg, Wsn, ids, gates, workspace);
+  if (!hier_state_aligned(st)) return MOE_ERR_INVALID_ARG;
   if (noise && (!Wpn || !Wsn || !st->std_p || !st->std_s)) return MOE_ERR_INVALID_ARG;
   if (!st->ids_p || !st->gates_p || !st->clean_p || !st->row_stats_p || !st->pos_p ||
       !st->accepted_p || !st->counts_p || !st->offsets_p || !st->row_token_p || !st->clean_s ||
@@ -271,6 +299,8 @@ moe_status moe_aux_loss_hier(const moe_problem* p, const moe_hier* h, const moe_
   MOE_TRY(validate_hier(p, h, &d));
   const bool noise = d.noise != 0;
   if (!st || !out) return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(importance, load, out, workspace);
+  if (!hier_state_aligned(st)) return MOE_ERR_INVALID_ARG;
   if (noise && (!st->std_p || !st->std_s)) return MOE_ERR_INVALID_ARG;
   if (!st->ids_p || !st->gates_p || !st->clean_p || !st->row_stats_p || !st->counts_p ||
       !st->offsets_p || !st->row_token_p || !st->clean_s || !st->row_stats_s || !st->ids_s ||
@@ -288,7 +318,9 @@ static moe_status validate_batchwise(const moe_problem* p, Dims* d) {
 
 static bool batchwise_state_ok(const moe_batchwise_state* st) {
   return st && st->probs_t && st->sel && st->offsets && st->mask && st->tok_count && st->tok_off &&
-         st->tok_row && st->tok_gate && st->slot_pair;
+         st->tok_row && st->tok_gate && st->slot_pair &&
+         aligned16(st->probs_t, st->sel, st->offsets, st->mask, st->tok_count, st->tok_off,
+                   st->tok_row, st->tok_gate, st->slot_pair);
 }
 
 int32_t moe_batchwise_m(const moe_problem* p) {
@@ -312,6 +344,7 @@ moe_status moe_route_batchwise(const moe_problem* p, const void* X, const float*
   Dims d;
   MOE_TRY(validate_batchwise(p, &d));
   if (!X || !Wg || !clean || !batchwise_state_ok(st)) return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(X, Wg, bias, clean, workspace);
   if (!workspace || workspace_bytes < batchwise_route_workspace(d)) return MOE_ERR_WORKSPACE;
   int* flag;
   MOE_TRY(flag_for(p, &flag));
@@ -323,6 +356,7 @@ moe_status moe_dispatch_batchwise(const moe_problem* p, const void* X,
   Dims d;
   MOE_TRY(validate_batchwise(p, &d));
   if (!X || !Xd || !batchwise_state_ok(st)) return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(X, Xd);
   return batchwise_dispatch_launch(d, X, st, Xd, as_stream(hip_stream));
 }
 
@@ -331,6 +365,7 @@ moe_status moe_combine_batchwise(const moe_problem* p, const void* Z, const moe_
   Dims d;
   MOE_TRY(validate_batchwise(p, &d));
   if (!Z || !Y || !batchwise_state_ok(st)) return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(Z, residual, Y);
   int* flag;
   MOE_TRY(flag_for(p, &flag));
   return batchwise_combine_launch(d, Z, st, residual, Y, flag, as_stream(hip_stream));
@@ -342,6 +377,7 @@ moe_status moe_aux_loss_batchwise(const moe_problem* p, const moe_batchwise_stat
   Dims d;
   MOE_TRY(validate_batchwise(p, &d));
   if (!out || !batchwise_state_ok(st)) return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(thresholds, importance, out, workspace);
   if (!workspace || workspace_bytes < batchwise_aux_workspace(d)) return MOE_ERR_WORKSPACE;
   return batchwise_aux_launch(d, st, thresholds, importance, out, workspace, as_stream(hip_stream));
 }
@@ -359,6 +395,7 @@ moe_status moe_pack_expert_weights_t(const moe_problem* p, const void* W1, const
   Dims d;
   MOE_TRY(validate(p, &d));
   if ((W1 && !W1t) || (W2 && !W2t) || (!W1 && !W2)) return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(W1, W2, W1t, W2t);
   if (W2) MOE_TRY(pack_launch(d, 3, W2, W2t, as_stream(hip_stream)));
   if (W1) MOE_TRY(pack_launch(d, 4, W1, W1t, as_stream(hip_stream)));
   return MOE_OK;
@@ -372,6 +409,7 @@ moe_status moe_combine_backward(const moe_problem* p, const void* dY, const void
   MOE_TRY(validate_backward(p, &d));
   if (!dY || !Z || !ids || !gates || !pos || !accepted || !offsets || !dZ || !dgates)
     return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(dY, Z, ids, gates, pos, accepted, offsets, dZ, dgates);
   return combine_backward_launch(d, dY, Z, ids, gates, pos, accepted, offsets, dZ, dgates,
                                  as_stream(hip_stream));
 }
@@ -383,6 +421,7 @@ moe_status moe_expert_ffn_backward(const moe_problem* p, const void* Xd, const v
   Dims d;
   MOE_TRY(validate_backward(p, &d));
   if (!Xd || !Hd || !dZ || !W1t || !W2t || !offsets || !dHp || !dXd) return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(Xd, Hd, dZ, W1t, W2t, offsets, dHp, dXd, dW1, dW2);
   return ffn_backward_launch(d, Xd, Hd, dZ, W1t, W2t, offsets, dHp, dXd, dW1, dW2,
                              as_stream(hip_stream));
 }
@@ -396,6 +435,7 @@ moe_status moe_expert_ffn_backward_recompute(const moe_problem* p, const void* X
   MOE_TRY(validate_backward(p, &d));
   if (!Xd || !W1p || !dZ || !W1t || !W2t || !offsets || !Hd_scratch || !dHp || !dXd)
     return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(Xd, W1p, dZ, W1t, W2t, offsets, Hd_scratch, dHp, dXd, dW1, dW2);
   const hipStream_t s = as_stream(hip_stream);
   MOE_TRY(gemm_launch(d, 1, Xd, W1p, offsets, Hd_scratch, nullptr, s));
   return ffn_backward_launch(d, Xd, Hd_scratch, dZ, W1t, W2t, offsets, dHp, dXd, dW1, dW2, s);
@@ -408,6 +448,7 @@ moe_status moe_expert_weight_grad(const moe_problem* p, int32_t which, const voi
   MOE_TRY(validate_backward(p, &d));
   if (which != 1 && which != 2) return MOE_ERR_INVALID_ARG;
   if (!A || !B || !offsets || !C) return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(A, B, offsets, C);
   return which == 1 ? wgrad_launch(d, A, B, offsets, d.E, d.D, d.H, C, as_stream(hip_stream))
                     : wgrad_launch(d, A, B, offsets, d.E, d.H, d.D, C, as_stream(hip_stream));
 }
@@ -442,6 +483,9 @@ moe_status moe_route_backward(const moe_problem* p, const void* X, const float* 
   if (!X || !Wg || !ids || !gates || !clean || !row_stats || !dgates || !dXd || !pos ||
       !accepted || !offsets || !dX || !dWg)
     return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(X, Wg, Wnoise, eps, scores, ids, gates, clean, noise_std, row_stats, dgates,
+              importance, load, dY_residual, dXd, pos, accepted, offsets, dX, dWg, dWnoise, dbias,
+              workspace);
   if (noise && (!Wnoise || !noise_std || !dWnoise)) return MOE_ERR_INVALID_ARG;
   if (w_imp != 0.f && !importance) return MOE_ERR_INVALID_ARG;
   if (w_load != 0.f && noise && !load) return MOE_ERR_INVALID_ARG;
@@ -466,6 +510,8 @@ moe_status moe_route_backward_switch(const moe_problem* p, const void* X, const 
   if (!X || !Wg || !ids || !clean || !dgates || !dXd || !pos || !accepted || !offsets || !dX ||
       !dWg)
     return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(X, Wg, ids, clean, dgates, importance, counts, dY_residual, dXd, pos, accepted,
+              offsets, dX, dWg, dbias, workspace);
   if (w_imp != 0.f && !importance) return MOE_ERR_INVALID_ARG;
   if (w_switch != 0.f && !counts) return MOE_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < route_backward_workspace(d)) return MOE_ERR_WORKSPACE;

@@ -150,6 +150,41 @@ def test_hier_validation(m):
                                     fake, fake, fake, fake, 1 << 30, None) == -1
 
 
+
+def test_unaligned_pointers_rejected(m):
+    """A tensor pointer that is not 16-byte aligned is an argument error, returned before
+    anything is enqueued (each call below is otherwise complete; the fake addresses are never
+    dereferenced)."""
+    p = _p(m)
+    ok, bad = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1004)
+    big = 1 << 30
+
+    def route(i):  # X, Wg, Wnoise, bias, eps, ids, gates, clean, noise_std, row_stats, ws
+        a = [ok] * 11
+        a[i] = bad
+        return m._lib.moe_route(ctypes.byref(p), *a[:10], a[10], big, None)
+    for i in range(11):
+        assert route(i) == -1, i
+    a = [ok] * 9
+    a[7] = bad  # Xd
+    assert m._lib.moe_dispatch(ctypes.byref(p), *a, big, None) == -1
+    assert m._lib.moe_grouped_gemm(ctypes.byref(p), 1, ok, ok, ok, bad, None) == -1
+    assert m._lib.moe_expert_ffn(ctypes.byref(p), ok, ok, ok, ok, ok, bad, None) == -1
+    # residual (optional) misaligned
+    assert m._lib.moe_combine(ctypes.byref(p), ok, ok, ok, ok, ok, ok, bad, ok, None) == -1
+    assert m._lib.moe_pack_expert_weights(ctypes.byref(p), bad, None, ok, None, None) == -1
+    assert m._lib.moe_expert_weight_grad(ctypes.byref(p), 1, ok, ok, ok, bad, None) == -1
+    assert m._lib.moe_expert_weight_grad(ctypes.byref(p), 2, bad, ok, ok, ok, None) == -1
+    pb = _p(m, T=64, E=8, k=2, gating="batchwise", noise=False)
+    st = m.BatchwiseState(**{n: 0x1000 for n in m.BATCHWISE_STATE_FIELDS})
+    st.tok_gate = 0x1008
+    assert m._lib.moe_dispatch_batchwise(ctypes.byref(pb), ok, ctypes.byref(st), ok, None) == -1
+    ph, h = _p(m, T=64, E=8, k=2), m.hier(2, 1)
+    hs = m.HierState(**{n: 0x1000 for n in m.HIER_STATE_FIELDS})
+    hs.clean_s = 0x1002
+    assert m._lib.moe_route_hier(ctypes.byref(ph), ctypes.byref(h), *([ok] * 7),
+                                 ctypes.byref(hs), ok, big, None) == -1
+
 def test_batchwise_validation(m):
     p = _p(m, T=64, E=8, k=2, gating="batchwise", noise=False)
     assert m.moe_batchwise_m(p) == 16

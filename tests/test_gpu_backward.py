@@ -322,3 +322,4 @@ def test_backward_deterministic(moe):
         else:
             for k in keys:
                 assert torch.equal(g[k], first[k]), k
+
