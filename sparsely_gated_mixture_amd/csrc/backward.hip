@@ -46,6 +46,15 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Lanes of one wave exchanging values through LDS: the wave executes in lockstep and its LDS
+// accesses complete in issue order, so it is enough to keep the compiler from moving memory
+// operations across this point.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
@@ -189,8 +198,9 @@ __global__ __launch_bounds__(kThreads) void gate_backward(GateArgs a) {
       dcl[e] = 0.f;
       dsd[e] = 0.f;
     }
-    __syncthreads();
+    wave_sync();
     // softmax backward over the kept scores (plus the importance term)
+    float nz = 0.f;  // lanes < k: the noise of the lane's kept expert
     {
       float gj = 0.f, dgj = 0.f;
       int ej = 0;
@@ -204,10 +214,13 @@ __global__ __launch_bounds__(kThreads) void gate_backward(GateArgs a) {
       if (live && lane < k) {
         const float dh = gj * (dgj - s);
         dcl[ej] += dh;  // a row's experts are distinct: no two lanes share ej
-        if (a.noise) dsd[ej] += dh * noise_at(a, t, base, ej);
+        if (a.noise) {
+          nz = noise_at(a, t, base, ej);
+          dsd[ej] += dh * nz;
+        }
       }
     }
-    __syncthreads();
+    wave_sync();
     // load term: P(t,e) = Phi((clean - thr) / std) for every expert; the threshold is v_{k+1}
     // for the kept experts and v_k for the others. A lane takes 4 consecutive experts (one
     // Philox draw) at a time.
@@ -265,17 +278,18 @@ __global__ __launch_bounds__(kThreads) void gate_backward(GateArgs a) {
         }
       }
     }
-    __syncthreads();
+    const float nz_k = __shfl(nz, k - 1);  // v_k's expert is lane k - 1's kept expert
+    wave_sync();
     if (load_term && live && lane == 0) {
       const int ik = rid[k - 1];  // v_k: the last kept expert
       dcl[ik] -= s_out;
-      dsd[ik] -= s_out * noise_at(a, t, base, ik);
+      dsd[ik] -= s_out * nz_k;
       if (k < E && bi < E) {  // v_{k+1}: the best other expert
         dcl[bi] -= s_in;
         dsd[bi] -= s_in * noise_at(a, t, base, bi);
       }
     }
-    __syncthreads();
+    wave_sync();
     // write [dclean | draw]; d raw = d std * sigmoid(raw) = d std * (1 - exp(-std))
     if (live) {
       const int64_t o = static_cast<int64_t>(t) * a.ldc;
