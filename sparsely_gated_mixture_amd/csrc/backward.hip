@@ -1,4 +1,4 @@
-// Backward pass of the noisy top-k MoE layer.
+// Backward pass of the MoE layer with a per-token gate (noisy top-k or Switch top-1).
 //
 // The pages' purpose is training: "Outrageously Large Neural Networks" summary,
 // section 3.4 (k > 1 so the gate receives gradient through the softmax over the
@@ -8,9 +8,13 @@
 // proportion to their gates, and masked experts are absent from it. The
 // selection and the capacity mask are piecewise constant and held fixed, as is
 // the noise sample (H = clean + eps * Softplus(raw)); the load estimator's
-// threshold is another expert's score and passes its gradient to it.
+// threshold is another expert's score and passes its gradient to it. The
+// "Switch Transformer" explainer, steps 2 and 8: the Switch gate is the selected
+// expert's full-softmax probability, and the balancing term reaches every
+// probability through its batch mean (the dispatch fractions are counts, fixed).
 //
-// Objective: <Y, dY> + w_imp CV^2(Importance) + w_load CV^2(Load).
+// Objective: <Y, dY> + w_imp CV^2(Importance) + w_load CV^2(Load) (noisy top-k) or
+// <Y, dY> + w_imp CV^2(Importance) + w_switch E sum_e f_e Pbar_e (Switch).
 //
 // Kernels:
 //   cb_backward      a wave per token: dZ[row] = g * dY[t] for each accepted
@@ -19,13 +23,16 @@
 //   gate_backward    4 token rows per wave, one at a time: softmax backward over
 //                    the kept scores (plus the importance term), the load term of
 //                    every expert through Phi (with the threshold's share going to
-//                    the k-th / (k+1)-th expert), noise redrawn by Philox, then
-//                    d raw = d std * sigmoid(raw); writes [dclean | draw] [T, 2E]
-//                    and per-block sums of dclean (the bias gradient)
+//                    the k-th / (k+1)-th expert; their noise redrawn by Philox),
+//                    then d raw = d std * sigmoid(raw); writes [dclean | draw]
+//                    [T, 2E] and per-block sums of dclean (the bias gradient)
+//   switch_dprob,    the Switch gate: the balancing term's share of every
+//   switch_gate_backward  probability, then per row dclean = p (dp - <p, dp>)
 //   column_sums      the per-block sums, in two passes, in a fixed order
 //   wgrad_gemm_tr    per group (and row split), C = A^T B over the group's rows (fp32
-//                    output), bf16: operands row-major in LDS, transposed by the LDS
-//                    transpose read into MFMA fragments; 128 x 256 tiles; fixed row order
+//                    output), bf16 with widths that are multiples of 8: operands
+//                    row-major in LDS, transposed by the LDS transpose read into MFMA
+//                    fragments; 128 x 256 tiles; fixed row order
 //   wgrad_gemm       the same for fp32 and for widths that are not multiples of 8:
 //                    4x4 / 8x8 register transposes put both operands k-contiguous in
 //                    LDS; 128 x 128 tiles. Either way the router's weight gradient (one
