@@ -248,6 +248,23 @@ def bench_backward(args, torch, w, inp, p, L, X, t_gen):
                                 for s_ in range(args.steps)]))
            for i, name in enumerate(stages)}
     step_ev = [events[s_][0].elapsed_time(events[s_][-1]) for s_ in range(args.steps)]
+
+    # Re-laying out the expert weights (W1, W2 into MFMA fragment order for the forward, their
+    # transposes for the backward) is needed once per weight update; the training step above
+    # takes the packed weights as given. Timed apart, median of 5.
+    def pack_ms(fn):
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+    repack = {"forward": pack_ms(lambda: moe.moe_pack_expert_weights(p, L.W1, L.W2, L.W1p, L.W2p)),
+              "transposed": pack_ms(lambda: moe.moe_pack_expert_weights_t(p, L.W1, L.W2, L.W1t,
+                                                                          L.W2t))}
     offs = b.offsets.cpu().numpy()
     A = int(offs[-1])
     U = int(np.count_nonzero(np.diff(offs)))
@@ -275,6 +292,7 @@ def bench_backward(args, torch, w, inp, p, L, X, t_gen):
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline("wgrad_gemm", flops, wg_bytes, wg_ms, peak, traffic),
         "forward_ms": fwd_ms, "backward_ms": bwd_ms, "stages_ms": per,
+        "weight_repack_ms_per_update": repack,
         "step_ms_events": {"p10": float(np.percentile(step_ev, 10)),
                            "p50": float(np.median(step_ev)),
                            "p90": float(np.percentile(step_ev, 90))},

@@ -322,6 +322,52 @@ __global__ void pack_weights(const T* __restrict__ W, int E, int K, int N, int N
   out[idx] = *reinterpret_cast<const uint4*>(v);
 }
 
+// The kTrans source ([E, N, K]: a lane's 16-byte operand is contiguous in a row) through LDS:
+// a block takes 32 rows (one column block) x 16 k-steps, reads them as whole row segments
+// (512 bytes a row, 16 bytes a thread), and writes the 16 fragments in slot order (16 bytes
+// a thread, 1 KB a wave). kVec: K % V == 0 and W 16-byte aligned (vector loads).
+constexpr int kPackKs = 16;  // k-steps per block
+template <typename T, bool kVec>
+__global__ __launch_bounds__(256) void pack_weights_t(const T* __restrict__ W, int E, int K, int N,
+                                                      int NB, int KS, uint4* __restrict__ out) {
+  constexpr int V = Elem<T>::kVec;
+  constexpr int kRowBytes = kPackKs * 2 * V * static_cast<int>(sizeof(T));  // 512
+  constexpr int kStride = kRowBytes + 16;
+  __shared__ __align__(16) unsigned char tile[32 * kStride];
+  const int kc = blockIdx.x, nb = blockIdx.y, e = blockIdx.z;
+  const int k_base = kc * kPackKs * 2 * V;
+#pragma unroll
+  for (int p = 0; p < 32 * (kRowBytes / 16) / 256; ++p) {
+    const int c = threadIdx.x + 256 * p;
+    const int r = c / (kRowBytes / 16), seg = c % (kRowBytes / 16);
+    const int n = nb * 32 + r, k0 = k_base + seg * V;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (n < N) {
+      const T* row = W + (static_cast<int64_t>(e) * N + n) * K;
+      if (kVec) {
+        if (k0 < K) v = *reinterpret_cast<const uint4*>(row + k0);
+      } else {
+        T t[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) t[i] = k0 + i < K ? row[k0 + i] : T(0);
+        v = *reinterpret_cast<const uint4*>(t);
+      }
+    }
+    *reinterpret_cast<uint4*>(&tile[r * kStride + seg * 16]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < kPackKs * kWave / 256; ++p) {
+    const int sl = threadIdx.x + 256 * p;
+    const int ksl = sl / kWave, lane = sl % kWave;
+    const int ks = kc * kPackKs + ksl;
+    if (ks >= KS) break;  // uniform over the thread's remaining slots
+    const int r = lane & 31, kb = (ksl * 2 + (lane >> 5)) * V * static_cast<int>(sizeof(T));
+    out[((static_cast<int64_t>(e) * NB + nb) * KS + ks) * kWave + lane] =
+        *reinterpret_cast<const uint4*>(&tile[r * kStride + kb]);
+  }
+}
+
 constexpr int kBM = 128;
 
 }  // namespace
@@ -352,6 +398,21 @@ moe_status pack_launch(const Dims& d, int layer, const void* W, void* Wp, hipStr
   const int64_t total = static_cast<int64_t>(d.E) * NB * KS * kWave;
   const int grid = static_cast<int>(ceil_div64(total, 256));
   const bool tr = layer >= 3;
+  if (tr) {  // the LDS-tiled re-layout of an [E, N, K] source
+    const dim3 g3(ceil_div(KS, kPackKs), NB, d.E);
+    const int V = d.dtype == MOE_BF16 ? 8 : 4;
+    const bool vec = K % V == 0 && reinterpret_cast<uintptr_t>(W) % 16 == 0;
+    if (d.dtype == MOE_BF16) {
+      const auto* w = static_cast<const uint16_t*>(W);
+      if (vec) pack_weights_t<uint16_t, true><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
+      else pack_weights_t<uint16_t, false><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
+    } else {
+      const auto* w = static_cast<const float*>(W);
+      if (vec) pack_weights_t<float, true><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
+      else pack_weights_t<float, false><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
+    }
+    return launch_status();
+  }
   if (d.dtype == MOE_BF16) {
     const auto* w = static_cast<const uint16_t*>(W);
     if (tr) pack_weights<uint16_t, true><<<grid, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));

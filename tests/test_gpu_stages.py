@@ -281,6 +281,49 @@ def test_grouped_gemm_ragged(moe, act):
         assert rel_err(host(Z)[:T], ref2) < TOL[act]
 
 
+
+def _fragment_layout(B, V, KS):
+    """The packed operand layout moe.h states, from B [E, K, N]: slot (e, nb, ks, lane)
+    holds column nb*32 + lane%32, rows ks*2V + (lane//32)*V .. +V-1, zeros past K or N."""
+    E, K, N = B.shape
+    NB = -(-N // 32)
+    Bp = np.zeros((E, KS * 2 * V, NB * 32), dtype=B.dtype)
+    Bp[:, :K, :N] = B
+    # [E, ks, half, i, nb, col] -> [E, nb, ks, half, col, i]
+    t = Bp.reshape(E, KS, 2, V, NB, 32).transpose(0, 4, 1, 2, 5, 3)
+    return np.ascontiguousarray(t).reshape(E, NB, KS, 64, V)
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_weight_pack_layouts(moe, act):
+    """moe_pack_expert_weights (layers 1, 2) and moe_pack_expert_weights_t (layers 3, 4: the
+    transposes W2^T and W1^T for the backward) against the fragment layout built on the host,
+    bit-exact, with widths that are not multiples of the fragment (zero padding) and, for
+    D = 37, rows that are not whole 16-byte vectors."""
+    import torch
+    rng = np.random.default_rng(21)
+    for (E, D, H) in ((3, 40, 72), (2, 37, 100), (2, 256, 520)):
+        w = I.Workload("pk", T=8, D=D, E=E, k=1, H=H, act=act, gating="noisy", noise=False,
+                       capacity_factor=0.0, seed=0)
+        p = problem_for(moe, w)
+        cast = (lambda a: I.f32_to_bf16_bits(a)) if act == "bf16" else (lambda a: a)
+        W1 = cast(rng.standard_normal((E, D, H)).astype(np.float32))
+        W2 = cast(rng.standard_normal((E, H, D)).astype(np.float32))
+        V = 8 if act == "bf16" else 4
+        bufs = [torch.zeros(moe.moe_packed_weight_bytes(p, layer), dtype=torch.uint8,
+                            device="cuda") for layer in (1, 2, 3, 4)]
+        moe.moe_pack_expert_weights(p, dev(W1), dev(W2), bufs[0], bufs[1])
+        moe.moe_pack_expert_weights_t(p, dev(W1), dev(W2), bufs[3], bufs[2])  # W1t, W2t
+        # B of each layer as [E, K, N]: W1, W2, W2^T, W1^T
+        Bs = [W1, W2, W2.transpose(0, 2, 1), W1.transpose(0, 2, 1)]
+        for layer, (buf, B) in enumerate(zip(bufs, Bs), start=1):
+            K = B.shape[1]
+            KS = -(-K // (16 * V // 2)) * 4  # k stages of 128 bytes, 4 k-steps each
+            want = _fragment_layout(B, V, KS)
+            got = host(buf).view(B.dtype)
+            assert got.size == want.size, (layer, got.size, want.size)
+            assert (got.reshape(want.shape).view(np.uint8) == want.view(np.uint8)).all(), (layer, D, H)
+
 @pytest.mark.parametrize("name", ALL)
 def test_combine(moe, name):
     import torch
