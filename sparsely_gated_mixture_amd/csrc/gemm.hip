@@ -368,8 +368,6 @@ __global__ __launch_bounds__(256) void pack_weights_t(const T* __restrict__ W, i
   }
 }
 
-constexpr int kBM = 128;
-
 }  // namespace
 
 // ------------------------------------------------------------------ host side
@@ -425,22 +423,44 @@ moe_status pack_launch(const Dims& d, int layer, const void* W, void* Wp, hipStr
   return launch_status();
 }
 
-template <typename T, int kEpi>
+template <typename T, int BM, int kEpi>
 static void launch_k(const GemmArgs& g, int grid, size_t lds, hipStream_t stream) {
   constexpr int V = Elem<T>::kVec;
   const bool full = g.K % (128 / static_cast<int>(sizeof(T))) == 0;
   const bool vout = g.N % V == 0;
-  if (full && vout) grouped_gemm<T, kBM, kEpi, true, true><<<grid, kThreads, lds, stream>>>(g);
-  else if (full) grouped_gemm<T, kBM, kEpi, true, false><<<grid, kThreads, lds, stream>>>(g);
-  else if (vout) grouped_gemm<T, kBM, kEpi, false, true><<<grid, kThreads, lds, stream>>>(g);
-  else grouped_gemm<T, kBM, kEpi, false, false><<<grid, kThreads, lds, stream>>>(g);
+  if (full && vout) grouped_gemm<T, BM, kEpi, true, true><<<grid, kThreads, lds, stream>>>(g);
+  else if (full) grouped_gemm<T, BM, kEpi, true, false><<<grid, kThreads, lds, stream>>>(g);
+  else if (vout) grouped_gemm<T, BM, kEpi, false, true><<<grid, kThreads, lds, stream>>>(g);
+  else grouped_gemm<T, BM, kEpi, false, false><<<grid, kThreads, lds, stream>>>(g);
 }
 
-template <typename T>
+template <typename T, int BM>
 static void launch_typed(const GemmArgs& g, int layer, int grid, size_t lds, hipStream_t stream) {
-  if (layer == 1) launch_k<T, 1>(g, grid, lds, stream);
-  else if (g.mask) launch_k<T, 2>(g, grid, lds, stream);
-  else launch_k<T, 0>(g, grid, lds, stream);
+  if (layer == 1) launch_k<T, BM, 1>(g, grid, lds, stream);
+  else if (g.mask) launch_k<T, BM, 2>(g, grid, lds, stream);
+  else launch_k<T, BM, 0>(g, grid, lds, stream);
+}
+
+// Upper bound on the tiles of BM rows: per expert at most ceil(min(C,T)/BM) row tiles;
+// overall at most (rows + E*(BM-1))/BM.
+static int64_t gemm_tiles(const Dims& d, int N, int bm) {
+  const int64_t cap = std::min<int64_t>(d.C, d.T);
+  const int64_t by_expert = static_cast<int64_t>(d.E) * ceil_div64(cap, bm);
+  const int64_t by_rows = (d.max_rows + static_cast<int64_t>(d.E) * (bm - 1)) / bm;
+  return std::min(by_expert, by_rows) * ceil_div(N, kBN);
+}
+
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp, const int32_t* offsets,
@@ -459,21 +479,21 @@ moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp, 
   g.N = N;
   g.NB = ceil_div(N, 32);
   g.KS = gemm_ks(d, K);
-  // upper bound on row tiles: per expert at most ceil(min(C,T)/BM); overall at
-  // most (rows + E*(BM-1))/BM
-  const int64_t cap = std::min<int64_t>(d.C, d.T);
-  const int64_t by_expert = static_cast<int64_t>(d.E) * ceil_div64(cap, kBM);
-  const int64_t by_rows = (d.max_rows + static_cast<int64_t>(d.E) * (kBM - 1)) / kBM;
-  const int64_t mtiles = std::min(by_expert, by_rows);
-  const int64_t tiles = mtiles * ceil_div(N, kBN);
+  // 128-row tiles, or 64-row ones when the 128-row tiles would not give every CU's two block
+  // slots two tiles each (a small or narrow layer): twice the blocks then share the work
+  const int bm = gemm_tiles(d, N, 128) < 4LL * device_cus() ? 64 : 128;
+  const int64_t tiles = gemm_tiles(d, N, bm);
   const int64_t grid = ceil_div64(std::max<int64_t>(tiles, 1), kXcds) * kXcds;
   if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
   const size_t lds = (static_cast<size_t>(d.E) + 1) * sizeof(int);
   const int gr = static_cast<int>(grid);
-  if (d.dtype == MOE_BF16)
-    launch_typed<uint16_t>(g, layer, gr, lds, stream);
-  else
-    launch_typed<float>(g, layer, gr, lds, stream);
+  if (d.dtype == MOE_BF16) {
+    if (bm == 64) launch_typed<uint16_t, 64>(g, layer, gr, lds, stream);
+    else launch_typed<uint16_t, 128>(g, layer, gr, lds, stream);
+  } else {
+    if (bm == 64) launch_typed<float, 64>(g, layer, gr, lds, stream);
+    else launch_typed<float, 128>(g, layer, gr, lds, stream);
+  }
   return launch_status();
 }
 
