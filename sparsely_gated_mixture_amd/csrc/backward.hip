@@ -196,6 +196,18 @@ __global__ __launch_bounds__(kThreads) void gate_backward(GateArgs a) {
   float* acc = dsd + E;
   const bool load_term = a.noise && a.dload;
   for (int e = lane; e < E; e += 64) acc[e] = 0.f;
+  // The noise the gradient needs is drawn for the wave's rows together, so that one Philox and
+  // Box-Muller evaluation serves many lanes: lane it * k + j draws row it's j-th kept expert's
+  // noise here; the (k+1)-th expert's noise term of each row is applied after the loop (lane
+  // it keeps that row's pending term).
+  float nzk = 0.f;
+  if (a.noise && lane < kGateRowsPerWave * k) {
+    const int it = lane / k, j = lane - it * k;
+    const int t = (blockIdx.x * kGateRowsPerWave + it) * W + wave;
+    if (t < a.T) nzk = noise_at(a, t, static_cast<int64_t>(t) * E, a.ids[static_cast<int64_t>(t) * k + j]);
+  }
+  int pend_bi = -1, pend_t = 0;
+  float pend_s = 0.f, pend_d = 0.f;
   for (int it = 0; it < kGateRowsPerWave; ++it) {
     const int t = (blockIdx.x * kGateRowsPerWave + it) * W + wave;
     const bool live = t < a.T;
@@ -207,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void gate_backward(GateArgs a) {
     }
     wave_sync();
     // softmax backward over the kept scores (plus the importance term)
-    float nz = 0.f;  // lanes < k: the noise of the lane's kept expert
+    const float nz = __shfl(nzk, it * k + (lane < k ? lane : 0));  // lanes < k: their kept expert's
     {
       float gj = 0.f, dgj = 0.f;
       int ej = 0;
@@ -221,10 +233,7 @@ __global__ __launch_bounds__(kThreads) void gate_backward(GateArgs a) {
       if (live && lane < k) {
         const float dh = gj * (dgj - s);
         dcl[ej] += dh;  // a row's experts are distinct: no two lanes share ej
-        if (a.noise) {
-          nz = noise_at(a, t, base, ej);
-          dsd[ej] += dh * nz;
-        }
+        if (a.noise) dsd[ej] += dh * nz;
       }
     }
     wave_sync();
@@ -285,18 +294,23 @@ __global__ __launch_bounds__(kThreads) void gate_backward(GateArgs a) {
         }
       }
     }
-    const float nz_k = __shfl(nz, k - 1);  // v_k's expert is lane k - 1's kept expert
+    const float nz_k = __shfl(nzk, it * k + k - 1);  // v_k's expert is the k-th kept one
+    // v_{k+1}: the best other expert; its d std term (noise x s_in) is deferred
+    const bool defer = load_term && live && k < E && bi < E;
     wave_sync();
     if (load_term && live && lane == 0) {
       const int ik = rid[k - 1];  // v_k: the last kept expert
       dcl[ik] -= s_out;
       dsd[ik] -= s_out * nz_k;
-      if (k < E && bi < E) {  // v_{k+1}: the best other expert
-        dcl[bi] -= s_in;
-        dsd[bi] -= s_in * noise_at(a, t, base, bi);
-      }
+      if (defer) dcl[bi] -= s_in;
     }
     wave_sync();
+    if (defer && lane == it) {
+      pend_bi = bi;
+      pend_t = t;
+      pend_s = s_in;
+      pend_d = dsd[bi];
+    }
     // write [dclean | draw]; d raw = d std * sigmoid(raw) = d std * (1 - exp(-std))
     if (live) {
       const int64_t o = static_cast<int64_t>(t) * a.ldc;
@@ -304,16 +318,26 @@ __global__ __launch_bounds__(kThreads) void gate_backward(GateArgs a) {
         if (a.dtype == MOE_BF16) {
           uint16_t* d = static_cast<uint16_t*>(a.dcat);
           d[o + e] = f32_to_bf16(dcl[e]);
-          if (a.noise) d[o + E + e] = f32_to_bf16(dsd[e] * (1.f - expf(-a.std_in[base + e])));
+          if (a.noise && !(defer && e == bi))
+            d[o + E + e] = f32_to_bf16(dsd[e] * (1.f - expf(-a.std_in[base + e])));
         } else {
           float* d = static_cast<float*>(a.dcat);
           d[o + e] = dcl[e];
-          if (a.noise) d[o + E + e] = dsd[e] * (1.f - expf(-a.std_in[base + e]));
+          if (a.noise && !(defer && e == bi)) d[o + E + e] = dsd[e] * (1.f - expf(-a.std_in[base + e]));
         }
         acc[e] += dcl[e];
       }
     }
     // the next row clears this lane's own entries before its first barrier
+  }
+  // the deferred d raw of each row's (k+1)-th expert: its d std less s_in x its noise
+  if (pend_bi >= 0) {
+    const int64_t bt = static_cast<int64_t>(pend_t) * E;
+    const float v = pend_d - pend_s * noise_at(a, pend_t, bt, pend_bi);
+    const float r = v * (1.f - expf(-a.std_in[bt + pend_bi]));
+    const int64_t o = static_cast<int64_t>(pend_t) * a.ldc + E + pend_bi;
+    if (a.dtype == MOE_BF16) static_cast<uint16_t*>(a.dcat)[o] = f32_to_bf16(r);
+    else static_cast<float*>(a.dcat)[o] = r;
   }
   // bias gradient partial: each wave's rows in order, then the waves in order
   if (a.dbias_part) {
