@@ -42,7 +42,13 @@ CASES = [
     (_w("b_wideE", 300, 32, 3000, 2, 16, "f32", 0.0, 48), 0.1, 0.1, False),
     (_w("b_emax_kmax", 200, 32, 4096, 8, 16, "f32", 1.5, 49), 0.1, 0.1, True),
     (_w("b_medium", 2048, 256, 16, 2, 512, "bf16", 1.0, 45), 0.01, 0.01, False),
+    # degenerate layers: one token; one expert (k = E = 1: P = 1, the gate is constant);
+    # capacity 1 (almost every assignment dropped)
+    (_w("b_T1", 1, 16, 4, 2, 8, "f32", 0.0, 51), 0.2, 0.3, True),
+    (_w("b_E1", 64, 16, 1, 1, 8, "f32", 0.0, 52), 0.1, 0.1, True),
+    (_w("b_drop", 256, 24, 4, 2, 16, "bf16", 0.01, 53), 0.2, 0.2, False),
 ]
+BY_NAME = {c[0].name: c[0] for c in CASES}
 
 
 def _tol(w):
@@ -155,7 +161,8 @@ def test_backward_full_top2(moe):
     assert eg < tol and en < tol and eb < tol
 
 
-@pytest.mark.parametrize("w", [CASES[2][0], CASES[-1][0], CASES[5][0]], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [BY_NAME[n] for n in ("b_bf16", "b_medium", "b_ragged", "b_drop")],
+                         ids=lambda w: w.name)
 def test_recompute_hidden_matches_stored(moe, w):
     """Recomputing Hd in the backward (instead of keeping the forward's) gives bitwise the
     same gradients: the same kernel on the same inputs."""
@@ -276,7 +283,7 @@ def test_backward_full_switch(moe):
     assert eg < tol and eb < tol
 
 
-@pytest.mark.parametrize("w", [CASES[1][0], CASES[2][0]], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [BY_NAME[n] for n in ("b_f32_aux", "b_bf16")], ids=lambda w: w.name)
 def test_route_backward_scores_or_redraw(moe, w):
     """moe_route_backward given the forward's noisy scores (moe_route_scores) and given none
     (the noise redrawn for every expert) agree bitwise: the same H either way."""
