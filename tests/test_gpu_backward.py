@@ -200,6 +200,9 @@ SWITCH_CASES = [
     (_sw("s_f32_bal", 200, 40, 6, 24, "f32", 0.7, 51), 0.2, 0.5, True),
     (_sw("s_bf16_zipf", 257, 72, 12, 48, "bf16", 1.25, 52, zipf=1.1), 0.0, 0.01, False),
     (_sw("s_ragged", 133, 37, 5, 21, "f32", 1.0, 53), 0.1, 0.3, True),
+    # one token; one expert (p = 1 whatever the logit: no gate gradient)
+    (_sw("s_T1", 1, 16, 4, 8, "f32", 1.0, 54), 0.2, 0.3, True),
+    (_sw("s_E1", 64, 16, 1, 8, "bf16", 1.0, 55), 0.1, 0.1, True),
 ]
 
 
