@@ -47,6 +47,12 @@ struct GemmArgs {
   int KS;  // k-steps per column block in Wp (multiple of 4)
 };
 
+// ReLU on the bit pattern: a float whose pattern read as a signed integer is negative has its
+// sign bit set, so max(bits, 0) maps every negative value and -0 to +0 and keeps the rest (a
+// NaN from the accumulation stays NaN, where it can be seen by the non-finite check). One
+// integer max instead of the canonicalising float max.
+__device__ __forceinline__ float relu(float v) { return __int_as_float(max(__float_as_int(v), 0)); }
+
 // Operands live in native vector registers (the HIP uint4 struct defeats
 // register promotion of arrays).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -239,12 +245,12 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int cbase = n0 + wave * 64 + j * 32;
-        const bool col_ok = cbase + (lane & 31) < g.N;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float v = acc[m][j][i];
-          if (kEpi == 1) v = fmaxf(v, 0.f);
-          if (kEpi != 2) bad |= col_ok && m * 32 + acc_row(lane, i) < rows && !isfinite(v);
+          if (kEpi == 1) v = relu(v);
+          // rows and columns past the tile's edge hold copies of real ones (clamped loads)
+          if (kEpi != 2) bad |= !isfinite(v);
           Ts[acc_row(lane, i) * kTStride + (lane & 31)] = Elem<T>::from_f32(v);
         }
 #pragma unroll
@@ -280,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
           const int row = m * 32 + acc_row(lane, i);
           if (row < rows) {
             float v = acc[m][j][i];
-            if (kEpi == 1) v = fmaxf(v, 0.f);
+            if (kEpi == 1) v = relu(v);
             if (kEpi == 2 &&
                 !(Elem<T>::to_f32(static_cast<const T*>(g.mask)[static_cast<int64_t>(r0 + row) * g.N + col]) > 0.f))
               v = 0.f;
