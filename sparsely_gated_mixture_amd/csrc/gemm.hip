@@ -53,6 +53,10 @@ struct GemmArgs {
 // integer max instead of the canonicalising float max.
 __device__ __forceinline__ float relu(float v) { return __int_as_float(max(__float_as_int(v), 0)); }
 
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 // Operands live in native vector registers (the HIP uint4 struct defeats
 // register promotion of arrays).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -73,7 +77,8 @@ template <> __device__ __forceinline__ f32x16 mma<float>(u32x4 a, u32x4 b, f32x1
 // derivative in the backward pass: zero where the forward's hidden value is not positive).
 // kFullK: K is a multiple of the 128-byte k stage (no tail, no bounds checks on A).
 // kVecOut: N * sizeof(T) is a multiple of 16 (row-contiguous 16-byte output stores).
-template <typename T, int BM, int kEpi, bool kFullK, bool kVecOut>
+// kCheck: record NaN / Inf outputs in g.nonfinite (only then is the test compiled in).
+template <typename T, int BM, int kEpi, bool kFullK, bool kVecOut, bool kCheck>
 __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
   constexpr int V = Elem<T>::kVec;
   constexpr int kStageElems = 128 / static_cast<int>(sizeof(T));
@@ -215,7 +220,6 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
 
   // ---- epilogue: (ReLU), round to T, store
   T* C = static_cast<T*>(g.C);
-  const bool check = g.nonfinite != nullptr;
   bool bad = false;
   if constexpr (kVecOut) {
     // each 32x32 tile goes through a wave-private LDS tile so rows leave as 16-byte stores
@@ -245,13 +249,27 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int cbase = n0 + wave * 64 + j * 32;
+        if constexpr (sizeof(T) == 2 && !kCheck) {
+          // bf16: registers i, i+1 hold rows r, r+1 of the lane's column; one conversion
+          // rounds the pair, and the ReLU is a packed 16-bit integer max on the rounded
+          // patterns (rounding keeps the sign, so this equals rounding the ReLU)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float v = acc[m][j][i];
-          if (kEpi == 1) v = relu(v);
-          // rows and columns past the tile's edge hold copies of real ones (clamped loads)
-          if (kEpi != 2) bad |= !isfinite(v);
-          Ts[acc_row(lane, i) * kTStride + (lane & 31)] = Elem<T>::from_f32(v);
+          for (int i = 0; i < 16; i += 2) {
+            s16x2 h = __builtin_bit_cast(
+                s16x2, __builtin_convertvector((f32x2){acc[m][j][i], acc[m][j][i + 1]}, bf16x2));
+            if (kEpi == 1) h = __builtin_elementwise_max(h, (s16x2){0, 0});
+            Ts[acc_row(lane, i) * kTStride + (lane & 31)] = static_cast<uint16_t>(h.x);
+            Ts[(acc_row(lane, i) + 1) * kTStride + (lane & 31)] = static_cast<uint16_t>(h.y);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float v = acc[m][j][i];
+            if (kEpi == 1) v = relu(v);
+            // rows and columns past the tile's edge hold copies of real ones (clamped loads)
+            if (kCheck && kEpi != 2) bad |= !isfinite(v);
+            Ts[acc_row(lane, i) * kTStride + (lane & 31)] = Elem<T>::from_f32(v);
+          }
         }
 #pragma unroll
         for (int h = 0; h < kH; ++h) {
@@ -267,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
 #pragma unroll
               for (int q = 0; q < V; ++q) {
                 if (!(Elem<T>::to_f32(me[q]) > 0.f)) ve[q] = T(0);
-                bad |= !isfinite(Elem<T>::to_f32(ve[q]));
+                if (kCheck) bad |= !isfinite(Elem<T>::to_f32(ve[q]));
               }
             }
             *reinterpret_cast<u32x4*>(&C[o]) = v;
@@ -290,13 +308,13 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
             if (kEpi == 2 &&
                 !(Elem<T>::to_f32(static_cast<const T*>(g.mask)[static_cast<int64_t>(r0 + row) * g.N + col]) > 0.f))
               v = 0.f;
-            bad |= !isfinite(v);
+            if (kCheck) bad |= !isfinite(v);
             C[static_cast<int64_t>(r0 + row) * g.N + col] = Elem<T>::from_f32(v);
           }
         }
     }
   }
-  if (check) note_nonfinite(g.nonfinite, bad);
+  if (kCheck) note_nonfinite(g.nonfinite, bad);
 }
 
 // One thread per (expert, column block, k-step, lane): lane's 16-byte B operand.
@@ -429,15 +447,27 @@ moe_status pack_launch(const Dims& d, int layer, const void* W, void* Wp, hipStr
   return launch_status();
 }
 
-template <typename T, int BM, int kEpi>
-static void launch_k(const GemmArgs& g, int grid, size_t lds, hipStream_t stream) {
+template <typename T, int BM, int kEpi, bool kCheck>
+static void launch_kc(const GemmArgs& g, int grid, size_t lds, hipStream_t stream) {
   constexpr int V = Elem<T>::kVec;
   const bool full = g.K % (128 / static_cast<int>(sizeof(T))) == 0;
   const bool vout = g.N % V == 0;
-  if (full && vout) grouped_gemm<T, BM, kEpi, true, true><<<grid, kThreads, lds, stream>>>(g);
-  else if (full) grouped_gemm<T, BM, kEpi, true, false><<<grid, kThreads, lds, stream>>>(g);
-  else if (vout) grouped_gemm<T, BM, kEpi, false, true><<<grid, kThreads, lds, stream>>>(g);
-  else grouped_gemm<T, BM, kEpi, false, false><<<grid, kThreads, lds, stream>>>(g);
+  if (full && vout) grouped_gemm<T, BM, kEpi, true, true, kCheck><<<grid, kThreads, lds, stream>>>(g);
+  else if (full) grouped_gemm<T, BM, kEpi, true, false, kCheck><<<grid, kThreads, lds, stream>>>(g);
+  else if (vout) grouped_gemm<T, BM, kEpi, false, true, kCheck><<<grid, kThreads, lds, stream>>>(g);
+  else grouped_gemm<T, BM, kEpi, false, false, kCheck><<<grid, kThreads, lds, stream>>>(g);
+}
+
+// Only the plain epilogue is ever given a non-finite flag (the forward's layer 2).
+template <typename T, int BM, int kEpi>
+static void launch_k(const GemmArgs& g, int grid, size_t lds, hipStream_t stream) {
+  if constexpr (kEpi == 0) {
+    if (g.nonfinite) {
+      launch_kc<T, BM, kEpi, true>(g, grid, lds, stream);
+      return;
+    }
+  }
+  launch_kc<T, BM, kEpi, false>(g, grid, lds, stream);
 }
 
 template <typename T, int BM>
