@@ -25,6 +25,12 @@
 //   * Every block derives the tile table itself from offsets (one block-wide
 //     scan of per-expert row-tile counts); blocks past the real tile count
 //     exit at once (the grid is sized by the upper bound on rows).
+//   * BM is 128 rows, or 64 when 128-row tiles would leave the CUs short of
+//     work (small or narrow layers).
+//   * The epilogue runs while the block's MFMAs are idle, so it is kept lean:
+//     hardware bf16 rounding, ReLU as an integer max on the bit pattern, the
+//     non-finite test compiled in only where a flag is given; rows leave as
+//     16-byte stores through a wave-private LDS tile.
 #include "common.h"
 
 namespace moe {
