@@ -4,7 +4,9 @@
 
 A step is one pass of the whole hot path over one batch of synthetic tokens
 already resident in HBM: route -> dispatch -> expert FFN (two grouped GEMMs)
--> combine -> aux, each through the C ABI on one stream. W untimed warm-up
+-> combine -> aux, each through the C ABI on one stream (the flat and
+hierarchical gates: the dispatch computes slots and groups, and layer 1 reads
+its rows from X through row_token). W untimed warm-up
 steps, then exactly K timed steps between two device synchronisations. HIP
 events recorded on that same stream between the stages give every stage's
 average duration; the grouped GEMM (the one dense contraction) is the
@@ -373,6 +375,9 @@ def main():
         return
 
     stages = ["route", "dispatch", "gemm1", "gemm2", "combine", "aux"]
+    # flat and hierarchical gates: the dispatch computes slots and groups only and layer 1
+    # reads its rows from X through row_token (the gather done by the GEMM's row loads)
+    gather = isinstance(L, moe.Layer)
 
     def step(ev=None):
         if ev is not None:
@@ -380,10 +385,16 @@ def main():
         L.route(X)
         if ev is not None:
             ev[1].record()
-        L.dispatch(X)
+        if gather:
+            L.dispatch(X, rows=False)
+        else:
+            L.dispatch(X)
         if ev is not None:
             ev[2].record()
-        L.gemm(1)
+        if gather:
+            L.gemm(1, X)
+        else:
+            L.gemm(1)
         if ev is not None:
             ev[3].record()
         L.gemm(2)
@@ -442,7 +453,8 @@ def main():
     gemm_ms = 0.5 * (per["gemm1"] + per["gemm2"])
     peak = PEAK_TFLOPS[w.act]
     traffic = measured_traffic("grouped_gemm", w.name)
-    disp_bytes = w.T * w.D * el + A * w.D * el + w.T * w.k * (4 + 4 + 1) + A * 4
+    # ids in; pos, accepted, row_token out; the rows themselves when the dispatch copies them
+    disp_bytes = w.T * w.k * (4 + 4 + 1) + A * 4 + (0 if gather else w.T * w.D * el + A * w.D * el)
     comb_bytes = A * w.D * el + 2 * w.T * w.D * el + w.T * w.k * 13
     out = {
         "metric": "MoE layer fwd tokens/s at 1 GPU; grouped-GEMM % MFMA peak; dispatch GB/s",
@@ -474,6 +486,7 @@ def main():
         "dispatch_GBps": disp_bytes / (per["dispatch"] * 1e-3) / 1e9,
         "combine_GBps": comb_bytes / (per["combine"] * 1e-3) / 1e9,
         "dispatch_hbm_frac": disp_bytes / (per["dispatch"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "dispatch_rows": "gathered by layer 1's row loads" if gather else "copied into Xd",
         "combine_hbm_frac": comb_bytes / (per["combine"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "input_gen_s": t_gen,
     }

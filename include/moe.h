@@ -163,7 +163,9 @@ const float* moe_route_scores(const moe_problem* p, const void* route_workspace)
  *   pos       [T,k] int32 out     accepted [T,k] uint8 out (1 kept, 0 dropped)
  *   counts    [E] int32 out       offsets [E+1] int32 out
  *   row_token [moe_max_rows] int32 out (rows past offsets[E] untouched)
- *   Xd        [moe_max_rows, D] p->dtype out (rows past offsets[E] untouched)
+ *   Xd        [moe_max_rows, D] p->dtype out (rows past offsets[E] untouched),
+ *             or NULL: no rows are copied, and the gathered entry points below
+ *             read X through row_token instead
  *   workspace moe_workspace_size(p, MOE_WS_DISPATCH) bytes
  * ids outside [0,E) give undefined results (not checked on the device).
  */
@@ -201,6 +203,23 @@ moe_status moe_grouped_gemm(const moe_problem* p, int layer, const void* A,
 moe_status moe_expert_ffn(const moe_problem* p, const void* Xd, const void* W1p,
                           const void* W2p, const int32_t* offsets, void* Hd,
                           void* Z, void* hip_stream);
+
+/* moe_grouped_gemm_gather / moe_expert_ffn_gather -- layer 1 (and, for the
+ * ffn, layer 2) with the dispatch's gather ([SWITCH] step 5) done by the
+ * GEMM's row loads: row r of expert e's group is X[row_token[r]], so the
+ * dispatch may be called with Xd = NULL. Results are bit-identical to
+ * moe_grouped_gemm(layer 1) / moe_expert_ffn on the Xd that moe_dispatch
+ * would have written.
+ *   X [T,D] p->dtype   row_token [moe_max_rows] int32 from moe_dispatch
+ *   W1p, W2p, offsets, Hd, Z as above */
+moe_status moe_grouped_gemm_gather(const moe_problem* p, const void* X,
+                                   const int32_t* row_token, const void* W1p,
+                                   const int32_t* offsets, void* Hd,
+                                   void* hip_stream);
+moe_status moe_expert_ffn_gather(const moe_problem* p, const void* X,
+                                 const int32_t* row_token, const void* W1p,
+                                 const void* W2p, const int32_t* offsets,
+                                 void* Hd, void* Z, void* hip_stream);
 
 /* ---------------------------------------------------------------- combine */
 

@@ -188,7 +188,7 @@ moe_status moe_dispatch(const moe_problem* p, const void* X, const int32_t* ids,
                         void* Xd, void* workspace, size_t workspace_bytes, void* hip_stream) {
   Dims d;
   MOE_TRY(validate_topk(p, &d));
-  if (!X || !ids || !pos || !accepted || !counts || !offsets || !row_token || !Xd)
+  if (!X || !ids || !pos || !accepted || !counts || !offsets || !row_token)
     return MOE_ERR_INVALID_ARG;
   MOE_ALIGNED(X, ids, pos, accepted, counts, offsets, row_token, Xd, workspace);
   if (!workspace || workspace_bytes < dispatch_workspace(d)) return MOE_ERR_WORKSPACE;
@@ -228,6 +228,29 @@ moe_status moe_expert_ffn(const moe_problem* p, const void* Xd, const void* W1p,
   int* flag;
   MOE_TRY(flag_for(p, &flag));
   MOE_TRY(gemm_launch(d, 1, Xd, W1p, offsets, Hd, nullptr, as_stream(hip_stream)));
+  return gemm_launch(d, 2, Hd, W2p, offsets, Z, flag, as_stream(hip_stream));
+}
+
+moe_status moe_grouped_gemm_gather(const moe_problem* p, const void* X, const int32_t* row_token,
+                                   const void* W1p, const int32_t* offsets, void* Hd,
+                                   void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate(p, &d));
+  if (!X || !row_token || !W1p || !offsets || !Hd) return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(X, row_token, W1p, offsets, Hd);
+  return gemm_launch(d, 1, X, W1p, offsets, Hd, nullptr, as_stream(hip_stream), nullptr, row_token);
+}
+
+moe_status moe_expert_ffn_gather(const moe_problem* p, const void* X, const int32_t* row_token,
+                                 const void* W1p, const void* W2p, const int32_t* offsets,
+                                 void* Hd, void* Z, void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate(p, &d));
+  if (!X || !row_token || !W1p || !W2p || !offsets || !Hd || !Z) return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(X, row_token, W1p, W2p, offsets, Hd, Z);
+  int* flag;
+  MOE_TRY(flag_for(p, &flag));
+  MOE_TRY(gemm_launch(d, 1, X, W1p, offsets, Hd, nullptr, as_stream(hip_stream), nullptr, row_token));
   return gemm_launch(d, 2, Hd, W2p, offsets, Z, flag, as_stream(hip_stream));
 }
 

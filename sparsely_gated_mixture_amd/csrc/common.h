@@ -149,7 +149,7 @@ moe_status dispatch_launch(const Dims& d, const void* X, const int32_t* ids, int
 moe_status pack_launch(const Dims& d, int layer, const void* W, void* Wp, hipStream_t stream);
 moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp,
                        const int32_t* offsets, void* C, int* nonfinite, hipStream_t stream,
-                       const void* mask = nullptr);
+                       const void* mask = nullptr, const int32_t* row_token = nullptr);
 moe_status combine_launch(const Dims& d, const void* Z, const int32_t* ids, const float* gates,
                           const int32_t* pos, const uint8_t* accepted, const int32_t* offsets,
                           const void* residual, void* Y, int* nonfinite, hipStream_t stream);

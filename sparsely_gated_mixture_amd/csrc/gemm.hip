@@ -48,6 +48,7 @@ struct GemmArgs {
   void* C;
   int* nonfinite;
   const void* mask;  // epilogue mode 2: output zeroed where mask[row, col] <= 0 ([rows, N])
+  const int32_t* row_token;  // gathered A: row r of the groups is row row_token[r] of A
   int E, K, N;
   int NB;  // 32-column blocks per expert in Wp
   int KS;  // k-steps per column block in Wp (multiple of 4)
@@ -84,7 +85,8 @@ template <> __device__ __forceinline__ f32x16 mma<float>(u32x4 a, u32x4 b, f32x1
 // kFullK: K is a multiple of the 128-byte k stage (no tail, no bounds checks on A).
 // kVecOut: N * sizeof(T) is a multiple of 16 (row-contiguous 16-byte output stores).
 // kCheck: record NaN / Inf outputs in g.nonfinite (only then is the test compiled in).
-template <typename T, int BM, int kEpi, bool kFullK, bool kVecOut, bool kCheck>
+// kGather: A rows are read through g.row_token (the dispatch's gather done by the A loads).
+template <typename T, int BM, int kEpi, bool kFullK, bool kVecOut, bool kCheck, bool kGather>
 __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
   constexpr int V = Elem<T>::kVec;
   constexpr int kStageElems = 128 / static_cast<int>(sizeof(T));
@@ -143,13 +145,18 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
   // ---- A stream: thread's chunk i is row arow0 + i*32 (clamped into the group), 16-byte
   // segment aseg of the 128-byte k stage; LDS rows are padded to kAStride bytes.
   const int aseg = tid & 7, arow0 = tid >> 3;
-  const T* abase = A + static_cast<int64_t>(r0) * K;
+  const T* abase = A + (kGather ? 0 : static_cast<int64_t>(r0) * K);
   const bool vec_ok = (K % V) == 0;
+  int atok[kGather ? kChunks : 1];  // gathered: the A row of each chunk
+  if constexpr (kGather) {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) atok[i] = g.row_token[r0 + min(arow0 + i * (kThreads / 8), rows - 1)];
+  }
   u32x4 areg[kChunks];
   auto load_a = [&](int st) {
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
-      const T* row = abase + static_cast<int64_t>(min(arow0 + i * (kThreads / 8), rows - 1)) * K;
+      const T* row = abase + static_cast<int64_t>(kGather ? atok[i] : min(arow0 + i * (kThreads / 8), rows - 1)) * K;
       if constexpr (kFullK) {
         areg[i] = *reinterpret_cast<const u32x4*>(row + st * kStageElems + aseg * V);
       } else {
@@ -453,27 +460,34 @@ moe_status pack_launch(const Dims& d, int layer, const void* W, void* Wp, hipStr
   return launch_status();
 }
 
-template <typename T, int BM, int kEpi, bool kCheck>
+template <typename T, int BM, int kEpi, bool kCheck, bool kGather>
 static void launch_kc(const GemmArgs& g, int grid, size_t lds, hipStream_t stream) {
   constexpr int V = Elem<T>::kVec;
   const bool full = g.K % (128 / static_cast<int>(sizeof(T))) == 0;
   const bool vout = g.N % V == 0;
-  if (full && vout) grouped_gemm<T, BM, kEpi, true, true, kCheck><<<grid, kThreads, lds, stream>>>(g);
-  else if (full) grouped_gemm<T, BM, kEpi, true, false, kCheck><<<grid, kThreads, lds, stream>>>(g);
-  else if (vout) grouped_gemm<T, BM, kEpi, false, true, kCheck><<<grid, kThreads, lds, stream>>>(g);
-  else grouped_gemm<T, BM, kEpi, false, false, kCheck><<<grid, kThreads, lds, stream>>>(g);
+  if (full && vout) grouped_gemm<T, BM, kEpi, true, true, kCheck, kGather><<<grid, kThreads, lds, stream>>>(g);
+  else if (full) grouped_gemm<T, BM, kEpi, true, false, kCheck, kGather><<<grid, kThreads, lds, stream>>>(g);
+  else if (vout) grouped_gemm<T, BM, kEpi, false, true, kCheck, kGather><<<grid, kThreads, lds, stream>>>(g);
+  else grouped_gemm<T, BM, kEpi, false, false, kCheck, kGather><<<grid, kThreads, lds, stream>>>(g);
 }
 
-// Only the plain epilogue is ever given a non-finite flag (the forward's layer 2).
+// Only the plain epilogue is ever given a non-finite flag (the forward's layer 2), and only
+// layer 1 reads gathered rows.
 template <typename T, int BM, int kEpi>
 static void launch_k(const GemmArgs& g, int grid, size_t lds, hipStream_t stream) {
   if constexpr (kEpi == 0) {
     if (g.nonfinite) {
-      launch_kc<T, BM, kEpi, true>(g, grid, lds, stream);
+      launch_kc<T, BM, kEpi, true, false>(g, grid, lds, stream);
       return;
     }
   }
-  launch_kc<T, BM, kEpi, false>(g, grid, lds, stream);
+  if constexpr (kEpi == 1) {
+    if (g.row_token) {
+      launch_kc<T, BM, kEpi, false, true>(g, grid, lds, stream);
+      return;
+    }
+  }
+  launch_kc<T, BM, kEpi, false, false>(g, grid, lds, stream);
 }
 
 template <typename T, int BM>
@@ -506,7 +520,8 @@ static int device_cus() {
 }
 
 moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp, const int32_t* offsets,
-                       void* C, int* nonfinite, hipStream_t stream, const void* mask) {
+                       void* C, int* nonfinite, hipStream_t stream, const void* mask,
+                       const int32_t* row_token) {
   int K, N;
   layer_dims(d, layer, &K, &N);
   GemmArgs g;
@@ -516,6 +531,7 @@ moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp, 
   g.C = C;
   g.nonfinite = nonfinite;
   g.mask = mask;
+  g.row_token = layer == 1 ? row_token : nullptr;
   g.E = d.E;
   g.K = K;
   g.N = N;

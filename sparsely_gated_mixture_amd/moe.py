@@ -35,6 +35,7 @@ ENTRY_POINTS = [
     "moe_pack_expert_weights_t", "moe_combine_backward", "moe_expert_ffn_backward",
     "moe_route_backward", "moe_backward_workspace_size", "moe_expert_weight_grad",
     "moe_expert_ffn_backward_recompute", "moe_route_backward_switch", "moe_route_scores",
+    "moe_grouped_gemm_gather", "moe_expert_ffn_gather",
 ]
 
 
@@ -96,6 +97,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_pack_expert_weights": (ctypes.c_int, [P, vp, vp, vp, vp, vp]),
         "moe_grouped_gemm": (ctypes.c_int, [P, ctypes.c_int, vp, vp, vp, vp, vp]),
         "moe_expert_ffn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp]),
+        "moe_grouped_gemm_gather": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp]),
+        "moe_expert_ffn_gather": (ctypes.c_int, [P] + [vp] * 8),
         "moe_combine": (ctypes.c_int, [P] + [vp] * 8 + [vp]),
         "moe_aux_loss": (ctypes.c_int, [P] + [vp] * 9 + [vp, sz, vp]),
         "moe_check_finite": (ctypes.c_int, [vp]),
@@ -218,6 +221,18 @@ def moe_pack_expert_weights(p, W1, W2, W1p, W2p, stream=None):
 def moe_grouped_gemm(p, layer, A, Wp, offsets, C, stream=None):
     _check(_lib.moe_grouped_gemm(ctypes.byref(p), layer, _ptr(A), _ptr(Wp), _ptr(offsets), _ptr(C),
                                  _stream(stream)), "moe_grouped_gemm")
+
+
+def moe_grouped_gemm_gather(p, X, row_token, W1p, offsets, Hd, stream=None):
+    _check(_lib.moe_grouped_gemm_gather(ctypes.byref(p), _ptr(X), _ptr(row_token), _ptr(W1p),
+                                        _ptr(offsets), _ptr(Hd), _stream(stream)),
+           "moe_grouped_gemm_gather")
+
+
+def moe_expert_ffn_gather(p, X, row_token, W1p, W2p, offsets, Hd, Z, stream=None):
+    _check(_lib.moe_expert_ffn_gather(ctypes.byref(p), _ptr(X), _ptr(row_token), _ptr(W1p),
+                                      _ptr(W2p), _ptr(offsets), _ptr(Hd), _ptr(Z),
+                                      _stream(stream)), "moe_expert_ffn_gather")
 
 
 def moe_expert_ffn(p, Xd, W1p, W2p, offsets, Hd, Z, stream=None):
@@ -445,18 +460,25 @@ class Layer:
         moe_route(self.p, X, self.Wg, self.Wnoise, self.bias, eps, b.ids, b.gates, b.clean,
                   b.noise_std, b.row_stats, b.ws_route)
 
-    def dispatch(self, X):
+    def dispatch(self, X, rows=True):
+        """rows=False: slots and groups only; layer 1 then gathers X itself (gemm(1, X))."""
         b = self.b
-        moe_dispatch(self.p, X, b.ids, b.pos, b.accepted, b.counts, b.offsets, b.row_token, b.Xd,
-                     b.ws_dispatch)
+        moe_dispatch(self.p, X, b.ids, b.pos, b.accepted, b.counts, b.offsets, b.row_token,
+                     b.Xd if rows else None, b.ws_dispatch)
 
-    def ffn(self):
+    def ffn(self, X=None):
+        """X given: layer 1 reads its rows through row_token (no Xd needed)."""
         b = self.b
-        moe_expert_ffn(self.p, b.Xd, self.W1p, self.W2p, b.offsets, b.Hd, b.Z)
+        if X is not None:
+            moe_expert_ffn_gather(self.p, X, b.row_token, self.W1p, self.W2p, b.offsets, b.Hd, b.Z)
+        else:
+            moe_expert_ffn(self.p, b.Xd, self.W1p, self.W2p, b.offsets, b.Hd, b.Z)
 
-    def gemm(self, layer):
+    def gemm(self, layer, X=None):
         b = self.b
-        if layer == 1:
+        if layer == 1 and X is not None:
+            moe_grouped_gemm_gather(self.p, X, b.row_token, self.W1p, b.offsets, b.Hd)
+        elif layer == 1:
             moe_grouped_gemm(self.p, 1, b.Xd, self.W1p, b.offsets, b.Hd)
         else:
             moe_grouped_gemm(self.p, 2, b.Hd, self.W2p, b.offsets, b.Z)
@@ -545,10 +567,11 @@ class Layer:
         self.backward_route(X, dY, w_imp, w_load, residual, eps, w_switch)
         return self.grads
 
-    def forward(self, X, eps=None, residual=True, aux=True) -> Buffers:
+    def forward(self, X, eps=None, residual=True, aux=True, gather=False) -> Buffers:
+        """gather: the dispatch copies no rows and layer 1 reads X through row_token."""
         self.route(X, eps)
-        self.dispatch(X)
-        self.ffn()
+        self.dispatch(X, rows=not gather)
+        self.ffn(X if gather else None)
         self.combine(X, residual)
         if aux:
             self.aux()

@@ -199,3 +199,40 @@ def test_check_finite_flags_nan(moe):
         moe.moe_check_finite()
     assert ei.value.status == -3
     moe.moe_check_finite()  # the record was cleared
+
+
+GATHER_CASES = ["switch_toy", "noisy_fp32", "shrinking_bf16", "top2_bf16"] + ["t1", "e1", "rag", "wide"]
+
+
+@pytest.mark.parametrize("name", GATHER_CASES)
+def test_gathered_rows_match_copied_rows(moe, name):
+    """Layer 1 reading X through row_token (no Xd) gives bit-identical Hd, Z and Y to the
+    path that copies the rows into Xd first; the gathered path never reads Xd."""
+    import torch
+    log(f"[gather] {name}")
+    by_name = {w.name: w for w in EDGE}
+    w = by_name[name] if name in by_name else I.WORKLOADS[name]
+    inp = I.make_inputs(w)
+    L = _layer(moe, w, inp)
+    X = dev(inp["X"])
+    b = L.forward(X)
+    torch.cuda.synchronize()
+    A = int(host(b.offsets)[-1])
+    ref = {k: host(getattr(b, k)).copy() for k in ("pos", "accepted", "counts", "offsets", "Y")}
+    ref["row_token"] = host(b.row_token)[:A].copy()
+    ref["Hd"], ref["Z"] = host(b.Hd)[:A].copy(), host(b.Z)[:A].copy()
+    for t in (b.Xd, b.Hd, b.Z, b.Y):
+        t.fill_(float("nan"))
+    b = L.forward(X, gather=True)
+    torch.cuda.synchronize()
+    got = {k: host(getattr(b, k)) for k in ("pos", "accepted", "counts", "offsets", "Y")}
+    got["row_token"] = host(b.row_token)[:A]
+    got["Hd"], got["Z"] = host(b.Hd)[:A], host(b.Z)[:A]
+    for k in ref:
+        assert np.array_equal(ref[k].view(np.uint8), got[k].view(np.uint8)), k
+    assert np.isnan(f64(host(b.Xd))).all()  # no row was copied
+    if w.T <= 2048:  # and against the oracle directly
+        r = O.route(inp["X"], inp["Wg"], inp["Wnoise"], inp["bias"], w.k, w.gating, w.noise,
+                    seed=w.seed)
+        d = O.dispatch(r.ids, w.E, O.capacity(w.T, w.k, w.capacity_factor, w.E, w.min_capacity))
+        _check_forward(moe, w, inp, r, d, b, full_y=True)
