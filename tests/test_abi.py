@@ -170,6 +170,14 @@ def test_unaligned_pointers_rejected(m):
     assert m._lib.moe_dispatch(ctypes.byref(p), *a, big, None) == -1
     assert m._lib.moe_grouped_gemm(ctypes.byref(p), 1, ok, ok, ok, bad, None) == -1
     assert m._lib.moe_expert_ffn(ctypes.byref(p), ok, ok, ok, ok, ok, bad, None) == -1
+    for i in range(5):  # X, row_token, W1p, offsets, Hd
+        a = [ok] * 5
+        a[i] = bad
+        assert m._lib.moe_grouped_gemm_gather(ctypes.byref(p), *a, None) == -1, i
+    for i in range(7):  # X, row_token, W1p, W2p, offsets, Hd, Z
+        a = [ok] * 7
+        a[i] = bad
+        assert m._lib.moe_expert_ffn_gather(ctypes.byref(p), *a, None) == -1, i
     # residual (optional) misaligned
     assert m._lib.moe_combine(ctypes.byref(p), ok, ok, ok, ok, ok, ok, bad, ok, None) == -1
     assert m._lib.moe_pack_expert_weights(ctypes.byref(p), bad, None, ok, None, None) == -1
@@ -268,3 +276,21 @@ def test_route_scores_address(m):
     assert m._lib.moe_route_scores(ctypes.byref(off), ctypes.c_void_p(base)) is None
     sw = _p(m, T=64, E=8, k=1, gating="switch", noise=False)
     assert m._lib.moe_route_scores(ctypes.byref(sw), ctypes.c_void_p(base)) is None
+
+
+def test_gathered_entry_points_need_their_pointers(m):
+    """The gathered layer-1 entry points reject a missing pointer (argument error, nothing
+    enqueued); moe_dispatch accepts Xd = NULL (slots only) but not a missing row_token."""
+    p = _p(m)
+    ok = ctypes.c_void_p(0x1000)
+    for i in range(5):
+        a = [ok] * 5
+        a[i] = None
+        assert m._lib.moe_grouped_gemm_gather(ctypes.byref(p), *a, None) == -1, i
+    for i in range(7):
+        a = [ok] * 7
+        a[i] = None
+        assert m._lib.moe_expert_ffn_gather(ctypes.byref(p), *a, None) == -1, i
+    a = [ok] * 9  # X, ids, pos, accepted, counts, offsets, row_token, Xd, workspace
+    a[6] = None
+    assert m._lib.moe_dispatch(ctypes.byref(p), *a, 1 << 30, None) == -1
