@@ -161,3 +161,32 @@ def test_m_is_rounded_down():
     assert r.m == 2 and r.mask.sum() == 8
     with pytest.raises(ValueError):
         BO.route_batchwise(inp["X"][:3], inp["Wg"], None, 1)  # k T < E: no token per expert
+
+
+def _route_two_experts(a, k=1):
+    """Two experts with logits (a_t, 0): expert 0 scores sigmoid(a_t), expert 1 sigmoid(-a_t)."""
+    X = np.asarray(a, dtype=np.float64)[:, None]
+    return BO.route_batchwise(X, np.array([[1.0, 0.0]]), None, k)
+
+
+def test_near_tie_margin_is_relative_to_the_mth_score():
+    """Near-tie reading: the m-th and (m+1)-th scores of an expert closer than 2e-6 of the m-th
+    score (relative). Four tokens, k = 1, E = 2, so m = 2."""
+    r = _route_two_experts([1.0, 0.5, 0.5 - 2e-6, -1.0])  # 4.7e-7 apart at 0.62 and 0.38
+    assert r.m == 2 and r.near_tie.tolist() == [True, True]
+    r = _route_two_experts([1.0, 0.5, 0.4, -1.0])
+    assert r.near_tie.tolist() == [False, False]
+    # 5e-7 apart at scores near 0.05 (relative 1e-5: not near) and near 0.95 (5e-7: near)
+    r = _route_two_experts([-2.0, -2.944, -2.944 - 1.05e-5, -4.0])
+    assert r.near_tie.tolist() == [False, True]
+
+
+def test_exact_tie_is_decided_by_the_token_index():
+    """Identical rows tie exactly: the lower token is kept and the expert is no near-tie, unless a
+    distinct score lies within the margin of the tied value."""
+    r = _route_two_experts([1.0, 0.5, 0.5, -1.0])
+    assert r.sel.tolist() == [[0, 1], [1, 3]]
+    assert r.near_tie.tolist() == [False, False]
+    r = _route_two_experts([0.5 + 2e-6, 0.5, 0.5, -1.0])
+    assert r.sel.tolist() == [[0, 1], [1, 3]]
+    assert r.near_tie.tolist() == [True, True]

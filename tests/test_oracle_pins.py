@@ -471,3 +471,123 @@ def test_gaussian_noise_is_counter_keyed():
     big = P.gaussian_noise(9, 20000, 8).astype(np.float64)
     c = np.corrcoef(big.T)
     assert np.abs(c - np.eye(8)).max() < 0.04
+
+
+# ------------------------------------------------------------ bf16 widening
+
+def test_widen_bf16_hand_patterns():
+    """bfloat16 is the upper half of an IEEE binary32 (sign, 8 exponent bits, 7 fraction bits);
+    each value here is worked out by hand from that layout, not by another conversion."""
+    cases = {
+        0x3F80: 1.0,                        # exponent 127, fraction 0
+        0xC000: -2.0,                       # sign, exponent 128
+        0x3F81: 1.0 + 2.0 ** -7,            # lowest fraction bit at exponent 127
+        0x4049: 3.140625,                   # 1.5703125 * 2
+        0x0001: 2.0 ** -133,                # smallest subnormal: 2^-126 * 2^-7
+        0x0080: 2.0 ** -126,                # smallest normal
+        0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127,  # largest finite
+        0x7F80: math.inf,
+        0xFF80: -math.inf,
+        0x0000: 0.0,
+    }
+    bits = np.array(list(cases), dtype=np.uint16)
+    got = O.widen(bits)
+    assert got.dtype == np.float64
+    assert got.tolist() == list(cases.values())
+    neg0 = O.widen(np.array([0x8000], np.uint16))[0]
+    assert neg0 == 0.0 and math.copysign(1.0, neg0) == -1.0
+    assert np.isnan(O.widen(np.array([0x7FC0, 0xFFC1], np.uint16))).all()
+
+
+def test_widen_bf16_matches_torch_bfloat16():
+    """Every finite bf16 pattern widened as torch's bfloat16 -> float64 conversion does
+    (an independent implementation); NaN patterns stay NaN."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns
+        got = O.widen(bits)
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_widen_fp32_is_exact():
+    x = np.array([1.0, -3.5, 1e-40, 3.4e38, np.float32(0.1)], np.float32)
+    np.testing.assert_array_equal(O.widen(x), [float(v) for v in x])
+
+
+# ------------------------------------------------------------ near-tie margin (1e-6 on the score)
+
+def _route_scores(score, k, gating="noisy", eps=None, noise_logits=None):
+    """One token whose clean logits are `score` (fp64: D = 1, X = 1, Wg = the logits)."""
+    Wg = np.atleast_2d(np.asarray(score, dtype=np.float64))
+    X = np.ones((1, 1))
+    if noise_logits is not None:
+        Wn = np.atleast_2d(np.asarray(noise_logits, dtype=np.float64))
+        return O.route(X, Wg, Wn, None, k, gating, True, eps=np.atleast_2d(eps))
+    return O.route(X, Wg, None, None, k, gating, False)
+
+
+def test_near_tie_flags_gaps_inside_the_margin():
+    """North-star margin (absolute, on the fp64 score): the k-th and (k+1)-th scores 0.5e-6
+    apart make a near-tie, 2e-6 apart do not."""
+    for gap, want in ((0.5e-6, True), (2e-6, False), (0.0, True), (1e-3, False)):
+        r = _route_scores([3.0, 2.0, 2.0 - gap, 0.0], k=2)
+        assert bool(r.near_tie[0]) is want, gap
+        assert r.gap[0] == pytest.approx(gap, abs=1e-15)
+
+
+def test_near_tie_is_decided_at_the_kth_boundary_only():
+    """Only the margin between the k-th and (k+1)-th score decides the kept set: a close pair
+    inside the kept set (or wholly outside it) is not a near-tie."""
+    r = _route_scores([2.0, 2.0 - 0.5e-6, 0.0, -1.0], k=2)  # 1st and 2nd close, set is stable
+    assert not r.near_tie[0] and r.gap[0] == pytest.approx(2.0 - 0.5e-6)
+    r = _route_scores([2.0, 1.0, -1.0, -1.0 - 0.5e-6], k=2)  # 3rd and 4th close
+    assert not r.near_tie[0]
+    r = _route_scores([2.0, 1.0, 1.0 - 0.5e-6, -1.0], k=1)  # k = 1: 1st vs 2nd
+    assert not r.near_tie[0] and r.gap[0] == pytest.approx(1.0)
+    r = _route_scores([2.0, 2.0 - 0.5e-6, 1.0, -1.0], k=1)
+    assert r.near_tie[0]
+    r = _route_scores([2.0, 1.0, 0.0, -3.0 + 0.5e-6, -3.0], k=3)  # k = 3: 3rd vs 4th
+    assert not r.near_tie[0]
+    r = _route_scores([2.0, 1.0, 0.0, -0.5e-6, -3.0], k=3)
+    assert r.near_tie[0]
+
+
+def test_near_tie_never_at_k_equal_E():
+    """k = E keeps every expert whatever the scores: no decision, never a near-tie."""
+    r = _route_scores([1.0, 1.0, 1.0], k=3)
+    assert not r.near_tie[0] and r.gap[0] == math.inf
+
+
+def test_near_tie_on_the_noisy_score_and_the_switch_logit():
+    """Noisy gate: the margin is on H = clean + eps * std, not on clean. Switch: on the top-2
+    gap of the logits (clean + bias)."""
+    # clean far apart, noise brings experts 1 and 2 within 0.5e-6 on H (std = 1)
+    clean = [3.0, 1.0, 0.0, -2.0]
+    eps = np.array([0.0, 0.0, 1.0 - 0.5e-6, 0.0])
+    r = _route_scores(clean, k=2, eps=eps, noise_logits=[LN_E_MINUS_1] * 4)
+    np.testing.assert_allclose(r.std, 1.0, atol=1e-15)
+    assert r.near_tie[0]
+    r = _route_scores(clean, k=2, eps=np.zeros(4), noise_logits=[LN_E_MINUS_1] * 4)
+    assert not r.near_tie[0]
+    for gap, want in ((0.5e-6, True), (2e-6, False)):
+        r = _route_scores([0.5, 0.5 - gap, -1.0], k=1, gating="switch")
+        assert bool(r.near_tie[0]) is want
+
+
+def test_fp32_decision_equals_fp64_order_outside_the_margin():
+    """The oracle decides on the fp32 rounding of its fp64 scores (the kernel's precision). Round
+    to nearest is monotone, and two scores below 16 in magnitude that round to one fp32 value lie
+    within one fp32 ulp (2^-20 < 1e-6) of each other; so on every token outside the 1e-6 margin
+    the fp32 decision keeps the same set as the fp64 order. Checked on all five workloads."""
+    for name in ("switch_toy", "noisy_fp32", "shrinking_bf16", "switch_bf16", "top2_bf16"):
+        w = I.WORKLOADS[name]
+        inp = I.make_inputs(w, experts=False)
+        r = O.route(inp["X"], inp["Wg"], inp["Wnoise"], inp["bias"], w.k, w.gating, w.noise,
+                    seed=w.seed)
+        assert np.abs(r.score).max() < 16.0, name
+        ok = ~r.near_tie
+        f64 = np.argsort(-r.score, axis=1, kind="stable")[:, :w.k]
+        assert np.array_equal(np.sort(f64[ok], axis=1), np.sort(r.ids[ok], axis=1)), name
