@@ -428,7 +428,9 @@ moe_status moe_combine_backward(const moe_problem* p, const void* dY, const void
 
 /* dHp = (dZ W2_e^T) masked where Hd <= 0 (the ReLU derivative) [rows, H];
  * dXd = dHp W1_e^T [rows, D]; dW2_e = Hd_e^T dZ_e [E,H,D] and dW1_e = Xd_e^T dHp_e
- * [E,D,H] (fp32; either may be NULL). Xd, Hd from the forward. */
+ * [E,D,H] (fp32; either may be NULL). Xd, Hd from the forward; Xd must hold the rows,
+ * i.e. come from a moe_dispatch called with a non-NULL Xd (a dispatch with Xd = NULL,
+ * for the gathered layer 1, leaves it unwritten and the gradients would be wrong). */
 moe_status moe_expert_ffn_backward(const moe_problem* p, const void* Xd, const void* Hd,
                                    const void* dZ, const void* W1t_packed,
                                    const void* W2t_packed, const int32_t* offsets, void* dHp,

@@ -187,9 +187,12 @@ def dispatch(ids: np.ndarray, E: int, C: int) -> Dispatch:
 
 # --------------------------------------------------------------------------- experts + combine
 
-def expert(x64: np.ndarray, W1e64: np.ndarray, W2e64: np.ndarray) -> np.ndarray:
-    """One expert on one token: ReLU(x.W1) . W2, no biases ([SWITCH] step 6)."""
-    return np.maximum(x64 @ W1e64, 0.0) @ W2e64
+def expert(x64: np.ndarray, W1e64: np.ndarray, W2e64: np.ndarray, hidden: bool = False):
+    """One expert on one token (or on a batch of rows): ReLU(x.W1) . W2, no biases
+    ([SWITCH] step 6). hidden: return (ReLU(x.W1), output)."""
+    h = np.maximum(x64 @ W1e64, 0.0)
+    z = h @ W2e64
+    return (h, z) if hidden else z
 
 
 class ExpertBank:
@@ -211,18 +214,25 @@ class ExpertBank:
         return v
 
 
-def expert_rows(X, d: Dispatch, ids: np.ndarray, bank: ExpertBank, rows) -> np.ndarray:
+def expert_rows(X, d: Dispatch, ids: np.ndarray, bank: ExpertBank, rows, hidden: bool = False):
     """Expert outputs for expert-major rows: row r holds token row_token[r] of
     the expert whose range contains r ([SWITCH] steps 5-6). Rows of one expert
     go through that expert together, as one gathered batch ([LESSON] ch. 1,
-    forward_batched)."""
+    forward_batched). hidden: return (hidden activations, outputs)."""
     rows = np.asarray(rows, dtype=np.int64)
     experts = np.searchsorted(d.offsets, rows, side="right") - 1
     out = np.zeros((rows.size, X.shape[1]))
+    hid = None
     for e in np.unique(experts):
         sel = np.nonzero(experts == e)[0]
         W1e, W2e = bank(int(e))
-        out[sel] = expert(widen(X[d.row_token[rows[sel]]]), W1e, W2e)
+        h, out[sel] = expert(widen(X[d.row_token[rows[sel]]]), W1e, W2e, hidden=True)
+        if hidden:
+            if hid is None:
+                hid = np.zeros((rows.size, W1e.shape[1]))
+            hid[sel] = h
+    if hidden:
+        return (np.zeros((rows.size, 0)) if hid is None else hid), out
     return out
 
 

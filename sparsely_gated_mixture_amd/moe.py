@@ -439,6 +439,9 @@ class Layer:
         self.Wg, self.Wnoise, self.bias = Wg, Wnoise, bias
         self.W1, self.W2 = W1, W2
         self.grads = None
+        # True once a dispatch has copied the current rows into Xd; a slots-only dispatch
+        # (rows gathered by layer 1) leaves Xd unwritten, and the backward needs it
+        self.xd_current = False
         self.W1p = e(moe_packed_weight_bytes(p, 1), dtype=torch.uint8)
         self.W2p = e(moe_packed_weight_bytes(p, 2), dtype=torch.uint8)
         moe_pack_expert_weights(p, W1, W2, self.W1p, self.W2p)
@@ -463,8 +466,10 @@ class Layer:
     def dispatch(self, X, rows=True):
         """rows=False: slots and groups only; layer 1 then gathers X itself (gemm(1, X))."""
         b = self.b
+        self.xd_current = False
         moe_dispatch(self.p, X, b.ids, b.pos, b.accepted, b.counts, b.offsets, b.row_token,
                      b.Xd if rows else None, b.ws_dispatch)
+        self.xd_current = rows
 
     def ffn(self, X=None):
         """X given: layer 1 reads its rows through row_token (no Xd needed)."""
@@ -523,6 +528,10 @@ class Layer:
         """recompute: Hd is recomputed from Xd into a scratch buffer instead of read from
         the forward's (the memory-for-compute trade of not storing it)."""
         b, g = self.b, self.grads
+        if not self.xd_current:
+            raise RuntimeError("the expert backward reads the dispatched rows Xd, which the last "
+                               "dispatch did not copy (forward(gather=True)); call "
+                               "dispatch(X, rows=True) first, as backward(X, ...) does")
         dW1 = g["dW1"] if weight_grads else None
         dW2 = g["dW2"] if weight_grads else None
         if recompute:
@@ -562,6 +571,8 @@ class Layer:
         terms use): dX, dWg, dWnoise, dbias, dW1, dW2 (fp32 weight gradients) of the
         objective <Y, dY> + w_imp CV^2(importance) + w_load CV^2(load)."""
         self.backward_buffers(weight_grads)
+        if not self.xd_current:  # a gathered forward: copy the rows now (the same slots)
+            self.dispatch(X, rows=True)
         self.backward_combine(dY)
         self.backward_ffn(weight_grads, recompute)
         self.backward_route(X, dY, w_imp, w_load, residual, eps, w_switch)

@@ -102,3 +102,34 @@ def gates_by_id(ids_gpu, gates_gpu, ids_ref, rows):
         m = {int(e): g for e, g in zip(ids_gpu[t], gates_gpu[t])}
         out[n] = [m[int(e)] for e in ids_ref[t]]
     return out
+
+
+def max_abs(got, ref) -> float:
+    return float(np.abs(f64(got) - f64(ref)).max()) if np.size(ref) else 0.0
+
+
+_Z_CACHE: dict = {}
+
+
+def oracle_expert_outputs(key, w: I.Workload, inp: dict, d: O.Dispatch, on_expert=None):
+    """The oracle's expert output Z [A, D] (fp64) for every accepted row of its dispatch, one
+    expert's rows at a time ([LESSON] ch. 1's gathered form, pinned equal to the per-token loop);
+    on_expert(e, r0, r1, h, z) also sees each expert's hidden rows h as they are made. The
+    result for one key (a workload name) is kept for the next caller."""
+    if key is not None and key in _Z_CACHE and on_expert is None:
+        return _Z_CACHE[key]
+    A = int(d.offsets[-1])
+    Z = np.zeros((A, w.D))
+    bank = O.ExpertBank(inp["W1"], inp["W2"], keep=2)
+    for e in range(w.E):
+        r0, r1 = int(d.offsets[e]), int(d.offsets[e + 1])
+        if r1 == r0:
+            continue
+        h, z = O.expert_rows(inp["X"], d, None, bank, np.arange(r0, r1), hidden=True)
+        Z[r0:r1] = z
+        if on_expert is not None:
+            on_expert(e, r0, r1, h, z)
+    _Z_CACHE.clear()
+    if key is not None:
+        _Z_CACHE[key] = Z
+    return Z

@@ -333,3 +333,34 @@ def test_backward_deterministic(moe):
             for k in keys:
                 assert torch.equal(g[k], first[k]), k
 
+
+
+@pytest.mark.parametrize("w", [BY_NAME[n] for n in ("b_bf16", "b_drop")], ids=lambda w: w.name)
+def test_backward_after_gathered_forward(moe, w):
+    """A forward whose layer 1 gathered its rows (no Xd written) followed by the backward gives
+    bitwise the gradients of the row-copying forward: the backward copies the rows first. The
+    expert backward on its own refuses to run on an unwritten Xd."""
+    import torch
+    inp = I.make_inputs(w)
+    p = problem_for(moe, w)
+    L = moe.Layer(p, dev(inp["Wg"]), dev(inp["Wnoise"]), dev(inp["bias"]), dev(inp["W1"]),
+                  dev(inp["W2"]))
+    X = dev(inp["X"])
+    dY = dev(I.make_output_grad(w))
+    L.forward(X)
+    g = L.backward(X, dY, w_imp=0.1, w_load=0.1)
+    torch.cuda.synchronize()
+    ref = {k: host(v).copy() for k, v in g.items() if v is not None and k != "ws"}
+    L.b.Xd.fill_(float("nan"))
+    L.forward(X, gather=True)
+    assert not L.xd_current
+    with pytest.raises(RuntimeError):
+        L.backward_ffn()
+    g = L.backward(X, dY, w_imp=0.1, w_load=0.1)
+    torch.cuda.synchronize()
+    rows = int(host(L.b.offsets)[-1])
+    for k, v in ref.items():
+        got = host(g[k])
+        if k in ("dZ", "dHp", "dXd"):
+            got, v = got[:rows], v[:rows]
+        assert np.array_equal(got.view(np.uint8), v.view(np.uint8)), k

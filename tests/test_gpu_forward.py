@@ -8,8 +8,9 @@ slots are compared on every expert that no flipped token touched.
 import numpy as np
 import pytest
 
-from gpu_helpers import (TOL, dev, f64, gates_by_id, host, log, oracle_routing, problem_for,
-                         rel_err, sample_tokens, set_mismatch, workload_inputs)
+from gpu_helpers import (TOL, dev, f64, gates_by_id, host, log, max_abs, oracle_expert_outputs,
+                         oracle_routing, problem_for, rel_err, sample_tokens, set_mismatch,
+                         workload_inputs)
 from oracle import moe as O
 from sparsely_gated_mixture_amd import inputs as I
 
@@ -30,7 +31,9 @@ def _layer(moe, w, inp, **kw):
                      dev(inp["bias"]), dev(inp["W1"]), dev(inp["W2"]))
 
 
-def _check_forward(moe, w, inp, r, d, b, full_y: bool, flat_aux: bool = True):
+def _check_forward(moe, w, inp, r, d, b, full_y: bool = True, flat_aux: bool = True, zkey=None):
+    """full_y: Y on every token whose routing matched (the oracle's expert outputs made expert
+    by expert, kept under zkey for the next caller); else on a seeded sample of tokens."""
     ids = host(b.ids)
     bad = set_mismatch(ids, r.ids)
     log(f"  near-ties {int(r.near_tie.sum())}, flipped {bad.size}")
@@ -52,15 +55,25 @@ def _check_forward(moe, w, inp, r, d, b, full_y: bool, flat_aux: bool = True):
     cnt = host(b.counts)
     assert (cnt[clean_e] == d.counts[clean_e]).all()
     # outputs
-    bank = O.ExpertBank(inp["W1"], inp["W2"], keep=16)
     toks = np.arange(w.T) if full_y else sample_tokens(w, d)
-    ok_set = set(ok.tolist())
-    toks = np.array([t for t in toks if t in ok_set and m[t].all()], dtype=np.int64)
-    ref = O.combine_tokens(inp["X"], r, d, bank, toks)
+    keep = np.zeros(w.T, bool)
+    keep[ok] = True
+    toks = toks[keep[toks] & m[toks].all(axis=1)]
+    if full_y:
+        Zo = oracle_expert_outputs(zkey, w, inp, d)
+        ref = O.combine_rows(Zo, r, d, inp["X"], tokens=toks)
+    else:
+        ref = O.combine_tokens(inp["X"], r, d, O.ExpertBank(inp["W1"], inp["W2"], keep=16), toks)
     Y = host(b.Y)
     err = rel_err(Y[toks], ref)
-    log(f"  Y checked on {toks.size} tokens, rel err {err:.2e}")
-    assert err < TOL[w.act]
+    # the expert branch alone, Y - X (the residual does not dilute it)
+    X64 = f64(inp["X"][toks])
+    got_b, ref_b = f64(Y[toks]) - X64, ref - X64
+    err_b = rel_err(got_b, ref_b)
+    log(f"  Y checked on {toks.size} of {w.T} tokens: rel err {err:.2e} (max abs "
+        f"{max_abs(Y[toks], ref):.2e}); branch Y - X rel err {err_b:.2e} (max abs "
+        f"{max_abs(got_b, ref_b):.2e}, max |branch| {np.abs(ref_b).max() if toks.size else 0:.2e})")
+    assert err < TOL[w.act] and err_b < TOL[w.act]
     dropped = [t for t in toks if not d.accepted[t].any()]
     if dropped:
         np.testing.assert_array_equal(Y[dropped], inp["X"][dropped])
@@ -82,19 +95,19 @@ def test_forward(moe, name):
     X = dev(inp["X"])
     b = L.forward(X)
     torch.cuda.synchronize()
-    _check_forward(moe, w, inp, r, d, b, full_y=w.T <= 4096)
+    _check_forward(moe, w, inp, r, d, b, full_y=True, zkey=name)
 
 
 def test_forward_flat1024(moe):
     """The flat gate over 1024 experts at T = 16384 (the hierarchical workload's shapes):
-    routing in full, Y on a seeded token sample."""
+    routing and Y in full."""
     import torch
     w, inp = workload_inputs("flat1024_bf16")
     r, d = oracle_routing("flat1024_bf16")
     L = _layer(moe, w, inp)
     b = L.forward(dev(inp["X"]))
     torch.cuda.synchronize()
-    _check_forward(moe, w, inp, r, d, b, full_y=False)
+    _check_forward(moe, w, inp, r, d, b, full_y=True)
 
 
 def test_forward_deterministic(moe):
@@ -201,7 +214,8 @@ def test_check_finite_flags_nan(moe):
     moe.moe_check_finite()  # the record was cleared
 
 
-GATHER_CASES = ["switch_toy", "noisy_fp32", "shrinking_bf16", "top2_bf16"] + ["t1", "e1", "rag", "wide"]
+GATHER_CASES = ["switch_toy", "noisy_fp32", "shrinking_bf16", "switch_bf16", "top2_bf16",
+                "hier_bf16"] + ["t1", "e1", "rag", "wide"]
 
 
 @pytest.mark.parametrize("name", GATHER_CASES)
@@ -213,7 +227,12 @@ def test_gathered_rows_match_copied_rows(moe, name):
     by_name = {w.name: w for w in EDGE}
     w = by_name[name] if name in by_name else I.WORKLOADS[name]
     inp = I.make_inputs(w)
-    L = _layer(moe, w, inp)
+    if w.groups > 0:  # the hierarchical gate, then the same flat dispatch / FFN / combine
+        L = moe.HierLayer(problem_for(moe, w), moe.hier(w.groups, w.k_primary), dev(inp["Wpg"]),
+                          dev(inp["Wpn"]), dev(inp["Wsg"]), dev(inp["Wsn"]), dev(inp["W1"]),
+                          dev(inp["W2"]))
+    else:
+        L = _layer(moe, w, inp)
     X = dev(inp["X"])
     b = L.forward(X)
     torch.cuda.synchronize()
@@ -231,7 +250,7 @@ def test_gathered_rows_match_copied_rows(moe, name):
     for k in ref:
         assert np.array_equal(ref[k].view(np.uint8), got[k].view(np.uint8)), k
     assert np.isnan(f64(host(b.Xd))).all()  # no row was copied
-    if w.T <= 2048:  # and against the oracle directly
+    if w.T <= 2048 and w.groups == 0:  # and against the oracle directly
         r = O.route(inp["X"], inp["Wg"], inp["Wnoise"], inp["bias"], w.k, w.gating, w.noise,
                     seed=w.seed)
         d = O.dispatch(r.ids, w.E, O.capacity(w.T, w.k, w.capacity_factor, w.E, w.min_capacity))

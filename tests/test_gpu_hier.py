@@ -95,7 +95,7 @@ def _check_aux(w, f, Lb, hr_bad):
 
 def _run(moe, w, inp, full_y):
     import torch
-    f = HO.forward_hier(inp, w, tokens=None if full_y else np.arange(0))
+    f = HO.forward_hier(inp, w, tokens=np.arange(0))  # Y: _check_forward, expert by expert
     hr, r, d = f["hier"], f["routing"], f["dispatch"]
     L = _layer(moe, w, inp)
     Lb = L.forward(dev(inp["X"]))
@@ -114,10 +114,10 @@ def test_hier_small(moe, w):
 
 def test_hier_bf16_full_size(moe):
     """The measured hierarchical workload (16 groups of 64 experts, 2 + 2 choices) at full
-    size: both levels, grouping, final assignments, aux; Y on a seeded token sample."""
+    size: both levels, grouping, final assignments, aux; Y on every token."""
     w = I.WORKLOADS["hier_bf16"]
     log(f"[hier full] {w}")
-    _run(moe, w, I.make_inputs(w), full_y=False)
+    _run(moe, w, I.make_inputs(w), full_y=True)
 
 
 def test_hier_empty_group(moe):

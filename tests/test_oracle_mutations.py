@@ -45,7 +45,7 @@ MUTATIONS = [
     ("moe", "residual dropped",
      "y = x.copy() if residual else np.zeros(D)", "y = np.zeros(D)"),
     ("moe", "expert ReLU dropped",
-     "np.maximum(x64 @ W1e64, 0.0) @ W2e64", "(x64 @ W1e64) @ W2e64"),
+     "h = np.maximum(x64 @ W1e64, 0.0)", "h = x64 @ W1e64"),
     ("moe", "dropped assignments combined", "if d.accepted[t, j]:", "if True:"),
     ("moe", "importance counts instead of gates",
      "np.add.at(imp, r.ids.ravel(), r.gates.ravel())", "np.add.at(imp, r.ids.ravel(), 1.0)"),
