@@ -46,10 +46,10 @@ TRAFFIC = {  # kernel -> (committed counter summary, the sources the kernel is b
 }
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
-    (FETCH_SIZE + WRITE_SIZE, copy-calibrated); None if absent, for another workload,
-    or taken on a different version of the kernel's source."""
+def measured_traffic(kernel: str, workload: str, layer: int | None = None):
+    """HBM bytes per launch of `kernel` (of one expert layer, if given) from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated); None if absent, for
+    another workload, or taken on a different version of the kernel's source."""
     import hashlib
     path, sources = TRAFFIC[kernel]
     try:
@@ -60,6 +60,9 @@ def measured_traffic(kernel: str, workload: str):
         return None
     if t.get("workload") != workload or t.get("source_sha256") != hashlib.sha256(src).hexdigest():
         return None
+    if layer is not None:
+        f, w_ = t.get(f"layer{layer}_fetch"), t.get(f"layer{layer}_write")
+        return None if f is None or w_ is None else float(f) + float(w_)
     return float(t["bytes_per_launch"])
 
 
@@ -93,16 +96,19 @@ def _dev(torch, a):
     return torch.from_numpy(a).to("cuda")
 
 
-def cpu_baseline(w, inp, budget_tokens: int):
-    """The oracle as it stands on the first `budget_tokens` tokens (slots exact for a prefix)."""
-    from oracle import moe as O
+def cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
-    S = min(budget_tokens, w.T)
-    t0 = time.perf_counter()
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_forward_prefix(w, inp, S: int):
+    from oracle import moe as O
     if w.gating == "batchwise":
         from oracle import batchwise as BO
         # the prefix as a batch of its own (m then follows the prefix size)
@@ -113,10 +119,29 @@ def cpu_baseline(w, inp, budget_tokens: int):
         HO.forward_hier(dict(inp, X=inp["X"][:S]), w.replace(T=S))
     else:
         O.forward(inp, w, t_count=S)
+
+
+def cpu_baseline(w, inp, budget_tokens: int, budget_tokens_1t: int):
+    """The oracle as it stands on the first `budget_tokens` tokens (slots exact for a prefix)
+    with every BLAS thread the host gives it, then on the first `budget_tokens_1t` tokens with
+    one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    S = min(budget_tokens, w.T)
+    t0 = time.perf_counter()
+    _oracle_forward_prefix(w, inp, S)
     dt = time.perf_counter() - t0
+    S1 = min(budget_tokens_1t, w.T)
+    with threadpool_limits(1):
+        t1 = time.perf_counter()
+        _oracle_forward_prefix(w, inp, S1)
+        dt1 = time.perf_counter() - t1
     return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {S} of {w.T} tokens of {w.name}: route, slots, per-token expert "
-                      f"FFN loop + combine, aux; fp64 numpy; {dt:.1f} s"}
+            "value_1_thread": S1 / dt1, "cpu_model": cpu_model(),
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"first {S} of {w.T} tokens of {w.name} on {threads} BLAS threads "
+                      f"({dt:.1f} s), first {S1} on 1 thread ({dt1:.1f} s): route, slots, "
+                      f"per-token expert FFN loop + combine, aux; fp64 numpy"}
 
 
 def copy_probe(torch, nbytes: int, reps: int):
@@ -314,6 +339,7 @@ def main():
     ap.add_argument("--workload", default="top2_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-tokens-1t", type=int, default=64)
     ap.add_argument("--cpu-tokens-backward", type=int, default=2048)
     ap.add_argument("--copy-probe", type=int, default=0, help="bytes; run copies only")
     ap.add_argument("--backward", action="store_true",
@@ -442,6 +468,26 @@ def main():
                                                    for s in range(args.steps)]))
                               for i, name in enumerate(stages)}}
 
+    def timed(fn, n):
+        """Mean event time of n back-to-back launches of fn on the current stream."""
+        fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        for i in range(n):
+            ev[i].record()
+            fn()
+        ev[n].record()
+        torch.cuda.synchronize()
+        return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(n)]))
+
+    # Outside the step: the dispatch that copies the rows into Xd (the stage of the pages'
+    # dispatch the gathered layer 1 replaces), and layer 1 reading those copied rows
+    copied = None
+    if gather:
+        n_extra = max(min(args.steps, 50), 1)
+        copied = {"dispatch_ms": timed(lambda: L.dispatch(X, rows=True), n_extra),
+                  "gemm1_on_Xd_ms": timed(lambda: L.gemm(1), n_extra), "launches": n_extra}
+
     offs = (L.st["offsets"] if w.gating == "batchwise" else L.b.offsets).cpu().numpy()
     A = int(offs[-1])
     U = int(np.count_nonzero(np.diff(offs)))  # experts that received rows
@@ -450,11 +496,16 @@ def main():
     # per launch, either layer: the used experts' weights once, the input rows once,
     # the output rows once
     gemm_bytes = U * w.D * w.H * el + A * (w.D + w.H) * el
-    gemm_ms = 0.5 * (per["gemm1"] + per["gemm2"])
     peak = PEAK_TFLOPS[w.act]
-    traffic = measured_traffic("grouped_gemm", w.name)
+    layers = {}
+    for n_, name in ((1, "gemm1"), (2, "gemm2")):
+        layers[name] = roofline(f"grouped_gemm layer {n_}", gemm_flops, gemm_bytes, per[name],
+                                peak, measured_traffic("grouped_gemm", w.name, n_))
+    slow = max(layers, key=lambda k_: per[k_])  # the headline is the slower layer
     # ids in; pos, accepted, row_token out; the rows themselves when the dispatch copies them
-    disp_bytes = w.T * w.k * (4 + 4 + 1) + A * 4 + (0 if gather else w.T * w.D * el + A * w.D * el)
+    slot_bytes = w.T * w.k * (4 + 4 + 1) + A * 4
+    row_bytes = w.T * w.D * el + A * w.D * el
+    disp_bytes = slot_bytes + (0 if gather else row_bytes)
     comb_bytes = A * w.D * el + 2 * w.T * w.D * el + w.T * w.k * 13
     out = {
         "metric": "MoE layer fwd tokens/s at 1 GPU; grouped-GEMM % MFMA peak; dispatch GB/s",
@@ -477,7 +528,8 @@ def main():
                    "capacity_factor": w.capacity_factor,
                    "capacity": moe.moe_capacity(p), "accepted_rows": A,
                    "dropped": w.T * w.k - A, "parallelism": "none (1 GPU)"},
-        "roofline": roofline("grouped_gemm", gemm_flops, gemm_bytes, gemm_ms, peak, traffic),
+        "roofline": layers[slow],
+        "roofline_layers": layers,
         "step_ms_events": {"p10": float(np.percentile(step_ev, 10)),
                            "p50": float(np.median(step_ev)),
                            "p90": float(np.percentile(step_ev, 90))},
@@ -490,10 +542,20 @@ def main():
         "combine_hbm_frac": comb_bytes / (per["combine"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "input_gen_s": t_gen,
     }
+    if copied is not None:
+        cb = slot_bytes + row_bytes
+        out["dispatch_copying_rows"] = {
+            "ms": copied["dispatch_ms"], "alg_bytes": cb,
+            "GBps": cb / (copied["dispatch_ms"] * 1e-3) / 1e9,
+            "hbm_frac": cb / (copied["dispatch_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "launches": copied["launches"],
+            "note": "moe_dispatch with Xd: reads each token row once, writes its accepted rows"}
+        out["gemm1_on_copied_rows_ms"] = copied["gemm1_on_Xd_ms"]
+        out["gather_cost_in_gemm1_ms"] = per["gemm1"] - copied["gemm1_on_Xd_ms"]
     if cold is not None:
         out["cold"] = cold
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_tokens, args.cpu_tokens_1t)
     print(json.dumps(out), flush=True)
 
 
