@@ -174,6 +174,22 @@ moe_status moe_dispatch(const moe_problem* p, const void* X, const int32_t* ids,
                         int32_t* offsets, int32_t* row_token, void* Xd,
                         void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* moe_dispatch_noalloc -- moe_dispatch without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, results and error rules as
+ * moe_dispatch (bit-identical outputs); the scratch it needs (the per-block histogram,
+ * E * ceil(T / 64) int32) lives in a fixed device array of MOE_NOALLOC_SCRATCH_BYTES
+ * inside the library, which each device holds until the process ends. A problem whose
+ * scratch would exceed it returns MOE_ERR_WORKSPACE before anything is enqueued. The call
+ * allocates nothing (its first call on a device looks up the array's address once). Every
+ * call on one device shares that device's array: calls that may overlap on one device
+ * (different streams, or host threads) race and must be serialised by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES (4u << 20)
+moe_status moe_dispatch_noalloc(const moe_problem* p, const void* X, const int32_t* ids,
+                                int32_t* pos, uint8_t* accepted, int32_t* counts,
+                                int32_t* offsets, int32_t* row_token, void* Xd,
+                                void* hip_stream);
+
 /* ---------------------------------------------------------------- experts */
 
 /* moe_pack_expert_weights -- re-lay the expert weights for the grouped GEMM.

@@ -196,6 +196,20 @@ moe_status moe_dispatch(const moe_problem* p, const void* X, const int32_t* ids,
                          as_stream(hip_stream));
 }
 
+moe_status moe_dispatch_noalloc(const moe_problem* p, const void* X, const int32_t* ids,
+                                int32_t* pos, uint8_t* accepted, int32_t* counts,
+                                int32_t* offsets, int32_t* row_token, void* Xd,
+                                void* hip_stream) {
+  Dims d;
+  MOE_TRY(validate_topk(p, &d));
+  if (!X || !ids || !pos || !accepted || !counts || !offsets || !row_token)
+    return MOE_ERR_INVALID_ARG;
+  MOE_ALIGNED(X, ids, pos, accepted, counts, offsets, row_token, Xd);
+  if (dispatch_workspace(d) > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  return dispatch_noalloc_launch(d, X, ids, pos, accepted, counts, offsets, row_token, Xd,
+                                 as_stream(hip_stream));
+}
+
 moe_status moe_pack_expert_weights(const moe_problem* p, const void* W1, const void* W2, void* W1p,
                                    void* W2p, void* hip_stream) {
   Dims d;

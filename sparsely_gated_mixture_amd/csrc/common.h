@@ -146,6 +146,9 @@ moe_status route_launch(const Dims& d, const moe_problem* p, const void* X, cons
 moe_status dispatch_launch(const Dims& d, const void* X, const int32_t* ids, int32_t* pos,
                            uint8_t* accepted, int32_t* counts, int32_t* offsets,
                            int32_t* row_token, void* Xd, void* ws, hipStream_t stream);
+moe_status dispatch_noalloc_launch(const Dims& d, const void* X, const int32_t* ids, int32_t* pos,
+                                   uint8_t* accepted, int32_t* counts, int32_t* offsets,
+                                   int32_t* row_token, void* Xd, hipStream_t stream);
 moe_status pack_launch(const Dims& d, int layer, const void* W, void* Wp, hipStream_t stream);
 moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp,
                        const int32_t* offsets, void* C, int* nonfinite, hipStream_t stream,

@@ -14,6 +14,8 @@
 //      min(count, C)), ranks its assignments in token order with wave ballots,
 //      writes pos / accepted / row_token, then copies each token row once
 //      into every accepted destination row with 16-byte vectors.
+#include <mutex>
+
 #include "common.h"
 
 namespace moe {
@@ -177,12 +179,43 @@ __global__ __launch_bounds__(kThreads) void dispatch_place(
   }
 }
 
+// Scratch of the allocation-free dispatch: the per-block histogram columns live in this
+// fixed array (every word is written by dispatch_count before it is read, so nothing needs
+// clearing between calls). Host code never passes the array's name to a kernel: in host code
+// that name is a stand-in, not the device address. It uses the address hipGetSymbolAddress
+// returns for the current device (each device holds its own copy).
+__device__ __align__(256) int32_t scratch[MOE_NOALLOC_SCRATCH_BYTES / sizeof(int32_t)];
+
 }  // namespace
 
 static int dispatch_blocks(const Dims& d) { return ceil_div(d.T, kTok); }
 
 size_t dispatch_workspace(const Dims& d) {
   return align256(static_cast<size_t>(d.E) * dispatch_blocks(d) * sizeof(int32_t));
+}
+
+// The device address of `scratch` on the current device, looked up once per device.
+static void* noalloc_scratch() {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptrs[dev] = ptr;
+  }
+  return ptrs[dev];
+}
+
+moe_status dispatch_noalloc_launch(const Dims& d, const void* X, const int32_t* ids, int32_t* pos,
+                                   uint8_t* accepted, int32_t* counts, int32_t* offsets,
+                                   int32_t* row_token, void* Xd, hipStream_t stream) {
+  if (dispatch_workspace(d) > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = noalloc_scratch();
+  if (!ws) return MOE_ERR_HIP;
+  return dispatch_launch(d, X, ids, pos, accepted, counts, offsets, row_token, Xd, ws, stream);
 }
 
 moe_status dispatch_launch(const Dims& d, const void* X, const int32_t* ids, int32_t* pos,

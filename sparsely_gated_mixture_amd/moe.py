@@ -35,7 +35,7 @@ ENTRY_POINTS = [
     "moe_pack_expert_weights_t", "moe_combine_backward", "moe_expert_ffn_backward",
     "moe_route_backward", "moe_backward_workspace_size", "moe_expert_weight_grad",
     "moe_expert_ffn_backward_recompute", "moe_route_backward_switch", "moe_route_scores",
-    "moe_grouped_gemm_gather", "moe_expert_ffn_gather",
+    "moe_grouped_gemm_gather", "moe_expert_ffn_gather", "moe_dispatch_noalloc",
 ]
 
 
@@ -94,6 +94,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_packed_weight_bytes": (sz, [P, ctypes.c_int]),
         "moe_route": (ctypes.c_int, [P] + [vp] * 10 + [vp, sz, vp]),
         "moe_dispatch": (ctypes.c_int, [P] + [vp] * 8 + [vp, sz, vp]),
+        "moe_dispatch_noalloc": (ctypes.c_int, [P] + [vp] * 8 + [vp]),
         "moe_pack_expert_weights": (ctypes.c_int, [P, vp, vp, vp, vp, vp]),
         "moe_grouped_gemm": (ctypes.c_int, [P, ctypes.c_int, vp, vp, vp, vp, vp]),
         "moe_expert_ffn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp]),
@@ -211,6 +212,13 @@ def moe_dispatch(p, X, ids, pos, accepted, counts, offsets, row_token, Xd, ws, s
     _check(_lib.moe_dispatch(ctypes.byref(p), _ptr(X), _ptr(ids), _ptr(pos), _ptr(accepted),
                              _ptr(counts), _ptr(offsets), _ptr(row_token), _ptr(Xd), _ptr(ws),
                              ws.numel() if ws is not None else 0, _stream(stream)), "moe_dispatch")
+
+
+def moe_dispatch_noalloc(p, X, ids, pos, accepted, counts, offsets, row_token, Xd, stream=None):
+    _check(_lib.moe_dispatch_noalloc(ctypes.byref(p), _ptr(X), _ptr(ids), _ptr(pos),
+                                     _ptr(accepted), _ptr(counts), _ptr(offsets),
+                                     _ptr(row_token), _ptr(Xd), _stream(stream)),
+           "moe_dispatch_noalloc")
 
 
 def moe_pack_expert_weights(p, W1, W2, W1p, W2p, stream=None):
