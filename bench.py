@@ -339,7 +339,7 @@ def main():
     ap.add_argument("--workload", default="top2_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
-    ap.add_argument("--cpu-tokens-1t", type=int, default=64)
+    ap.add_argument("--cpu-tokens-1t", type=int, default=512)
     ap.add_argument("--cpu-tokens-backward", type=int, default=2048)
     ap.add_argument("--copy-probe", type=int, default=0, help="bytes; run copies only")
     ap.add_argument("--backward", action="store_true",

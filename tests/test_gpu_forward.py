@@ -59,6 +59,8 @@ def _check_forward(moe, w, inp, r, d, b, full_y: bool = True, flat_aux: bool = T
     keep = np.zeros(w.T, bool)
     keep[ok] = True
     toks = toks[keep[toks] & m[toks].all(axis=1)]
+    if full_y:  # every token but those a near-tie flip touched
+        assert toks.size == int((keep & m.all(axis=1)).sum())
     if full_y:
         Zo = oracle_expert_outputs(zkey, w, inp, d)
         ref = O.combine_rows(Zo, r, d, inp["X"], tokens=toks)

@@ -226,9 +226,10 @@ def test_expert_ffn(moe, name):
     A = int(d.offsets[-1])
     # every accepted row of both layers against the oracle, expert by expert
     Hh, Zh = host(Hd), host(Z)
-    st = dict(dh=0.0, rh=0.0, dz=0.0, rz=0.0)
+    st = dict(dh=0.0, rh=0.0, dz=0.0, rz=0.0, n=0)
 
     def one(e, r0, r1, h, z):
+        st["n"] += r1 - r0
         st["dh"] = max(st["dh"], max_abs(Hh[r0:r1], h))
         st["rh"] = max(st["rh"], float(np.abs(h).max()))
         st["dz"] = max(st["dz"], max_abs(Zh[r0:r1], z))
@@ -238,6 +239,7 @@ def test_expert_ffn(moe, name):
     eh, ez = st["dh"] / st["rh"], st["dz"] / st["rz"]
     log(f"  all {A} rows: Hd rel err {eh:.2e} (max abs {st['dh']:.2e}), "
         f"Z rel err {ez:.2e} (max abs {st['dz']:.2e})")
+    assert st["n"] == A  # every accepted row was compared
     assert eh < TOL[w.act] and ez < TOL[w.act]
     # rows past the accepted ones are untouched
     if A < rows:
