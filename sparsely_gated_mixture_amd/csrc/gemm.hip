@@ -31,6 +31,9 @@
 //     hardware bf16 rounding, ReLU as an integer max on the bit pattern, the
 //     non-finite test compiled in only where a flag is given; rows leave as
 //     16-byte stores through a wave-private LDS tile.
+#include <mutex>
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -330,6 +333,330 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
   if (kCheck) note_nonfinite(g.nonfinite, bad);
 }
 
+// ------------------------------------------------------------------ 256 x 256 tiles
+// The large-group kernel (bf16, K a multiple of 64): one persistent block of 4 waves per CU
+// walks a list of 256 x 256 output tiles, each wave computing a 128 x 128 quarter (256 fp32
+// accumulators a lane). Both operands go through LDS, so each byte brought to the CU feeds
+// 256 rows or columns (the 128 x 256 kernel above re-streams B for every 128 rows): a third
+// fewer operand bytes per FLOP.
+//   * Operands land in LDS by direct loads (global_load_lds_dwordx4: lane l of a wave writes
+//     its 16 bytes at M0 + 16 l), with no registers spent on staging. A stage is 64 deep in k.
+//     A: each load instruction moves 8 whole 128-byte row segments (lane l: row l / 8), so
+//     every request is a full cache line; rows are gathered through row_token for layer 1. In
+//     LDS a row's eight 16-byte segments are XOR-permuted by the row's low three bits (lane
+//     l fetches the segment that belongs at its slot), so the MFMA reads, 32 rows at one k
+//     offset, hit distinct banks. B: the packed weights' 1 KB fragments (32 columns x 16 k)
+//     are copied as they are and read back as whole 1 KB runs.
+//   * LDS holds two stages of A and three of B (32 KB each, 160 KB). One barrier a stage,
+//     before its last k-step; the loads of A stage st+2 go out between that k-step's MFMAs and
+//     those of B stage st+2 between the MFMAs of stage st's first three k-steps (B's third
+//     slot lets them start a stage early), a few at a time, so the wave's in-order issue never
+//     stalls behind a burst of loads. The loads are issued in
+//     inline assembly so the compiler, which cannot tell the ring slots apart, does not wait
+//     for every load in flight before each LDS read; the kernel waits for its own loads
+//     (vmcnt: a wave's vector memory operations complete in issue order) and its own reads
+//     (lgkmcnt) before the barrier.
+//   * Tiles: every thread counts the row tiles of its share of the experts once; a tile's
+//     expert is then found by the one thread whose share holds it. After a tile's last k-step
+//     the next tile's first stage is requested before the epilogue, so its latency overlaps
+//     the epilogue's work, and no block launch separates the tiles. Each XCD's 32 CUs walk a
+//     contiguous run of the tile order (expert, column tile, row tile) together, sharing
+//     operands in their L2.
+//   * The MFMA takes the weight fragment as its first operand, so the accumulator holds the
+//     tile transposed: lane l owns output row l % 32 of its 32 x 32 block and, in registers
+//     4q .. 4q+3, four adjacent columns 8q + 4 (l / 32) .. +3. The epilogue stages a 32 x 64
+//     piece of each wave's quarter at a time in LDS and stores it back as whole 128-byte row
+//     runs (full cache lines).
+constexpr int kBig = 256;                  // tile rows and columns
+constexpr int kMaxGemmExperts = 4096;      // the library's largest E
+constexpr int kFragBytes = 1024;           // one 64-lane x 16-byte fragment
+constexpr int kStageBytes = kBig * 128;    // one operand's stage: 256 rows (columns) x 64 bf16
+constexpr int kBOff = 2 * kStageBytes;     // B's three slots follow A's two
+constexpr int kSlot2 = kBOff + 2 * kStageBytes;  // B's third slot: also staging and scratch
+constexpr int kStageTile = 4096;           // epilogue staging per wave: 32 rows x 128 bytes
+constexpr int kScratch = kSlot2 + kStageBytes - 64;  // scan scratch and the tile broadcast
+constexpr size_t kBigLds = 5 * static_cast<size_t>(kStageBytes);  // 160 KB
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(p)));
+}
+// 16 bytes a lane from global memory at base + voff (base wave-uniform, voff a 32-bit byte
+// offset) into LDS at lds + 16 * lane (lds wave-uniform).
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base)
+               : "memory");
+}
+// This wave's vector memory operations (all but the last N) and LDS reads done, then the
+// workgroup barrier.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int kEpi, bool kCheck, bool kGather>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int* wt = reinterpret_cast<int*>(smem + kScratch);       // 4 ints: block scan
+  int* bc = reinterpret_cast<int*>(smem + kScratch + 32);  // 3 ints: tile broadcast
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int E = g.E;
+  const int32_t* off = g.offsets;
+
+  // ---- row tiles per expert: thread tid owns experts e0 .. e1-1 and keeps the number of row
+  // tiles before them (excl) and in them (mine)
+  const int per = (E + kThreads - 1) / kThreads;
+  const int e0 = tid * per, e1 = min(E, e0 + per);
+  int mine = 0;
+  for (int e = e0; e < e1; ++e) mine += (off[e + 1] - off[e] + kBig - 1) / kBig;
+  int excl;
+  const int row_tiles = block_exclusive_scan<kThreads>(mine, &excl, wt);
+  const int NT = (g.N + kBig - 1) / kBig;
+  const int total_tiles = row_tiles * NT;
+  const int per_xcd = (total_tiles + kXcds - 1) / kXcds;
+  const int nblk_xcd = gridDim.x / kXcds;
+  const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
+  const int first = xcd * per_xcd + local, last = min(total_tiles, (xcd + 1) * per_xcd);
+  const int n_my = first < last ? (last - first + nblk_xcd - 1) / nblk_xcd : 0;
+  if (n_my == 0) return;
+
+  const int K = g.K;
+  const int nst = K / 64;
+  const unsigned char* Ab = static_cast<const unsigned char*>(g.A);
+  const unsigned char* Wp = reinterpret_cast<const unsigned char*>(g.Wp);
+  const int aseg = ((lane & 7) ^ ((lane >> 3) & 7)) * 16;  // the segment this lane's slot holds
+  const uint32_t ring = lds_offset(smem);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // per-tile state: group rows, output origin, this wave's load sources (A rows 64w .. 64w+63
+  // as 8 instructions of 8 rows, B column blocks 2w and 2w+1). Rows past the group repeat its
+  // last row and column blocks past N repeat the last one (neither is ever stored). The tile's
+  // expert is found by the thread whose experts hold its row tile and broadcast through LDS
+  // (B's third slot, free between tiles).
+  int r0 = 0, rows = 1, n0 = 0;
+  uint32_t aoff[8];
+  const unsigned char* bbase[2];  // wave-uniform: the packed weights of this wave's column blocks
+  uint32_t boff = lane * 16;
+  auto setup = [&](int m) {
+    const int logical = first + m * nblk_xcd;
+    const int q = logical / NT;
+    if (q >= excl && q < excl + mine) {
+      int e = e0, cum = excl, t = (off[e0 + 1] - off[e0] + kBig - 1) / kBig;
+      while (cum + t <= q) {
+        cum += t;
+        ++e;
+        t = (off[e + 1] - off[e] + kBig - 1) / kBig;
+      }
+      bc[0] = e;
+      bc[1] = cum;
+      bc[2] = t;
+    }
+    __syncthreads();
+    const int e = __builtin_amdgcn_readfirstlane(bc[0]);
+    const int cum = __builtin_amdgcn_readfirstlane(bc[1]), mt = __builtin_amdgcn_readfirstlane(bc[2]);
+    const int loc = logical - cum * NT;
+    const int n_tile = loc / mt, m_tile = loc - n_tile * mt;
+    r0 = off[e] + m_tile * kBig;
+    rows = min(kBig, off[e + 1] - r0);
+    n0 = n_tile * kBig;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = min(64 * wave + 8 * i + (lane >> 3), rows - 1);
+      const int64_t arow = kGather ? g.row_token[r0 + r] : r0 + r;
+      aoff[i] = static_cast<uint32_t>(arow * K * 2 + aseg);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int nb = min(n0 / 32 + 2 * wave + j, g.NB - 1);
+      bbase[j] = Wp + (static_cast<int64_t>(e) * g.NB + nb) * g.KS * kFragBytes;
+    }
+  };
+  // A stage st goes to A slot st % 2, B stage st to B slot st % 3 (8 loads a wave each)
+  auto dma_a = [&](int st, int i) {
+    dma16(Ab, aoff[i] + st * 128, ring + (st & 1) * kStageBytes + (64 * wave + 8 * i) * 128);
+  };
+  auto dma_b = [&](int st, int n) {
+    const int j = n >> 2, ks = n & 3;
+    dma16(bbase[j], boff + (st * 4 + ks) * kFragBytes,
+          ring + kBOff + (st % 3) * kStageBytes + ((2 * wave + j) * 4 + ks) * kFragBytes);
+  };
+  auto issue_ab = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma_a(st, i);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) dma_b(st, n);
+  };
+
+  f32x16 acc[4][4];
+  // A fragment of row block mb, k-step ks: lane l reads row mb*32 + l%32, 16-byte chunk
+  // 2 ks + l/32 of the row, stored at slot chunk ^ (row & 7) = chunk ^ (l & 7)
+  int a_lane = (lane & 31) * 128;
+  int a_xor = lane & 7, a_half = lane >> 5;
+  u32x4 fa[2][4], fb[2][4];
+  auto read = [&](int st, int ks, int b) {
+    const unsigned char* pa = smem + (st & 1) * kStageBytes;
+    const unsigned char* pb = smem + kBOff + (st % 3) * kStageBytes;
+    const int slot = ((2 * ks + a_half) ^ a_xor) * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      fa[b][i] = *reinterpret_cast<const u32x4*>(pa + (wm * 4 + i) * 32 * 128 + a_lane + slot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      fb[b][j] = *reinterpret_cast<const u32x4*>(pb + ((wn * 4 + j) * 4 + ks) * kFragBytes + lane * 16);
+  };
+  // One k-step's 16 MFMAs in four groups; after group i, dmas(i) issues this k-step's share
+  // of the loads. The scheduling barriers keep the compiler from regrouping them.
+  auto mma_all = [&](int b, auto dmas) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mma<uint16_t>(fb[b][j], fa[b][i], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+      dmas(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto none = [](int) {};
+
+  // Stage st: k-steps 1..3 are read one ahead of the MFMAs; the loads of B stage st+2 (into
+  // the B slot stage st-1 freed) go out between the MFMAs of k-steps 0..2. Before the last
+  // k-step, wait for stage st+1 (this wave's loads by count: only B stage st+2 may still be in
+  // flight; every wave's by the barrier, after which every wave has also finished reading
+  // stage st) and read its first k-step; the loads of A stage st+2 (into the A slot stage st
+  // freed) go out between the last k-step's MFMAs. The loads and the wait count depend on
+  // uniform branches; the LDS reads do not (after the last stage the read is of a stale slot
+  // and unused), so the compiler's own accounting of them is the same on every path.
+  auto body = [&](int st) {
+    const bool refill = st + 2 < nst;
+    auto b_part = [&](int first_n, int count) {
+      return [&, first_n, count](int grp) {
+        if (refill) {
+          for (int n = first_n + (grp * count) / 4; n < first_n + ((grp + 1) * count) / 4; ++n)
+            dma_b(st + 2, n);
+        }
+      };
+    };
+    read(st, 1, 1);
+    mma_all(0, b_part(0, 3));
+    read(st, 2, 0);
+    mma_all(1, b_part(3, 3));
+    read(st, 3, 1);
+    mma_all(0, b_part(6, 2));
+    if (refill) wait_barrier<8>();
+    else wait_barrier<0>();
+    read(st + 1, 0, 0);
+    mma_all(1, [&](int grp) {
+      if (refill) {
+        dma_a(st + 2, 2 * grp);
+        dma_a(st + 2, 2 * grp + 1);
+      }
+    });
+  };
+  uint16_t* C = static_cast<uint16_t*>(g.C);
+  unsigned char* stile = smem + kSlot2 + wave * kStageTile;
+  bool bad = false;
+
+  __syncthreads();  // the scan scratch is read by every thread before the tile lookup reuses it
+  setup(0);
+  issue_ab(0);
+  if (nst > 1) issue_ab(1);
+  for (int m = 0; m < n_my; ++m) {
+    // The lane-derived offsets are recomputed from an opaque copy of the lane index every
+    // tile: left loop-invariant, the compiler hoists every address of the unrolled body out of
+    // the tile loop and runs out of registers holding them.
+    int lq = lane;
+    asm volatile("" : "+v"(lq));
+    a_lane = (lq & 31) * 128;
+    a_xor = lq & 7;
+    a_half = lq >> 5;
+    boff = lq * 16;
+    // stage 0 of this tile has landed: after the first tile, its two stages were issued
+    // before the previous tile's 32 epilogue stores (every one of them is issued), so all
+    // but the last 16 + 32 operations are done
+    if (m == 0) {
+      if (nst > 1) wait_barrier<16>();
+      else wait_barrier<0>();
+    } else {
+      if (nst > 1) wait_barrier<48>();
+      else wait_barrier<32>();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    read(0, 0, 0);
+    for (int st = 0; st < nst; ++st) body(st);
+
+    // ---- every wave has finished reading this tile's stages once past the barrier; the next
+    // tile's first two stages go out before this tile's epilogue, so their latency overlaps it
+    const int r0c = r0, rowsc = rows, n0c = n0;
+    wait_barrier<0>();
+    if (m + 1 < n_my) {
+      setup(m + 1);
+      issue_ab(0);
+      if (nst > 1) issue_ab(1);
+    }
+    // keep the epilogue's conversions below the loads (hoisted above them, their results would
+    // all be live at once)
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- epilogue: lane owns output row (wm*4+i)*32 + l%32; register 4q+s is column
+    // (wn*4+j)*32 + 8q + 4(l/32) + s. Each wave stages a 32 x 64 piece (rows i, columns of
+    // j-pair h) in its own LDS tile (in B's third slot, idle until the next tile's third stage),
+    // then stores it as 128-byte runs, 8 rows an instruction. The staged rows are 128 bytes with
+    // their 16-byte chunks XOR-permuted by the row's low three bits, so neither the writes nor
+    // the reads conflict on banks.
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const f32x16& a = acc[i][2 * h + jj];
+            if (kCheck)
+              bad |= !isfinite(a[4 * qd]) || !isfinite(a[4 * qd + 1]) || !isfinite(a[4 * qd + 2]) ||
+                     !isfinite(a[4 * qd + 3]);
+            s16x2 h0 = __builtin_bit_cast(s16x2, __builtin_convertvector((f32x2){a[4 * qd], a[4 * qd + 1]}, bf16x2));
+            s16x2 h1 = __builtin_bit_cast(s16x2, __builtin_convertvector((f32x2){a[4 * qd + 2], a[4 * qd + 3]}, bf16x2));
+            if (kEpi == 1) {
+              h0 = __builtin_elementwise_max(h0, (s16x2){0, 0});
+              h1 = __builtin_elementwise_max(h1, (s16x2){0, 0});
+            }
+            uint2 v;
+            v.x = __builtin_bit_cast(uint32_t, h0);
+            v.y = __builtin_bit_cast(uint32_t, h1);
+            // column byte offset inside the 128-byte staged row: jj*64 + qd*16 + (l/32)*8
+            const int row = lq & 31;
+            const int cb = jj * 64 + qd * 16 + (lq >> 5) * 8;
+            const int sw = ((cb >> 4) ^ (row & 7)) * 16 + (cb & 15);
+            *reinterpret_cast<uint2*>(stile + row * 128 + sw) = v;
+          }
+        // read back: instruction p covers rows 8p .. 8p+7, lane l: row 8p + l/8, chunk l % 8
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int row = 8 * p + (lq >> 3), ch = lq & 7;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(stile + row * 128 + ((ch ^ (row & 7)) * 16));
+          // a row past the group holds exactly the group's last row (its A row was repeated),
+          // so it is written there again, unchanged: every store is issued, keeping the count
+          // the next tile's first wait relies on
+          const int grow = min(wm * 128 + i * 32 + row, rowsc - 1);
+          const int col = n0c + wn * 128 + h * 64 + ch * 8;
+          *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(r0c + grow) * g.N + col) = v;
+        }
+        // one piece at a time: converting every accumulator up front would need 128 more
+        // registers than the wave has
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+  if (kCheck) note_nonfinite(g.nonfinite, bad);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // One thread per (expert, column block, k-step, lane): lane's 16-byte B operand.
 // Column n = nb*32 + lane%32, k = ks*2V + (lane/32)*V + i; zero padded. kTrans: the
 // source is stored [E, N, K] (B = the transpose of a weight, for the backward pass).
@@ -519,6 +846,26 @@ static int device_cus() {
   return cus[dev];
 }
 
+// The 256 x 256 kernel needs more LDS than the default per-block limit: raise it once per
+// device for each instance.
+template <int kEpi, bool kCheck, bool kGather>
+static moe_status launch_big(const GemmArgs& g, int grid, hipStream_t stream) {
+  static std::once_flag once[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  const size_t lds = kBigLds;
+  bool ok = true;
+  std::call_once(once[dev], [&] {
+    ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_big<kEpi, kCheck, kGather>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             static_cast<int>(kBigLds)) ==
+         hipSuccess;
+  });
+  if (!ok) return MOE_ERR_HIP;
+  grouped_gemm_big<kEpi, kCheck, kGather><<<grid, kThreads, lds, stream>>>(g);
+  return launch_status();
+}
+
 moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp, const int32_t* offsets,
                        void* C, int* nonfinite, hipStream_t stream, const void* mask,
                        const int32_t* row_token) {
@@ -537,6 +884,20 @@ moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp, 
   g.N = N;
   g.NB = ceil_div(N, 32);
   g.KS = gemm_ks(d, K);
+  // Large groups (bf16, at least 192 rows per expert on average, enough 256 x 256 tiles to give
+  // every CU one): the 256 x 256 LDS-staged kernel
+  // (its A row offsets are 32-bit byte offsets)
+  const int64_t a_rows = row_token ? d.T : d.max_rows;
+  if (d.dtype == MOE_BF16 && K % 64 == 0 && N % kBig == 0 && !mask && a_rows * K * 2 < (1LL << 32) &&
+      d.E <= kMaxGemmExperts && d.max_rows >= 192LL * d.E &&
+      gemm_tiles(d, N, kBig) >= device_cus()) {
+    // persistent: one block per CU
+    const int grid = std::max(kXcds, device_cus() / kXcds * kXcds);
+    if (g.row_token) return launch_big<1, false, true>(g, grid, stream);
+    if (layer == 1) return launch_big<1, false, false>(g, grid, stream);
+    if (nonfinite) return launch_big<0, true, false>(g, grid, stream);
+    return launch_big<0, false, false>(g, grid, stream);
+  }
   // 128-row tiles, or 64-row ones when the 128-row tiles would not give every CU's two block
   // slots two tiles each (a small or narrow layer): twice the blocks then share the work
   const int bm = gemm_tiles(d, N, 128) < 4LL * device_cus() ? 64 : 128;
