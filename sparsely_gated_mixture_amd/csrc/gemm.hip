@@ -398,7 +398,6 @@ template <int kEpi, bool kCheck, bool kGather>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
   extern __shared__ __align__(16) unsigned char smem[];
   int* wt = reinterpret_cast<int*>(smem + kScratch);       // 4 ints: block scan
-  int* bc = reinterpret_cast<int*>(smem + kScratch + 32);  // 3 ints: tile broadcast
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int E = g.E;
@@ -429,63 +428,69 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
   const uint32_t ring = lds_offset(smem);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // per-tile state: group rows, output origin, this wave's load sources (A rows 64w .. 64w+63
-  // as 8 instructions of 8 rows, B column blocks 2w and 2w+1). Rows past the group repeat its
-  // last row and column blocks past N repeat the last one (neither is ever stored). The tile's
-  // expert is found by the thread whose experts hold its row tile and broadcast through LDS
-  // (B's third slot, free between tiles).
-  int r0 = 0, rows = 1, n0 = 0;
-  uint32_t aoff[8];
-  const unsigned char* bbase[2];  // wave-uniform: the packed weights of this wave's column blocks
-  uint32_t boff = lane * 16;
-  auto setup = [&](int m) {
+  // ---- tiles and their load sources. A tile is an expert's 256-row tile and a 256-column
+  // tile; the block's tiles have increasing row-tile indices, so a walk over the experts
+  // (uniform loads of the offsets) finds each one's expert. This wave's load sources: A rows
+  // 64w .. 64w+63 as 8 instructions of 8 rows (byte offsets into A), B column blocks 2w and
+  // 2w+1 (wave-uniform bases into the packed weights). Rows past the group repeat its last row
+  // and column blocks past N repeat the last one (neither is ever stored).
+  struct Tile {
+    int e, r0, rows, n0;
+  };
+  int we = 0, wcum = 0;  // walk state: expert we's first row tile is wcum
+  auto locate = [&](int m) {
     const int logical = first + m * nblk_xcd;
     const int q = logical / NT;
-    if (q >= excl && q < excl + mine) {
-      int e = e0, cum = excl, t = (off[e0 + 1] - off[e0] + kBig - 1) / kBig;
-      while (cum + t <= q) {
-        cum += t;
-        ++e;
-        t = (off[e + 1] - off[e] + kBig - 1) / kBig;
-      }
-      bc[0] = e;
-      bc[1] = cum;
-      bc[2] = t;
+    int t = (off[we + 1] - off[we] + kBig - 1) / kBig;
+    while (wcum + t <= q) {
+      wcum += t;
+      ++we;
+      t = (off[we + 1] - off[we] + kBig - 1) / kBig;
     }
-    __syncthreads();
-    const int e = __builtin_amdgcn_readfirstlane(bc[0]);
-    const int cum = __builtin_amdgcn_readfirstlane(bc[1]), mt = __builtin_amdgcn_readfirstlane(bc[2]);
-    const int loc = logical - cum * NT;
-    const int n_tile = loc / mt, m_tile = loc - n_tile * mt;
-    r0 = off[e] + m_tile * kBig;
-    rows = min(kBig, off[e + 1] - r0);
-    n0 = n_tile * kBig;
+    const int loc = logical - wcum * NT;
+    const int n_tile = loc / t, m_tile = loc - n_tile * t;
+    Tile T;
+    T.e = we;
+    T.r0 = off[we] + m_tile * kBig;
+    T.rows = min(kBig, off[we + 1] - T.r0);
+    T.n0 = n_tile * kBig;
+    return T;
+  };
+  // in two halves: the rows (gathered through row_token) are requested first and turned into
+  // offsets later, so the wait for them can come after other work
+  int tok[8];
+  auto request_rows = [&](const Tile& T) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int r = min(64 * wave + 8 * i + (lane >> 3), rows - 1);
-      const int64_t arow = kGather ? g.row_token[r0 + r] : r0 + r;
-      aoff[i] = static_cast<uint32_t>(arow * K * 2 + aseg);
+      const int r = min(64 * wave + 8 * i + (lane >> 3), T.rows - 1);
+      tok[i] = kGather ? g.row_token[T.r0 + r] : T.r0 + r;
     }
+  };
+  auto sources = [&](const Tile& T, uint32_t (&ao)[8], const unsigned char* (&bb)[2]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ao[i] = static_cast<uint32_t>(static_cast<int64_t>(tok[i]) * K * 2 + aseg);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int nb = min(n0 / 32 + 2 * wave + j, g.NB - 1);
-      bbase[j] = Wp + (static_cast<int64_t>(e) * g.NB + nb) * g.KS * kFragBytes;
+      const int nb = min(T.n0 / 32 + 2 * wave + j, g.NB - 1);
+      bb[j] = Wp + (static_cast<int64_t>(T.e) * g.NB + nb) * g.KS * kFragBytes;
     }
   };
-  // A stage st goes to A slot st % 2, B stage st to B slot st % 3 (8 loads a wave each)
-  auto dma_a = [&](int st, int i) {
-    dma16(Ab, aoff[i] + st * 128, ring + (st & 1) * kStageBytes + (64 * wave + 8 * i) * 128);
+  // the current tile's sources and the next tile's (its first two stages are loaded while the
+  // current tile's last two compute)
+  uint32_t ao_cur[8], ao_nxt[8];
+  const unsigned char* bb_cur[2];
+  const unsigned char* bb_nxt[2];
+  uint32_t boff = lane * 16;
+
+  // The stages form one stream across the block's tiles: stage s (the k-stage s % nst of tile
+  // s / nst) goes to A slot s % 2 and B slot s % 3 (8 loads a wave each).
+  auto dma_a = [&](int s, int kst, int i) {
+    dma16(Ab, ao_cur[i] + kst * 128, ring + (s & 1) * kStageBytes + (64 * wave + 8 * i) * 128);
   };
-  auto dma_b = [&](int st, int n) {
+  auto dma_b = [&](int s, int kst, int n) {
     const int j = n >> 2, ks = n & 3;
-    dma16(bbase[j], boff + (st * 4 + ks) * kFragBytes,
-          ring + kBOff + (st % 3) * kStageBytes + ((2 * wave + j) * 4 + ks) * kFragBytes);
-  };
-  auto issue_ab = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dma_a(st, i);
-#pragma unroll
-    for (int n = 0; n < 8; ++n) dma_b(st, n);
+    dma16(bb_cur[j], boff + (kst * 4 + ks) * kFragBytes,
+          ring + kBOff + (s % 3) * kStageBytes + ((2 * wave + j) * 4 + ks) * kFragBytes);
   };
 
   f32x16 acc[4][4];
@@ -494,9 +499,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
   int a_lane = (lane & 31) * 128;
   int a_xor = lane & 7, a_half = lane >> 5;
   u32x4 fa[2][4], fb[2][4];
-  auto read = [&](int st, int ks, int b) {
-    const unsigned char* pa = smem + (st & 1) * kStageBytes;
-    const unsigned char* pb = smem + kBOff + (st % 3) * kStageBytes;
+  auto read = [&](int s, int ks, int b) {
+    const unsigned char* pa = smem + (s & 1) * kStageBytes;
+    const unsigned char* pb = smem + kBOff + (s % 3) * kStageBytes;
     const int slot = ((2 * ks + a_half) ^ a_xor) * 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -517,98 +522,105 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto none = [](int) {};
 
-  // Stage st: k-steps 1..3 are read one ahead of the MFMAs; the loads of B stage st+2 (into
-  // the B slot stage st-1 freed) go out between the MFMAs of k-steps 0..2. Before the last
-  // k-step, wait for stage st+1 (this wave's loads by count: only B stage st+2 may still be in
-  // flight; every wave's by the barrier, after which every wave has also finished reading
-  // stage st) and read its first k-step; the loads of A stage st+2 (into the A slot stage st
-  // freed) go out between the last k-step's MFMAs. The loads and the wait count depend on
-  // uniform branches; the LDS reads do not (after the last stage the read is of a stale slot
-  // and unused), so the compiler's own accounting of them is the same on every path.
-  auto body = [&](int st) {
-    const bool refill = st + 2 < nst;
+  // Stage s (k-stage st of tile m): k-steps 1..3 are read one ahead of the MFMAs; the B loads of
+  // stage s+2 (into the B slot stage s-1 freed) go out between the MFMAs of k-steps 0..2.
+  // Before the last k-step, wait for stage s+1 (this wave's loads by count: only B of stage s+2
+  // may still be in flight; every wave's by the barrier, after which every wave has also
+  // finished reading stage s) and read its first k-step; the A loads of stage s+2 (into the A
+  // slot stage s freed) go out between the last k-step's MFMAs. Stage s+2 belongs to the next
+  // tile for a tile's last two stages. The loads and the wait count depend on uniform branches;
+  // the LDS reads do not (after the block's last stage the read is of a stale slot and unused),
+  // so the compiler's own accounting of them is the same on every path.
+  const int S = n_my * nst;
+  auto body = [&](int s, int st) {
+    const bool refill = s + 2 < S;
+    const int kst2 = st + 2 >= nst ? st + 2 - nst : st + 2;
+    // the current tile's last refill was stage nst-1 (in body nst-3): from here on the refills
+    // are the next tile's
+    if (st == nst - 2 && refill) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ao_cur[i] = ao_nxt[i];
+      bb_cur[0] = bb_nxt[0];
+      bb_cur[1] = bb_nxt[1];
+    }
     auto b_part = [&](int first_n, int count) {
       return [&, first_n, count](int grp) {
         if (refill) {
           for (int n = first_n + (grp * count) / 4; n < first_n + ((grp + 1) * count) / 4; ++n)
-            dma_b(st + 2, n);
+            dma_b(s + 2, kst2, n);
         }
       };
     };
-    read(st, 1, 1);
+    read(s, 1, 1);
     mma_all(0, b_part(0, 3));
-    read(st, 2, 0);
+    read(s, 2, 0);
     mma_all(1, b_part(3, 3));
-    read(st, 3, 1);
+    read(s, 3, 1);
     mma_all(0, b_part(6, 2));
     if (refill) wait_barrier<8>();
     else wait_barrier<0>();
-    read(st + 1, 0, 0);
+    read(s + 1, 0, 0);
     mma_all(1, [&](int grp) {
       if (refill) {
-        dma_a(st + 2, 2 * grp);
-        dma_a(st + 2, 2 * grp + 1);
+        dma_a(s + 2, kst2, 2 * grp);
+        dma_a(s + 2, kst2, 2 * grp + 1);
       }
     });
   };
-  uint16_t* C = static_cast<uint16_t*>(g.C);
-  unsigned char* stile = smem + kSlot2 + wave * kStageTile;
-  bool bad = false;
 
-  __syncthreads();  // the scan scratch is read by every thread before the tile lookup reuses it
-  setup(0);
-  issue_ab(0);
-  if (nst > 1) issue_ab(1);
+  uint16_t* C = static_cast<uint16_t*>(g.C);
+  bool bad = false;
+  __syncthreads();  // the scan scratch is read by every thread before any load reuses LDS
+  Tile cur = locate(0), nxt_t = cur;
+  request_rows(cur);
+  sources(cur, ao_cur, bb_cur);
+  if (n_my > 1) {
+    nxt_t = locate(1);
+    request_rows(nxt_t);
+    sources(nxt_t, ao_nxt, bb_nxt);
+  }
+  // stages 0 and 1 (tile 0), then wait for stage 0
+#pragma unroll
+  for (int s0 = 0; s0 < 2; ++s0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma_a(s0, s0, i);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) dma_b(s0, s0, n);
+  }
+  wait_barrier<16>();
+  read(0, 0, 0);
+
+  int s = 0;
   for (int m = 0; m < n_my; ++m) {
-    // The lane-derived offsets are recomputed from an opaque copy of the lane index every
-    // tile: left loop-invariant, the compiler hoists every address of the unrolled body out of
-    // the tile loop and runs out of registers holding them.
-    int lq = lane;
-    asm volatile("" : "+v"(lq));
-    a_lane = (lq & 31) * 128;
-    a_xor = lq & 7;
-    a_half = lq >> 5;
-    boff = lq * 16;
-    // stage 0 of this tile has landed: after the first tile, its two stages were issued
-    // before the previous tile's 32 epilogue stores (every one of them is issued), so all
-    // but the last 16 + 32 operations are done
-    if (m == 0) {
-      if (nst > 1) wait_barrier<16>();
-      else wait_barrier<0>();
-    } else {
-      if (nst > 1) wait_barrier<48>();
-      else wait_barrier<32>();
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    read(0, 0, 0);
-    for (int st = 0; st < nst; ++st) body(st);
+    for (int st = 0; st < nst; ++st, ++s) body(s, st);
 
-    // ---- every wave has finished reading this tile's stages once past the barrier; the next
-    // tile's first two stages go out before this tile's epilogue, so their latency overlaps it
-    const int r0c = r0, rowsc = rows, n0c = n0;
-    wait_barrier<0>();
-    if (m + 1 < n_my) {
-      setup(m + 1);
-      issue_ab(0);
-      if (nst > 1) issue_ab(1);
+    // ---- epilogue (the next tile's first two stages are already in flight). The next-but-one
+    // tile's sources are requested first, so their latency overlaps the epilogue.
+    const Tile done = cur;
+    cur = nxt_t;
+    const bool more2 = m + 2 < n_my;
+    if (more2) {
+      nxt_t = locate(m + 2);
+      request_rows(nxt_t);
     }
-    // keep the epilogue's conversions below the loads (hoisted above them, their results would
-    // all be live at once)
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- epilogue: lane owns output row (wm*4+i)*32 + l%32; register 4q+s is column
-    // (wn*4+j)*32 + 8q + 4(l/32) + s. Each wave stages a 32 x 64 piece (rows i, columns of
-    // j-pair h) in its own LDS tile (in B's third slot, idle until the next tile's third stage),
-    // then stores it as 128-byte runs, 8 rows an instruction. The staged rows are 128 bytes with
-    // their 16-byte chunks XOR-permuted by the row's low three bits, so neither the writes nor
-    // the reads conflict on banks.
+    // lane owns output row (wm*4+i)*32 + l%32; register 4q+s is column (wn*4+j)*32 + 8q +
+    // 4(l/32) + s. Each wave stages a 32 x 64 piece (rows i, columns of j-pair h) in its own LDS
+    // tile (in the B slot of the tile's last stage, free until the next tile's first refill),
+    // then stores it as 128-byte runs, 8 rows an instruction. The staged rows are 128 bytes
+    // with their 16-byte chunks XOR-permuted by the row's low three bits, so neither the writes
+    // nor the reads conflict on banks. The lane-derived offsets come from an opaque copy of the
+    // lane index: left loop-invariant, the compiler hoists every address of the unrolled code
+    // out of the tile loop and runs out of registers holding them.
+    int lq = lane;
+    asm volatile("" : "+v"(lq));
+    unsigned char* stile = smem + kBOff + ((s - 1) % 3) * kStageBytes + wave * kStageTile;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -642,16 +654,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
           const int row = 8 * p + (lq >> 3), ch = lq & 7;
           const u32x4 v = *reinterpret_cast<const u32x4*>(stile + row * 128 + ((ch ^ (row & 7)) * 16));
           // a row past the group holds exactly the group's last row (its A row was repeated),
-          // so it is written there again, unchanged: every store is issued, keeping the count
-          // the next tile's first wait relies on
-          const int grow = min(wm * 128 + i * 32 + row, rowsc - 1);
-          const int col = n0c + wn * 128 + h * 64 + ch * 8;
-          *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(r0c + grow) * g.N + col) = v;
+          // so it is written there again, unchanged
+          const int grow = min(wm * 128 + i * 32 + row, done.rows - 1);
+          const int col = done.n0 + wn * 128 + h * 64 + ch * 8;
+          *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(done.r0 + grow) * g.N + col) = v;
         }
         // one piece at a time: converting every accumulator up front would need 128 more
         // registers than the wave has
         __builtin_amdgcn_sched_barrier(0);
       }
+    // every wave is done with the staging slot before the next tile's first refill reuses it
+    __syncthreads();
+    if (more2) sources(nxt_t, ao_nxt, bb_nxt);
   }
   if (kCheck) note_nonfinite(g.nonfinite, bad);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -888,7 +902,8 @@ moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp, 
   // every CU one): the 256 x 256 LDS-staged kernel
   // (its A row offsets are 32-bit byte offsets)
   const int64_t a_rows = row_token ? d.T : d.max_rows;
-  if (d.dtype == MOE_BF16 && K % 64 == 0 && N % kBig == 0 && !mask && a_rows * K * 2 < (1LL << 32) &&
+  if (d.dtype == MOE_BF16 && K % 64 == 0 && K >= 256 && N % kBig == 0 && !mask &&
+      a_rows * K * 2 < (1LL << 32) &&
       d.E <= kMaxGemmExperts && d.max_rows >= 192LL * d.E &&
       gemm_tiles(d, N, kBig) >= device_cus()) {
     // persistent: one block per CU
