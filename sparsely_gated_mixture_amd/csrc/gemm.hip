@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
 //     its 16 bytes at M0 + 16 l), with no registers spent on staging. A stage is 64 deep in k.
 //     A: each load instruction moves 8 whole 128-byte row segments (lane l: row l / 8), so
 //     every request is a full cache line; rows are gathered through row_token for layer 1. In
-//     LDS a row's eight 16-byte segments are XOR-permuted by the row's low three bits (lane
+//     LDS a row's eight 16-byte segments are XOR-permuted by bits 1-3 of the row index (lane
 //     l fetches the segment that belongs at its slot), so the MFMA reads, 32 rows at one k
 //     offset, hit distinct banks. B: the packed weights' 1 KB fragments (32 columns x 16 k)
 //     are copied as they are and read back as whole 1 KB runs.
@@ -424,7 +424,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
   const int nst = K / 64;
   const unsigned char* Ab = static_cast<const unsigned char*>(g.A);
   const unsigned char* Wp = reinterpret_cast<const unsigned char*>(g.Wp);
-  const int aseg = ((lane & 7) ^ ((lane >> 3) & 7)) * 16;  // the segment this lane's slot holds
+  // lane l of A load instruction i writes row 8i + l/8 of its 8-row group, slot l % 8, and
+  // fetches the row segment that belongs at that slot (see the read below)
+  auto aseg = [&](int i) { return ((lane & 7) ^ ((4 * i + (lane >> 4)) & 7)) * 16; };
   const uint32_t ring = lds_offset(smem);
   const int wm = wave >> 1, wn = wave & 1;
 
@@ -468,7 +470,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
   };
   auto sources = [&](const Tile& T, uint32_t (&ao)[8], const unsigned char* (&bb)[2]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ao[i] = static_cast<uint32_t>(static_cast<int64_t>(tok[i]) * K * 2 + aseg);
+    for (int i = 0; i < 8; ++i) ao[i] = static_cast<uint32_t>(static_cast<int64_t>(tok[i]) * K * 2 + aseg(i));
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int nb = min(T.n0 / 32 + 2 * wave + j, g.NB - 1);
@@ -495,9 +497,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
 
   f32x16 acc[4][4];
   // A fragment of row block mb, k-step ks: lane l reads row mb*32 + l%32, 16-byte chunk
-  // 2 ks + l/32 of the row, stored at slot chunk ^ (row & 7) = chunk ^ (l & 7)
+  // 2 ks + l/32 of the row, stored at slot chunk ^ ((row >> 1) & 7) = chunk ^ ((l >> 1) & 7):
+  // the 16 lanes the LDS serves together (rows 16g .. 16g+15) then cover all 64 banks, since
+  // a 128-byte row spans half of them and rows r, r+1 share the XOR term but not the half.
   int a_lane = (lane & 31) * 128;
-  int a_xor = lane & 7, a_half = lane >> 5;
+  int a_xor = (lane >> 1) & 7, a_half = lane >> 5;
   u32x4 fa[2][4], fb[2][4];
   auto read = [&](int s, int ks, int b) {
     const unsigned char* pa = smem + (s & 1) * kStageBytes;
