@@ -6,9 +6,10 @@
 // input is added back; a dropped assignment contributes nothing, so a token
 // with every assignment dropped leaves the layer unchanged.
 //
-// One wave per token: the token's (row, gate) pairs are uniform across the
-// wave; lanes stride over the row in 16-byte vectors, accumulate in fp32 in
-// ascending j (a fixed order, no atomics), and round once.
+// One wave per token (its index made wave-uniform, so the token's ids, gates and
+// slots come through scalar loads): lanes take two 16-byte vectors of the row at a
+// time and issue every load of both (residual and the accepted expert rows) before
+// the FMAs; fp32 accumulation in ascending j (a fixed order, no atomics), one rounding.
 #include "common.h"
 
 namespace moe {
@@ -16,6 +17,13 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Every row is read once and Y is written once: the loads and stores carry the non-temporal
+// hint (streamed, not kept in the caches), which measurably raises the achieved bandwidth.
+typedef unsigned int u32v4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ntl(const uint4* p) {
+  const u32v4 v = __builtin_nontemporal_load(reinterpret_cast<const u32v4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 template <typename T>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const T* __restrict__ Z, const int32_t* __restrict__ ids, const float* __restrict__ gates,
@@ -24,10 +32,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     int k, int E, int* nonfinite) {
   constexpr int V = Elem<T>::kVec;
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6));
   if (t >= Tn) return;
-  // row of each assignment in Z, -1 when dropped (kept in registers: the
-  // loops below are unrolled over MOE_MAX_K so every index is static)
   int64_t row[MOE_MAX_K];
   float gv[MOE_MAX_K];
 #pragma unroll
@@ -47,32 +53,47 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
   bool bad = false;
   if ((D % V) == 0) {
     const int nv = D / V;
-    for (int c = lane; c < nv; c += 64) {
-      float y[V];
+    // two 16-byte vectors a lane at a time, every load of both issued before the FMAs
+    for (int c0 = lane; c0 < nv; c0 += 128) {
+      const int c1 = c0 + 64;
+      const bool two = c1 < nv;
+      uint4 rv[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+      uint4 zv[MOE_MAX_K][2];
+      const uint4* rrow = R ? reinterpret_cast<const uint4*>(R + static_cast<int64_t>(t) * D) : nullptr;
       if (R) {
-        const uint4 rv = reinterpret_cast<const uint4*>(R + static_cast<int64_t>(t) * D)[c];
-        const T* rp = reinterpret_cast<const T*>(&rv);
-#pragma unroll
-        for (int i = 0; i < V; ++i) y[i] = Elem<T>::to_f32(rp[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < V; ++i) y[i] = 0.f;
+        rv[0] = ntl(rrow + c0);
+        if (two) rv[1] = ntl(rrow + c1);
       }
 #pragma unroll
       for (int j = 0; j < MOE_MAX_K; ++j) {
         if (row[j] < 0) continue;
-        const uint4 zv = reinterpret_cast<const uint4*>(Z + row[j] * D)[c];
-        const T* zp = reinterpret_cast<const T*>(&zv);
-#pragma unroll
-        for (int i = 0; i < V; ++i) y[i] = fmaf(gv[j], Elem<T>::to_f32(zp[i]), y[i]);
+        const uint4* zr = reinterpret_cast<const uint4*>(Z + row[j] * D);
+        zv[j][0] = ntl(zr + c0);
+        if (two) zv[j][1] = ntl(zr + c1);
       }
-      T out[V];
 #pragma unroll
-      for (int i = 0; i < V; ++i) {
-        bad |= !isfinite(y[i]);
-        out[i] = Elem<T>::from_f32(y[i]);
+      for (int h = 0; h < 2; ++h) {
+        if (h == 1 && !two) break;
+        float y[V];
+        const T* rp = reinterpret_cast<const T*>(&rv[h]);
+#pragma unroll
+        for (int i = 0; i < V; ++i) y[i] = R ? Elem<T>::to_f32(rp[i]) : 0.f;
+#pragma unroll
+        for (int j = 0; j < MOE_MAX_K; ++j) {
+          if (row[j] < 0) continue;
+          const T* zp = reinterpret_cast<const T*>(&zv[j][h]);
+#pragma unroll
+          for (int i = 0; i < V; ++i) y[i] = fmaf(gv[j], Elem<T>::to_f32(zp[i]), y[i]);
+        }
+        T out[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          bad |= !isfinite(y[i]);
+          out[i] = Elem<T>::from_f32(y[i]);
+        }
+        uint4* dst = reinterpret_cast<uint4*>(Y + static_cast<int64_t>(t) * D) + (h ? c1 : c0);
+        __builtin_nontemporal_store(*reinterpret_cast<const u32v4*>(out), reinterpret_cast<u32v4*>(dst));
       }
-      reinterpret_cast<uint4*>(Y + static_cast<int64_t>(t) * D)[c] = *reinterpret_cast<const uint4*>(out);
     }
   } else {
     for (int c = lane; c < D; c += 64) {
