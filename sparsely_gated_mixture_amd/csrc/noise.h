@@ -63,9 +63,14 @@ __device__ __forceinline__ void sincos_2pi(double u, double& s, double& c) {
   pc = fma(pc, x2, -1.0 / 24.0);
   pc = fma(pc, x2, 0.5);
   const double cx = fma(-x2, pc, 1.0);
-  const int qi = static_cast<int>(q) & 3;  // angle = q pi/2 + x
-  s = qi == 0 ? sx : qi == 1 ? cx : qi == 2 ? -sx : -cx;
-  c = qi == 0 ? cx : qi == 1 ? -sx : qi == 2 ? -cx : sx;
+  // angle = q pi/2 + x: an odd quadrant swaps sin and cos; sin changes sign in quadrants 2
+  // and 3, cos in quadrants 1 and 2 (sign-bit flips, no branches)
+  const int qi = static_cast<int>(q) & 3;
+  const bool odd = (qi & 1) != 0;
+  const double sa = odd ? cx : sx, ca = odd ? sx : cx;
+  const uint64_t fs = static_cast<uint64_t>(qi & 2) << 62, fc = static_cast<uint64_t>((qi + 1) & 2) << 62;
+  s = __longlong_as_double(static_cast<long long>(static_cast<uint64_t>(__double_as_longlong(sa)) ^ fs));
+  c = __longlong_as_double(static_cast<long long>(static_cast<uint64_t>(__double_as_longlong(ca)) ^ fc));
 }
 
 // log(n 2^-53) in fp64 for an integer n in [1, 2^53]: n = 2^e m with m in [sqrt(1/2),

@@ -66,6 +66,15 @@ ROUTE_SHAPES = [
                capacity_factor=0.0, seed=15),
     I.Workload("sw64", T=40000, D=40, E=24, k=1, H=16, act="bf16", gating="switch", noise=False,
                capacity_factor=1.0, seed=16),
+    # more tokens than one 128-row tile wave of the machine: 128 experts with noise, a router
+    # bias and a ragged last tile (T = 256 tiles + 77 rows); 256 experts without noise; 256
+    # experts with noise, k = 1 and D = 128 (two k-stages)
+    I.Workload("fused_e128", T=32845, D=512, E=128, k=3, H=16, act="bf16", gating="noisy",
+               noise=True, capacity_factor=0.0, seed=17, zipf_bias=1.1),
+    I.Workload("fused_clean", T=32768, D=192, E=256, k=2, H=16, act="bf16", gating="noisy",
+               noise=False, capacity_factor=0.0, seed=18),
+    I.Workload("fused_top1", T=33000, D=128, E=256, k=1, H=16, act="bf16", gating="noisy",
+               noise=True, capacity_factor=0.0, seed=19),
 ]
 
 
@@ -76,6 +85,16 @@ def test_route_tile_shapes(moe, w):
     r = O.route(inp["X"], inp["Wg"], inp["Wnoise"], inp["bias"], w.k, w.gating, w.noise,
                 seed=w.seed)
     _check_route(w, r, _route_gpu(moe, w, inp))
+
+
+def test_route_external_noise_full_size(moe):
+    """top2_bf16's shape with the noise given by the caller: the scores use it exactly (the
+    oracle given the same noise)."""
+    w, inp = workload_inputs("top2_bf16")
+    eps = np.random.default_rng(5).standard_normal((w.T, w.E)).astype(np.float32)
+    r = O.route(inp["X"], inp["Wg"], inp["Wnoise"], inp["bias"], w.k, w.gating, w.noise,
+                seed=w.seed, eps=eps)
+    _check_route(w, r, _route_gpu(moe, w, inp, eps=eps))
 
 
 def _check_route(w, r, g):
