@@ -148,8 +148,17 @@ __global__ void router_pack(const float* __restrict__ Wg, const float* __restric
 // ------------------------------------------------------------------ router GEMM + epilogue
 // BM token rows per block (128, or 64 / 32 when T is small). kGrouped: rows grouped by
 // gate (tile table from goff in dynamic LDS, G + 1 ints).
-template <typename XT, bool kFullK, int BM, bool kGrouped>
-__global__ __launch_bounds__(kThreads, 2) void router_gemm(GemmArgs a) {
+// kNoiseWaves (noise drawn here, 128-row tiles, not grouped): the block has 8 waves. Waves
+// 0-3 compute the tile as in the 4-wave form; wave 4 + w shares a SIMD with wave w and, while
+// wave w runs its MFMAs, draws the Gaussian noise its epilogue will need into an LDS tile, in
+// the order that epilogue reads it (one (token, 4 experts) group a lane per k-stage at
+// D = 1024). The noise is then vector-ALU work of a second wave beside the MFMAs instead of
+// work after them: on this chip the two overlap when they come from different waves.
+constexpr int kNoiseGroups = 16;  // noise groups a lane of a noise wave draws per tile
+template <typename XT, bool kFullK, int BM, bool kGrouped, bool kNoiseWaves = false>
+__global__ __launch_bounds__(kNoiseWaves ? 2 * kThreads : kThreads, kNoiseWaves ? 1 : 2)
+void router_gemm(GemmArgs a) {
+  static_assert(!kNoiseWaves || (BM == 128 && !kGrouped), "noise waves: 128-row tiles, flat gate");
   constexpr int V = Elem<XT>::kVec;
   constexpr int kPieces = sizeof(XT) == 2 ? 3 : 1;
   constexpr int kStageElems = 128 / static_cast<int>(sizeof(XT));
@@ -161,6 +170,8 @@ __global__ __launch_bounds__(kThreads, 2) void router_gemm(GemmArgs a) {
 
   __shared__ __align__(16) unsigned char sA[2][kStage];
   extern __shared__ int sCum[];  // grouped: G + 1 running row-tile counts
+  // noise tile: [MFMA wave w][32-row block m][pass h][lane] float4, the epilogue's order
+  __shared__ __align__(16) float4 sE[kNoiseWaves ? (kThreads / 64) * MB * 4 * 64 : 1];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int T = a.T, D = a.D, E = a.E;
@@ -214,6 +225,32 @@ __global__ __launch_bounds__(kThreads, 2) void router_gemm(GemmArgs a) {
     rows = min(BM, T - r0);
   }
   const int nst = a.KS / 4;
+
+  if constexpr (kNoiseWaves) {
+    if (wave >= kThreads / 64) {
+      // noise wave: the groups MFMA wave w = wave - 4 reads in its epilogue (32 experts of
+      // block n_tile * 4 + w, 128 rows), spread over the k-stages, one barrier a stage as
+      // the MFMA waves have (their prologue's and every stage's)
+      const int w = wave - kThreads / 64;
+      const int eb = n_tile * 4 + w;
+      auto draw = [&](int gi) {  // gi = 4 m + h
+        const int m = gi >> 2, h = gi & 3;
+        const int it = lane + 64 * h;
+        const int row = it >> 3, g4 = it & 7;
+        const int e0 = eb * 32 + 4 * g4;
+        if (m * 32 + row >= rows || e0 >= E) return;
+        float ep[4];
+        noise4(a.seed, 0, r0 + m * 32 + row, e0 >> 2, ep);
+        sE[((w * MB + m) * 4 + h) * 64 + lane] = make_float4(ep[0], ep[1], ep[2], ep[3]);
+      };
+      __syncthreads();
+      for (int st = 0; st < nst; ++st) {
+        for (int gi = st * kNoiseGroups / nst; gi < (st + 1) * kNoiseGroups / nst; ++gi) draw(gi);
+        __syncthreads();
+      }
+      return;
+    }
+  }
 
   const XT* X = static_cast<const XT*>(a.X);
   const int aseg = tid & 7, arow0 = tid >> 3;
@@ -341,7 +378,13 @@ __global__ __launch_bounds__(kThreads, 2) void router_gemm(GemmArgs a) {
           sd[i] = softplus(raw);
         }
         const int64_t base = static_cast<int64_t>(t) * E + e0;
-        if (a.eps) {
+        if constexpr (kNoiseWaves) {
+          const float4 e4 = sE[((wave * MB + m) * 4 + h) * 64 + lane];
+          ep[0] = e4.x;
+          ep[1] = e4.y;
+          ep[2] = e4.z;
+          ep[3] = e4.w;
+        } else if (a.eps) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) ep[i] = (e0 + i < E) ? a.eps[base + i] : 0.f;
         } else {
@@ -570,6 +613,13 @@ const float* route_scores(const Dims& d, const void* ws) {
 template <typename XT, bool kFullK, bool kGrouped>
 static void router_gemm_bm(int bm, int grid, const GemmArgs& g, hipStream_t stream) {
   const size_t lds = kGrouped ? (static_cast<size_t>(g.G) + 1) * sizeof(int) : 0;
+  // the noise drawn here over 128-row tiles: the 8-wave form (noise waves beside the MFMAs)
+  if constexpr (!kGrouped) {
+    if (bm == 128 && g.use_noise && !g.eps) {
+      router_gemm<XT, kFullK, 128, false, true><<<grid, 2 * kThreads, 0, stream>>>(g);
+      return;
+    }
+  }
   if (bm == 128) router_gemm<XT, kFullK, 128, kGrouped><<<grid, kThreads, lds, stream>>>(g);
   else if (bm == 64) router_gemm<XT, kFullK, 64, kGrouped><<<grid, kThreads, lds, stream>>>(g);
   else router_gemm<XT, kFullK, 32, kGrouped><<<grid, kThreads, lds, stream>>>(g);
