@@ -66,11 +66,17 @@ ROUTE_SHAPES = [
                capacity_factor=0.0, seed=15),
     I.Workload("sw64", T=40000, D=40, E=24, k=1, H=16, act="bf16", gating="switch", noise=False,
                capacity_factor=1.0, seed=16),
-    # more tokens than one 128-row tile wave of the machine: 128 experts with noise, a router
-    # bias and a ragged last tile (T = 256 tiles + 77 rows); 256 experts without noise; 256
-    # experts with noise, k = 1 and D = 128 (two k-stages)
-    I.Workload("fused_e128", T=32845, D=512, E=128, k=3, H=16, act="bf16", gating="noisy",
+    # 128-row tiles (at least 512 blocks: the router's 8-wave form, noise waves beside the
+    # MFMA waves): 128 experts with a router bias and a ragged last tile (512 tiles + 77 rows);
+    # 202 experts (a partial 4-expert group and a partial 32-expert block, k = 3, half a last
+    # tile); fp32 X over 64 experts; 256 experts without noise (the 4-wave form); 256 experts
+    # with noise, k = 1 and D = 128 (two k-stages: the noise waves draw several groups a stage)
+    I.Workload("lists_e128", T=65613, D=512, E=128, k=3, H=16, act="bf16", gating="noisy",
                noise=True, capacity_factor=0.0, seed=17, zipf_bias=1.1),
+    I.Workload("lists_e202", T=65600, D=64, E=202, k=3, H=16, act="bf16", gating="noisy",
+               noise=True, capacity_factor=0.0, seed=20),
+    I.Workload("lists_f32", T=65536, D=96, E=64, k=2, H=16, act="f32", gating="noisy",
+               noise=True, capacity_factor=0.0, seed=21),
     I.Workload("fused_clean", T=32768, D=192, E=256, k=2, H=16, act="bf16", gating="noisy",
                noise=False, capacity_factor=0.0, seed=18),
     I.Workload("fused_top1", T=33000, D=128, E=256, k=1, H=16, act="bf16", gating="noisy",
