@@ -23,8 +23,9 @@
 //   aux_partial  (any other E) block b: 64 tokens; per-row softmax statistics
 //                of clean (wave reductions), then thread-per-expert column
 //                sums of the gates, P(x,i) and softmax(clean) over the rows.
-//   aux_reduce   32 experts x 8 partial lanes per block, strided fixed-order
-//                sums over blocks, then a fixed tree; fp64.
+//   aux_reduce   32 experts x 8 partial lanes per block, in 16 slices of the row
+//                blocks (grid.y), strided fixed-order sums, then a fixed tree; fp64.
+//   aux_slices   a thread per expert adds the 16 slices in order.
 //   aux_final    one block: CV^2 (two-pass, fp64), Switch term, diagnostics.
 #include "common.h"
 
@@ -33,6 +34,7 @@ namespace {
 
 constexpr int kRows = 64;  // most token rows per block (fewer when T is small)
 constexpr int kThreads = 256;
+constexpr int kSlices = 16;  // row-block slices of the column sums (each its own blocks)
 
 struct AuxArgs {
   const int32_t* ids;
@@ -45,13 +47,33 @@ struct AuxArgs {
   float* load;
   float* out;
   float* partial;  // [3][nblk][E]
-  double* sums;    // [3][E]
+  double* sums;    // [kSlices][3][E]; after aux_slices, [3][E] in slice 0
   int T, E, k, C, nblk, use_noise;
   int rows;  // token rows per block, <= kRows
   int vec;  // E % 4 == 0 and clean / std 16-byte aligned: float4 row reads
 };
 
-__device__ __forceinline__ float phi(float z) { return 0.5f * erfcf(-z * 0.70710678118654752f); }
+// erfc by the Chebyshev fit of Numerical Recipes in C (2nd ed., section 6.2, "erfcc"):
+// erfc(x) = t exp(-x^2 + P(t)) with t = 1 / (1 + |x| / 2), fractional error below 1.2e-7 in
+// exact arithmetic; evaluated in fp32 with the hardware exp and reciprocal, Phi = erfc / 2
+// stays within about 2.2e-7 of the exact value. Branch-free, unlike the library's erfcf,
+// which takes a different path per range of |x| and so splits a wave's lanes.
+__device__ __forceinline__ float erfc_cheb(float x) {
+  const float z = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.f));
+  float p = 0.17087277f;
+  p = fmaf(t, p, -0.82215223f);
+  p = fmaf(t, p, 1.48851587f);
+  p = fmaf(t, p, -1.13520398f);
+  p = fmaf(t, p, 0.27886807f);
+  p = fmaf(t, p, -0.18628806f);
+  p = fmaf(t, p, 0.09678418f);
+  p = fmaf(t, p, 0.37409196f);
+  p = fmaf(t, p, 1.00002368f);
+  const float ans = t * __expf(fmaf(-z, z, fmaf(t, p, -1.26551223f)));
+  return x >= 0.f ? ans : 2.f - ans;
+}
+__device__ __forceinline__ float phi(float z) { return 0.5f * erfc_cheb(-z * 0.70710678118654752f); }
 
 __global__ __launch_bounds__(kThreads) void aux_partial(AuxArgs a) {
   constexpr int kU = 8;  // rows in flight per thread in the column pass
@@ -211,10 +233,10 @@ __global__ __launch_bounds__(kThreads) void aux_rows(AuxArgs a) {
       float ex[NV][4], s = 0.f;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        ex[v][0] = expf(c[u][v].x - m);
-        ex[v][1] = expf(c[u][v].y - m);
-        ex[v][2] = expf(c[u][v].z - m);
-        ex[v][3] = expf(c[u][v].w - m);
+        ex[v][0] = __expf(c[u][v].x - m);
+        ex[v][1] = __expf(c[u][v].y - m);
+        ex[v][2] = __expf(c[u][v].z - m);
+        ex[v][3] = __expf(c[u][v].w - m);
         s += (ex[v][0] + ex[v][1]) + (ex[v][2] + ex[v][3]);
       }
       const float inv = 1.f / wave_sum(s);
@@ -246,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void aux_rows(AuxArgs a) {
           if (noise) {
             const float diff = cv[i] - (in[v][i] ? r1 : r0);
             float pr;
-            if (sv[i] > 0.f) pr = phi(diff / sv[i]);
+            if (sv[i] > 0.f) pr = phi(__fdividef(diff, sv[i]));
             else pr = diff > 0.f ? 1.f : (diff == 0.f ? 0.5f : 0.f);
             lsum[v][i] += pr;
           }
@@ -291,15 +313,19 @@ __global__ __launch_bounds__(kThreads) void aux_rows(AuxArgs a) {
   }
 }
 
+// Block (expert group x, slice y): 32 experts x 8 partial lanes over the slice's share of the
+// row blocks (fixed order), then a fixed tree; the slice's sums go to sums[y] (fp64).
 __global__ __launch_bounds__(kThreads) void aux_reduce(AuxArgs a) {
   __shared__ double s[3][8][32];
   const int el = threadIdx.x & 31, bl = threadIdx.x >> 5;
   const int e = blockIdx.x * 32 + el;
   const int64_t plane = static_cast<int64_t>(a.nblk) * a.E;
+  const int per = (a.nblk + kSlices - 1) / kSlices;
+  const int b0 = blockIdx.y * per, b1 = min(a.nblk, b0 + per);
   double acc[3] = {0.0, 0.0, 0.0};
   if (e < a.E) {
-    int b = bl;
-    for (; b + 24 < a.nblk; b += 32) {  // four blocks of loads in flight, summed in order
+    int b = b0 + bl;
+    for (; b + 24 < b1; b += 32) {  // four blocks of loads in flight, summed in order
       float v[3][4];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -310,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void aux_reduce(AuxArgs a) {
 #pragma unroll
         for (int q = 0; q < 3; ++q) acc[q] += v[q][u];
     }
-    for (; b < a.nblk; b += 8)
+    for (; b < b1; b += 8)
 #pragma unroll
       for (int q = 0; q < 3; ++q) acc[q] += a.partial[q * plane + static_cast<int64_t>(b) * a.E + e];
   }
@@ -318,16 +344,26 @@ __global__ __launch_bounds__(kThreads) void aux_reduce(AuxArgs a) {
   for (int q = 0; q < 3; ++q) s[q][bl][el] = acc[q];
   __syncthreads();
   if (bl == 0 && e < a.E) {
-    double v[3];
+    double* out = a.sums + static_cast<int64_t>(blockIdx.y) * 3 * a.E;
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      v[q] = ((s[q][0][el] + s[q][1][el]) + (s[q][2][el] + s[q][3][el])) +
-             ((s[q][4][el] + s[q][5][el]) + (s[q][6][el] + s[q][7][el]));
-      a.sums[q * a.E + e] = v[q];
-    }
-    if (a.importance) a.importance[e] = static_cast<float>(v[0]);
-    if (a.load) a.load[e] = static_cast<float>(v[1]);
+    for (int q = 0; q < 3; ++q)
+      out[q * a.E + e] = ((s[q][0][el] + s[q][1][el]) + (s[q][2][el] + s[q][3][el])) +
+                         ((s[q][4][el] + s[q][5][el]) + (s[q][6][el] + s[q][7][el]));
   }
+}
+
+// The slices added in order (slice 0 first) into sums[0], the per-expert results written.
+__global__ __launch_bounds__(kThreads) void aux_slices(AuxArgs a) {
+  const int e = blockIdx.x * kThreads + threadIdx.x;
+  if (e >= a.E) return;
+  double v[3] = {0.0, 0.0, 0.0};
+  for (int y = 0; y < kSlices; ++y)
+#pragma unroll
+    for (int q = 0; q < 3; ++q) v[q] += a.sums[(static_cast<int64_t>(y) * 3 + q) * a.E + e];
+#pragma unroll
+  for (int q = 0; q < 3; ++q) a.sums[q * a.E + e] = v[q];
+  if (a.importance) a.importance[e] = static_cast<float>(v[0]);
+  if (a.load) a.load[e] = static_cast<float>(v[1]);
 }
 
 // Fixed-order block sum (kThreads threads) in fp64.
@@ -412,7 +448,7 @@ static int aux_blocks(const Dims& d) { return ceil_div(d.T, aux_rows_per_block(d
 
 size_t aux_workspace(const Dims& d) {
   return align256(3 * static_cast<size_t>(aux_blocks(d)) * d.E * sizeof(float)) +
-         align256(3 * static_cast<size_t>(d.E) * sizeof(double));
+         align256(static_cast<size_t>(kSlices) * 3 * d.E * sizeof(double));
 }
 
 moe_status aux_launch(const Dims& d, const int32_t* ids, const float* gates, const float* clean,
@@ -445,7 +481,9 @@ moe_status aux_launch(const Dims& d, const int32_t* ids, const float* gates, con
   else if (a.vec && d.E <= 1024) aux_rows<4><<<a.nblk, kThreads, 0, stream>>>(a);
   else aux_partial<<<a.nblk, kThreads, 0, stream>>>(a);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
-  aux_reduce<<<ceil_div(d.E, 32), kThreads, 0, stream>>>(a);
+  aux_reduce<<<dim3(ceil_div(d.E, 32), kSlices), kThreads, 0, stream>>>(a);
+  if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  aux_slices<<<ceil_div(d.E, kThreads), kThreads, 0, stream>>>(a);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   aux_final<<<1, kThreads, 0, stream>>>(a);
   return launch_status();
