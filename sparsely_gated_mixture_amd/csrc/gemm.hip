@@ -625,20 +625,43 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
     int lq = lane;
     asm volatile("" : "+v"(lq));
     unsigned char* stile = smem + kBOff + ((s - 1) % 3) * kStageBytes + wave * kStageTile;
+    // mode 2 (the backward's dH): the mask's 16 bytes at each stored vector, requested one
+    // 32 x 64 piece ahead so their latency overlaps the previous piece's work
+    u32x4 mk[kEpi == 2 ? 2 : 1][4];
+    auto load_mask = [&](int piece) {
+      const int i = piece >> 1, h = piece & 1;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int row = 8 * p + (lq >> 3), ch = lq & 7;
+        const int grow = min(wm * 128 + i * 32 + row, done.rows - 1);
+        const int col = done.n0 + wn * 128 + h * 64 + ch * 8;
+        mk[piece & 1][p] = *reinterpret_cast<const u32x4*>(
+            static_cast<const uint16_t*>(g.mask) + static_cast<int64_t>(done.r0 + grow) * g.N + col);
+      }
+    };
+    if constexpr (kEpi == 2) load_mask(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        if constexpr (kEpi == 2) {
+          if (2 * i + h + 1 < 8) load_mask(2 * i + h + 1);
+        }
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
           for (int qd = 0; qd < 4; ++qd) {
             const f32x16& a = acc[i][2 * h + jj];
-            if (kCheck)
-              bad |= !isfinite(a[4 * qd]) || !isfinite(a[4 * qd + 1]) || !isfinite(a[4 * qd + 2]) ||
-                     !isfinite(a[4 * qd + 3]);
             s16x2 h0 = __builtin_bit_cast(s16x2, __builtin_convertvector((f32x2){a[4 * qd], a[4 * qd + 1]}, bf16x2));
             s16x2 h1 = __builtin_bit_cast(s16x2, __builtin_convertvector((f32x2){a[4 * qd + 2], a[4 * qd + 3]}, bf16x2));
+            if (kCheck) {
+              // on the rounded pair (rounding keeps NaN and infinity, and a value past the
+              // bf16 range becomes infinite in the output): an all-ones exponent, before any
+              // ReLU; integer tests on the packed values, no accumulator read twice
+              const uint32_t u0 = __builtin_bit_cast(uint32_t, h0), u1 = __builtin_bit_cast(uint32_t, h1);
+              bad |= ((u0 & 0x7f80u) == 0x7f80u) | ((u0 & 0x7f800000u) == 0x7f800000u) |
+                     ((u1 & 0x7f80u) == 0x7f80u) | ((u1 & 0x7f800000u) == 0x7f800000u);
+            }
             if (kEpi == 1) {
               h0 = __builtin_elementwise_max(h0, (s16x2){0, 0});
               h1 = __builtin_elementwise_max(h1, (s16x2){0, 0});
@@ -656,7 +679,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const int row = 8 * p + (lq >> 3), ch = lq & 7;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(stile + row * 128 + ((ch ^ (row & 7)) * 16));
+          u32x4 v = *reinterpret_cast<const u32x4*>(stile + row * 128 + ((ch ^ (row & 7)) * 16));
+          if constexpr (kEpi == 2) {  // zero where the mask is not > 0 (a NaN mask keeps it)
+            const u32x4 mq = mk[(2 * i + h) & 1][p];
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) {
+              const uint32_t mw = mq[w2];
+              uint32_t vw = v[w2];
+              if (!(__uint_as_float(mw << 16) > 0.f)) vw &= 0xffff0000u;
+              if (!(__uint_as_float(mw & 0xffff0000u) > 0.f)) vw &= 0x0000ffffu;
+              v[w2] = vw;
+            }
+          }
           // a row past the group holds exactly the group's last row (its A row was repeated),
           // so it is written there again, unchanged
           const int grow = min(wm * 128 + i * 32 + row, done.rows - 1);
@@ -906,12 +940,13 @@ moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp, 
   // every CU one): the 256 x 256 LDS-staged kernel
   // (its A row offsets are 32-bit byte offsets)
   const int64_t a_rows = row_token ? d.T : d.max_rows;
-  if (d.dtype == MOE_BF16 && K % 64 == 0 && K >= 256 && N % kBig == 0 && !mask &&
+  if (d.dtype == MOE_BF16 && K % 64 == 0 && K >= 256 && N % kBig == 0 && !(mask && nonfinite) &&
       a_rows * K * 2 < (1LL << 32) &&
       d.E <= kMaxGemmExperts && d.max_rows >= 192LL * d.E &&
       gemm_tiles(d, N, kBig) >= device_cus()) {
     // persistent: one block per CU
     const int grid = std::max(kXcds, device_cus() / kXcds * kXcds);
+    if (mask) return launch_big<2, false, false>(g, grid, stream);
     if (g.row_token) return launch_big<1, false, true>(g, grid, stream);
     if (layer == 1) return launch_big<1, false, false>(g, grid, stream);
     if (nonfinite) return launch_big<0, true, false>(g, grid, stream);

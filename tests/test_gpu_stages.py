@@ -309,6 +309,35 @@ def test_grouped_gemm_ragged(moe, act):
         assert rel_err(host(Z)[:T], ref2) < TOL[act]
 
 
+def test_grouped_gemm_check_finite_large(moe):
+    """The non-finite check of the 256 x 256 kernel (top2_bf16's layer-2 shapes, 512 rows an
+    expert): clean rows raise nothing, one NaN in one expert's rows raises MOE_ERR_NONFINITE
+    at the next check, and the record is cleared after it is reported."""
+    import torch
+    w = I.Workload("chk", T=65536, D=1024, E=256, k=2, H=4096, act="bf16", gating="noisy",
+                   noise=True, capacity_factor=1.0, seed=22)
+    p = problem_for(moe, w, check_finite=True)
+    rows = moe.moe_max_rows(p)
+    assert rows == 256 * 512
+    torch.manual_seed(22)
+    W2 = (torch.randn(w.E, w.H, w.D, device="cuda") / 64).to(torch.bfloat16)
+    W2p = torch.empty(moe.moe_packed_weight_bytes(p, 2), dtype=torch.uint8, device="cuda")
+    moe.moe_pack_expert_weights(p, None, W2, None, W2p)
+    offs = dev((np.arange(w.E + 1) * 512).astype(np.int32))
+    Hd = (torch.randn(rows, w.H, device="cuda") / 8).to(torch.bfloat16)
+    Z = torch.empty(rows, w.D, dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm(p, 2, Hd, W2p, offs, Z)
+    moe.moe_check_finite()  # clean: no error
+    Hd[77 * 512 + 300, 1234] = float("nan")
+    moe.moe_grouped_gemm(p, 2, Hd, W2p, offs, Z)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_check_finite()
+    assert ei.value.status == -3
+    z = Z.float()
+    assert torch.isnan(z[77 * 512 + 300]).all() and not torch.isnan(z[77 * 512 + 299]).any()
+    moe.moe_check_finite()  # the record was cleared
+
+
 
 def _fragment_layout(B, V, KS):
     """The packed operand layout moe.h states, from B [E, K, N]: slot (e, nb, ks, lane)
