@@ -309,6 +309,49 @@ def test_grouped_gemm_ragged(moe, act):
         assert rel_err(host(Z)[:T], ref2) < TOL[act]
 
 
+def test_grouped_gemm_large_ragged(moe):
+    """The 256 x 256 kernel (bf16, at least 192 rows an expert on average, one tile per CU)
+    on ragged groups: empty experts, 1-row groups, 255 / 256 / 257 rows, long groups, a
+    short last tile; both layers (ReLU, then plain) against numpy fp64 on every row."""
+    import torch
+    rng = np.random.default_rng(23)
+    E, D, H = 64, 1024, 1024  # 484 tiles of 256 x 256 in either layer
+    sizes = rng.integers(300, 520, E)
+    sizes[[3, 17, 40]] = 0
+    sizes[[5, 33]] = 1
+    sizes[[8, 9, 10]] = (255, 256, 257)
+    sizes[20] = 1100
+    T = int(sizes.sum())
+    w = I.Workload("bigrag", T=T, D=D, E=E, k=1, H=H, act="bf16", gating="noisy", noise=False,
+                   capacity_factor=0.0, seed=0)
+    p = problem_for(moe, w)
+    rows = moe.moe_max_rows(p)
+    assert rows >= 192 * E
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    A = I.f32_to_bf16_bits(rng.standard_normal((rows, D)).astype(np.float32))
+    W1 = I.f32_to_bf16_bits((rng.standard_normal((E, D, H)) / math.sqrt(D)).astype(np.float32))
+    W2 = I.f32_to_bf16_bits((rng.standard_normal((E, H, D)) / math.sqrt(H)).astype(np.float32))
+    W1p = torch.empty(moe.moe_packed_weight_bytes(p, 1), dtype=torch.uint8, device="cuda")
+    W2p = torch.empty(moe.moe_packed_weight_bytes(p, 2), dtype=torch.uint8, device="cuda")
+    moe.moe_pack_expert_weights(p, dev(W1), dev(W2), W1p, W2p)
+    Hd = torch.empty(rows, H, dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty(rows, D, dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm(p, 1, dev(A), W1p, dev(offs), Hd)
+    moe.moe_grouped_gemm(p, 2, Hd, W2p, dev(offs), Z)
+    Hh, Zh = f64(host(Hd)), f64(host(Z))
+    e1 = e2 = 0.0
+    for e in range(E):
+        s_ = slice(offs[e], offs[e + 1])
+        if offs[e + 1] == offs[e]:
+            continue
+        r1 = np.maximum(f64(A[s_]) @ f64(W1[e]), 0.0)
+        r2 = Hh[s_] @ f64(W2[e])  # layer 2 on the GPU's own layer-1 output
+        e1 = max(e1, np.abs(Hh[s_] - r1).max() / max(np.abs(r1).max(), 1e-30))
+        e2 = max(e2, np.abs(Zh[s_] - r2).max() / max(np.abs(r2).max(), 1e-30))
+    log(f"[gemm large ragged] {T} rows over {E} experts: layer 1 {e1:.2e}, layer 2 {e2:.2e}")
+    assert e1 < TOL["bf16"] and e2 < TOL["bf16"]
+
+
 def test_grouped_gemm_check_finite_large(moe):
     """The non-finite check of the 256 x 256 kernel (top2_bf16's layer-2 shapes, 512 rows an
     expert): clean rows raise nothing, one NaN in one expert's rows raises MOE_ERR_NONFINITE
