@@ -196,7 +196,12 @@ moe_status moe_dispatch_noalloc(const moe_problem* p, const void* X, const int32
  * Input is the pages' layout ([SWITCH] step 6): W1 [E,D,H], W2 [E,H,D]
  * (p->dtype). Output buffers hold moe_packed_weight_bytes(p, 1) and (p, 2)
  * bytes. Weights are parameters: pack once, reuse for every forward call.
- * Either input may be NULL to skip that layer. */
+ * Either input may be NULL to skip that layer.
+ * Packed layout of a [E,K,N] weight (V = 8 bf16 or 4 fp32 per 16 bytes;
+ * NB = ceil(N/32) column blocks; KS = 4 ceil(K / 8V) k-steps of 2V): 1 KB
+ * fragments, fragment (e, nb, ks) at index ((e KS/4 + ks/4) NB + nb) 4 + ks%4;
+ * its 16 bytes for lane l (0..63) hold column nb 32 + l%32, rows
+ * ks 2V + (l/32) V .. +V-1; zeros past K or N. */
 moe_status moe_pack_expert_weights(const moe_problem* p, const void* W1,
                                    const void* W2, void* W1p, void* W2p,
                                    void* hip_stream);

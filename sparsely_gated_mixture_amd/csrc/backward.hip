@@ -446,7 +446,8 @@ __global__ __launch_bounds__(kThreads) void column_sums(const float* __restrict_
 }
 
 // [Wg | Wnoise]^T packed for the router's input gradient: B[k][n] = Wg[n][k] (k < E) or
-// Wnoise[n][k - E], cast to the activation dtype; one thread per (column block, k-step, lane).
+// Wnoise[n][k - E], cast to the activation dtype; one thread per (k stage, column block,
+// k-step in the stage, lane), in the grouped GEMM's fragment order (one expert).
 template <typename T>
 __global__ void router_pack_t(const float* __restrict__ Wg, const float* __restrict__ Wn, int D,
                               int E, int NB, int KS, uint4* __restrict__ out) {
@@ -454,8 +455,9 @@ __global__ void router_pack_t(const float* __restrict__ Wg, const float* __restr
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= static_cast<int64_t>(NB) * KS * kWave) return;
   const int lane = static_cast<int>(idx % kWave);
-  const int ks = static_cast<int>((idx / kWave) % KS);
-  const int nb = static_cast<int>(idx / (static_cast<int64_t>(kWave) * KS));
+  const int64_t frag = idx / kWave;
+  const int nb = static_cast<int>((frag / 4) % NB);
+  const int ks = static_cast<int>(frag / (4 * static_cast<int64_t>(NB))) * 4 + static_cast<int>(frag % 4);
   const int n = nb * 32 + (lane & 31);
   const int k0 = ks * 2 * V + (lane >> 5) * V;
   T v[V];

@@ -10,9 +10,12 @@
 // Design (gfx950):
 //   * Weights are packed once (moe_pack_expert_weights) into MFMA fragment
 //     order: for expert e, 32-column block nb and k-step ks, the 64 lanes'
-//     16-byte B operands are contiguous. A wave then streams its B operand
-//     straight from memory with one coalesced 1 KB load per fragment; B never
-//     touches LDS.
+//     16-byte B operands are contiguous (one 1 KB fragment), and the fragments
+//     are ordered [e][ks / 4][nb][ks % 4]: one k stage (4 k-steps) of all of an
+//     expert's column blocks is one contiguous run, so a tile's stage of B is a
+//     few KB-long runs in one region rather than 4 KB pieces a whole column
+//     block apart. A wave then streams its B operand straight from memory with
+//     one coalesced 1 KB load per fragment; B never touches LDS.
 //   * A block computes a BM x 256 tile; its 4 waves split the 256 columns
 //     (64 each) and all read the same A rows, which are staged through LDS
 //     (128-byte-wide k stages, double buffered, rows padded against bank
@@ -54,7 +57,8 @@ struct GemmArgs {
   const int32_t* row_token;  // gathered A: row r of the groups is row row_token[r] of A
   int E, K, N;
   int NB;  // 32-column blocks per expert in Wp
-  int KS;  // k-steps per column block in Wp (multiple of 4)
+  int KS;  // k-steps per column block in Wp (multiple of 4); fragment (e, nb, ks) is at
+           // ((e * KS / 4 + ks / 4) * NB + nb) * 4 + ks % 4
 };
 
 // ReLU on the bit pattern: a float whose pattern read as a signed integer is negative has its
@@ -176,8 +180,9 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
 
   // ---- B stream: column blocks past N read a valid block (those results are never stored)
   const u32x4* Wb = reinterpret_cast<const u32x4*>(g.Wp);
-  const u32x4* W0 = Wb + (static_cast<int64_t>(e) * g.NB + min(n0 / 32 + wave * 2, g.NB - 1)) * g.KS * kWave + lane;
-  const u32x4* W1 = Wb + (static_cast<int64_t>(e) * g.NB + min(n0 / 32 + wave * 2 + 1, g.NB - 1)) * g.KS * kWave + lane;
+  const u32x4* W0 = Wb + (static_cast<int64_t>(e) * g.NB * g.KS + min(n0 / 32 + wave * 2, g.NB - 1) * 4) * kWave + lane;
+  const u32x4* W1 = Wb + (static_cast<int64_t>(e) * g.NB * g.KS + min(n0 / 32 + wave * 2 + 1, g.NB - 1) * 4) * kWave + lane;
+  const int64_t wstage = static_cast<int64_t>(g.NB) * 4 * kWave;  // one k stage of the expert
 
   f32x16 acc[MB][2];
 #pragma unroll
@@ -226,7 +231,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
         acc[m][1] = mma<T>(af[ks & 1][m], bq[ks][1], acc[m][1]);
       }
       __builtin_amdgcn_s_setprio(0);
-      const int64_t kn = static_cast<int64_t>(stn * 4 + ks) * kWave;
+      const int64_t kn = stn * wstage + ks * kWave;
       bq[ks][0] = W0[kn];
       bq[ks][1] = W1[kn];
     }
@@ -474,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int nb = min(T.n0 / 32 + 2 * wave + j, g.NB - 1);
-      bb[j] = Wp + (static_cast<int64_t>(T.e) * g.NB + nb) * g.KS * kFragBytes;
+      bb[j] = Wp + (static_cast<int64_t>(T.e) * g.NB * g.KS + nb * 4) * kFragBytes;
     }
   };
   // the current tile's sources and the next tile's (its first two stages are loaded while the
@@ -491,7 +496,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
   };
   auto dma_b = [&](int s, int kst, int n) {
     const int j = n >> 2, ks = n & 3;
-    dma16(bb_cur[j], boff + (kst * 4 + ks) * kFragBytes,
+    dma16(bb_cur[j], boff + static_cast<uint32_t>(kst * g.NB * 4 + ks) * kFragBytes,
           ring + kBOff + (s % 3) * kStageBytes + ((2 * wave + j) * 4 + ks) * kFragBytes);
   };
 
@@ -709,9 +714,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// One thread per (expert, column block, k-step, lane): lane's 16-byte B operand.
-// Column n = nb*32 + lane%32, k = ks*2V + (lane/32)*V + i; zero padded. kTrans: the
-// source is stored [E, N, K] (B = the transpose of a weight, for the backward pass).
+// One thread per (expert, k stage, column block, k-step in the stage, lane), in slot order:
+// lane's 16-byte B operand. Column n = nb*32 + lane%32, k = ks*2V + (lane/32)*V + i; zero
+// padded. kTrans: the source is stored [E, N, K] (B = the transpose of a weight, for the
+// backward pass).
 template <typename T, bool kTrans>
 __global__ void pack_weights(const T* __restrict__ W, int E, int K, int N, int NB, int KS,
                              uint4* __restrict__ out) {
@@ -721,10 +727,12 @@ __global__ void pack_weights(const T* __restrict__ W, int E, int K, int N, int N
   if (idx >= total) return;
   const int lane = static_cast<int>(idx % kWave);
   int64_t rest = idx / kWave;
-  const int ks = static_cast<int>(rest % KS);
-  rest /= KS;
+  const int r = static_cast<int>(rest % 4);
+  rest /= 4;
   const int nb = static_cast<int>(rest % NB);
-  const int e = static_cast<int>(rest / NB);
+  rest /= NB;
+  const int ks = static_cast<int>(rest % (KS / 4)) * 4 + r;
+  const int e = static_cast<int>(rest / (KS / 4));
   const int n = nb * 32 + (lane & 31);
   const int k0 = ks * 2 * V + (lane >> 5) * V;
   T v[V];
@@ -779,7 +787,7 @@ __global__ __launch_bounds__(256) void pack_weights_t(const T* __restrict__ W, i
     const int ks = kc * kPackKs + ksl;
     if (ks >= KS) break;  // uniform over the thread's remaining slots
     const int r = lane & 31, kb = (ksl * 2 + (lane >> 5)) * V * static_cast<int>(sizeof(T));
-    out[((static_cast<int64_t>(e) * NB + nb) * KS + ks) * kWave + lane] =
+    out[(((static_cast<int64_t>(e) * (KS / 4) + ks / 4) * NB + nb) * 4 + ks % 4) * kWave + lane] =
         *reinterpret_cast<const uint4*>(&tile[r * kStride + kb]);
   }
 }
@@ -938,10 +946,11 @@ moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp, 
   g.KS = gemm_ks(d, K);
   // Large groups (bf16, at least 192 rows per expert on average, enough 256 x 256 tiles to give
   // every CU one): the 256 x 256 LDS-staged kernel
-  // (its A row offsets are 32-bit byte offsets)
+  // (its A row offsets and its B offsets within an expert are 32-bit byte offsets)
   const int64_t a_rows = row_token ? d.T : d.max_rows;
   if (d.dtype == MOE_BF16 && K % 64 == 0 && K >= 256 && N % kBig == 0 && !(mask && nonfinite) &&
       a_rows * K * 2 < (1LL << 32) &&
+      static_cast<int64_t>(g.KS) * g.NB * kFragBytes < (1LL << 32) &&
       d.E <= kMaxGemmExperts && d.max_rows >= 192LL * d.E &&
       gemm_tiles(d, N, kBig) >= device_cus()) {
     // persistent: one block per CU

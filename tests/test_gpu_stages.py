@@ -309,13 +309,18 @@ def test_grouped_gemm_ragged(moe, act):
         assert rel_err(host(Z)[:T], ref2) < TOL[act]
 
 
-def test_grouped_gemm_large_ragged(moe):
+@pytest.mark.parametrize("D,H", [(1024, 1024), (256, 1024), (448, 1280)])
+def test_grouped_gemm_large_ragged(moe, D, H):
     """The 256 x 256 kernel (bf16, at least 192 rows an expert on average, one tile per CU)
     on ragged groups: empty experts, 1-row groups, 255 / 256 / 257 rows, long groups, a
-    short last tile; both layers (ReLU, then plain) against numpy fp64 on every row."""
+    short last tile; both layers (ReLU, then plain) against numpy fp64 on every row. With
+    D = 256 and 448, layer 1's tiles are 4 and 7 k-stages of 64 long: shorter than the 8
+    stages over which a tile's output leaves during the next tile, so the rest is stored
+    before the next epilogue (layer 2 then runs on the 128 x 256 kernel where D is not a
+    multiple of 256)."""
     import torch
     rng = np.random.default_rng(23)
-    E, D, H = 64, 1024, 1024  # 484 tiles of 256 x 256 in either layer
+    E = 64  # with D = H = 1024: 484 tiles of 256 x 256 in either layer
     sizes = rng.integers(300, 520, E)
     sizes[[3, 17, 40]] = 0
     sizes[[5, 33]] = 1
@@ -348,7 +353,8 @@ def test_grouped_gemm_large_ragged(moe):
         r2 = Hh[s_] @ f64(W2[e])  # layer 2 on the GPU's own layer-1 output
         e1 = max(e1, np.abs(Hh[s_] - r1).max() / max(np.abs(r1).max(), 1e-30))
         e2 = max(e2, np.abs(Zh[s_] - r2).max() / max(np.abs(r2).max(), 1e-30))
-    log(f"[gemm large ragged] {T} rows over {E} experts: layer 1 {e1:.2e}, layer 2 {e2:.2e}")
+    log(f"[gemm large ragged] {T} rows over {E} experts, D {D} H {H}: layer 1 {e1:.2e}, "
+        f"layer 2 {e2:.2e}")
     assert e1 < TOL["bf16"] and e2 < TOL["bf16"]
 
 
@@ -383,15 +389,17 @@ def test_grouped_gemm_check_finite_large(moe):
 
 
 def _fragment_layout(B, V, KS):
-    """The packed operand layout moe.h states, from B [E, K, N]: slot (e, nb, ks, lane)
-    holds column nb*32 + lane%32, rows ks*2V + (lane//32)*V .. +V-1, zeros past K or N."""
+    """The packed operand layout moe.h states, from B [E, K, N]: the fragment of
+    (e, nb, ks) sits at ((e * KS/4 + ks // 4) * NB + nb) * 4 + ks % 4, and its lane holds
+    column nb*32 + lane%32, rows ks*2V + (lane//32)*V .. +V-1, zeros past K or N."""
     E, K, N = B.shape
     NB = -(-N // 32)
+    Q = KS // 4
     Bp = np.zeros((E, KS * 2 * V, NB * 32), dtype=B.dtype)
     Bp[:, :K, :N] = B
-    # [E, ks, half, i, nb, col] -> [E, nb, ks, half, col, i]
-    t = Bp.reshape(E, KS, 2, V, NB, 32).transpose(0, 4, 1, 2, 5, 3)
-    return np.ascontiguousarray(t).reshape(E, NB, KS, 64, V)
+    # [E, q, r, half, i, nb, col] -> [E, q, nb, r, half, col, i]  (ks = 4q + r)
+    t = Bp.reshape(E, Q, 4, 2, V, NB, 32).transpose(0, 1, 5, 2, 3, 6, 4)
+    return np.ascontiguousarray(t).reshape(E, Q, NB, 4, 64, V)
 
 
 @pytest.mark.parametrize("act", ["f32", "bf16"])
