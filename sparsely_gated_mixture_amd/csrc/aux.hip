@@ -19,14 +19,16 @@
 //                float4 per lane: the row's softmax statistics come from two
 //                wave reductions over registers, so clean is read once; each
 //                lane keeps running sums for its experts over the wave's rows,
-//                and the four waves are added in fixed order at the end.
+//                and the block's waves (8 for E <= 256, else 4) are added in
+//                fixed order at the end.
 //   aux_partial  (any other E) block b: 64 tokens; per-row softmax statistics
 //                of clean (wave reductions), then thread-per-expert column
 //                sums of the gates, P(x,i) and softmax(clean) over the rows.
 //   aux_reduce   32 experts x 8 partial lanes per block, in 16 slices of the row
 //                blocks (grid.y), strided fixed-order sums, then a fixed tree; fp64.
-//   aux_slices   a thread per expert adds the 16 slices in order.
-//   aux_final    one block: CV^2 (two-pass, fp64), Switch term, diagnostics.
+//   aux_final    one block: the 16 slices added in order per expert, then CV^2
+//                (two-pass, fp64), the Switch term and the diagnostics, with
+//                wave butterflies and one barrier per group of block sums.
 #include "common.h"
 
 namespace moe {
@@ -47,7 +49,7 @@ struct AuxArgs {
   float* load;
   float* out;
   float* partial;  // [3][nblk][E]
-  double* sums;    // [kSlices][3][E]; after aux_slices, [3][E] in slice 0
+  double* sums;    // [kSlices][3][E]
   int T, E, k, C, nblk, use_noise;
   int rows;  // token rows per block, <= kRows
   int vec;  // E % 4 == 0 and clean / std 16-byte aligned: float4 row reads
@@ -163,22 +165,47 @@ __global__ __launch_bounds__(kThreads) void aux_partial(AuxArgs a) {
   }
 }
 
+// Wave reductions without the LDS permute path: inside each row of 16 lanes, data-parallel
+// moves exchange partners (lane ^ 1, lane ^ 2 by quad permutes, then the half-row and row
+// mirrors, which pair whole quads and whole half-rows), so every lane of a row holds the
+// same bits; the four rows are then read out and combined in a fixed order. The result is
+// the same in every lane.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xb1;        // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4e;        // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
+  v = fmaxf(v, dpp<kQuadXor1>(v));
+  v = fmaxf(v, dpp<kQuadXor2>(v));
+  v = fmaxf(v, dpp<kRowHalfMirror>(v));
+  v = fmaxf(v, dpp<kRowMirror>(v));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v += dpp<kQuadXor1>(v);
+  v += dpp<kQuadXor2>(v);
+  v += dpp<kRowHalfMirror>(v);
+  v += dpp<kRowMirror>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
-// NV float4 chunks per lane per row: lane l holds experts 256*v + 4*l + i.
-template <int NV>
-__global__ __launch_bounds__(kThreads) void aux_rows(AuxArgs a) {
-  constexpr int kWaves = kThreads / 64;
-  constexpr int U = 4 / NV;  // rows of loads in flight per wave
+// NV float4 chunks per lane per row: lane l holds experts 256*v + 4*l + i. kT threads a
+// block, U rows of loads in flight per wave.
+template <int NV, int kT, int U>
+__global__ __launch_bounds__(kT) void aux_rows(AuxArgs a) {
+  constexpr int kWaves = kT / 64;
   __shared__ float sR0[kRows], sR1[kRows];
   __shared__ int sId[kRows * MOE_MAX_K];
   __shared__ float sG[kRows * MOE_MAX_K];
@@ -189,12 +216,12 @@ __global__ __launch_bounds__(kThreads) void aux_rows(AuxArgs a) {
   const int E = a.E, k = a.k;
   const bool noise = a.use_noise != 0;
 
-  for (int i = tid; i < nr * k; i += kThreads) {
+  for (int i = tid; i < nr * k; i += kT) {
     sId[i] = a.ids[static_cast<int64_t>(t0) * k + i];
     sG[i] = a.gates[static_cast<int64_t>(t0) * k + i];
   }
   if (noise)
-    for (int r = tid; r < nr; r += kThreads) {
+    for (int r = tid; r < nr; r += kT) {
       sR0[r] = a.row_stats[2 * static_cast<int64_t>(t0 + r)];
       sR1[r] = a.row_stats[2 * static_cast<int64_t>(t0 + r) + 1];
     }
@@ -313,24 +340,65 @@ __global__ __launch_bounds__(kThreads) void aux_rows(AuxArgs a) {
   }
 }
 
+// Fixed-order fp64 reductions over the block's kThreads threads: a butterfly in each wave,
+// then the waves added in order (w0 + w1) + (w2 + w3). Every thread gets the result.
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ __forceinline__ double wave_max_d(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmax(v, __shfl_xor(v, off));
+  return v;
+}
+template <int N>
+__device__ void block_sums(double (&v)[N], double (*sh)[kThreads / 64]) {
+  static_assert(kThreads == 256, "four waves");
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    const double w = wave_sum_d(v[q]);
+    if (lane == 0) sh[q][wave] = w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < N; ++q) v[q] = (sh[q][0] + sh[q][1]) + (sh[q][2] + sh[q][3]);
+  __syncthreads();
+}
+template <int N>
+__device__ void block_maxes(double (&v)[N], double (*sh)[kThreads / 64]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    const double w = wave_max_d(v[q]);
+    if (lane == 0) sh[q][wave] = w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < N; ++q) v[q] = fmax(fmax(sh[q][0], sh[q][1]), fmax(sh[q][2], sh[q][3]));
+  __syncthreads();
+}
+
 // Block (expert group x, slice y): 32 experts x 8 partial lanes over the slice's share of the
 // row blocks (fixed order), then a fixed tree; the slice's sums go to sums[y] (fp64).
 __global__ __launch_bounds__(kThreads) void aux_reduce(AuxArgs a) {
   __shared__ double s[3][8][32];
   const int el = threadIdx.x & 31, bl = threadIdx.x >> 5;
   const int e = blockIdx.x * 32 + el;
-  const int64_t plane = static_cast<int64_t>(a.nblk) * a.E;
+  const int E = a.E;
+  const int64_t plane = static_cast<int64_t>(a.nblk) * E;
   const int per = (a.nblk + kSlices - 1) / kSlices;
   const int b0 = blockIdx.y * per, b1 = min(a.nblk, b0 + per);
   double acc[3] = {0.0, 0.0, 0.0};
-  if (e < a.E) {
+  if (e < E) {
     int b = b0 + bl;
     for (; b + 24 < b1; b += 32) {  // four blocks of loads in flight, summed in order
       float v[3][4];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int q = 0; q < 3; ++q) v[q][u] = a.partial[q * plane + static_cast<int64_t>(b + 8 * u) * a.E + e];
+        for (int q = 0; q < 3; ++q) v[q][u] = a.partial[q * plane + static_cast<int64_t>(b + 8 * u) * E + e];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -338,97 +406,71 @@ __global__ __launch_bounds__(kThreads) void aux_reduce(AuxArgs a) {
     }
     for (; b < b1; b += 8)
 #pragma unroll
-      for (int q = 0; q < 3; ++q) acc[q] += a.partial[q * plane + static_cast<int64_t>(b) * a.E + e];
+      for (int q = 0; q < 3; ++q) acc[q] += a.partial[q * plane + static_cast<int64_t>(b) * E + e];
   }
 #pragma unroll
   for (int q = 0; q < 3; ++q) s[q][bl][el] = acc[q];
   __syncthreads();
-  if (bl == 0 && e < a.E) {
-    double* out = a.sums + static_cast<int64_t>(blockIdx.y) * 3 * a.E;
+  if (bl == 0 && e < E) {
+    double* out = a.sums + static_cast<int64_t>(blockIdx.y) * 3 * E;
 #pragma unroll
     for (int q = 0; q < 3; ++q)
-      out[q * a.E + e] = ((s[q][0][el] + s[q][1][el]) + (s[q][2][el] + s[q][3][el])) +
-                         ((s[q][4][el] + s[q][5][el]) + (s[q][6][el] + s[q][7][el]));
+      out[q * E + e] = ((s[q][0][el] + s[q][1][el]) + (s[q][2][el] + s[q][3][el])) +
+                       ((s[q][4][el] + s[q][5][el]) + (s[q][6][el] + s[q][7][el]));
   }
 }
 
-// The slices added in order (slice 0 first) into sums[0], the per-expert results written.
-__global__ __launch_bounds__(kThreads) void aux_slices(AuxArgs a) {
-  const int e = blockIdx.x * kThreads + threadIdx.x;
-  if (e >= a.E) return;
-  double v[3] = {0.0, 0.0, 0.0};
-  for (int y = 0; y < kSlices; ++y)
-#pragma unroll
-    for (int q = 0; q < 3; ++q) v[q] += a.sums[(static_cast<int64_t>(y) * 3 + q) * a.E + e];
-#pragma unroll
-  for (int q = 0; q < 3; ++q) a.sums[q * a.E + e] = v[q];
-  if (a.importance) a.importance[e] = static_cast<float>(v[0]);
-  if (a.load) a.load[e] = static_cast<float>(v[1]);
-}
-
-// Fixed-order block sum (kThreads threads) in fp64.
-__device__ double block_sum(double v, double* sh) {
-  sh[threadIdx.x] = v;
-  __syncthreads();
-  for (int w = kThreads / 2; w >= 1; w >>= 1) {
-    if (threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
-    __syncthreads();
-  }
-  const double r = sh[0];
-  __syncthreads();
-  return r;
-}
-__device__ double block_max(double v, double* sh) {
-  sh[threadIdx.x] = v;
-  __syncthreads();
-  for (int w = kThreads / 2; w >= 1; w >>= 1) {
-    if (threadIdx.x < w) sh[threadIdx.x] = fmax(sh[threadIdx.x], sh[threadIdx.x + w]);
-    __syncthreads();
-  }
-  const double r = sh[0];
-  __syncthreads();
-  return r;
-}
-
+// One block: per expert the slices in order (slice 0 first), then the scalars.
 __global__ __launch_bounds__(kThreads) void aux_final(AuxArgs a) {
-  __shared__ double sh[kThreads];
+  __shared__ double sh[5][kThreads / 64];
   const int E = a.E;
-  const double* imp = a.sums;
-  const double* load = a.sums + E;
-  const double* pb = a.sums + 2 * E;
+  // the slices in order, per expert; thread t takes experts t, t + kThreads, ... and leaves
+  // their totals in slice 0's place (no other thread reads those columns)
   double si = 0, sl = 0, sfp = 0, sc = 0, mxl = -INFINITY, mxc = -INFINITY, drop = 0;
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    si += imp[e];
-    sl += load[e];
-    const double c = a.counts[e];
-    sfp += (c / a.T) * (pb[e] / a.T);
+  for (int x = threadIdx.x; x < E; x += kThreads) {
+    double v[3] = {0.0, 0.0, 0.0};
+    for (int y = 0; y < kSlices; ++y)
+#pragma unroll
+      for (int q = 0; q < 3; ++q) v[q] += a.sums[(static_cast<int64_t>(y) * 3 + q) * E + x];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) a.sums[q * E + x] = v[q];
+    if (a.importance) a.importance[x] = static_cast<float>(v[0]);
+    if (a.load) a.load[x] = static_cast<float>(v[1]);
+    si += v[0];
+    sl += v[1];
+    const double c = a.counts[x];
+    sfp += (c / a.T) * (v[2] / a.T);
     sc += c;
-    mxl = fmax(mxl, load[e]);
+    mxl = fmax(mxl, v[1]);
     mxc = fmax(mxc, c);
     drop += fmax(c - a.C, 0.0);
   }
-  si = block_sum(si, sh);
-  sl = block_sum(sl, sh);
-  sfp = block_sum(sfp, sh);
-  sc = block_sum(sc, sh);
-  mxl = block_max(mxl, sh);
-  mxc = block_max(mxc, sh);
-  drop = block_sum(drop, sh);
+  double sums5[5] = {si, sl, sfp, sc, drop};
+  block_sums(sums5, sh);
+  double maxes[2] = {mxl, mxc};
+  block_maxes(maxes, sh);
+  si = sums5[0];
+  sl = sums5[1];
+  sfp = sums5[2];
+  sc = sums5[3];
+  drop = sums5[4];
   const double mi = si / E, ml = sl / E;
-  double vi = 0, vl = 0;
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    vi += (imp[e] - mi) * (imp[e] - mi);
-    vl += (load[e] - ml) * (load[e] - ml);
+  // second pass (the deviations from the means) over the thread's own totals
+  double dev[2] = {0.0, 0.0};
+  for (int x = threadIdx.x; x < E; x += kThreads) {
+    const double v0 = a.sums[x], v1 = a.sums[E + x];
+    dev[0] += (v0 - mi) * (v0 - mi);
+    dev[1] += (v1 - ml) * (v1 - ml);
   }
-  vi = block_sum(vi, sh) / E;
-  vl = block_sum(vl, sh) / E;
+  block_sums(dev, sh);
   if (threadIdx.x == 0) {
+    const double vi = dev[0] / E, vl = dev[1] / E;
     const double mc = sc / E;
     a.out[0] = static_cast<float>(mi != 0 ? vi / (mi * mi) : 0.0);
     a.out[1] = static_cast<float>(ml != 0 ? vl / (ml * ml) : 0.0);
     a.out[2] = static_cast<float>(E * sfp);
-    a.out[3] = static_cast<float>(ml > 0 ? mxl / ml : 0.0);
-    a.out[4] = static_cast<float>(mc > 0 ? mxc / mc : 0.0);
+    a.out[3] = static_cast<float>(ml > 0 ? maxes[0] / ml : 0.0);
+    a.out[4] = static_cast<float>(mc > 0 ? maxes[1] / mc : 0.0);
     a.out[5] = static_cast<float>(drop);
     a.out[6] = static_cast<float>(si);
     a.out[7] = 0.f;
@@ -476,14 +518,12 @@ moe_status aux_launch(const Dims& d, const int32_t* ids, const float* gates, con
   a.C = d.C;
   a.vec = (d.E % 4 == 0 && (reinterpret_cast<uintptr_t>(clean) | reinterpret_cast<uintptr_t>(a.std_in)) % 16 == 0)
               ? 1 : 0;
-  if (a.vec && d.E <= 256) aux_rows<1><<<a.nblk, kThreads, 0, stream>>>(a);
-  else if (a.vec && d.E <= 512) aux_rows<2><<<a.nblk, kThreads, 0, stream>>>(a);
-  else if (a.vec && d.E <= 1024) aux_rows<4><<<a.nblk, kThreads, 0, stream>>>(a);
+  if (a.vec && d.E <= 256) aux_rows<1, 512, 2><<<a.nblk, 512, 0, stream>>>(a);
+  else if (a.vec && d.E <= 512) aux_rows<2, 256, 2><<<a.nblk, 256, 0, stream>>>(a);
+  else if (a.vec && d.E <= 1024) aux_rows<4, 256, 1><<<a.nblk, 256, 0, stream>>>(a);
   else aux_partial<<<a.nblk, kThreads, 0, stream>>>(a);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   aux_reduce<<<dim3(ceil_div(d.E, 32), kSlices), kThreads, 0, stream>>>(a);
-  if (launch_status() != MOE_OK) return MOE_ERR_HIP;
-  aux_slices<<<ceil_div(d.E, kThreads), kThreads, 0, stream>>>(a);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   aux_final<<<1, kThreads, 0, stream>>>(a);
   return launch_status();
