@@ -428,10 +428,19 @@ __global__ __launch_bounds__(kThreads) void aux_final(AuxArgs a) {
   // their totals in slice 0's place (no other thread reads those columns)
   double si = 0, sl = 0, sfp = 0, sc = 0, mxl = -INFINITY, mxc = -INFINITY, drop = 0;
   for (int x = threadIdx.x; x < E; x += kThreads) {
-    double v[3] = {0.0, 0.0, 0.0};
+    // every slice's value requested before the first addition (one block: the loads'
+    // latency, not their bytes, is what this pass waits on)
+    double buf[kSlices][3];
+#pragma unroll
     for (int y = 0; y < kSlices; ++y)
 #pragma unroll
-      for (int q = 0; q < 3; ++q) v[q] += a.sums[(static_cast<int64_t>(y) * 3 + q) * E + x];
+      for (int q = 0; q < 3; ++q) buf[y][q] = a.sums[(static_cast<int64_t>(y) * 3 + q) * E + x];
+    __builtin_amdgcn_sched_barrier(0);  // keeps the scheduler from interleaving them with the sums
+    double v[3] = {0.0, 0.0, 0.0};
+#pragma unroll
+    for (int y = 0; y < kSlices; ++y)
+#pragma unroll
+      for (int q = 0; q < 3; ++q) v[q] += buf[y][q];
 #pragma unroll
     for (int q = 0; q < 2; ++q) a.sums[q * E + x] = v[q];
     if (a.importance) a.importance[x] = static_cast<float>(v[0]);
