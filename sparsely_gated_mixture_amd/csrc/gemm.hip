@@ -714,36 +714,56 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// One thread per (expert, k stage, column block, k-step in the stage, lane), in slot order:
-// lane's 16-byte B operand. Column n = nb*32 + lane%32, k = ks*2V + (lane/32)*V + i; zero
-// padded. kTrans: the source is stored [E, N, K] (B = the transpose of a weight, for the
-// backward pass).
-template <typename T, bool kTrans>
-__global__ void pack_weights(const T* __restrict__ W, int E, int K, int N, int NB, int KS,
-                             uint4* __restrict__ out) {
+// The [E, K, N] source (W1, W2 as the pages lay them out) through LDS: a block takes one k
+// stage (4 k-steps, 8V rows of k) of kPackNb column blocks, reads those rows as whole
+// kPackNb * 32-column segments, and writes the stage's kPackNb * 4 fragments, one contiguous
+// run of the packed layout (16 bytes a thread, 1 KB a wave). Lane l of fragment (nb, ks) holds
+// column nb*32 + l%32, k = ks*2V + (l/32)*V + i; zeros past K or N. kVec: N % V == 0 and W
+// 16-byte aligned (vector loads).
+constexpr int kPackNb = 8;  // column blocks per block
+template <typename T, bool kVec>
+__global__ __launch_bounds__(256) void pack_weights(const T* __restrict__ W, int E, int K, int N, int NB,
+                                                    int KS, uint4* __restrict__ out) {
   constexpr int V = Elem<T>::kVec;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = static_cast<int64_t>(E) * NB * KS * kWave;
-  if (idx >= total) return;
-  const int lane = static_cast<int>(idx % kWave);
-  int64_t rest = idx / kWave;
-  const int r = static_cast<int>(rest % 4);
-  rest /= 4;
-  const int nb = static_cast<int>(rest % NB);
-  rest /= NB;
-  const int ks = static_cast<int>(rest % (KS / 4)) * 4 + r;
-  const int e = static_cast<int>(rest / (KS / 4));
-  const int n = nb * 32 + (lane & 31);
-  const int k0 = ks * 2 * V + (lane >> 5) * V;
-  T v[V];
+  constexpr int kRows = 8 * V;                                          // k rows of a stage
+  constexpr int kRowBytes = kPackNb * 32 * static_cast<int>(sizeof(T));  // 512 or 1024
+  constexpr int kStride = kRowBytes + 16;
+  constexpr int kSegs = kRowBytes / 16;
+  __shared__ __align__(16) unsigned char tile[kRows * kStride];
+  const int cb = blockIdx.x, q = blockIdx.y, e = blockIdx.z;
+  const int n_base = cb * kPackNb * 32, k_base = q * kRows;
+  static_assert(kRows * kSegs % 256 == 0, "whole passes");
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const int k = k0 + i;
-    v[i] = (n < N && k < K) ? W[kTrans ? (static_cast<int64_t>(e) * N + n) * K + k
-                                        : (static_cast<int64_t>(e) * K + k) * N + n]
-                            : T(0);
+  for (int p = 0; p < kRows * kSegs / 256; ++p) {
+    const int c = threadIdx.x + 256 * p;
+    const int r = c / kSegs, seg = c % kSegs;
+    const int k = k_base + r, n0 = n_base + seg * V;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (k < K) {
+      const T* row = W + (static_cast<int64_t>(e) * K + k) * N;
+      if (kVec) {
+        if (n0 < N) v = *reinterpret_cast<const uint4*>(row + n0);
+      } else {
+        T t[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) t[i] = n0 + i < N ? row[n0 + i] : T(0);
+        v = *reinterpret_cast<const uint4*>(t);
+      }
+    }
+    *reinterpret_cast<uint4*>(&tile[r * kStride + seg * 16]) = v;
   }
-  out[idx] = *reinterpret_cast<const uint4*>(v);
+  __syncthreads();
+  const int nbs = min(kPackNb, NB - cb * kPackNb);
+  const int ksl = threadIdx.x >> 6, lane = threadIdx.x & 63;  // k-step in the stage, lane
+  const int col = lane & 31, kr0 = ksl * 2 * V + (lane >> 5) * V;
+  for (int nb = 0; nb < nbs; ++nb) {
+    T t[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      t[i] = *reinterpret_cast<const T*>(&tile[(kr0 + i) * kStride + (nb * 32 + col) * static_cast<int>(sizeof(T))]);
+    out[(((static_cast<int64_t>(e) * (KS / 4) + q) * NB + cb * kPackNb + nb) * 4 + ksl) * kWave + lane] =
+        *reinterpret_cast<const uint4*>(t);
+  }
 }
 
 // The kTrans source ([E, N, K]: a lane's 16-byte operand is contiguous in a row) through LDS:
@@ -817,8 +837,6 @@ moe_status pack_launch(const Dims& d, int layer, const void* W, void* Wp, hipStr
   int K, N;
   layer_dims(d, layer, &K, &N);
   const int NB = ceil_div(N, 32), KS = gemm_ks(d, K);
-  const int64_t total = static_cast<int64_t>(d.E) * NB * KS * kWave;
-  const int grid = static_cast<int>(ceil_div64(total, 256));
   const bool tr = layer >= 3;
   if (tr) {  // the LDS-tiled re-layout of an [E, N, K] source
     const dim3 g3(ceil_div(KS, kPackKs), NB, d.E);
@@ -835,14 +853,18 @@ moe_status pack_launch(const Dims& d, int layer, const void* W, void* Wp, hipStr
     }
     return launch_status();
   }
+  // the [E, K, N] source: a block per (kPackNb column blocks, k stage, expert)
+  const dim3 g3(ceil_div(NB, kPackNb), KS / 4, d.E);
+  const int V = d.dtype == MOE_BF16 ? 8 : 4;
+  const bool vec = N % V == 0 && reinterpret_cast<uintptr_t>(W) % 16 == 0;
   if (d.dtype == MOE_BF16) {
     const auto* w = static_cast<const uint16_t*>(W);
-    if (tr) pack_weights<uint16_t, true><<<grid, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
-    else pack_weights<uint16_t, false><<<grid, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
+    if (vec) pack_weights<uint16_t, true><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
+    else pack_weights<uint16_t, false><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
   } else {
     const auto* w = static_cast<const float*>(W);
-    if (tr) pack_weights<float, true><<<grid, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
-    else pack_weights<float, false><<<grid, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
+    if (vec) pack_weights<float, true><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
+    else pack_weights<float, false><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
   }
   return launch_status();
 }
