@@ -199,9 +199,12 @@ moe_status moe_dispatch_noalloc(const moe_problem* p, const void* X, const int32
  * Either input may be NULL to skip that layer.
  * Packed layout of a [E,K,N] weight (V = 8 bf16 or 4 fp32 per 16 bytes;
  * NB = ceil(N/32) column blocks; KS = 4 ceil(K / 8V) k-steps of 2V): 1 KB
- * fragments, fragment (e, nb, ks) at index ((e KS/4 + ks/4) NB + nb) 4 + ks%4;
- * its 16 bytes for lane l (0..63) hold column nb 32 + l%32, rows
- * ks 2V + (l/32) V .. +V-1; zeros past K or N. */
+ * fragments; the 16 bytes of fragment (e, nb, ks) for lane l (0..63) hold
+ * column nb 32 + l%32, rows ks 2V + (l/32) V .. +V-1; zeros past K or N.
+ * Fragment (e, nb, ks) is at index e NB KS + nb B + (ks/4) S + ks%4 with
+ * (B, S) = (4, 4 NB) (k-stage order) when moe_max_rows(p) >= 128 E, else
+ * (KS, 4) (column-block order). The transposed packs of
+ * moe_pack_expert_weights_t follow the same rule. */
 moe_status moe_pack_expert_weights(const moe_problem* p, const void* W1,
                                    const void* W2, void* W1p, void* W2p,
                                    void* hip_stream);

@@ -446,18 +446,17 @@ __global__ __launch_bounds__(kThreads) void column_sums(const float* __restrict_
 }
 
 // [Wg | Wnoise]^T packed for the router's input gradient: B[k][n] = Wg[n][k] (k < E) or
-// Wnoise[n][k - E], cast to the activation dtype; one thread per (k stage, column block,
-// k-step in the stage, lane), in the grouped GEMM's fragment order (one expert).
+// Wnoise[n][k - E], cast to the activation dtype; one thread per (column block, k-step, lane),
+// written where the grouped GEMM's fragment strides put it (one expert).
 template <typename T>
 __global__ void router_pack_t(const float* __restrict__ Wg, const float* __restrict__ Wn, int D,
-                              int E, int NB, int KS, uint4* __restrict__ out) {
+                              int E, int NB, int KS, PackStrides ps, uint4* __restrict__ out) {
   constexpr int V = Elem<T>::kVec;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= static_cast<int64_t>(NB) * KS * kWave) return;
   const int lane = static_cast<int>(idx % kWave);
-  const int64_t frag = idx / kWave;
-  const int nb = static_cast<int>((frag / 4) % NB);
-  const int ks = static_cast<int>(frag / (4 * static_cast<int64_t>(NB))) * 4 + static_cast<int>(frag % 4);
+  const int ks = static_cast<int>((idx / kWave) % KS);
+  const int nb = static_cast<int>(idx / (static_cast<int64_t>(kWave) * KS));
   const int n = nb * 32 + (lane & 31);
   const int k0 = ks * 2 * V + (lane >> 5) * V;
   T v[V];
@@ -469,7 +468,7 @@ __global__ void router_pack_t(const float* __restrict__ Wg, const float* __restr
                                         : (Wn ? Wn[static_cast<int64_t>(n) * E + kk - E] : 0.f);
     v[i] = Elem<T>::from_f32(x);
   }
-  out[idx] = *reinterpret_cast<const uint4*>(v);
+  out[(nb * ps.block + (ks / 4) * ps.stage + ks % 4) * kWave + lane] = *reinterpret_cast<const uint4*>(v);
 }
 
 __global__ void set_offsets(int32_t* off, int T) {
@@ -1104,12 +1103,13 @@ moe_status route_backward_launch(const Dims& d, uint64_t seed, const void* X, co
   dr.max_rows = d.T;
   const int NB = ceil_div(d.D, 32), KS = router_bwd_ks(d);
   const int64_t items = static_cast<int64_t>(NB) * KS * kWave;
+  const PackStrides ps = pack_strides(dr, 3);
   if (d.dtype == MOE_BF16)
     router_pack_t<uint16_t><<<static_cast<int>(ceil_div64(items, 256)), 256, 0, stream>>>(
-        Wg, noise ? Wnoise : nullptr, d.D, d.E, NB, KS, wpack);
+        Wg, noise ? Wnoise : nullptr, d.D, d.E, NB, KS, ps, wpack);
   else
     router_pack_t<float><<<static_cast<int>(ceil_div64(items, 256)), 256, 0, stream>>>(
-        Wg, noise ? Wnoise : nullptr, d.D, d.E, NB, KS, wpack);
+        Wg, noise ? Wnoise : nullptr, d.D, d.E, NB, KS, ps, wpack);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   set_offsets<<<1, 64, 0, stream>>>(off, d.T);
   moe_status s = gemm_launch(dr, 3, dcat, wpack, off, dxr, nullptr, stream);

@@ -137,6 +137,16 @@ const float* route_scores(const Dims& d, const void* ws);
 size_t dispatch_workspace(const Dims& d);
 size_t aux_workspace(const Dims& d);
 size_t packed_weight_bytes(const Dims& d, int layer);
+// Where the packed expert weights of a layer keep their 1 KB fragments: fragment (e, nb, ks)
+// (expert, 32-column block, k-step; 4 k-steps make a k stage) sits at
+// e * expert + nb * block + (ks / 4) * stage + ks % 4. Stage order (block 4, stage 4 NB) when
+// the layer's groups average at least kStageOrderRows rows, else column-block order (block
+// KS, stage 4); expert = NB * KS either way. Every packer and every GEMM takes them from here.
+constexpr int64_t kStageOrderRows = 128;
+struct PackStrides {
+  int64_t expert, block, stage;
+};
+PackStrides pack_strides(const Dims& d, int layer);
 
 // Stage launchers (arguments already validated).
 moe_status route_launch(const Dims& d, const moe_problem* p, const void* X, const float* Wg,

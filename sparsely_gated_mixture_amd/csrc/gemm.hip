@@ -10,12 +10,14 @@
 // Design (gfx950):
 //   * Weights are packed once (moe_pack_expert_weights) into MFMA fragment
 //     order: for expert e, 32-column block nb and k-step ks, the 64 lanes'
-//     16-byte B operands are contiguous (one 1 KB fragment), and the fragments
-//     are ordered [e][ks / 4][nb][ks % 4]: one k stage (4 k-steps) of all of an
-//     expert's column blocks is one contiguous run, so a tile's stage of B is a
-//     few KB-long runs in one region rather than 4 KB pieces a whole column
-//     block apart. A wave then streams its B operand straight from memory with
-//     one coalesced 1 KB load per fragment; B never touches LDS.
+//     16-byte B operands are contiguous (one 1 KB fragment). Where the groups are
+//     large (kStageOrderRows rows an expert on average) the fragments are ordered
+//     [e][ks / 4][nb][ks % 4]: one k stage (4 k-steps) of all of an expert's
+//     column blocks is one contiguous run, so a tile's stage of B is one region
+//     rather than 4 KB pieces a whole column block apart; with small groups,
+//     where each block streams an expert's weights once, [e][nb][ks] (one long
+//     run per column block) is faster. A wave then streams its B operand straight
+//     from memory with one coalesced 1 KB load per fragment; B never touches LDS.
 //   * A block computes a BM x 256 tile; its 4 waves split the 256 columns
 //     (64 each) and all read the same A rows, which are staged through LDS
 //     (128-byte-wide k stages, double buffered, rows padded against bank
@@ -57,8 +59,8 @@ struct GemmArgs {
   const int32_t* row_token;  // gathered A: row r of the groups is row row_token[r] of A
   int E, K, N;
   int NB;  // 32-column blocks per expert in Wp
-  int KS;  // k-steps per column block in Wp (multiple of 4); fragment (e, nb, ks) is at
-           // ((e * KS / 4 + ks / 4) * NB + nb) * 4 + ks % 4
+  int KS;  // k-steps per column block in Wp (multiple of 4)
+  int64_t ws_expert, ws_block, ws_stage;  // fragment strides (PackStrides)
 };
 
 // ReLU on the bit pattern: a float whose pattern read as a signed integer is negative has its
@@ -180,9 +182,9 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
 
   // ---- B stream: column blocks past N read a valid block (those results are never stored)
   const u32x4* Wb = reinterpret_cast<const u32x4*>(g.Wp);
-  const u32x4* W0 = Wb + (static_cast<int64_t>(e) * g.NB * g.KS + min(n0 / 32 + wave * 2, g.NB - 1) * 4) * kWave + lane;
-  const u32x4* W1 = Wb + (static_cast<int64_t>(e) * g.NB * g.KS + min(n0 / 32 + wave * 2 + 1, g.NB - 1) * 4) * kWave + lane;
-  const int64_t wstage = static_cast<int64_t>(g.NB) * 4 * kWave;  // one k stage of the expert
+  const u32x4* W0 = Wb + (e * g.ws_expert + min(n0 / 32 + wave * 2, g.NB - 1) * g.ws_block) * kWave + lane;
+  const u32x4* W1 = Wb + (e * g.ws_expert + min(n0 / 32 + wave * 2 + 1, g.NB - 1) * g.ws_block) * kWave + lane;
+  const int64_t wstage = g.ws_stage * kWave;  // one k stage
 
   f32x16 acc[MB][2];
 #pragma unroll
@@ -479,7 +481,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int nb = min(T.n0 / 32 + 2 * wave + j, g.NB - 1);
-      bb[j] = Wp + (static_cast<int64_t>(T.e) * g.NB * g.KS + nb * 4) * kFragBytes;
+      bb[j] = Wp + (T.e * g.ws_expert + nb * g.ws_block) * kFragBytes;
     }
   };
   // the current tile's sources and the next tile's (its first two stages are loaded while the
@@ -496,7 +498,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
   };
   auto dma_b = [&](int s, int kst, int n) {
     const int j = n >> 2, ks = n & 3;
-    dma16(bb_cur[j], boff + static_cast<uint32_t>(kst * g.NB * 4 + ks) * kFragBytes,
+    dma16(bb_cur[j], boff + static_cast<uint32_t>(kst * static_cast<int>(g.ws_stage) + ks) * kFragBytes,
           ring + kBOff + (s % 3) * kStageBytes + ((2 * wave + j) * 4 + ks) * kFragBytes);
   };
 
@@ -717,13 +719,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
 // The [E, K, N] source (W1, W2 as the pages lay them out) through LDS: a block takes one k
 // stage (4 k-steps, 8V rows of k) of kPackNb column blocks, reads those rows as whole
 // kPackNb * 32-column segments, and writes the stage's kPackNb * 4 fragments, one contiguous
-// run of the packed layout (16 bytes a thread, 1 KB a wave). Lane l of fragment (nb, ks) holds
+// run in stage order (16 bytes a thread, 1 KB a wave). Lane l of fragment (nb, ks) holds
 // column nb*32 + l%32, k = ks*2V + (l/32)*V + i; zeros past K or N. kVec: N % V == 0 and W
 // 16-byte aligned (vector loads).
 constexpr int kPackNb = 8;  // column blocks per block
 template <typename T, bool kVec>
 __global__ __launch_bounds__(256) void pack_weights(const T* __restrict__ W, int E, int K, int N, int NB,
-                                                    int KS, uint4* __restrict__ out) {
+                                                    PackStrides ps, uint4* __restrict__ out) {
   constexpr int V = Elem<T>::kVec;
   constexpr int kRows = 8 * V;                                          // k rows of a stage
   constexpr int kRowBytes = kPackNb * 32 * static_cast<int>(sizeof(T));  // 512 or 1024
@@ -761,7 +763,7 @@ __global__ __launch_bounds__(256) void pack_weights(const T* __restrict__ W, int
 #pragma unroll
     for (int i = 0; i < V; ++i)
       t[i] = *reinterpret_cast<const T*>(&tile[(kr0 + i) * kStride + (nb * 32 + col) * static_cast<int>(sizeof(T))]);
-    out[(((static_cast<int64_t>(e) * (KS / 4) + q) * NB + cb * kPackNb + nb) * 4 + ksl) * kWave + lane] =
+    out[(e * ps.expert + (cb * kPackNb + nb) * ps.block + q * ps.stage + ksl) * kWave + lane] =
         *reinterpret_cast<const uint4*>(t);
   }
 }
@@ -773,7 +775,8 @@ __global__ __launch_bounds__(256) void pack_weights(const T* __restrict__ W, int
 constexpr int kPackKs = 16;  // k-steps per block
 template <typename T, bool kVec>
 __global__ __launch_bounds__(256) void pack_weights_t(const T* __restrict__ W, int E, int K, int N,
-                                                      int NB, int KS, uint4* __restrict__ out) {
+                                                      int NB, int KS, PackStrides ps,
+                                                      uint4* __restrict__ out) {
   constexpr int V = Elem<T>::kVec;
   constexpr int kRowBytes = kPackKs * 2 * V * static_cast<int>(sizeof(T));  // 512
   constexpr int kStride = kRowBytes + 16;
@@ -807,7 +810,7 @@ __global__ __launch_bounds__(256) void pack_weights_t(const T* __restrict__ W, i
     const int ks = kc * kPackKs + ksl;
     if (ks >= KS) break;  // uniform over the thread's remaining slots
     const int r = lane & 31, kb = (ksl * 2 + (lane >> 5)) * V * static_cast<int>(sizeof(T));
-    out[(((static_cast<int64_t>(e) * (KS / 4) + ks / 4) * NB + nb) * 4 + ks % 4) * kWave + lane] =
+    out[(e * ps.expert + nb * ps.block + (ks / 4) * ps.stage + ks % 4) * kWave + lane] =
         *reinterpret_cast<const uint4*>(&tile[r * kStride + kb]);
   }
 }
@@ -827,6 +830,18 @@ static int gemm_ks(const Dims& d, int K) {
   return ceil_div(K, stage) * 4;
 }
 
+PackStrides pack_strides(const Dims& d, int layer) {
+  int K, N;
+  layer_dims(d, layer, &K, &N);
+  const int64_t NB = ceil_div(N, 32), KS = gemm_ks(d, K);
+  const bool stage_order = d.max_rows >= kStageOrderRows * d.E;
+  PackStrides ps;
+  ps.expert = NB * KS;
+  ps.block = stage_order ? 4 : KS;
+  ps.stage = stage_order ? 4 * NB : 4;
+  return ps;
+}
+
 size_t packed_weight_bytes(const Dims& d, int layer) {
   int K, N;
   layer_dims(d, layer, &K, &N);
@@ -837,6 +852,7 @@ moe_status pack_launch(const Dims& d, int layer, const void* W, void* Wp, hipStr
   int K, N;
   layer_dims(d, layer, &K, &N);
   const int NB = ceil_div(N, 32), KS = gemm_ks(d, K);
+  const PackStrides ps = pack_strides(d, layer);
   const bool tr = layer >= 3;
   if (tr) {  // the LDS-tiled re-layout of an [E, N, K] source
     const dim3 g3(ceil_div(KS, kPackKs), NB, d.E);
@@ -844,12 +860,12 @@ moe_status pack_launch(const Dims& d, int layer, const void* W, void* Wp, hipStr
     const bool vec = K % V == 0 && reinterpret_cast<uintptr_t>(W) % 16 == 0;
     if (d.dtype == MOE_BF16) {
       const auto* w = static_cast<const uint16_t*>(W);
-      if (vec) pack_weights_t<uint16_t, true><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
-      else pack_weights_t<uint16_t, false><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
+      if (vec) pack_weights_t<uint16_t, true><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, ps, static_cast<uint4*>(Wp));
+      else pack_weights_t<uint16_t, false><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, ps, static_cast<uint4*>(Wp));
     } else {
       const auto* w = static_cast<const float*>(W);
-      if (vec) pack_weights_t<float, true><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
-      else pack_weights_t<float, false><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
+      if (vec) pack_weights_t<float, true><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, ps, static_cast<uint4*>(Wp));
+      else pack_weights_t<float, false><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, ps, static_cast<uint4*>(Wp));
     }
     return launch_status();
   }
@@ -859,12 +875,12 @@ moe_status pack_launch(const Dims& d, int layer, const void* W, void* Wp, hipStr
   const bool vec = N % V == 0 && reinterpret_cast<uintptr_t>(W) % 16 == 0;
   if (d.dtype == MOE_BF16) {
     const auto* w = static_cast<const uint16_t*>(W);
-    if (vec) pack_weights<uint16_t, true><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
-    else pack_weights<uint16_t, false><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
+    if (vec) pack_weights<uint16_t, true><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, ps, static_cast<uint4*>(Wp));
+    else pack_weights<uint16_t, false><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, ps, static_cast<uint4*>(Wp));
   } else {
     const auto* w = static_cast<const float*>(W);
-    if (vec) pack_weights<float, true><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
-    else pack_weights<float, false><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, KS, static_cast<uint4*>(Wp));
+    if (vec) pack_weights<float, true><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, ps, static_cast<uint4*>(Wp));
+    else pack_weights<float, false><<<g3, 256, 0, stream>>>(w, d.E, K, N, NB, ps, static_cast<uint4*>(Wp));
   }
   return launch_status();
 }
@@ -966,6 +982,10 @@ moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp, 
   g.N = N;
   g.NB = ceil_div(N, 32);
   g.KS = gemm_ks(d, K);
+  const PackStrides ps = pack_strides(d, layer);
+  g.ws_expert = ps.expert;
+  g.ws_block = ps.block;
+  g.ws_stage = ps.stage;
   // Large groups (bf16, at least 192 rows per expert on average, enough 256 x 256 tiles to give
   // every CU one): the 256 x 256 LDS-staged kernel
   // (its A row offsets and its B offsets within an expert are 32-bit byte offsets)

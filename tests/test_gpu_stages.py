@@ -388,18 +388,22 @@ def test_grouped_gemm_check_finite_large(moe):
 
 
 
-def _fragment_layout(B, V, KS):
-    """The packed operand layout moe.h states, from B [E, K, N]: the fragment of
-    (e, nb, ks) sits at ((e * KS/4 + ks // 4) * NB + nb) * 4 + ks % 4, and its lane holds
-    column nb*32 + lane%32, rows ks*2V + (lane//32)*V .. +V-1, zeros past K or N."""
+def _fragment_layout(B, V, KS, stage_order):
+    """The packed operand layout moe.h states, from B [E, K, N]: fragment (e, nb, ks) holds,
+    for lane l, column nb*32 + l%32, rows ks*2V + (l//32)*V .. +V-1, zeros past K or N; the
+    fragments are ordered [e][ks // 4][nb][ks % 4] in k-stage order, else [e][nb][ks]."""
     E, K, N = B.shape
     NB = -(-N // 32)
     Q = KS // 4
     Bp = np.zeros((E, KS * 2 * V, NB * 32), dtype=B.dtype)
     Bp[:, :K, :N] = B
-    # [E, q, r, half, i, nb, col] -> [E, q, nb, r, half, col, i]  (ks = 4q + r)
-    t = Bp.reshape(E, Q, 4, 2, V, NB, 32).transpose(0, 1, 5, 2, 3, 6, 4)
-    return np.ascontiguousarray(t).reshape(E, Q, NB, 4, 64, V)
+    # [E, q, r, half, i, nb, col] (ks = 4q + r)
+    t = Bp.reshape(E, Q, 4, 2, V, NB, 32)
+    if stage_order:  # -> [E, q, nb, r, half, col, i]
+        t = t.transpose(0, 1, 5, 2, 3, 6, 4)
+    else:  # -> [E, nb, q, r, half, col, i]
+        t = t.transpose(0, 5, 1, 2, 3, 6, 4)
+    return np.ascontiguousarray(t).reshape(-1, 64, V)
 
 
 @pytest.mark.parametrize("act", ["f32", "bf16"])
@@ -407,13 +411,16 @@ def test_weight_pack_layouts(moe, act):
     """moe_pack_expert_weights (layers 1, 2) and moe_pack_expert_weights_t (layers 3, 4: the
     transposes W2^T and W1^T for the backward) against the fragment layout built on the host,
     bit-exact, with widths that are not multiples of the fragment (zero padding) and, for
-    D = 37, rows that are not whole 16-byte vectors."""
+    D = 37, rows that are not whole 16-byte vectors; in column-block order (few rows an
+    expert) and in k-stage order (at least 128 rows an expert: T = 256, 512 below)."""
     import torch
     rng = np.random.default_rng(21)
-    for (E, D, H) in ((3, 40, 72), (2, 37, 100), (2, 256, 520)):
-        w = I.Workload("pk", T=8, D=D, E=E, k=1, H=H, act=act, gating="noisy", noise=False,
+    for (E, D, H, T) in ((3, 40, 72, 8), (2, 37, 100, 8), (2, 256, 520, 8), (2, 256, 520, 256),
+                         (3, 40, 72, 512), (2, 37, 100, 300)):
+        w = I.Workload("pk", T=T, D=D, E=E, k=1, H=H, act=act, gating="noisy", noise=False,
                        capacity_factor=0.0, seed=0)
         p = problem_for(moe, w)
+        stage_order = moe.moe_max_rows(p) >= 128 * E
         cast = (lambda a: I.f32_to_bf16_bits(a)) if act == "bf16" else (lambda a: a)
         W1 = cast(rng.standard_normal((E, D, H)).astype(np.float32))
         W2 = cast(rng.standard_normal((E, H, D)).astype(np.float32))
@@ -427,10 +434,11 @@ def test_weight_pack_layouts(moe, act):
         for layer, (buf, B) in enumerate(zip(bufs, Bs), start=1):
             K = B.shape[1]
             KS = -(-K // (16 * V // 2)) * 4  # k stages of 128 bytes, 4 k-steps each
-            want = _fragment_layout(B, V, KS)
+            want = _fragment_layout(B, V, KS, stage_order)
             got = host(buf).view(B.dtype)
             assert got.size == want.size, (layer, got.size, want.size)
-            assert (got.reshape(want.shape).view(np.uint8) == want.view(np.uint8)).all(), (layer, D, H)
+            assert (got.reshape(want.shape).view(np.uint8) == want.view(np.uint8)).all(), \
+                (layer, D, H, T)
 
 @pytest.mark.parametrize("name", ALL)
 def test_combine(moe, name):
