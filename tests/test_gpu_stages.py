@@ -474,12 +474,41 @@ def test_combine(moe, name):
     assert err0 < TOL[w.act]
 
 
+# Shapes that reach every instance of the aux row pass: E in (256, 512] (two 16-byte
+# vectors a lane), E not a multiple of 4 (the column pass), a small T (4 rows a block, fewer
+# blocks than slices), Switch gating over 96 experts, and a ragged last block.
+AUX_SHAPES = [
+    I.Workload("aux_e512", T=4100, D=64, E=512, k=2, H=16, act="bf16", gating="noisy",
+               noise=True, capacity_factor=1.0, seed=31),
+    I.Workload("aux_e202", T=3001, D=48, E=202, k=3, H=16, act="f32", gating="noisy",
+               noise=True, capacity_factor=0.0, seed=32),
+    I.Workload("aux_t60", T=60, D=32, E=40, k=2, H=16, act="f32", gating="noisy", noise=True,
+               capacity_factor=1.25, seed=33),
+    I.Workload("aux_sw96", T=5000, D=40, E=96, k=1, H=16, act="bf16", gating="switch",
+               noise=False, capacity_factor=1.0, seed=34),
+]
+
+
+@pytest.mark.parametrize("w", AUX_SHAPES, ids=[w.name for w in AUX_SHAPES])
+def test_aux_shapes(moe, w):
+    log(f"[aux shape] {w}")
+    inp = I.make_inputs(w, experts=False)
+    r = O.route(inp["X"], inp["Wg"], inp["Wnoise"], inp["bias"], w.k, w.gating, w.noise,
+                seed=w.seed)
+    d = O.dispatch(r.ids, w.E, O.capacity(w.T, w.k, w.capacity_factor, w.E, w.min_capacity))
+    _check_aux(moe, w, r, d)
+
+
 @pytest.mark.parametrize("name", ALL)
 def test_aux(moe, name):
-    import torch
     log(f"[aux] {name}")
     w, inp = workload_inputs(name)
     r, d = oracle_routing(name)
+    _check_aux(moe, w, r, d)
+
+
+def _check_aux(moe, w, r, d):
+    import torch
     a = O.aux(r, d, w.k)
     p = problem_for(moe, w)
     noisy = r.std is not None
