@@ -633,7 +633,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
     asm volatile("" : "+v"(lq));
     unsigned char* stile = smem + kBOff + ((s - 1) % 3) * kStageBytes + wave * kStageTile;
     // mode 2 (the backward's dH): the mask's 16 bytes at each stored vector, requested one
-    // 32 x 64 piece ahead so their latency overlaps the previous piece's work
+    // pipeline step before the piece is stored
     u32x4 mk[kEpi == 2 ? 2 : 1][4];
     auto load_mask = [&](int piece) {
       const int i = piece >> 1, h = piece & 1;
@@ -646,68 +646,91 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
             static_cast<const uint16_t*>(g.mask) + static_cast<int64_t>(done.r0 + grow) * g.N + col);
       }
     };
-    if constexpr (kEpi == 2) load_mask(0);
+    // The eight 32 x 64 pieces (pc = 2 i + h) go through two staging tiles in a pipeline: in
+    // step pc the wave converts and stages piece pc, stores piece pc - 2 (read back in the
+    // step before, after that step's conversions, so the read's latency is covered) and
+    // reads back piece pc - 1. LDS operations of one wave complete in order, so a tile is
+    // written again only after its previous piece has been read.
+    unsigned char* st2[2] = {stile, stile + 4 * kStageTile};
+    u32x4 rb[2][4];
+    auto stage_piece = [&](int pc) {
+      const int i = pc >> 1, h = pc & 1;
+      unsigned char* t = st2[pc & 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if constexpr (kEpi == 2) {
-          if (2 * i + h + 1 < 8) load_mask(2 * i + h + 1);
-        }
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const f32x16& a = acc[i][2 * h + jj];
-            s16x2 h0 = __builtin_bit_cast(s16x2, __builtin_convertvector((f32x2){a[4 * qd], a[4 * qd + 1]}, bf16x2));
-            s16x2 h1 = __builtin_bit_cast(s16x2, __builtin_convertvector((f32x2){a[4 * qd + 2], a[4 * qd + 3]}, bf16x2));
-            if (kCheck) {
-              // on the rounded pair (rounding keeps NaN and infinity, and a value past the
-              // bf16 range becomes infinite in the output): an all-ones exponent, before any
-              // ReLU; integer tests on the packed values, no accumulator read twice
-              const uint32_t u0 = __builtin_bit_cast(uint32_t, h0), u1 = __builtin_bit_cast(uint32_t, h1);
-              bad |= ((u0 & 0x7f80u) == 0x7f80u) | ((u0 & 0x7f800000u) == 0x7f800000u) |
-                     ((u1 & 0x7f80u) == 0x7f80u) | ((u1 & 0x7f800000u) == 0x7f800000u);
-            }
-            if (kEpi == 1) {
-              h0 = __builtin_elementwise_max(h0, (s16x2){0, 0});
-              h1 = __builtin_elementwise_max(h1, (s16x2){0, 0});
-            }
-            uint2 v;
-            v.x = __builtin_bit_cast(uint32_t, h0);
-            v.y = __builtin_bit_cast(uint32_t, h1);
-            // column byte offset inside the 128-byte staged row: jj*64 + qd*16 + (l/32)*8
-            const int row = lq & 31;
-            const int cb = jj * 64 + qd * 16 + (lq >> 5) * 8;
-            const int sw = ((cb >> 4) ^ (row & 7)) * 16 + (cb & 15);
-            *reinterpret_cast<uint2*>(stile + row * 128 + sw) = v;
+        for (int qd = 0; qd < 4; ++qd) {
+          const f32x16& a = acc[i][2 * h + jj];
+          s16x2 h0 = __builtin_bit_cast(s16x2, __builtin_convertvector((f32x2){a[4 * qd], a[4 * qd + 1]}, bf16x2));
+          s16x2 h1 = __builtin_bit_cast(s16x2, __builtin_convertvector((f32x2){a[4 * qd + 2], a[4 * qd + 3]}, bf16x2));
+          if (kCheck) {
+            // on the rounded pair (rounding keeps NaN and infinity, and a value past the
+            // bf16 range becomes infinite in the output): an all-ones exponent, before any
+            // ReLU; integer tests on the packed values, no accumulator read twice
+            const uint32_t u0 = __builtin_bit_cast(uint32_t, h0), u1 = __builtin_bit_cast(uint32_t, h1);
+            bad |= ((u0 & 0x7f80u) == 0x7f80u) | ((u0 & 0x7f800000u) == 0x7f800000u) |
+                   ((u1 & 0x7f80u) == 0x7f80u) | ((u1 & 0x7f800000u) == 0x7f800000u);
           }
-        // read back: instruction p covers rows 8p .. 8p+7, lane l: row 8p + l/8, chunk l % 8
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int row = 8 * p + (lq >> 3), ch = lq & 7;
-          u32x4 v = *reinterpret_cast<const u32x4*>(stile + row * 128 + ((ch ^ (row & 7)) * 16));
-          if constexpr (kEpi == 2) {  // zero where the mask is not > 0 (a NaN mask keeps it)
-            const u32x4 mq = mk[(2 * i + h) & 1][p];
-#pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2) {
-              const uint32_t mw = mq[w2];
-              uint32_t vw = v[w2];
-              if (!(__uint_as_float(mw << 16) > 0.f)) vw &= 0xffff0000u;
-              if (!(__uint_as_float(mw & 0xffff0000u) > 0.f)) vw &= 0x0000ffffu;
-              v[w2] = vw;
-            }
+          if (kEpi == 1) {
+            h0 = __builtin_elementwise_max(h0, (s16x2){0, 0});
+            h1 = __builtin_elementwise_max(h1, (s16x2){0, 0});
           }
-          // a row past the group holds exactly the group's last row (its A row was repeated),
-          // so it is written there again, unchanged
-          const int grow = min(wm * 128 + i * 32 + row, done.rows - 1);
-          const int col = done.n0 + wn * 128 + h * 64 + ch * 8;
-          *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(done.r0 + grow) * g.N + col) = v;
+          uint2 v;
+          v.x = __builtin_bit_cast(uint32_t, h0);
+          v.y = __builtin_bit_cast(uint32_t, h1);
+          // column byte offset inside the 128-byte staged row: jj*64 + qd*16 + (l/32)*8
+          const int row = lq & 31;
+          const int cb = jj * 64 + qd * 16 + (lq >> 5) * 8;
+          const int sw = ((cb >> 4) ^ (row & 7)) * 16 + (cb & 15);
+          *reinterpret_cast<uint2*>(t + row * 128 + sw) = v;
         }
-        // one piece at a time: converting every accumulator up front would need 128 more
-        // registers than the wave has
-        __builtin_amdgcn_sched_barrier(0);
+    };
+    // read back: instruction p covers rows 8p .. 8p+7, lane l: row 8p + l/8, chunk l % 8
+    auto read_piece = [&](int pc) {
+      const unsigned char* t = st2[pc & 1];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int row = 8 * p + (lq >> 3), ch = lq & 7;
+        rb[pc & 1][p] = *reinterpret_cast<const u32x4*>(t + row * 128 + ((ch ^ (row & 7)) * 16));
       }
+    };
+    auto store_piece = [&](int pc) {
+      const int i = pc >> 1, h = pc & 1;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int row = 8 * p + (lq >> 3), ch = lq & 7;
+        u32x4 v = rb[pc & 1][p];
+        if constexpr (kEpi == 2) {  // zero where the mask is not > 0 (a NaN mask keeps it)
+          const u32x4 mq = mk[pc & 1][p];
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2) {
+            const uint32_t mw = mq[w2];
+            uint32_t vw = v[w2];
+            if (!(__uint_as_float(mw << 16) > 0.f)) vw &= 0xffff0000u;
+            if (!(__uint_as_float(mw & 0xffff0000u) > 0.f)) vw &= 0x0000ffffu;
+            v[w2] = vw;
+          }
+        }
+        // a row past the group holds exactly the group's last row (its A row was repeated),
+        // so it is written there again, unchanged
+        const int grow = min(wm * 128 + i * 32 + row, done.rows - 1);
+        const int col = done.n0 + wn * 128 + h * 64 + ch * 8;
+        *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(done.r0 + grow) * g.N + col) = v;
+      }
+    };
+#pragma unroll
+    for (int pc = 0; pc < 10; ++pc) {
+      if (pc < 8) stage_piece(pc);
+      // mode 2: piece pc - 1's mask, used when that piece is stored in the next step
+      if constexpr (kEpi == 2) {
+        if (pc >= 1 && pc <= 8) load_mask(pc - 1);
+      }
+      if (pc >= 2) store_piece(pc - 2);
+      if (pc >= 1 && pc <= 8) read_piece(pc - 1);
+      // one piece at a time: converting every accumulator up front would need 128 more
+      // registers than the wave has
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // every wave is done with the staging slot before the next tile's first refill reuses it
     __syncthreads();
     if (more2) sources(nxt_t, ao_nxt, bb_nxt);
