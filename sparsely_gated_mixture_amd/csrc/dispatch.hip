@@ -13,7 +13,8 @@
 //   3. place: block b recomputes offsets (exclusive scan over experts of
 //      min(count, C)), ranks its assignments in token order with wave ballots,
 //      writes pos / accepted / row_token, then copies each token row once
-//      into every accepted destination row with 16-byte vectors.
+//      into every accepted destination row with 16-byte vectors (the first
+//      batch of row loads is issued at the block's start, before the ranking).
 #include <mutex>
 
 #include "common.h"
@@ -78,6 +79,26 @@ __global__ __launch_bounds__(kThreads) void dispatch_place(
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int t0 = b * kTok;
+  const int ntok = min(kTok, Tn - t0);
+
+  // The row copy's first batch of token-row loads is issued before anything else, so its
+  // latency overlaps the offsets scan and the ranking below (rows are read once: streamed
+  // with the non-temporal hint).
+  constexpr int V = Elem<T>::kVec;
+  constexpr int kU = 4;  // 16-byte vectors in flight per thread (8 is no faster)
+  const bool vec_copy = Xd != nullptr && (D % V) == 0;
+  const int nv = D / V;  // 16-byte vectors per row (vector path)
+  const int items = ntok * nv;
+  u32x4 v[kU];
+  auto load_batch = [&](int it0) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int it = min(it0 + u * kThreads, items - 1);
+      const int tl = it / nv, c = it - tl * nv;
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(X + static_cast<int64_t>(t0 + tl) * D) + c);
+    }
+  };
+  if (vec_copy) load_batch(tid);
 
   // offsets = exclusive scan over experts of min(counts, C)
   {
@@ -99,7 +120,6 @@ __global__ __launch_bounds__(kThreads) void dispatch_place(
     for (int e = tid; e <= E; e += kThreads) offsets[e] = sOff[e];
 
   // rank in token-major order: wave 0 walks the block's assignments 64 at a time
-  const int ntok = min(kTok, Tn - t0);
   const int n = ntok * k;
   if (tid < 64) {
     const int lane = tid;
@@ -140,26 +160,12 @@ __global__ __launch_bounds__(kThreads) void dispatch_place(
   }
   __syncthreads();
 
-  // gather: each token row is read once (non-temporal hint: streamed, not kept in the caches,
-  // which measurably raises the copy's bandwidth) and written to its accepted rows (none
-  // without Xd)
+  // gather: each token row is read once and written to its accepted rows (none without Xd);
+  // plain stores (the non-temporal hint on these scattered row writes made the copy slower)
   if (Xd == nullptr) return;
-  constexpr int V = Elem<T>::kVec;
-  const bool vec_ok = (D % V) == 0;
-  if (vec_ok) {
-    const int nv = D / V;  // 16-byte vectors per row
-    const int items = ntok * nv;
-    constexpr int kU = 4;  // vectors in flight per thread
+  if (vec_copy) {
     for (int it0 = tid; it0 < items; it0 += kThreads * kU) {
-      uint4 v[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int it = min(it0 + u * kThreads, items - 1);
-        const int tl = it / nv, c = it - tl * nv;
-        const u32x4 q = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(X + static_cast<int64_t>(t0 + tl) * D) + c);
-        v[u] = make_uint4(q.x, q.y, q.z, q.w);
-      }
+      if (it0 != tid) load_batch(it0);
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int it = it0 + u * kThreads;
@@ -167,18 +173,19 @@ __global__ __launch_bounds__(kThreads) void dispatch_place(
         const int tl = it / nv, c = it - tl * nv;
         for (int j = 0; j < k; ++j) {
           const int row = sRow[tl * k + j];
-          if (row >= 0) reinterpret_cast<uint4*>(Xd + static_cast<int64_t>(row) * D)[c] = v[u];
+          if (row >= 0)
+            reinterpret_cast<u32x4*>(Xd + static_cast<int64_t>(row) * D)[c] = v[u];
         }
       }
     }
   } else {
-    const int items = ntok * D;
-    for (int it = tid; it < items; it += kThreads) {
+    const int nsc = ntok * D;
+    for (int it = tid; it < nsc; it += kThreads) {
       const int tl = it / D, c = it - tl * D;
-      const T v = X[static_cast<int64_t>(t0 + tl) * D + c];
+      const T xv = X[static_cast<int64_t>(t0 + tl) * D + c];
       for (int j = 0; j < k; ++j) {
         const int row = sRow[tl * k + j];
-        if (row >= 0) Xd[static_cast<int64_t>(row) * D + c] = v;
+        if (row >= 0) Xd[static_cast<int64_t>(row) * D + c] = xv;
       }
     }
   }

@@ -70,7 +70,8 @@ ROUTE_SHAPES = [
     # MFMA waves): 128 experts with a router bias and a ragged last tile (512 tiles + 77 rows);
     # 202 experts (a partial 4-expert group and a partial 32-expert block, k = 3, half a last
     # tile); fp32 X over 64 experts; 256 experts without noise (the 4-wave form); 256 experts
-    # with noise, k = 1 and D = 128 (two k-stages: the noise waves draw several groups a stage)
+    # with noise, k = 1 and D = 128 (two k-stages: the noise waves draw several groups a stage);
+    # 256 experts with noise at D = 96 (the 8-wave form with a k tail: no whole 64-deep stages)
     I.Workload("lists_e128", T=65613, D=512, E=128, k=3, H=16, act="bf16", gating="noisy",
                noise=True, capacity_factor=0.0, seed=17, zipf_bias=1.1),
     I.Workload("lists_e202", T=65600, D=64, E=202, k=3, H=16, act="bf16", gating="noisy",
@@ -81,6 +82,8 @@ ROUTE_SHAPES = [
                noise=False, capacity_factor=0.0, seed=18),
     I.Workload("fused_top1", T=33000, D=128, E=256, k=1, H=16, act="bf16", gating="noisy",
                noise=True, capacity_factor=0.0, seed=19),
+    I.Workload("tail_d96", T=65536, D=96, E=256, k=2, H=16, act="bf16", gating="noisy",
+               noise=True, capacity_factor=0.0, seed=22),
 ]
 
 
