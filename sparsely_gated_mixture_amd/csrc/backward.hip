@@ -44,6 +44,7 @@
 // router's [dclean | draw] [Wg | Wnoise]^T) run on the forward's grouped GEMM
 // kernel with transposed packed weights.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "noise.h"
@@ -835,6 +836,284 @@ __global__ __launch_bounds__(kThreads) void wgrad_gemm_tr(WgradArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ 256 x 256 weight gradients
+// bf16 operands, M and N multiples of 256, one row split: one persistent block of 4 waves per
+// CU walks a list of (group, 256 x 256 output tile)s, each wave accumulating a 128 x 128
+// quarter (256 fp32 accumulators a lane). A tile's operand bytes per stage feed 256 rows and
+// 256 columns, half of what the 128 x 256 kernel above moves per FLOP.
+//   * A stage is 64 rows of the reduction: the tile's 256 columns of A and of B for those rows,
+//     512 bytes a row, brought to LDS by direct global-to-LDS loads (16 bytes a lane, two rows
+//     an instruction, whole 128-byte lines) from per-lane 64-bit addresses. Rows past the group
+//     are read from a row of zeros, so the tail of a group adds nothing and no row is read twice.
+//     In LDS the 16-byte chunks of row r sit at chunk ^ 4 (r % 4): the transpose reads of an
+//     MFMA fragment (four rows of 32 or 64 bytes) then fall on distinct banks (no bank-conflict
+//     cycles in the counters; chunk ^ 2 (r % 4) had 1.6 per LDS instruction).
+//   * The stages of all of a block's tiles form one stream (two stages of A and three of B in
+//     LDS, 160 KB): the loads of stage s + 2 are issued between the MFMAs of stage s, one barrier
+//     a stage, the first two stages of the next tile are requested before the epilogue. A group
+//     has at least two stages (more zero rows for a group of at most 64 rows).
+//   * Tiles run group-major, along the smaller output dimension first; each XCD's 32 CUs take a
+//     contiguous run of that order together, sharing operands in their L2.
+//   * Epilogue: each wave stages 32 x 32 fp32 pieces through two LDS tiles (128-byte rows, chunks
+//     permuted by the row's low three bits) in a two-step pipeline and stores whole 128-byte row
+//     segments.
+constexpr int kWG = 256;                    // tile rows (M) and columns (N)
+constexpr int kWGStage = 64 * 512;          // one operand's stage: 64 rows x 256 bf16
+constexpr int kWGBOff = 2 * kWGStage;       // B's three slots follow A's two
+constexpr int kWGPiece = 4096;              // epilogue staging tile: 32 rows x 128 bytes
+constexpr size_t kWGLds = 5 * static_cast<size_t>(kWGStage);  // 160 KB
+
+// The source of every row past a group's end.
+__device__ __align__(16) const uint4 kZeroRow[32] = {};
+
+typedef __attribute__((address_space(3))) void* wg_lds_t;
+__device__ __forceinline__ uint32_t wg_lds_offset(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((wg_lds_t)(p)));
+}
+// 16 bytes a lane from the lane's own global address into LDS at lds + 16 * lane (lds
+// wave-uniform).
+__device__ __forceinline__ void dma16_at(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory");
+}
+// This wave's vector memory operations (all but the last N) and LDS operations done, then the
+// workgroup barrier.
+template <int N>
+__device__ __forceinline__ void wg_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+__global__ __launch_bounds__(kThreads, 1) void wgrad_gemm_big(WgradArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int M = a.M, N = a.N;
+  const int MT = M / kWG, NT = N / kWG, per_group = MT * NT;
+  const int total = a.G * per_group;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int nblk_xcd = gridDim.x / kXcds;
+  const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
+  const int first = xcd * per_xcd + local, last = min(total, (xcd + 1) * per_xcd);
+  const int n_my = first < last ? (last - first + nblk_xcd - 1) / nblk_xcd : 0;
+  if (n_my == 0) return;
+
+  const uint16_t* A = static_cast<const uint16_t*>(a.A);
+  const uint16_t* B = static_cast<const uint16_t*>(a.B);
+  const int32_t* off = a.offsets;
+  struct Tile {
+    int g, m0, n0, rb, re, nst;
+  };
+  auto decode = [&](int m) {  // the block's m-th tile without its group bounds
+    const int q = first + m * nblk_xcd;
+    Tile T;
+    T.g = q / per_group;
+    const int rem = q - T.g * per_group;
+    const int mt = N > M ? rem % MT : rem / NT, nt = N > M ? rem / MT : rem % NT;
+    T.m0 = mt * kWG;
+    T.n0 = nt * kWG;
+    T.rb = T.re = 0;
+    T.nst = 2;
+    return T;
+  };
+  auto tile = [&](int m) {
+    Tile T = decode(m);
+    T.rb = off[T.g];
+    T.re = off[T.g + 1];
+    T.nst = max(2, (T.re - T.rb + 63) / 64);
+    return T;
+  };
+  const uint32_t ring = wg_lds_offset(smem);
+  // lane l of load instruction i of this wave writes row 16 w + 2 i + l / 32 of the stage, LDS
+  // chunk l % 32, and fetches the 16 bytes that belong there
+  const int lrow = 16 * wave + (lane >> 5), lslot = lane & 31;
+  auto dma = [&](bool opB, const Tile& T, int kst, int slot_base, int i) {
+    const int row = lrow + 2 * i;
+    const int chunk = lslot ^ (4 * (row & 3));
+    const int r = T.rb + kst * 64 + row;
+    const void* src = kZeroRow;
+    if (r < T.re)
+      src = opB ? static_cast<const void*>(B + static_cast<int64_t>(r) * N + T.n0 + chunk * 8)
+                : static_cast<const void*>(A + static_cast<int64_t>(r) * M + T.m0 + chunk * 8);
+    dma16_at(src, ring + slot_base + (16 * wave + 2 * i) * 512);
+  };
+  auto dma_a = [&](int s, const Tile& T, int kst, int i) { dma(false, T, kst, (s & 1) * kWGStage, i); };
+  auto dma_b = [&](int s, const Tile& T, int kst, int i) {
+    dma(true, T, kst, kWGBOff + (s % 3) * kWGStage, i);
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  // transpose-read fragments: lane (gq, jr, qc) reads 8 bytes at row 16 ks + 8 (gq / 2) + jr
+  // (and 4 rows on), column 32 block + 16 (gq % 2) + 4 qc
+  const int gq = lane >> 4, jr = (lane >> 2) & 3, qc = lane & 3;
+  const int rowq = 8 * (gq >> 1) + jr, colq = 16 * (gq & 1) + 4 * qc;
+  auto fr_off = [&](int ks, int c) {  // byte offset of (row 16 ks + rowq, column c) in a slot
+    return (ks * 16 + rowq) * 512 + ((((c >> 3) ^ (4 * jr))) << 4) + 8 * (qc & 1);
+  };
+  u32x4 fa[2][4], fb[2][4];
+  f32x16 acc[4][4];
+  auto read = [&](int s, int ks, int b) {
+    const unsigned char* pa = smem + (s & 1) * kWGStage;
+    const unsigned char* pb = smem + kWGBOff + (s % 3) * kWGStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int o = fr_off(ks, wm * 128 + i * 32 + colq);
+      const unsigned long long x0 = tr_read(pa, o), x1 = tr_read(pa, o + 4 * 512);
+      fa[b][i] = u32x4{static_cast<unsigned>(x0), static_cast<unsigned>(x0 >> 32),
+                       static_cast<unsigned>(x1), static_cast<unsigned>(x1 >> 32)};
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int o = fr_off(ks, wn * 128 + j * 32 + colq);
+      const unsigned long long x0 = tr_read(pb, o), x1 = tr_read(pb, o + 4 * 512);
+      fb[b][j] = u32x4{static_cast<unsigned>(x0), static_cast<unsigned>(x0 >> 32),
+                       static_cast<unsigned>(x1), static_cast<unsigned>(x1 >> 32)};
+    }
+  };
+  // one k-step's 16 MFMAs in four groups; after group i, dmas(i) issues this k-step's share of
+  // the loads
+  auto mma_all = [&](int b, auto dmas) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = wmma<uint16_t>(fb[b][j], fa[b][i], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+      dmas(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  Tile cur = tile(0), nxt = cur;
+  if (n_my > 1) nxt = tile(1);
+  // Stage s (stage st of the current tile): k-steps 1..3 read one ahead of the MFMAs; the B
+  // loads of stage s + 2 (into the B slot stage s - 1 freed) between the MFMAs of k-steps 0..2;
+  // before the last k-step, this wave's loads of stage s + 1 are waited for (only B of stage
+  // s + 2 may still be in flight) and the barrier passed, after which stage s is no longer read
+  // by any wave; the A loads of stage s + 2 (into stage s's A slot) between the last k-step's
+  // MFMAs. Stage s + 2 is the current tile's or, for its last two stages, the next tile's.
+  auto body = [&](int s, int st, bool more_tiles) {
+    const bool in_cur = st + 2 < cur.nst;
+    const bool refill = in_cur || more_tiles;
+    const Tile& T2 = in_cur ? cur : nxt;
+    const int k2 = in_cur ? st + 2 : st + 2 - cur.nst;
+    auto b_part = [&](int first_i, int count) {
+      return [&, first_i, count](int grp) {
+        if (refill) {
+          for (int i = first_i + (grp * count) / 4; i < first_i + ((grp + 1) * count) / 4; ++i)
+            dma_b(s + 2, T2, k2, i);
+        }
+      };
+    };
+    read(s, 1, 1);
+    mma_all(0, b_part(0, 3));
+    read(s, 2, 0);
+    mma_all(1, b_part(3, 3));
+    read(s, 3, 1);
+    mma_all(0, b_part(6, 2));
+    if (refill) wg_wait_barrier<8>();
+    else wg_wait_barrier<0>();
+    read(s + 1, 0, 0);
+    mma_all(1, [&](int grp) {
+      if (refill) {
+        dma_a(s + 2, T2, k2, 2 * grp);
+        dma_a(s + 2, T2, k2, 2 * grp + 1);
+      }
+    });
+  };
+
+  // stages 0 and 1 (tile 0), then wait for stage 0
+#pragma unroll
+  for (int s0 = 0; s0 < 2; ++s0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma_a(s0, cur, s0, i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma_b(s0, cur, s0, i);
+  }
+  wg_wait_barrier<16>();
+  read(0, 0, 0);
+
+  int s = 0;
+  for (int m = 0; m < n_my; ++m) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    const bool more = m + 1 < n_my;
+    for (int st = 0; st < cur.nst; ++st, ++s) body(s, st, more);
+
+    // ---- epilogue (the next tile's first two stages are in flight). Register 4q + t of
+    // acc[i][j] is C[m = 128 wm + 32 i + l % 32][n = 128 wn + 32 j + 8 q + 4 (l / 32) + t]. Each
+    // wave stages the 32 x 32 piece (i, j) in its own LDS tile (in the B slot of the tile's last
+    // stage, free until the next tile's first refill; chunk c of row r at c ^ (r % 8)), reads
+    // it back as 128-byte rows (instruction p: rows 8p .. 8p+7) and stores them. Step pc stages
+    // piece pc, stores piece pc - 2 and reads back piece pc - 1; a wave's LDS operations
+    // complete in order, so a staging tile is rewritten only after its last read.
+    const Tile done = cur;
+    // the group bounds of the next-but-one tile are requested before the epilogue's stores
+    // and used after them, so the wait for them is no wait for the stores (or for the next
+    // tile's first stages, requested before)
+    const bool have2 = m + 2 < n_my;
+    Tile t2 = nxt;
+    int rb2 = 0, re2 = 0;
+    if (have2) {
+      t2 = decode(m + 2);
+      rb2 = off[t2.g];
+      re2 = off[t2.g + 1];
+    }
+    int lq = lane;
+    asm volatile("" : "+v"(lq));  // keeps the lane-derived addresses from being hoisted
+    unsigned char* stile = smem + kWGBOff + ((s - 1) % 3) * kWGStage + wave * 2 * kWGPiece;
+    float* C = a.C + static_cast<int64_t>(done.g) * M * N;
+    u32x4 rb[2][4];
+    auto stage_piece = [&](int pc) {
+      const int i = pc >> 2, j = pc & 3;
+      unsigned char* t = stile + (pc & 1) * kWGPiece;
+      const int row = lq & 31;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ch = 2 * q + (lq >> 5);
+        *reinterpret_cast<f32x4*>(t + row * 128 + ((ch ^ (row & 7)) << 4)) =
+            f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+      }
+    };
+    auto read_piece = [&](int pc) {
+      const unsigned char* t = stile + (pc & 1) * kWGPiece;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int row = 8 * p + (lq >> 3), ch = lq & 7;
+        rb[pc & 1][p] = *reinterpret_cast<const u32x4*>(t + row * 128 + ((ch ^ (row & 7)) << 4));
+      }
+    };
+    auto store_piece = [&](int pc) {
+      const int i = pc >> 2, j = pc & 3;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int row = 8 * p + (lq >> 3), ch = lq & 7;
+        const int mrow = done.m0 + wm * 128 + i * 32 + row;
+        const int ncol = done.n0 + wn * 128 + j * 32 + 4 * ch;
+        *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(mrow) * N + ncol) = rb[pc & 1][p];
+      }
+    };
+#pragma unroll
+    for (int pc = 0; pc < 18; ++pc) {
+      if (pc < 16) stage_piece(pc);
+      if (pc >= 2) store_piece(pc - 2);
+      if (pc >= 1 && pc <= 16) read_piece(pc - 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // every wave is done with the staging slot before the next tile's first refill reuses it
+    __syncthreads();
+    cur = nxt;
+    if (have2) {
+      t2.rb = __builtin_amdgcn_readfirstlane(rb2);
+      t2.re = __builtin_amdgcn_readfirstlane(re2);
+      t2.nst = max(2, (t2.re - t2.rb + 63) / 64);
+      nxt = t2;
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // ------------------------------------------------------------------ input gradient
 template <typename T>
 __global__ __launch_bounds__(kThreads) void dx_final(
@@ -908,6 +1187,19 @@ moe_status combine_backward_launch(const Dims& d, const void* dY, const void* Z,
   return launch_status();
 }
 
+static int wg_device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 moe_status wgrad_launch(const Dims& d, const void* A, const void* B, const int32_t* offsets, int G,
                         int M, int N, float* C, hipStream_t stream, int splits) {
   WgradArgs a{A, B, offsets, C, G, M, N, splits};
@@ -916,6 +1208,25 @@ moe_status wgrad_launch(const Dims& d, const void* A, const void* B, const int32
                    (reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B) |
                     reinterpret_cast<uintptr_t>(C)) % 16 == 0;
   const bool tr = d.dtype == MOE_BF16 && vec;  // the transpose-read kernel
+  // 256 x 256 tiles, whole ones only, one row split, enough tiles to give every CU one: the
+  // persistent kernel (one block per CU)
+  if (tr && splits == 1 && M % kWG == 0 && N % kWG == 0 &&
+      static_cast<int64_t>(G) * (M / kWG) * (N / kWG) >= wg_device_cus()) {
+    static std::once_flag once[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+    bool ok = true;
+    std::call_once(once[dev], [&] {
+      ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_gemm_big),
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               static_cast<int>(kWGLds)) == hipSuccess;
+    });
+    if (!ok) return MOE_ERR_HIP;
+    const int cus = wg_device_cus();
+    const int grid = std::max(kXcds, cus / kXcds * kXcds);
+    wgrad_gemm_big<<<grid, kThreads, kWGLds, stream>>>(a);
+    return launch_status();
+  }
   const int64_t blocks = static_cast<int64_t>(G) * splits * ceil_div(M, kWT) * ceil_div(N, tr ? kTN2 : kWT);
   if (blocks > 0x7fffffffLL - kXcds) return MOE_ERR_UNSUPPORTED;
   const int grid = static_cast<int>(ceil_div64(blocks, kXcds) * kXcds);

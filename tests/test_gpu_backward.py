@@ -364,3 +364,47 @@ def test_backward_after_gathered_forward(moe, w):
         if k in ("dZ", "dHp", "dXd"):
             got, v = got[:rows], v[:rows]
         assert np.array_equal(got.view(np.uint8), v.view(np.uint8)), k
+
+
+@pytest.mark.parametrize("which,D,H", [(1, 256, 1024), (2, 256, 1024), (1, 512, 768)],
+                         ids=["dW1_256x1024", "dW2_1024x256", "dW1_512x768"])
+def test_weight_grad_large_tiles(moe, which, D, H):
+    """The persistent 256 x 256 weight-gradient kernel (bf16, widths multiples of 256, at
+    least one tile per CU) on ragged groups: empty experts, 1-row groups, 63 / 64 / 65 / 127 /
+    128 / 129 rows (a group's last 64-row stage partly past its end, or a group shorter than
+    the kernel's two stages), long groups; every expert's C_e = A_e^T B_e against numpy fp64
+    of the same bf16 values at the fp32 tolerance (1e-4 of the largest reference value). which = 1
+    runs along the smaller output dimension M first, which = 2 along N first."""
+    import torch
+    rng = np.random.default_rng(31 + which + D)
+    E = 64
+    sizes = rng.integers(200, 700, E)
+    sizes[[2, 30, 61]] = 0
+    sizes[[4, 44]] = 1
+    sizes[[7, 8, 9, 10, 11, 12]] = (63, 64, 65, 127, 128, 129)
+    sizes[25] = 1500
+    T = int(sizes.sum())
+    w = I.Workload("wgbig", T=T, D=D, E=E, k=1, H=H, act="bf16", gating="noisy", noise=False,
+                   capacity_factor=0.0, seed=0)
+    p = problem_for(moe, w)
+    M, N = (D, H) if which == 1 else (H, D)
+    assert E * (M // 256) * (N // 256) >= 256
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    A = I.f32_to_bf16_bits(rng.standard_normal((T, M)).astype(np.float32))
+    B = I.f32_to_bf16_bits(rng.standard_normal((T, N)).astype(np.float32))
+    C = torch.full((E, M, N), float("nan"), device="cuda")  # every element must be written
+    log(f"[wgrad large tiles] which {which}: {T} rows over {E} experts, C {M} x {N}")
+    moe.moe_expert_weight_grad(p, which, dev(A), dev(B), dev(offs), C)
+    Ch = host(C)
+    Af, Bf = O.widen(A), O.widen(B)
+    worst = 0.0
+    for e in range(E):
+        s_ = slice(offs[e], offs[e + 1])
+        ref = Af[s_].T @ Bf[s_]
+        if offs[e + 1] == offs[e]:
+            assert (Ch[e] == 0).all(), f"expert {e} (no rows) not zero"
+            continue
+        err = np.abs(Ch[e] - ref).max() / max(np.abs(ref).max(), 1e-30)
+        worst = max(worst, err)
+        assert err < TOL["f32"], f"expert {e} ({sizes[e]} rows): rel err {err:.2e}"
+    log(f"  every expert within {worst:.2e}")
