@@ -739,6 +739,279 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// ------------------------------------------------------------------ 256 x 256 tiles, 8 waves
+// The same tiles, LDS stages, stage stream and tile walk as grouped_gemm_big, with 8 waves: wave
+// w computes the 128 x 64 part (rows 128 (w / 4), columns 64 (w % 4)) in 128 accumulators, so
+// two waves share each SIMD. A wave's instruction stream issues in order, and one whose
+// global-to-LDS load or LDS read cannot issue holds back its own MFMAs; with a second wave on
+// the SIMD, that wave's MFMAs run meanwhile. Waves 0-3 issue every global-to-LDS load (wave w:
+// A rows 64 w .. 64 w + 63 and B column blocks 2 w, 2 w + 1 of each stage, 8 + 8 instructions);
+// waves 4-7 only read LDS and compute (about 1% faster than spreading the loads over all eight
+// waves). The epilogue stages a wave's 32 x 64 pieces through one 4 KB LDS tile each (the 8
+// tiles fill the free B slot). Plain and ReLU epilogues, no non-finite check (those go to the
+// 4-wave kernel).
+constexpr int kThreads8 = 512;
+
+template <int kEpi, bool kGather>
+__global__ __launch_bounds__(kThreads8, 1) void grouped_gemm_big8(GemmArgs g) {
+  static_assert(kEpi == 0 || kEpi == 1, "plain or ReLU epilogue");
+  extern __shared__ __align__(16) unsigned char smem[];
+  int* wt = reinterpret_cast<int*>(smem + kScratch);       // 8 ints: block scan
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int E = g.E;
+  const int32_t* off = g.offsets;
+
+  // ---- row tiles per expert (as in grouped_gemm_big, over 512 threads)
+  const int per = (E + kThreads8 - 1) / kThreads8;
+  const int e0 = tid * per, e1 = min(E, e0 + per);
+  int mine = 0;
+  for (int e = e0; e < e1; ++e) mine += (off[e + 1] - off[e] + kBig - 1) / kBig;
+  int excl;
+  const int row_tiles = block_exclusive_scan<kThreads8>(mine, &excl, wt);
+  const int NT = (g.N + kBig - 1) / kBig;
+  const int total_tiles = row_tiles * NT;
+  const int per_xcd = (total_tiles + kXcds - 1) / kXcds;
+  const int nblk_xcd = gridDim.x / kXcds;
+  const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
+  const int first = xcd * per_xcd + local, last = min(total_tiles, (xcd + 1) * per_xcd);
+  const int n_my = first < last ? (last - first + nblk_xcd - 1) / nblk_xcd : 0;
+  if (n_my == 0) return;
+
+  const int K = g.K;
+  const int nst = K / 64;
+  const unsigned char* Ab = static_cast<const unsigned char*>(g.A);
+  const unsigned char* Wp = reinterpret_cast<const unsigned char*>(g.Wp);
+  // lane l of loading wave w's A load instruction i writes row 64 w + 8 i + l / 8 of the stage,
+  // slot l % 8, and fetches the row segment that belongs at that slot
+  auto aseg = [&](int i) { return ((lane & 7) ^ ((4 * i + (lane >> 4)) & 7)) * 16; };
+  const uint32_t ring = lds_offset(smem);
+  const int wm = wave >> 2, wn = wave & 3;
+
+  struct Tile {
+    int e, r0, rows, n0;
+  };
+  int we = 0, wcum = 0;
+  auto locate = [&](int m) {
+    const int logical = first + m * nblk_xcd;
+    const int q = logical / NT;
+    int t = (off[we + 1] - off[we] + kBig - 1) / kBig;
+    while (wcum + t <= q) {
+      wcum += t;
+      ++we;
+      t = (off[we + 1] - off[we] + kBig - 1) / kBig;
+    }
+    const int loc = logical - wcum * NT;
+    const int n_tile = loc / t, m_tile = loc - n_tile * t;
+    Tile T;
+    T.e = we;
+    T.r0 = off[we] + m_tile * kBig;
+    T.rows = min(kBig, off[we + 1] - T.r0);
+    T.n0 = n_tile * kBig;
+    return T;
+  };
+  const int lw = wave & 3;  // loader index (waves 0-3 load)
+  const bool loader = wave < 4;
+  int tok[8];
+  auto request_rows = [&](const Tile& T) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = min(64 * lw + 8 * i + (lane >> 3), T.rows - 1);
+      tok[i] = kGather ? g.row_token[T.r0 + r] : T.r0 + r;
+    }
+  };
+  auto sources = [&](const Tile& T, uint32_t (&ao)[8], const unsigned char* (&bb)[2]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ao[i] = static_cast<uint32_t>(static_cast<int64_t>(tok[i]) * K * 2 + aseg(i));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int nb = min(T.n0 / 32 + 2 * lw + j, g.NB - 1);
+      bb[j] = Wp + (T.e * g.ws_expert + nb * g.ws_block) * kFragBytes;
+    }
+  };
+  uint32_t ao_cur[8], ao_nxt[8];
+  const unsigned char* bb_cur[2];
+  const unsigned char* bb_nxt[2];
+  const uint32_t boff = lane * 16;
+
+  auto dma_a = [&](int s, int kst, int i) {
+    dma16(Ab, ao_cur[i] + kst * 128, ring + (s & 1) * kStageBytes + (64 * lw + 8 * i) * 128);
+  };
+  auto dma_b = [&](int s, int kst, int n) {
+    const int j = n >> 2, ks = n & 3;
+    dma16(bb_cur[j], boff + static_cast<uint32_t>(kst * static_cast<int>(g.ws_stage) + ks) * kFragBytes,
+          ring + kBOff + (s % 3) * kStageBytes + ((2 * lw + j) * 4 + ks) * kFragBytes);
+  };
+
+  f32x16 acc[4][2];
+  int a_lane = (lane & 31) * 128;
+  int a_xor = (lane >> 1) & 7, a_half = lane >> 5;
+  u32x4 fa[2][4], fb[2][2];
+  auto read = [&](int s, int ks, int b) {
+    const unsigned char* pa = smem + (s & 1) * kStageBytes;
+    const unsigned char* pb = smem + kBOff + (s % 3) * kStageBytes;
+    const int slot = ((2 * ks + a_half) ^ a_xor) * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      fa[b][i] = *reinterpret_cast<const u32x4*>(pa + (wm * 4 + i) * 32 * 128 + a_lane + slot);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      fb[b][j] = *reinterpret_cast<const u32x4*>(pb + ((wn * 2 + j) * 4 + ks) * kFragBytes + lane * 16);
+  };
+  // one k-step's 8 MFMAs in four groups; after group i, dmas(i) issues this k-step's share of
+  // the loads
+  auto mma_all = [&](int b, auto dmas) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mma<uint16_t>(fb[b][j], fa[b][i], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+      dmas(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Stage s: the stage schedule of grouped_gemm_big; a loading wave issues 8 B loads over
+  // k-steps 0..2 (3, 3, 2) and 8 A loads in the last k-step (two a group). Before the last
+  // k-step its loads of stage s + 1 are waited for (only the B loads of stage s + 2 may still be
+  // in flight) and every wave passes the barrier.
+  const int S = n_my * nst;
+  auto body = [&](int s, int st) {
+    const bool refill = s + 2 < S;
+    const int kst2 = st + 2 >= nst ? st + 2 - nst : st + 2;
+    if (st == nst - 2 && refill) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ao_cur[i] = ao_nxt[i];
+      bb_cur[0] = bb_nxt[0];
+      bb_cur[1] = bb_nxt[1];
+    }
+    const bool rl = refill && loader;
+    read(s, 1, 1);
+    mma_all(0, [&](int grp) {
+      if (rl && grp < 3) dma_b(s + 2, kst2, grp);
+    });
+    read(s, 2, 0);
+    mma_all(1, [&](int grp) {
+      if (rl && grp < 3) dma_b(s + 2, kst2, 3 + grp);
+    });
+    read(s, 3, 1);
+    mma_all(0, [&](int grp) {
+      if (rl && grp < 2) dma_b(s + 2, kst2, 6 + grp);
+    });
+    if (rl) wait_barrier<8>();
+    else wait_barrier<0>();
+    read(s + 1, 0, 0);
+    mma_all(1, [&](int grp) {
+      if (rl) {
+        dma_a(s + 2, kst2, 2 * grp);
+        dma_a(s + 2, kst2, 2 * grp + 1);
+      }
+    });
+  };
+
+  uint16_t* C = static_cast<uint16_t*>(g.C);
+  __syncthreads();  // the scan scratch is read by every thread before any load reuses LDS
+  Tile cur = locate(0), nxt_t = cur;
+  request_rows(cur);
+  sources(cur, ao_cur, bb_cur);
+  bb_nxt[0] = bb_cur[0];
+  bb_nxt[1] = bb_cur[1];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ao_nxt[i] = ao_cur[i];
+  if (n_my > 1) {
+    nxt_t = locate(1);
+    request_rows(nxt_t);
+    sources(nxt_t, ao_nxt, bb_nxt);
+  }
+  if (loader) {
+#pragma unroll
+    for (int s0 = 0; s0 < 2; ++s0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dma_a(s0, s0, i);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) dma_b(s0, s0, n);
+    }
+    wait_barrier<16>();
+  } else {
+    wait_barrier<0>();
+  }
+  read(0, 0, 0);
+
+  int s = 0;
+  for (int m = 0; m < n_my; ++m) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int st = 0; st < nst; ++st, ++s) body(s, st);
+
+    // ---- epilogue: the wave's four 32 x 64 pieces (row block i, both column blocks) through
+    // its 4 KB LDS tile (in the B slot of the tile's last stage), rows stored as 128-byte runs
+    const Tile done = cur;
+    cur = nxt_t;
+    const bool more2 = m + 2 < n_my;
+    if (more2) {
+      nxt_t = locate(m + 2);
+      request_rows(nxt_t);
+    }
+    int lq = lane;
+    asm volatile("" : "+v"(lq));
+    unsigned char* stile = smem + kBOff + ((s - 1) % 3) * kStageBytes + wave * kStageTile;
+    u32x4 rb[4];
+    auto stage_piece = [&](int i) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const f32x16& a = acc[i][jj];
+          s16x2 h0 = __builtin_bit_cast(s16x2, __builtin_convertvector((f32x2){a[4 * qd], a[4 * qd + 1]}, bf16x2));
+          s16x2 h1 = __builtin_bit_cast(s16x2, __builtin_convertvector((f32x2){a[4 * qd + 2], a[4 * qd + 3]}, bf16x2));
+          if (kEpi == 1) {
+            h0 = __builtin_elementwise_max(h0, (s16x2){0, 0});
+            h1 = __builtin_elementwise_max(h1, (s16x2){0, 0});
+          }
+          uint2 v;
+          v.x = __builtin_bit_cast(uint32_t, h0);
+          v.y = __builtin_bit_cast(uint32_t, h1);
+          const int row = lq & 31;
+          const int cb = jj * 64 + qd * 16 + (lq >> 5) * 8;
+          const int sw = ((cb >> 4) ^ (row & 7)) * 16 + (cb & 15);
+          *reinterpret_cast<uint2*>(stile + row * 128 + sw) = v;
+        }
+    };
+    auto read_piece = [&]() {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int row = 8 * p + (lq >> 3), ch = lq & 7;
+        rb[p] = *reinterpret_cast<const u32x4*>(stile + row * 128 + ((ch ^ (row & 7)) * 16));
+      }
+    };
+    auto store_piece = [&](int i) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int row = 8 * p + (lq >> 3), ch = lq & 7;
+        const int grow = min(wm * 128 + i * 32 + row, done.rows - 1);
+        const int col = done.n0 + wn * 64 + ch * 8;
+        *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(done.r0 + grow) * g.N + col) = rb[p];
+      }
+    };
+    // a wave's LDS operations complete in order: piece i + 1 is staged only after piece i has
+    // been read back
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      stage_piece(i);
+      read_piece();
+      store_piece(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    if (more2) sources(nxt_t, ao_nxt, bb_nxt);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // The [E, K, N] source (W1, W2 as the pages lay them out) through LDS: a block takes one k
 // stage (4 k-steps, 8V rows of k) of kPackNb column blocks, reads those rows as whole
 // kPackNb * 32-column segments, and writes the stage's kPackNb * 4 fragments, one contiguous
@@ -987,6 +1260,22 @@ static moe_status launch_big(const GemmArgs& g, int grid, hipStream_t stream) {
   return launch_status();
 }
 
+template <int kEpi, bool kGather>
+static moe_status launch_big8(const GemmArgs& g, int grid, hipStream_t stream) {
+  static std::once_flag once[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  bool ok = true;
+  std::call_once(once[dev], [&] {
+    ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_big8<kEpi, kGather>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             static_cast<int>(kBigLds)) == hipSuccess;
+  });
+  if (!ok) return MOE_ERR_HIP;
+  grouped_gemm_big8<kEpi, kGather><<<grid, kThreads8, kBigLds, stream>>>(g);
+  return launch_status();
+}
+
 moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp, const int32_t* offsets,
                        void* C, int* nonfinite, hipStream_t stream, const void* mask,
                        const int32_t* row_token) {
@@ -1021,10 +1310,11 @@ moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp, 
     // persistent: one block per CU
     const int grid = std::max(kXcds, device_cus() / kXcds * kXcds);
     if (mask) return launch_big<2, false, false>(g, grid, stream);
-    if (g.row_token) return launch_big<1, false, true>(g, grid, stream);
-    if (layer == 1) return launch_big<1, false, false>(g, grid, stream);
+    // the plain and ReLU epilogues without the check: two waves a SIMD
+    if (g.row_token) return launch_big8<1, true>(g, grid, stream);
+    if (layer == 1) return launch_big8<1, false>(g, grid, stream);
     if (nonfinite) return launch_big<0, true, false>(g, grid, stream);
-    return launch_big<0, false, false>(g, grid, stream);
+    return launch_big8<0, false>(g, grid, stream);
   }
   // 128-row tiles, or 64-row ones when the 128-row tiles would not give every CU's two block
   // slots two tiles each (a small or narrow layer): twice the blocks then share the work
