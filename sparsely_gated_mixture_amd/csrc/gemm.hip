@@ -341,9 +341,12 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------ 256 x 256 tiles
-// The large-group kernel (bf16, K a multiple of 64): one persistent block of 4 waves per CU
-// walks a list of 256 x 256 output tiles, each wave computing a 128 x 128 quarter (256 fp32
-// accumulators a lane). Both operands go through LDS, so each byte brought to the CU feeds
+// The large-group kernel (bf16, K a multiple of 64): one persistent block of 8 waves per CU
+// walks a list of 256 x 256 output tiles. Wave w computes the 128 x 64 part at rows
+// 128 (w / 4), columns 64 (w % 4) in 128 fp32 accumulators a lane, so two waves share each
+// SIMD: a wave's instructions issue in order, and one whose load or LDS read cannot issue yet
+// holds back its own MFMAs while the SIMD's other wave runs its MFMAs (four waves of 128 x 128
+// each were 5-6% slower). Both operands go through LDS, so each byte brought to the CU feeds
 // 256 rows or columns (the 128 x 256 kernel above re-streams B for every 128 rows): a third
 // fewer operand bytes per FLOP.
 //   * Operands land in LDS by direct loads (global_load_lds_dwordx4: lane l of a wave writes
@@ -358,22 +361,26 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm(GemmArgs g) {
 //     before its last k-step; the loads of A stage st+2 go out between that k-step's MFMAs and
 //     those of B stage st+2 between the MFMAs of stage st's first three k-steps (B's third
 //     slot lets them start a stage early), a few at a time, so the wave's in-order issue never
-//     stalls behind a burst of loads. The loads are issued in
+//     stalls behind a burst of loads. Waves 0-3 issue every load (wave w: A rows 64 w .. 64 w
+//     + 63 and B column blocks 2 w, 2 w + 1 of the tile), waves 4-7 only read LDS and compute
+//     (about 1% faster than spreading the loads over all eight). The loads are issued in
 //     inline assembly so the compiler, which cannot tell the ring slots apart, does not wait
 //     for every load in flight before each LDS read; the kernel waits for its own loads
 //     (vmcnt: a wave's vector memory operations complete in issue order) and its own reads
 //     (lgkmcnt) before the barrier.
 //   * Tiles: every thread counts the row tiles of its share of the experts once; a tile's
-//     expert is then found by the one thread whose share holds it. After a tile's last k-step
-//     the next tile's first stage is requested before the epilogue, so its latency overlaps
-//     the epilogue's work, and no block launch separates the tiles. Each XCD's 32 CUs walk a
-//     contiguous run of the tile order (expert, column tile, row tile) together, sharing
-//     operands in their L2.
+//     expert is then found by a walk over the experts' offsets (uniform loads). After a tile's
+//     last k-step the next tile's first stages are already requested, so their latency
+//     overlaps the epilogue's work, and no block launch separates the tiles. Each XCD's 32 CUs
+//     walk a contiguous run of the tile order (expert, column tile, row tile) together,
+//     sharing operands in their L2.
 //   * The MFMA takes the weight fragment as its first operand, so the accumulator holds the
 //     tile transposed: lane l owns output row l % 32 of its 32 x 32 block and, in registers
-//     4q .. 4q+3, four adjacent columns 8q + 4 (l / 32) .. +3. The epilogue stages a 32 x 64
-//     piece of each wave's quarter at a time in LDS and stores it back as whole 128-byte row
-//     runs (full cache lines).
+//     4q .. 4q+3, four adjacent columns 8q + 4 (l / 32) .. +3. The epilogue stages a wave's
+//     32 x 64 pieces in a 4 KB LDS tile of its own (the eight tiles fill the B slot not in
+//     use) and stores them back as whole 128-byte row runs (full cache lines).
+//   * Epilogues: plain (kEpi 0), ReLU (1), or the backward's dH (2: zero where the stored
+//     activation at the same place is not > 0); kCheck records NaN / Inf outputs.
 constexpr int kBig = 256;                  // tile rows and columns
 constexpr int kMaxGemmExperts = 4096;      // the library's largest E
 constexpr int kFragBytes = 1024;           // one 64-lane x 16-byte fragment
@@ -401,360 +408,31 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int kEpi, bool kCheck, bool kGather>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_big(GemmArgs g) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  int* wt = reinterpret_cast<int*>(smem + kScratch);       // 4 ints: block scan
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int E = g.E;
-  const int32_t* off = g.offsets;
-
-  // ---- row tiles per expert: thread tid owns experts e0 .. e1-1 and keeps the number of row
-  // tiles before them (excl) and in them (mine)
-  const int per = (E + kThreads - 1) / kThreads;
-  const int e0 = tid * per, e1 = min(E, e0 + per);
-  int mine = 0;
-  for (int e = e0; e < e1; ++e) mine += (off[e + 1] - off[e] + kBig - 1) / kBig;
-  int excl;
-  const int row_tiles = block_exclusive_scan<kThreads>(mine, &excl, wt);
-  const int NT = (g.N + kBig - 1) / kBig;
-  const int total_tiles = row_tiles * NT;
-  const int per_xcd = (total_tiles + kXcds - 1) / kXcds;
-  const int nblk_xcd = gridDim.x / kXcds;
-  const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
-  const int first = xcd * per_xcd + local, last = min(total_tiles, (xcd + 1) * per_xcd);
-  const int n_my = first < last ? (last - first + nblk_xcd - 1) / nblk_xcd : 0;
-  if (n_my == 0) return;
-
-  const int K = g.K;
-  const int nst = K / 64;
-  const unsigned char* Ab = static_cast<const unsigned char*>(g.A);
-  const unsigned char* Wp = reinterpret_cast<const unsigned char*>(g.Wp);
-  // lane l of A load instruction i writes row 8i + l/8 of its 8-row group, slot l % 8, and
-  // fetches the row segment that belongs at that slot (see the read below)
-  auto aseg = [&](int i) { return ((lane & 7) ^ ((4 * i + (lane >> 4)) & 7)) * 16; };
-  const uint32_t ring = lds_offset(smem);
-  const int wm = wave >> 1, wn = wave & 1;
-
-  // ---- tiles and their load sources. A tile is an expert's 256-row tile and a 256-column
-  // tile; the block's tiles have increasing row-tile indices, so a walk over the experts
-  // (uniform loads of the offsets) finds each one's expert. This wave's load sources: A rows
-  // 64w .. 64w+63 as 8 instructions of 8 rows (byte offsets into A), B column blocks 2w and
-  // 2w+1 (wave-uniform bases into the packed weights). Rows past the group repeat its last row
-  // and column blocks past N repeat the last one (neither is ever stored).
-  struct Tile {
-    int e, r0, rows, n0;
-  };
-  int we = 0, wcum = 0;  // walk state: expert we's first row tile is wcum
-  auto locate = [&](int m) {
-    const int logical = first + m * nblk_xcd;
-    const int q = logical / NT;
-    int t = (off[we + 1] - off[we] + kBig - 1) / kBig;
-    while (wcum + t <= q) {
-      wcum += t;
-      ++we;
-      t = (off[we + 1] - off[we] + kBig - 1) / kBig;
-    }
-    const int loc = logical - wcum * NT;
-    const int n_tile = loc / t, m_tile = loc - n_tile * t;
-    Tile T;
-    T.e = we;
-    T.r0 = off[we] + m_tile * kBig;
-    T.rows = min(kBig, off[we + 1] - T.r0);
-    T.n0 = n_tile * kBig;
-    return T;
-  };
-  // in two halves: the rows (gathered through row_token) are requested first and turned into
-  // offsets later, so the wait for them can come after other work
-  int tok[8];
-  auto request_rows = [&](const Tile& T) {
+// 1 if either bf16 of a packed pair has an all-ones exponent (NaN or infinity; rounding keeps
+// both, and a value past the bf16 range becomes infinite)
+__device__ __forceinline__ bool bf16_pair_nonfinite(s16x2 h) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, h);
+  return ((u & 0x7f80u) == 0x7f80u) | ((u & 0x7f800000u) == 0x7f800000u);
+}
+// Eight bf16 values with each one zeroed where the mask's bf16 at the same place is not > 0
+// (a NaN mask zeroes it).
+__device__ __forceinline__ u32x4 relu_mask_bf16x8(u32x4 v, u32x4 mq) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = min(64 * wave + 8 * i + (lane >> 3), T.rows - 1);
-      tok[i] = kGather ? g.row_token[T.r0 + r] : T.r0 + r;
-    }
-  };
-  auto sources = [&](const Tile& T, uint32_t (&ao)[8], const unsigned char* (&bb)[2]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ao[i] = static_cast<uint32_t>(static_cast<int64_t>(tok[i]) * K * 2 + aseg(i));
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int nb = min(T.n0 / 32 + 2 * wave + j, g.NB - 1);
-      bb[j] = Wp + (T.e * g.ws_expert + nb * g.ws_block) * kFragBytes;
-    }
-  };
-  // the current tile's sources and the next tile's (its first two stages are loaded while the
-  // current tile's last two compute)
-  uint32_t ao_cur[8], ao_nxt[8];
-  const unsigned char* bb_cur[2];
-  const unsigned char* bb_nxt[2];
-  uint32_t boff = lane * 16;
-
-  // The stages form one stream across the block's tiles: stage s (the k-stage s % nst of tile
-  // s / nst) goes to A slot s % 2 and B slot s % 3 (8 loads a wave each).
-  auto dma_a = [&](int s, int kst, int i) {
-    dma16(Ab, ao_cur[i] + kst * 128, ring + (s & 1) * kStageBytes + (64 * wave + 8 * i) * 128);
-  };
-  auto dma_b = [&](int s, int kst, int n) {
-    const int j = n >> 2, ks = n & 3;
-    dma16(bb_cur[j], boff + static_cast<uint32_t>(kst * static_cast<int>(g.ws_stage) + ks) * kFragBytes,
-          ring + kBOff + (s % 3) * kStageBytes + ((2 * wave + j) * 4 + ks) * kFragBytes);
-  };
-
-  f32x16 acc[4][4];
-  // A fragment of row block mb, k-step ks: lane l reads row mb*32 + l%32, 16-byte chunk
-  // 2 ks + l/32 of the row, stored at slot chunk ^ ((row >> 1) & 7) = chunk ^ ((l >> 1) & 7):
-  // the 16 lanes the LDS serves together (rows 16g .. 16g+15) then cover all 64 banks, since
-  // a 128-byte row spans half of them and rows r, r+1 share the XOR term but not the half.
-  int a_lane = (lane & 31) * 128;
-  int a_xor = (lane >> 1) & 7, a_half = lane >> 5;
-  u32x4 fa[2][4], fb[2][4];
-  auto read = [&](int s, int ks, int b) {
-    const unsigned char* pa = smem + (s & 1) * kStageBytes;
-    const unsigned char* pb = smem + kBOff + (s % 3) * kStageBytes;
-    const int slot = ((2 * ks + a_half) ^ a_xor) * 16;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      fa[b][i] = *reinterpret_cast<const u32x4*>(pa + (wm * 4 + i) * 32 * 128 + a_lane + slot);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      fb[b][j] = *reinterpret_cast<const u32x4*>(pb + ((wn * 4 + j) * 4 + ks) * kFragBytes + lane * 16);
-  };
-  // One k-step's 16 MFMAs in four groups; after group i, dmas(i) issues this k-step's share
-  // of the loads. The scheduling barriers keep the compiler from regrouping them.
-  auto mma_all = [&](int b, auto dmas) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mma<uint16_t>(fb[b][j], fa[b][i], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
-      dmas(i);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // Stage s (k-stage st of tile m): k-steps 1..3 are read one ahead of the MFMAs; the B loads of
-  // stage s+2 (into the B slot stage s-1 freed) go out between the MFMAs of k-steps 0..2.
-  // Before the last k-step, wait for stage s+1 (this wave's loads by count: only B of stage s+2
-  // may still be in flight; every wave's by the barrier, after which every wave has also
-  // finished reading stage s) and read its first k-step; the A loads of stage s+2 (into the A
-  // slot stage s freed) go out between the last k-step's MFMAs. Stage s+2 belongs to the next
-  // tile for a tile's last two stages. The loads and the wait count depend on uniform branches;
-  // the LDS reads do not (after the block's last stage the read is of a stale slot and unused),
-  // so the compiler's own accounting of them is the same on every path.
-  const int S = n_my * nst;
-  auto body = [&](int s, int st) {
-    const bool refill = s + 2 < S;
-    const int kst2 = st + 2 >= nst ? st + 2 - nst : st + 2;
-    // the current tile's last refill was stage nst-1 (in body nst-3): from here on the refills
-    // are the next tile's
-    if (st == nst - 2 && refill) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ao_cur[i] = ao_nxt[i];
-      bb_cur[0] = bb_nxt[0];
-      bb_cur[1] = bb_nxt[1];
-    }
-    auto b_part = [&](int first_n, int count) {
-      return [&, first_n, count](int grp) {
-        if (refill) {
-          for (int n = first_n + (grp * count) / 4; n < first_n + ((grp + 1) * count) / 4; ++n)
-            dma_b(s + 2, kst2, n);
-        }
-      };
-    };
-    read(s, 1, 1);
-    mma_all(0, b_part(0, 3));
-    read(s, 2, 0);
-    mma_all(1, b_part(3, 3));
-    read(s, 3, 1);
-    mma_all(0, b_part(6, 2));
-    if (refill) wait_barrier<8>();
-    else wait_barrier<0>();
-    read(s + 1, 0, 0);
-    mma_all(1, [&](int grp) {
-      if (refill) {
-        dma_a(s + 2, kst2, 2 * grp);
-        dma_a(s + 2, kst2, 2 * grp + 1);
-      }
-    });
-  };
-
-  uint16_t* C = static_cast<uint16_t*>(g.C);
-  bool bad = false;
-  __syncthreads();  // the scan scratch is read by every thread before any load reuses LDS
-  Tile cur = locate(0), nxt_t = cur;
-  request_rows(cur);
-  sources(cur, ao_cur, bb_cur);
-  if (n_my > 1) {
-    nxt_t = locate(1);
-    request_rows(nxt_t);
-    sources(nxt_t, ao_nxt, bb_nxt);
+  for (int w2 = 0; w2 < 4; ++w2) {
+    const uint32_t mw = mq[w2];
+    uint32_t vw = v[w2];
+    if (!(__uint_as_float(mw << 16) > 0.f)) vw &= 0xffff0000u;
+    if (!(__uint_as_float(mw & 0xffff0000u) > 0.f)) vw &= 0x0000ffffu;
+    v[w2] = vw;
   }
-  // stages 0 and 1 (tile 0), then wait for stage 0
-#pragma unroll
-  for (int s0 = 0; s0 < 2; ++s0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dma_a(s0, s0, i);
-#pragma unroll
-    for (int n = 0; n < 8; ++n) dma_b(s0, s0, n);
-  }
-  wait_barrier<16>();
-  read(0, 0, 0);
-
-  int s = 0;
-  for (int m = 0; m < n_my; ++m) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    for (int st = 0; st < nst; ++st, ++s) body(s, st);
-
-    // ---- epilogue (the next tile's first two stages are already in flight). The next-but-one
-    // tile's sources are requested first, so their latency overlaps the epilogue.
-    const Tile done = cur;
-    cur = nxt_t;
-    const bool more2 = m + 2 < n_my;
-    if (more2) {
-      nxt_t = locate(m + 2);
-      request_rows(nxt_t);
-    }
-    // lane owns output row (wm*4+i)*32 + l%32; register 4q+s is column (wn*4+j)*32 + 8q +
-    // 4(l/32) + s. Each wave stages a 32 x 64 piece (rows i, columns of j-pair h) in its own LDS
-    // tile (in the B slot of the tile's last stage, free until the next tile's first refill),
-    // then stores it as 128-byte runs, 8 rows an instruction. The staged rows are 128 bytes
-    // with their 16-byte chunks XOR-permuted by the row's low three bits, so neither the writes
-    // nor the reads conflict on banks. The lane-derived offsets come from an opaque copy of the
-    // lane index: left loop-invariant, the compiler hoists every address of the unrolled code
-    // out of the tile loop and runs out of registers holding them.
-    int lq = lane;
-    asm volatile("" : "+v"(lq));
-    unsigned char* stile = smem + kBOff + ((s - 1) % 3) * kStageBytes + wave * kStageTile;
-    // mode 2 (the backward's dH): the mask's 16 bytes at each stored vector, requested one
-    // pipeline step before the piece is stored
-    u32x4 mk[kEpi == 2 ? 2 : 1][4];
-    auto load_mask = [&](int piece) {
-      const int i = piece >> 1, h = piece & 1;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int row = 8 * p + (lq >> 3), ch = lq & 7;
-        const int grow = min(wm * 128 + i * 32 + row, done.rows - 1);
-        const int col = done.n0 + wn * 128 + h * 64 + ch * 8;
-        mk[piece & 1][p] = *reinterpret_cast<const u32x4*>(
-            static_cast<const uint16_t*>(g.mask) + static_cast<int64_t>(done.r0 + grow) * g.N + col);
-      }
-    };
-    // The eight 32 x 64 pieces (pc = 2 i + h) go through two staging tiles in a pipeline: in
-    // step pc the wave converts and stages piece pc, stores piece pc - 2 (read back in the
-    // step before, after that step's conversions, so the read's latency is covered) and
-    // reads back piece pc - 1. LDS operations of one wave complete in order, so a tile is
-    // written again only after its previous piece has been read.
-    unsigned char* st2[2] = {stile, stile + 4 * kStageTile};
-    u32x4 rb[2][4];
-    auto stage_piece = [&](int pc) {
-      const int i = pc >> 1, h = pc & 1;
-      unsigned char* t = st2[pc & 1];
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          const f32x16& a = acc[i][2 * h + jj];
-          s16x2 h0 = __builtin_bit_cast(s16x2, __builtin_convertvector((f32x2){a[4 * qd], a[4 * qd + 1]}, bf16x2));
-          s16x2 h1 = __builtin_bit_cast(s16x2, __builtin_convertvector((f32x2){a[4 * qd + 2], a[4 * qd + 3]}, bf16x2));
-          if (kCheck) {
-            // on the rounded pair (rounding keeps NaN and infinity, and a value past the
-            // bf16 range becomes infinite in the output): an all-ones exponent, before any
-            // ReLU; integer tests on the packed values, no accumulator read twice
-            const uint32_t u0 = __builtin_bit_cast(uint32_t, h0), u1 = __builtin_bit_cast(uint32_t, h1);
-            bad |= ((u0 & 0x7f80u) == 0x7f80u) | ((u0 & 0x7f800000u) == 0x7f800000u) |
-                   ((u1 & 0x7f80u) == 0x7f80u) | ((u1 & 0x7f800000u) == 0x7f800000u);
-          }
-          if (kEpi == 1) {
-            h0 = __builtin_elementwise_max(h0, (s16x2){0, 0});
-            h1 = __builtin_elementwise_max(h1, (s16x2){0, 0});
-          }
-          uint2 v;
-          v.x = __builtin_bit_cast(uint32_t, h0);
-          v.y = __builtin_bit_cast(uint32_t, h1);
-          // column byte offset inside the 128-byte staged row: jj*64 + qd*16 + (l/32)*8
-          const int row = lq & 31;
-          const int cb = jj * 64 + qd * 16 + (lq >> 5) * 8;
-          const int sw = ((cb >> 4) ^ (row & 7)) * 16 + (cb & 15);
-          *reinterpret_cast<uint2*>(t + row * 128 + sw) = v;
-        }
-    };
-    // read back: instruction p covers rows 8p .. 8p+7, lane l: row 8p + l/8, chunk l % 8
-    auto read_piece = [&](int pc) {
-      const unsigned char* t = st2[pc & 1];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int row = 8 * p + (lq >> 3), ch = lq & 7;
-        rb[pc & 1][p] = *reinterpret_cast<const u32x4*>(t + row * 128 + ((ch ^ (row & 7)) * 16));
-      }
-    };
-    auto store_piece = [&](int pc) {
-      const int i = pc >> 1, h = pc & 1;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int row = 8 * p + (lq >> 3), ch = lq & 7;
-        u32x4 v = rb[pc & 1][p];
-        if constexpr (kEpi == 2) {  // zero where the mask is not > 0 (a NaN mask keeps it)
-          const u32x4 mq = mk[pc & 1][p];
-#pragma unroll
-          for (int w2 = 0; w2 < 4; ++w2) {
-            const uint32_t mw = mq[w2];
-            uint32_t vw = v[w2];
-            if (!(__uint_as_float(mw << 16) > 0.f)) vw &= 0xffff0000u;
-            if (!(__uint_as_float(mw & 0xffff0000u) > 0.f)) vw &= 0x0000ffffu;
-            v[w2] = vw;
-          }
-        }
-        // a row past the group holds exactly the group's last row (its A row was repeated),
-        // so it is written there again, unchanged
-        const int grow = min(wm * 128 + i * 32 + row, done.rows - 1);
-        const int col = done.n0 + wn * 128 + h * 64 + ch * 8;
-        *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(done.r0 + grow) * g.N + col) = v;
-      }
-    };
-#pragma unroll
-    for (int pc = 0; pc < 10; ++pc) {
-      if (pc < 8) stage_piece(pc);
-      // mode 2: piece pc - 1's mask, used when that piece is stored in the next step
-      if constexpr (kEpi == 2) {
-        if (pc >= 1 && pc <= 8) load_mask(pc - 1);
-      }
-      if (pc >= 2) store_piece(pc - 2);
-      if (pc >= 1 && pc <= 8) read_piece(pc - 1);
-      // one piece at a time: converting every accumulator up front would need 128 more
-      // registers than the wave has
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // every wave is done with the staging slot before the next tile's first refill reuses it
-    __syncthreads();
-    if (more2) sources(nxt_t, ao_nxt, bb_nxt);
-  }
-  if (kCheck) note_nonfinite(g.nonfinite, bad);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  return v;
 }
 
-// ------------------------------------------------------------------ 256 x 256 tiles, 8 waves
-// The same tiles, LDS stages, stage stream and tile walk as grouped_gemm_big, with 8 waves: wave
-// w computes the 128 x 64 part (rows 128 (w / 4), columns 64 (w % 4)) in 128 accumulators, so
-// two waves share each SIMD. A wave's instruction stream issues in order, and one whose
-// global-to-LDS load or LDS read cannot issue holds back its own MFMAs; with a second wave on
-// the SIMD, that wave's MFMAs run meanwhile. Waves 0-3 issue every global-to-LDS load (wave w:
-// A rows 64 w .. 64 w + 63 and B column blocks 2 w, 2 w + 1 of each stage, 8 + 8 instructions);
-// waves 4-7 only read LDS and compute (about 1% faster than spreading the loads over all eight
-// waves). The epilogue stages a wave's 32 x 64 pieces through one 4 KB LDS tile each (the 8
-// tiles fill the free B slot). Plain and ReLU epilogues, no non-finite check (those go to the
-// 4-wave kernel).
 constexpr int kThreads8 = 512;
 
-template <int kEpi, bool kGather>
-__global__ __launch_bounds__(kThreads8, 1) void grouped_gemm_big8(GemmArgs g) {
-  static_assert(kEpi == 0 || kEpi == 1, "plain or ReLU epilogue");
+template <int kEpi, bool kCheck, bool kGather>
+__global__ __launch_bounds__(kThreads8, 1) void grouped_gemm_big(GemmArgs g) {
+  static_assert(!kCheck || kEpi == 0, "the check is compiled for the plain epilogue only");
   extern __shared__ __align__(16) unsigned char smem[];
   int* wt = reinterpret_cast<int*>(smem + kScratch);       // 8 ints: block scan
   const int tid = threadIdx.x, lane = tid & 63;
@@ -762,7 +440,8 @@ __global__ __launch_bounds__(kThreads8, 1) void grouped_gemm_big8(GemmArgs g) {
   const int E = g.E;
   const int32_t* off = g.offsets;
 
-  // ---- row tiles per expert (as in grouped_gemm_big, over 512 threads)
+  // ---- row tiles per expert: thread tid owns experts e0 .. e1-1 and keeps the number of row
+  // tiles before them (excl) and in them (mine)
   const int per = (E + kThreads8 - 1) / kThreads8;
   const int e0 = tid * per, e1 = min(E, e0 + per);
   int mine = 0;
@@ -871,7 +550,7 @@ __global__ __launch_bounds__(kThreads8, 1) void grouped_gemm_big8(GemmArgs g) {
     }
   };
 
-  // Stage s: the stage schedule of grouped_gemm_big; a loading wave issues 8 B loads over
+  // Stage s: a loading wave issues 8 B loads over
   // k-steps 0..2 (3, 3, 2) and 8 A loads in the last k-step (two a group). Before the last
   // k-step its loads of stage s + 1 are waited for (only the B loads of stage s + 2 may still be
   // in flight) and every wave passes the barrier.
@@ -937,6 +616,7 @@ __global__ __launch_bounds__(kThreads8, 1) void grouped_gemm_big8(GemmArgs g) {
   }
   read(0, 0, 0);
 
+  bool bad = false;
   int s = 0;
   for (int m = 0; m < n_my; ++m) {
 #pragma unroll
@@ -968,6 +648,7 @@ __global__ __launch_bounds__(kThreads8, 1) void grouped_gemm_big8(GemmArgs g) {
           const f32x16& a = acc[i][jj];
           s16x2 h0 = __builtin_bit_cast(s16x2, __builtin_convertvector((f32x2){a[4 * qd], a[4 * qd + 1]}, bf16x2));
           s16x2 h1 = __builtin_bit_cast(s16x2, __builtin_convertvector((f32x2){a[4 * qd + 2], a[4 * qd + 3]}, bf16x2));
+          if (kCheck) bad |= bf16_pair_nonfinite(h0) | bf16_pair_nonfinite(h1);
           if (kEpi == 1) {
             h0 = __builtin_elementwise_max(h0, (s16x2){0, 0});
             h1 = __builtin_elementwise_max(h1, (s16x2){0, 0});
@@ -988,19 +669,35 @@ __global__ __launch_bounds__(kThreads8, 1) void grouped_gemm_big8(GemmArgs g) {
         rb[p] = *reinterpret_cast<const u32x4*>(stile + row * 128 + ((ch ^ (row & 7)) * 16));
       }
     };
+    // mode 2 (the backward's dH): the mask's 16 bytes at each stored vector, requested before
+    // the piece is staged so that their latency is covered
+    u32x4 mk[kEpi == 2 ? 4 : 1];
+    auto load_mask = [&](int i) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int row = 8 * p + (lq >> 3), ch = lq & 7;
+        const int grow = min(wm * 128 + i * 32 + row, done.rows - 1);
+        const int col = done.n0 + wn * 64 + ch * 8;
+        mk[p] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(g.mask) +
+                                                static_cast<int64_t>(done.r0 + grow) * g.N + col);
+      }
+    };
     auto store_piece = [&](int i) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const int row = 8 * p + (lq >> 3), ch = lq & 7;
         const int grow = min(wm * 128 + i * 32 + row, done.rows - 1);
         const int col = done.n0 + wn * 64 + ch * 8;
-        *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(done.r0 + grow) * g.N + col) = rb[p];
+        u32x4 v = rb[p];
+        if constexpr (kEpi == 2) v = relu_mask_bf16x8(v, mk[p]);
+        *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(done.r0 + grow) * g.N + col) = v;
       }
     };
     // a wave's LDS operations complete in order: piece i + 1 is staged only after piece i has
     // been read back
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      if constexpr (kEpi == 2) load_mask(i);
       stage_piece(i);
       read_piece();
       store_piece(i);
@@ -1009,6 +706,7 @@ __global__ __launch_bounds__(kThreads8, 1) void grouped_gemm_big8(GemmArgs g) {
     __syncthreads();
     if (more2) sources(nxt_t, ao_nxt, bb_nxt);
   }
+  if (kCheck) note_nonfinite(g.nonfinite, bad);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
@@ -1247,32 +945,14 @@ static moe_status launch_big(const GemmArgs& g, int grid, hipStream_t stream) {
   static std::once_flag once[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
-  const size_t lds = kBigLds;
   bool ok = true;
   std::call_once(once[dev], [&] {
     ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_big<kEpi, kCheck, kGather>),
                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                             static_cast<int>(kBigLds)) ==
-         hipSuccess;
-  });
-  if (!ok) return MOE_ERR_HIP;
-  grouped_gemm_big<kEpi, kCheck, kGather><<<grid, kThreads, lds, stream>>>(g);
-  return launch_status();
-}
-
-template <int kEpi, bool kGather>
-static moe_status launch_big8(const GemmArgs& g, int grid, hipStream_t stream) {
-  static std::once_flag once[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
-  bool ok = true;
-  std::call_once(once[dev], [&] {
-    ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_big8<kEpi, kGather>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize,
                              static_cast<int>(kBigLds)) == hipSuccess;
   });
   if (!ok) return MOE_ERR_HIP;
-  grouped_gemm_big8<kEpi, kGather><<<grid, kThreads8, kBigLds, stream>>>(g);
+  grouped_gemm_big<kEpi, kCheck, kGather><<<grid, kThreads8, kBigLds, stream>>>(g);
   return launch_status();
 }
 
@@ -1309,12 +989,12 @@ moe_status gemm_launch(const Dims& d, int layer, const void* A, const void* Wp, 
       gemm_tiles(d, N, kBig) >= device_cus()) {
     // persistent: one block per CU
     const int grid = std::max(kXcds, device_cus() / kXcds * kXcds);
+    // (only the plain epilogue is ever given a non-finite flag: the forward's layer 2)
     if (mask) return launch_big<2, false, false>(g, grid, stream);
-    // the plain and ReLU epilogues without the check: two waves a SIMD
-    if (g.row_token) return launch_big8<1, true>(g, grid, stream);
-    if (layer == 1) return launch_big8<1, false>(g, grid, stream);
+    if (g.row_token) return launch_big<1, false, true>(g, grid, stream);
+    if (layer == 1) return launch_big<1, false, false>(g, grid, stream);
     if (nonfinite) return launch_big<0, true, false>(g, grid, stream);
-    return launch_big8<0, false>(g, grid, stream);
+    return launch_big<0, false, false>(g, grid, stream);
   }
   // 128-row tiles, or 64-row ones when the 128-row tiles would not give every CU's two block
   // slots two tiles each (a small or narrow layer): twice the blocks then share the work
