@@ -923,22 +923,36 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_gemm_big(WgradArgs a) {
   };
   const uint32_t ring = wg_lds_offset(smem);
   // lane l of load instruction i of this wave writes row 16 w + 2 i + l / 32 of the stage, LDS
-  // chunk l % 32, and fetches the 16 bytes that belong there
+  // chunk l % 32, and fetches the 16 bytes that belong there. The lane's source addresses for
+  // the tile being loaded (stage 0; a stage is 64 rows further on) are formed once per tile,
+  // so a load costs one 64-bit add and the select of the zero row past the group's end: a
+  // wave's instructions issue in order, and a longer address computation before each load
+  // holds back its MFMAs.
   const int lrow = 16 * wave + (lane >> 5), lslot = lane & 31;
-  auto dma = [&](bool opB, const Tile& T, int kst, int slot_base, int i) {
-    const int row = lrow + 2 * i;
-    const int chunk = lslot ^ (4 * (row & 3));
-    const int r = T.rb + kst * 64 + row;
-    const void* src = kZeroRow;
-    if (r < T.re)
-      src = opB ? static_cast<const void*>(B + static_cast<int64_t>(r) * N + T.n0 + chunk * 8)
-                : static_cast<const void*>(A + static_cast<int64_t>(r) * M + T.m0 + chunk * 8);
-    dma16_at(src, ring + slot_base + (16 * wave + 2 * i) * 512);
+  const uint16_t* pa[8];
+  const uint16_t* pb[8];
+  int l_rows = 0;  // rows of the tile being loaded
+  auto load_tile = [&](const Tile& T) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = lrow + 2 * i;
+      const int chunk = lslot ^ (4 * (row & 3));
+      pa[i] = A + static_cast<int64_t>(T.rb + row) * M + T.m0 + chunk * 8;
+      pb[i] = B + static_cast<int64_t>(T.rb + row) * N + T.n0 + chunk * 8;
+    }
+    l_rows = T.re - T.rb;
   };
-  auto dma_a = [&](int s, const Tile& T, int kst, int i) { dma(false, T, kst, (s & 1) * kWGStage, i); };
-  auto dma_b = [&](int s, const Tile& T, int kst, int i) {
-    dma(true, T, kst, kWGBOff + (s % 3) * kWGStage, i);
+  const int64_t a_stage = 64LL * M, b_stage = 64LL * N;  // elements per stage
+  auto dma = [&](const uint16_t* p0, int64_t stage_elems, int kst, uint32_t slot, int i) {
+    const uint16_t* src = p0 + kst * stage_elems;
+    const void* from = lrow + 2 * i < l_rows - kst * 64 ? static_cast<const void*>(src)
+                                                        : static_cast<const void*>(kZeroRow);
+    dma16_at(from, slot + (16 * wave + 2 * i) * 512);
   };
+  auto dma_a = [&](uint32_t slot, int kst, int i) { dma(pa[i], a_stage, kst, slot, i); };
+  auto dma_b = [&](uint32_t slot, int kst, int i) { dma(pb[i], b_stage, kst, slot, i); };
+  auto a_slot = [&](int s) { return ring + static_cast<uint32_t>((s & 1) * kWGStage); };
+  auto b_slot = [&](int s) { return ring + static_cast<uint32_t>(kWGBOff + (s % 3) * kWGStage); };
 
   const int wm = wave >> 1, wn = wave & 1;
   // transpose-read fragments: lane (gq, jr, qc) reads 8 bytes at row 16 ks + 8 (gq / 2) + jr
@@ -992,13 +1006,15 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_gemm_big(WgradArgs a) {
   auto body = [&](int s, int st, bool more_tiles) {
     const bool in_cur = st + 2 < cur.nst;
     const bool refill = in_cur || more_tiles;
-    const Tile& T2 = in_cur ? cur : nxt;
     const int k2 = in_cur ? st + 2 : st + 2 - cur.nst;
+    // the loads switch to the next tile with its first stage
+    if (refill && k2 == 0) load_tile(nxt);
+    const uint32_t as2 = a_slot(s + 2), bs2 = b_slot(s + 2);
     auto b_part = [&](int first_i, int count) {
       return [&, first_i, count](int grp) {
         if (refill) {
           for (int i = first_i + (grp * count) / 4; i < first_i + ((grp + 1) * count) / 4; ++i)
-            dma_b(s + 2, T2, k2, i);
+            dma_b(bs2, k2, i);
         }
       };
     };
@@ -1013,19 +1029,20 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_gemm_big(WgradArgs a) {
     read(s + 1, 0, 0);
     mma_all(1, [&](int grp) {
       if (refill) {
-        dma_a(s + 2, T2, k2, 2 * grp);
-        dma_a(s + 2, T2, k2, 2 * grp + 1);
+        dma_a(as2, k2, 2 * grp);
+        dma_a(as2, k2, 2 * grp + 1);
       }
     });
   };
 
   // stages 0 and 1 (tile 0), then wait for stage 0
+  load_tile(cur);
 #pragma unroll
   for (int s0 = 0; s0 < 2; ++s0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma_a(s0, cur, s0, i);
+    for (int i = 0; i < 8; ++i) dma_a(a_slot(s0), s0, i);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma_b(s0, cur, s0, i);
+    for (int i = 0; i < 8; ++i) dma_b(b_slot(s0), s0, i);
   }
   wg_wait_barrier<16>();
   read(0, 0, 0);
