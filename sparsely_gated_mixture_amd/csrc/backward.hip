@@ -837,10 +837,13 @@ __global__ __launch_bounds__(kThreads) void wgrad_gemm_tr(WgradArgs a) {
 }
 
 // ------------------------------------------------------------------ 256 x 256 weight gradients
-// bf16 operands, M and N multiples of 256, one row split: one persistent block of 4 waves per
-// CU walks a list of (group, 256 x 256 output tile)s, each wave accumulating a 128 x 128
-// quarter (256 fp32 accumulators a lane). A tile's operand bytes per stage feed 256 rows and
-// 256 columns, half of what the 128 x 256 kernel above moves per FLOP.
+// bf16 operands, M and N multiples of 256, one row split: one persistent block of 8 waves per
+// CU walks a list of (group, 256 x 256 output tile)s, each wave accumulating a 128 x 64 part
+// (128 fp32 accumulators a lane), two waves a SIMD: a wave's instructions issue in order, and
+// while one is held at a load or LDS read the other's MFMAs run (4 waves of 128 x 128 were
+// 4-6% slower). Waves 0-3 issue the loads, waves 4-7 only read LDS and compute. A tile's
+// operand bytes per stage feed 256 rows and 256 columns, half of what the 128 x 256 kernel
+// above moves per FLOP.
 //   * A stage is 64 rows of the reduction: the tile's 256 columns of A and of B for those rows,
 //     512 bytes a row, brought to LDS by direct global-to-LDS loads (16 bytes a lane, two rows
 //     an instruction, whole 128-byte lines) from per-lane 64-bit addresses. Rows past the group
@@ -854,14 +857,15 @@ __global__ __launch_bounds__(kThreads) void wgrad_gemm_tr(WgradArgs a) {
 //     has at least two stages (more zero rows for a group of at most 64 rows).
 //   * Tiles run group-major, along the smaller output dimension first; each XCD's 32 CUs take a
 //     contiguous run of that order together, sharing operands in their L2.
-//   * Epilogue: each wave stages 32 x 32 fp32 pieces through two LDS tiles (128-byte rows, chunks
-//     permuted by the row's low three bits) in a two-step pipeline and stores whole 128-byte row
-//     segments.
+//   * Epilogue: each wave stages 32 x 32 fp32 pieces through a 4 KB LDS tile of its own
+//     (128-byte rows, chunks permuted by the row's low three bits), staging the next piece while
+//     the previous one's read-back is in flight, and stores whole 128-byte row segments.
 constexpr int kWG = 256;                    // tile rows (M) and columns (N)
 constexpr int kWGStage = 64 * 512;          // one operand's stage: 64 rows x 256 bf16
 constexpr int kWGBOff = 2 * kWGStage;       // B's three slots follow A's two
 constexpr int kWGPiece = 4096;              // epilogue staging tile: 32 rows x 128 bytes
 constexpr size_t kWGLds = 5 * static_cast<size_t>(kWGStage);  // 160 KB
+constexpr int kWGThreads = 512;             // 8 waves
 
 // The source of every row past a group's end.
 __device__ __align__(16) const uint4 kZeroRow[32] = {};
@@ -882,7 +886,7 @@ __device__ __forceinline__ void wg_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-__global__ __launch_bounds__(kThreads, 1) void wgrad_gemm_big(WgradArgs a) {
+__global__ __launch_bounds__(kWGThreads, 1) void wgrad_gemm_big(WgradArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -922,39 +926,43 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_gemm_big(WgradArgs a) {
     return T;
   };
   const uint32_t ring = wg_lds_offset(smem);
-  // lane l of load instruction i of this wave writes row 16 w + 2 i + l / 32 of the stage, LDS
-  // chunk l % 32, and fetches the 16 bytes that belong there. The lane's source addresses for
+  // Waves 0-3 load: lane l of loading wave w's load instruction i writes row 16 w + 2 i + l / 32
+  // of the stage, LDS chunk l % 32, and fetches the 16 bytes that belong there. The lane's source addresses for
   // the tile being loaded (stage 0; a stage is 64 rows further on) are formed once per tile,
   // so a load costs one 64-bit add and the select of the zero row past the group's end: a
   // wave's instructions issue in order, and a longer address computation before each load
   // holds back its MFMAs.
-  const int lrow = 16 * wave + (lane >> 5), lslot = lane & 31;
-  const uint16_t* pa[8];
-  const uint16_t* pb[8];
+  const int lw = wave & 3;
+  const bool loader = wave < 4;
+  const int lrow = 16 * lw + (lane >> 5), lslot = lane & 31;
+  // The permuted chunk of row lrow + 2 i depends on i only through its parity, so the lane
+  // keeps two addresses an operand (row lrow of the tile at the chunk of even / odd i) and a
+  // load adds the uniform 64 kst + 2 i rows.
+  const uint16_t* pa[2];
+  const uint16_t* pb[2];
   int l_rows = 0;  // rows of the tile being loaded
   auto load_tile = [&](const Tile& T) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = lrow + 2 * i;
-      const int chunk = lslot ^ (4 * (row & 3));
-      pa[i] = A + static_cast<int64_t>(T.rb + row) * M + T.m0 + chunk * 8;
-      pb[i] = B + static_cast<int64_t>(T.rb + row) * N + T.n0 + chunk * 8;
+    for (int par = 0; par < 2; ++par) {
+      const int chunk = lslot ^ (4 * ((lrow + 2 * par) & 3));
+      pa[par] = A + static_cast<int64_t>(T.rb + lrow) * M + T.m0 + chunk * 8;
+      pb[par] = B + static_cast<int64_t>(T.rb + lrow) * N + T.n0 + chunk * 8;
     }
     l_rows = T.re - T.rb;
   };
-  const int64_t a_stage = 64LL * M, b_stage = 64LL * N;  // elements per stage
-  auto dma = [&](const uint16_t* p0, int64_t stage_elems, int kst, uint32_t slot, int i) {
-    const uint16_t* src = p0 + kst * stage_elems;
+  auto dma = [&](const uint16_t* p0, int row_elems, int kst, uint32_t slot, int i) {
+    const uint16_t* src = p0 + static_cast<int64_t>(kst * 64 + 2 * i) * row_elems;
     const void* from = lrow + 2 * i < l_rows - kst * 64 ? static_cast<const void*>(src)
                                                         : static_cast<const void*>(kZeroRow);
-    dma16_at(from, slot + (16 * wave + 2 * i) * 512);
+    dma16_at(from, slot + (16 * lw + 2 * i) * 512);
   };
-  auto dma_a = [&](uint32_t slot, int kst, int i) { dma(pa[i], a_stage, kst, slot, i); };
-  auto dma_b = [&](uint32_t slot, int kst, int i) { dma(pb[i], b_stage, kst, slot, i); };
+  auto dma_a = [&](uint32_t slot, int kst, int i) { dma(pa[i & 1], M, kst, slot, i); };
+  auto dma_b = [&](uint32_t slot, int kst, int i) { dma(pb[i & 1], N, kst, slot, i); };
   auto a_slot = [&](int s) { return ring + static_cast<uint32_t>((s & 1) * kWGStage); };
   auto b_slot = [&](int s) { return ring + static_cast<uint32_t>(kWGBOff + (s % 3) * kWGStage); };
 
-  const int wm = wave >> 1, wn = wave & 1;
+  // wave w computes the 128 x 64 part at rows 128 (w / 4), columns 64 (w % 4): two waves a SIMD
+  const int wm = wave >> 2, wn = wave & 3;
   // transpose-read fragments: lane (gq, jr, qc) reads 8 bytes at row 16 ks + 8 (gq / 2) + jr
   // (and 4 rows on), column 32 block + 16 (gq % 2) + 4 qc
   const int gq = lane >> 4, jr = (lane >> 2) & 3, qc = lane & 3;
@@ -962,8 +970,8 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_gemm_big(WgradArgs a) {
   auto fr_off = [&](int ks, int c) {  // byte offset of (row 16 ks + rowq, column c) in a slot
     return (ks * 16 + rowq) * 512 + ((((c >> 3) ^ (4 * jr))) << 4) + 8 * (qc & 1);
   };
-  u32x4 fa[2][4], fb[2][4];
-  f32x16 acc[4][4];
+  u32x4 fa[2][4], fb[2][2];
+  f32x16 acc[4][2];
   auto read = [&](int s, int ks, int b) {
     const unsigned char* pa = smem + (s & 1) * kWGStage;
     const unsigned char* pb = smem + kWGBOff + (s % 3) * kWGStage;
@@ -975,20 +983,20 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_gemm_big(WgradArgs a) {
                        static_cast<unsigned>(x1), static_cast<unsigned>(x1 >> 32)};
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int o = fr_off(ks, wn * 128 + j * 32 + colq);
+    for (int j = 0; j < 2; ++j) {
+      const int o = fr_off(ks, wn * 64 + j * 32 + colq);
       const unsigned long long x0 = tr_read(pb, o), x1 = tr_read(pb, o + 4 * 512);
       fb[b][j] = u32x4{static_cast<unsigned>(x0), static_cast<unsigned>(x0 >> 32),
                        static_cast<unsigned>(x1), static_cast<unsigned>(x1 >> 32)};
     }
   };
-  // one k-step's 16 MFMAs in four groups; after group i, dmas(i) issues this k-step's share of
+  // one k-step's 8 MFMAs in four groups; after group i, dmas(i) issues this k-step's share of
   // the loads
   auto mma_all = [&](int b, auto dmas) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = wmma<uint16_t>(fb[b][j], fa[b][i], acc[i][j]);
+      for (int j = 0; j < 2; ++j) acc[i][j] = wmma<uint16_t>(fb[b][j], fa[b][i], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
       dmas(i);
       __builtin_amdgcn_sched_barrier(0);
@@ -1005,7 +1013,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_gemm_big(WgradArgs a) {
   // MFMAs. Stage s + 2 is the current tile's or, for its last two stages, the next tile's.
   auto body = [&](int s, int st, bool more_tiles) {
     const bool in_cur = st + 2 < cur.nst;
-    const bool refill = in_cur || more_tiles;
+    const bool refill = (in_cur || more_tiles) && loader;
     const int k2 = in_cur ? st + 2 : st + 2 - cur.nst;
     // the loads switch to the next tile with its first stage
     if (refill && k2 == 0) load_tile(nxt);
@@ -1037,14 +1045,18 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_gemm_big(WgradArgs a) {
 
   // stages 0 and 1 (tile 0), then wait for stage 0
   load_tile(cur);
+  if (loader) {
 #pragma unroll
-  for (int s0 = 0; s0 < 2; ++s0) {
+    for (int s0 = 0; s0 < 2; ++s0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma_a(a_slot(s0), s0, i);
+      for (int i = 0; i < 8; ++i) dma_a(a_slot(s0), s0, i);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma_b(b_slot(s0), s0, i);
+      for (int i = 0; i < 8; ++i) dma_b(b_slot(s0), s0, i);
+    }
+    wg_wait_barrier<16>();
+  } else {
+    wg_wait_barrier<0>();
   }
-  wg_wait_barrier<16>();
   read(0, 0, 0);
 
   int s = 0;
@@ -1052,19 +1064,20 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_gemm_big(WgradArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     const bool more = m + 1 < n_my;
     for (int st = 0; st < cur.nst; ++st, ++s) body(s, st, more);
 
     // ---- epilogue (the next tile's first two stages are in flight). Register 4q + t of
-    // acc[i][j] is C[m = 128 wm + 32 i + l % 32][n = 128 wn + 32 j + 8 q + 4 (l / 32) + t]. Each
-    // wave stages the 32 x 32 piece (i, j) in its own LDS tile (in the B slot of the tile's last
-    // stage, free until the next tile's first refill; chunk c of row r at c ^ (r % 8)), reads
-    // it back as 128-byte rows (instruction p: rows 8p .. 8p+7) and stores them. Step pc stages
-    // piece pc, stores piece pc - 2 and reads back piece pc - 1; a wave's LDS operations
-    // complete in order, so a staging tile is rewritten only after its last read.
+    // acc[i][j] is C[m = 128 wm + 32 i + l % 32][n = 64 wn + 32 j + 8 q + 4 (l / 32) + t]. Each
+    // wave stages the 32 x 32 piece (i, j) in its own 4 KB LDS tile (the eight tiles fill the B
+    // slot of the tile's last stage, free until the next tile's first refill; chunk c of row r
+    // at c ^ (r % 8)), reads it back as 128-byte rows (instruction p: rows 8p .. 8p+7) and
+    // stores them. Step pc stages piece pc, stores piece pc - 1 and reads back piece pc; a
+    // wave's LDS operations complete in order, so piece pc is staged only after piece pc - 1
+    // has been read back.
     const Tile done = cur;
     // the group bounds of the next-but-one tile are requested before the epilogue's stores
     // and used after them, so the wait for them is no wait for the stores (or for the next
@@ -1079,12 +1092,12 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_gemm_big(WgradArgs a) {
     }
     int lq = lane;
     asm volatile("" : "+v"(lq));  // keeps the lane-derived addresses from being hoisted
-    unsigned char* stile = smem + kWGBOff + ((s - 1) % 3) * kWGStage + wave * 2 * kWGPiece;
+    unsigned char* stile = smem + kWGBOff + ((s - 1) % 3) * kWGStage + wave * kWGPiece;
     float* C = a.C + static_cast<int64_t>(done.g) * M * N;
     u32x4 rb[2][4];
     auto stage_piece = [&](int pc) {
-      const int i = pc >> 2, j = pc & 3;
-      unsigned char* t = stile + (pc & 1) * kWGPiece;
+      const int i = pc >> 1, j = pc & 1;
+      unsigned char* t = stile;
       const int row = lq & 31;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -1094,7 +1107,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_gemm_big(WgradArgs a) {
       }
     };
     auto read_piece = [&](int pc) {
-      const unsigned char* t = stile + (pc & 1) * kWGPiece;
+      const unsigned char* t = stile;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const int row = 8 * p + (lq >> 3), ch = lq & 7;
@@ -1102,20 +1115,20 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_gemm_big(WgradArgs a) {
       }
     };
     auto store_piece = [&](int pc) {
-      const int i = pc >> 2, j = pc & 3;
+      const int i = pc >> 1, j = pc & 1;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const int row = 8 * p + (lq >> 3), ch = lq & 7;
         const int mrow = done.m0 + wm * 128 + i * 32 + row;
-        const int ncol = done.n0 + wn * 128 + j * 32 + 4 * ch;
+        const int ncol = done.n0 + wn * 64 + j * 32 + 4 * ch;
         *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(mrow) * N + ncol) = rb[pc & 1][p];
       }
     };
 #pragma unroll
-    for (int pc = 0; pc < 18; ++pc) {
-      if (pc < 16) stage_piece(pc);
-      if (pc >= 2) store_piece(pc - 2);
-      if (pc >= 1 && pc <= 16) read_piece(pc - 1);
+    for (int pc = 0; pc < 9; ++pc) {
+      if (pc < 8) stage_piece(pc);
+      if (pc >= 1) store_piece(pc - 1);
+      if (pc < 8) read_piece(pc);
       __builtin_amdgcn_sched_barrier(0);
     }
     // every wave is done with the staging slot before the next tile's first refill reuses it
@@ -1241,7 +1254,7 @@ moe_status wgrad_launch(const Dims& d, const void* A, const void* B, const int32
     if (!ok) return MOE_ERR_HIP;
     const int cus = wg_device_cus();
     const int grid = std::max(kXcds, cus / kXcds * kXcds);
-    wgrad_gemm_big<<<grid, kThreads, kWGLds, stream>>>(a);
+    wgrad_gemm_big<<<grid, kWGThreads, kWGLds, stream>>>(a);
     return launch_status();
   }
   const int64_t blocks = static_cast<int64_t>(G) * splits * ceil_div(M, kWT) * ceil_div(N, tr ? kTN2 : kWT);
