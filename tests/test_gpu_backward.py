@@ -408,3 +408,81 @@ def test_weight_grad_large_tiles(moe, which, D, H):
         worst = max(worst, err)
         assert err < TOL["f32"], f"expert {e} ({sizes[e]} rows): rel err {err:.2e}"
     log(f"  every expert within {worst:.2e}")
+
+
+def test_ffn_backward_large_ragged(moe):
+    """moe_expert_ffn_backward with every product on the 256 x 256 kernels (bf16, D = H = 1024,
+    64 experts, at least 192 rows an expert on average) on ragged groups: empty experts, 1-row
+    groups, 255 / 256 / 257 rows, a long group. The stored activations hold zeros, negatives,
+    -0.0 and NaN, so the masked epilogue's rule (keep where the activation is > 0) is tested on
+    each kind. Every row of dH = (dZ W2^T) * 1[Hd > 0] and of dXd = dH W1^T, and every expert's
+    dW1 = Xd^T dH and dW2 = Hd^T dZ, against numpy fp64 of the same bf16 values (dXd and dW1 on
+    the GPU's own dH); experts with no rows get zero gradients."""
+    import math
+    import torch
+    rng = np.random.default_rng(59)
+    E, D, H = 64, 1024, 1024
+    sizes = rng.integers(300, 520, E)
+    sizes[[3, 17, 40]] = 0
+    sizes[[5, 33]] = 1
+    sizes[[8, 9, 10]] = (255, 256, 257)
+    sizes[20] = 1100
+    T = int(sizes.sum())
+    w = I.Workload("bwrag", T=T, D=D, E=E, k=1, H=H, act="bf16", gating="noisy", noise=False,
+                   capacity_factor=0.0, seed=0)
+    p = problem_for(moe, w)
+    rows = moe.moe_max_rows(p)
+    assert rows >= 192 * E
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    bf = I.f32_to_bf16_bits
+    Xd = bf(rng.standard_normal((rows, D)).astype(np.float32))
+    h = rng.standard_normal((rows, H)).astype(np.float32)
+    h[h < -0.5] = 0.0          # a ReLU output's exact zeros, beside negatives ...
+    h[(h > 1.5) & (h < 1.6)] = -0.0
+    nan_e = 21                 # ... -0.0, and NaN in one expert's rows (its dW2 is then NaN)
+    blk = h[offs[nan_e]:offs[nan_e + 1]]
+    blk[(blk > 2.0) & (blk < 2.1)] = np.nan
+    Hd = bf(h)
+    dZ = bf(rng.standard_normal((rows, D)).astype(np.float32))
+    W1 = bf((rng.standard_normal((E, D, H)) / math.sqrt(D)).astype(np.float32))
+    W2 = bf((rng.standard_normal((E, H, D)) / math.sqrt(H)).astype(np.float32))
+    W1t = torch.empty(moe.moe_packed_weight_bytes(p, 4), dtype=torch.uint8, device="cuda")
+    W2t = torch.empty(moe.moe_packed_weight_bytes(p, 3), dtype=torch.uint8, device="cuda")
+    moe.moe_pack_expert_weights_t(p, dev(W1), dev(W2), W1t, W2t)
+    dHp = torch.empty(rows, H, dtype=torch.bfloat16, device="cuda")
+    dXd = torch.empty(rows, D, dtype=torch.bfloat16, device="cuda")
+    dW1 = torch.full((E, D, H), float("nan"), device="cuda")  # every element must be written
+    dW2 = torch.full((E, H, D), float("nan"), device="cuda")
+    log(f"[ffn backward large ragged] {T} rows over {E} experts, D {D} H {H}")
+    moe.moe_expert_ffn_backward(p, dev(Xd), dev(Hd), dev(dZ), W1t, W2t, dev(offs), dHp, dXd,
+                                dW1, dW2)
+    dHh, dXh, dW1h, dW2h = (host(t) for t in (dHp, dXd, dW1, dW2))
+    dHf = O.widen(dHh) if dHh.dtype == np.uint16 else dHh.astype(np.float64)
+    dXf = O.widen(dXh) if dXh.dtype == np.uint16 else dXh.astype(np.float64)
+    Xf, Hf, dZf = O.widen(Xd), O.widen(Hd), O.widen(dZ)
+    worst = dict(dH=0.0, dXd=0.0, dW1=0.0, dW2=0.0)
+    for e in range(E):
+        s_ = slice(offs[e], offs[e + 1])
+        if offs[e + 1] == offs[e]:
+            assert (dW1h[e] == 0).all() and (dW2h[e] == 0).all(), f"expert {e} (no rows) not zero"
+            continue
+        W1e, W2e = O.widen(W1[e]), O.widen(W2[e])
+        keep = np.nan_to_num(Hf[s_], nan=0.0) > 0.0
+        refs = dict(dH=(dZf[s_] @ W2e.T) * keep, dXd=dHf[s_] @ W1e.T,
+                    dW1=Xf[s_].T @ dHf[s_], dW2=np.nan_to_num(Hf[s_], nan=0.0).T @ dZf[s_])
+        gots = dict(dH=dHf[s_], dXd=dXf[s_], dW1=dW1h[e], dW2=dW2h[e])
+        for k_, ref in refs.items():
+            if k_ == "dW2" and e == nan_e:
+                # a NaN activation gives NaN in exactly its column of dW2 (row of Hd^T)
+                bad_h = np.isnan(Hf[s_]).any(axis=0)
+                assert bad_h.any() and np.isnan(gots[k_][bad_h]).all()
+                err = np.abs(gots[k_][~bad_h] - ref[~bad_h]).max() / max(np.abs(ref).max(), 1e-30)
+                assert err < TOL["f32"], f"expert {e} dW2 outside the NaN rows: {err:.2e}"
+                continue
+            err = np.abs(gots[k_] - ref).max() / max(np.abs(ref).max(), 1e-30)
+            worst[k_] = max(worst[k_], err)
+            tol = TOL["bf16"] if k_ in ("dH", "dXd") else TOL["f32"]
+            assert err < tol, f"expert {e} ({sizes[e]} rows) {k_}: rel err {err:.2e}"
+        # dH is exactly zero wherever the activation is not > 0 (zero, negative, -0.0, NaN)
+        assert (dHf[s_][~keep] == 0).all(), f"expert {e}: dH not masked"
+    log("  " + ", ".join(f"{k_} {v:.2e}" for k_, v in worst.items()))
