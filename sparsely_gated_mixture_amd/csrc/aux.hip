@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kT) void aux_rows(AuxArgs a) {
     }
   }
 
-  // fixed-order sum over the waves: wave 0 + wave 1 + wave 2 + wave 3
+  // fixed-order sum over the waves: wave 0 + wave 1 + wave 2 + ... in index order
   if (wave > 0)
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
