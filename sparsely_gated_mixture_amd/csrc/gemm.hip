@@ -16,8 +16,13 @@
 //     column blocks is one contiguous run, so a tile's stage of B is one region
 //     rather than 4 KB pieces a whole column block apart; with small groups,
 //     where each block streams an expert's weights once, [e][nb][ks] (one long
-//     run per column block) is faster. A wave then streams its B operand straight
-//     from memory with one coalesced 1 KB load per fragment; B never touches LDS.
+//     run per column block) is faster.
+//   * Two kernels. Large bf16 groups (at least 192 rows an expert on average, or
+//     96 with K >= 2048) run the persistent 256 x 256 kernel of 8 waves further
+//     down, which stages both operands in LDS by direct global-to-LDS loads. The
+//     rest run the BM x 256 kernel described here, in which a wave streams its B
+//     operand straight from memory with one coalesced 1 KB load per fragment (B
+//     never touches LDS).
 //   * A block computes a BM x 256 tile; its 4 waves split the 256 columns
 //     (64 each) and all read the same A rows, which are staged through LDS
 //     (128-byte-wide k stages, double buffered, rows padded against bank
