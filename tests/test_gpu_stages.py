@@ -361,6 +361,52 @@ def test_grouped_gemm_large_ragged(moe, D, H):
     assert e1 < TOL["bf16"] and e2 < TOL["bf16"]
 
 
+def test_grouped_gemm_long_k_half_tiles(moe):
+    """The 256 x 256 kernel where K >= 2048 lets it take groups of 96-191 rows an expert (its
+    row tiles then about half empty): 128 experts of about 130 rows, D = 512, H = 2048, with
+    empty experts, 1-row groups, 255 / 256 / 257 rows and a long group. Layer 2 (K = 2048)
+    runs on that kernel, layer 1 (K = 512) on the 128-row one; both against numpy fp64 on
+    every row (layer 2 on the GPU's own layer-1 output)."""
+    import torch
+    rng = np.random.default_rng(29)
+    E, D, H = 128, 512, 2048
+    sizes = rng.integers(100, 160, E)
+    sizes[[7, 70, 127]] = 0
+    sizes[[11, 90]] = 1
+    sizes[[30, 31, 32]] = (255, 256, 257)
+    sizes[64] = 600
+    T = int(sizes.sum())
+    w = I.Workload("longk", T=T, D=D, E=E, k=1, H=H, act="bf16", gating="noisy", noise=False,
+                   capacity_factor=0.0, seed=0)
+    p = problem_for(moe, w)
+    rows = moe.moe_max_rows(p)
+    assert 96 * E <= rows < 192 * E
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    A = I.f32_to_bf16_bits(rng.standard_normal((rows, D)).astype(np.float32))
+    W1 = I.f32_to_bf16_bits((rng.standard_normal((E, D, H)) / math.sqrt(D)).astype(np.float32))
+    W2 = I.f32_to_bf16_bits((rng.standard_normal((E, H, D)) / math.sqrt(H)).astype(np.float32))
+    W1p = torch.empty(moe.moe_packed_weight_bytes(p, 1), dtype=torch.uint8, device="cuda")
+    W2p = torch.empty(moe.moe_packed_weight_bytes(p, 2), dtype=torch.uint8, device="cuda")
+    moe.moe_pack_expert_weights(p, dev(W1), dev(W2), W1p, W2p)
+    Hd = torch.empty(rows, H, dtype=torch.bfloat16, device="cuda")
+    Z = torch.full((rows, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm(p, 1, dev(A), W1p, dev(offs), Hd)
+    moe.moe_grouped_gemm(p, 2, Hd, W2p, dev(offs), Z)
+    Hh, Zh = f64(host(Hd)), f64(host(Z))
+    e1 = e2 = 0.0
+    for e in range(E):
+        s_ = slice(offs[e], offs[e + 1])
+        if offs[e + 1] == offs[e]:
+            continue
+        r1 = np.maximum(f64(A[s_]) @ f64(W1[e]), 0.0)
+        r2 = Hh[s_] @ f64(W2[e])
+        e1 = max(e1, np.abs(Hh[s_] - r1).max() / max(np.abs(r1).max(), 1e-30))
+        e2 = max(e2, np.abs(Zh[s_] - r2).max() / max(np.abs(r2).max(), 1e-30))
+    assert np.isfinite(Zh[:T]).all(), "a row of Z was not written"
+    log(f"[gemm long K half tiles] {T} rows over {E} experts: layer 1 {e1:.2e}, layer 2 {e2:.2e}")
+    assert e1 < TOL["bf16"] and e2 < TOL["bf16"]
+
+
 def test_grouped_gemm_check_finite_large(moe):
     """The non-finite check of the 256 x 256 kernel (top2_bf16's layer-2 shapes, 512 rows an
     expert): clean rows raise nothing, one NaN in one expert's rows raises MOE_ERR_NONFINITE
